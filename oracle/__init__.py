@@ -1,0 +1,3 @@
+"""CPU oracle (test infrastructure only; see sage_oracle.py's header)."""
+from .sage_oracle import *  # noqa: F401,F403
+from . import sage_oracle  # noqa: F401

@@ -1,0 +1,427 @@
+"""Pins for the CPU oracle: each test checks it against something other than itself.
+
+Sources of truth used here: a library routine (torch's scaled_dot_product_attention
+on CPU in float64), brute-force pure-Python loops, exact rational arithmetic
+(fractions.Fraction), closed forms (O = V for one key, mean(V) for flat scores),
+and the invariance the SageAttention page states in "Approach" (subtracting
+the mean of K across tokens leaves softmax attention unchanged).
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synthetic import make_custom
+
+RNG = np.random.default_rng(1234)
+
+
+def _rand16(*shape, scale=1.0, rng=RNG):
+    return (rng.standard_normal(shape) * scale).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# exact attention (c1)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_matches_torch_sdpa_f64(causal):
+    q, k, v = _rand16(2, 3, 37, 16), _rand16(2, 3, 37, 16, scale=2.0), _rand16(2, 3, 37, 16)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64)), torch.from_numpy(k.astype(np.float64)),
+        torch.from_numpy(v.astype(np.float64)), is_causal=causal, scale=0.3).numpy()
+    got = O.exact_attention(q, k, v, causal=causal, sm_scale=0.3)
+    assert np.max(np.abs(got - ref)) < 1e-13
+
+
+def _brute_attention(q, k, v, causal, scale):
+    N, d = len(q), len(q[0])
+    out = []
+    for i in range(N):
+        s = [scale * sum(q[i][c] * k[j][c] for c in range(d)) if (not causal or j <= i) else None
+             for j in range(N)]
+        mx = max(x for x in s if x is not None)
+        w = [math.exp(x - mx) if x is not None else 0.0 for x in s]
+        tot = sum(w)
+        out.append([sum(w[j] * v[j][c] for j in range(N)) / tot for c in range(d)])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_matches_bruteforce_loops(causal):
+    q, k, v = _rand16(1, 1, 6, 3), _rand16(1, 1, 6, 3), _rand16(1, 1, 6, 3)
+    ref = _brute_attention(q[0, 0].astype(float).tolist(), k[0, 0].astype(float).tolist(),
+                           v[0, 0].astype(float).tolist(), causal, 0.7)
+    got = O.exact_attention(q, k, v, causal=causal, sm_scale=0.7)[0, 0]
+    assert np.max(np.abs(got - ref)) < 1e-14
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_rows_are_probability_distributions(causal):
+    N = 24
+    q, k = _rand16(1, 1, N, N, scale=2.0), _rand16(1, 1, N, N, scale=2.0)
+    eye = np.eye(N)[None, None]                       # V = I makes O equal to P
+    P = O.exact_attention(q, k, eye, causal=causal, sm_scale=0.5)[0, 0]
+    assert np.all(P >= 0)
+    assert np.max(np.abs(P.sum(axis=1) - 1.0)) < 1e-13
+    if causal:
+        assert np.all(P[np.triu_indices(N, 1)] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mean_smoothing_leaves_exact_attention_unchanged(causal):
+    # "Approach": subtracting the mean of K across tokens leaves softmax attention unchanged.
+    # Any per-channel shift shared by all tokens adds q.mu to a whole score row.
+    q, k, v = _rand16(1, 2, 40, 32), _rand16(1, 2, 40, 32), _rand16(1, 2, 40, 32)
+    mu = RNG.standard_normal((1, 2, 1, 32)) * 3.0
+    a = O.exact_attention(q, k.astype(np.float64), v, causal=causal, sm_scale=0.2)
+    b = O.exact_attention(q, k.astype(np.float64) - mu, v, causal=causal, sm_scale=0.2)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_exact_special_cases():
+    v = _rand16(1, 1, 9, 4)
+    # one key: O = V
+    one = O.exact_attention(_rand16(1, 1, 1, 4), _rand16(1, 1, 1, 4), v[:, :, :1], causal=False, sm_scale=1.0)
+    assert np.array_equal(one, v[:, :, :1].astype(np.float64))
+    # Q = 0: flat scores, O = mean(V); causal: prefix means
+    z = np.zeros((1, 1, 9, 4), np.float16)
+    k = _rand16(1, 1, 9, 4)
+    flat = O.exact_attention(z, k, v, causal=False, sm_scale=1.0)[0, 0]
+    assert np.max(np.abs(flat - v[0, 0].astype(float).mean(axis=0))) < 1e-15
+    pref = O.exact_attention(z, k, v, causal=True, sm_scale=1.0)[0, 0]
+    cm = np.cumsum(v[0, 0].astype(float), axis=0) / np.arange(1, 10)[:, None]
+    assert np.max(np.abs(pref - cm)) < 1e-15
+    # causal row 0 sees only key 0
+    c = O.exact_attention(_rand16(1, 1, 9, 4), k, v, causal=True, sm_scale=1.0)
+    assert np.array_equal(c[0, 0, 0], v[0, 0, 0].astype(np.float64))
+    # one dominant score: O ~= V_j
+    q1 = np.zeros((1, 1, 1, 4), np.float16); q1[..., 0] = 100
+    k1 = np.zeros((1, 1, 9, 4), np.float16); k1[0, 0, 5, 0] = 100
+    dom = O.exact_attention(q1, k1, v, causal=False, sm_scale=1.0)[0, 0, 0]
+    assert np.max(np.abs(dom - v[0, 0, 5].astype(float))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# K mean (reading R1) against exact rational arithmetic
+# ---------------------------------------------------------------------------
+
+def test_k_mean_matches_exact_rational_mean():
+    k = _rand16(2, 2, 77, 8, scale=3.0)
+    k[0, 0, :5, 0] = np.float16(6.0e-8)        # fp16 subnormals take part too
+    k[1, 1, :, 3] = np.float16(-65504.0)       # largest magnitude
+    mu = O.k_mean(k)
+    for b in range(2):
+        for h in range(2):
+            for c in range(8):
+                s = sum(Fraction(float(x)) for x in k[b, h, :, c])
+                want = np.float32(float(s / 77))   # Fraction -> float is correctly rounded
+                assert mu[b, h, c] == want
+
+
+def test_k_channel_sum_is_integer_exact():
+    k = _rand16(1, 1, 300, 4, scale=100.0)
+    tot = O.k_channel_sum(k)
+    for c in range(4):
+        exact = sum(Fraction(float(x)) for x in k[0, 0, :, c]) * 2 ** 24
+        assert exact.denominator == 1 and tot[0, 0, c] == exact.numerator
+
+
+# ---------------------------------------------------------------------------
+# INT8 quantization (readings R3, R4) against exact rationals and brute force
+# ---------------------------------------------------------------------------
+
+def _f32_round(fr: Fraction) -> Fraction:
+    """Round a rational to the nearest float32 (ties to even), normal range only."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    scaled = a / Fraction(2) ** (e - 23)               # in [2^23, 2^24)
+    m = scaled.numerator // scaled.denominator
+    rem = scaled - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    return sign * Fraction(m) * Fraction(2) ** (e - 23)
+
+
+def _round_half_even(fr: Fraction) -> int:
+    f = math.floor(fr)
+    rem = fr - f
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and f % 2 == 1):
+        return f + 1
+    return f
+
+
+@pytest.mark.parametrize("blk,N", [(64, 64), (64, 70), (1, 5), (128, 200)])
+def test_int8_codes_and_scales_exact(blk, N):
+    x = (RNG.standard_normal((1, 2, N, 8)) * 2.5).astype(np.float32)
+    codes, scales = O.int8_quant_blocks(x, blk)
+    assert scales.shape == (1, 2, -(-N // blk))
+    for h in range(2):
+        for bi in range(scales.shape[2]):
+            blkx = x[0, h, bi * blk:(bi + 1) * blk]
+            a = Fraction(float(np.abs(blkx).max()))
+            s = _f32_round(a / 127)
+            assert Fraction(float(scales[0, h, bi])) == s
+            for (r, c), xv in np.ndenumerate(blkx):
+                want = _round_half_even(_f32_round(Fraction(float(xv)) / s))
+                got = int(codes[0, h, bi * blk + r, c])
+                assert got == want
+                # near-optimal among all 255 codes: within half a step (+ one fp32 rounding)
+                assert abs(Fraction(got) - Fraction(float(xv)) / s) <= Fraction(1, 2) + Fraction(1, 2 ** 16)
+            # the block maximum lands on +-127
+            i = np.unravel_index(np.argmax(np.abs(blkx)), blkx.shape)
+            assert abs(int(codes[0, h, bi * blk + i[0], i[1]])) == 127
+    assert codes.min() >= -127
+
+
+def test_int8_exact_ties_round_to_even():
+    # block max 127 gives scale exactly 1, so x / s lands exactly on half-integers
+    x = np.zeros((1, 1, 1, 8), np.float32)
+    x[0, 0, 0] = [127.0, 0.5, 1.5, 2.5, -2.5, 126.5, -0.5, 3.5]
+    codes, scales = O.int8_quant_blocks(x, 1)
+    assert scales[0, 0, 0] == 1.0
+    assert codes[0, 0, 0].tolist() == [127, 0, 2, 2, -2, 126, 0, 4]
+
+
+def test_int8_zero_block():
+    x = np.zeros((1, 1, 64, 8), np.float32)
+    x[0, 0, 40:] = 1.0
+    codes, scales = O.int8_quant_blocks(x, 32)
+    assert scales[0, 0, 0] == 0 and np.all(codes[0, 0, :32] == 0)
+    assert np.all(codes[0, 0, 40:] == 127)
+
+
+def test_dequantized_scores_within_quantization_bound():
+    # Catches transposed operands and wrong scale indexing: |S_deq - S_exact| is bounded by
+    # the per-element code errors (|x - c*s| <= s/2 up to one fp32 rounding).
+    q, k, _ = make_custom(1, 1, 150, 32, seed=7)
+    d = O.quant_qk_int8(q, k, blk_q=64, blk_k=32)
+    ks = O.smooth_k(k, d["k_mean"]).astype(np.float64)[0, 0]
+    qf = q.astype(np.float64)[0, 0]
+    sq = d["q_scales"][0, 0][np.arange(150) // 64].astype(np.float64)
+    sk = d["k_scales"][0, 0][np.arange(150) // 32].astype(np.float64)
+    S_deq = (d["q_codes"][0, 0].astype(np.float64) @ d["k_codes"][0, 0].astype(np.float64).T) * sq[:, None] * sk[None, :]
+    S_ex = qf @ ks.T
+    bound = (np.abs(qf) @ np.ones((32, 150))) * sk[None, :] / 2 + (np.ones((150, 32)) @ np.abs(ks).T) * sq[:, None] / 2 \
+        + 32 * sq[:, None] * sk[None, :] / 4
+    assert np.all(np.abs(S_deq - S_ex) <= bound * (1 + 1e-5))
+
+
+# ---------------------------------------------------------------------------
+# INT8 attention emulation (c2)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_emulation_without_quantization_is_exact_attention(causal):
+    q, k, v = make_custom(1, 2, 150, 32, seed=3)
+    ex = O.exact_attention(q, k, v, causal=causal, sm_scale=0.25)
+    got = O.int8_attention(q, k, v, causal=causal, sm_scale=0.25, blk_q=64, blk_k=64,
+                           quantize=False, smooth=False)
+    assert np.max(np.abs(got - ex)) < 1e-12
+    # with smoothing on and no quantization: exact attention on the fp32 smoothed K
+    ks = O.smooth_k(k, O.k_mean(k)).astype(np.float64)
+    ex_s = O.exact_attention(q, ks, v, causal=causal, sm_scale=0.25)
+    got_s = O.int8_attention(q, k, v, causal=causal, sm_scale=0.25, blk_q=64, blk_k=64, quantize=False)
+    assert np.max(np.abs(got_s - ex_s)) < 1e-12
+
+
+def test_int8_emulation_tiling_changes_only_fp16_rounding():
+    q, k, v = make_custom(1, 1, 256, 64, seed=4)
+    a = O.int8_attention(q, k, v, causal=False, sm_scale=0.125, blk_q=64, blk_k=64, kv_tile=64)
+    b = O.int8_attention(q, k, v, causal=False, sm_scale=0.125, blk_q=64, blk_k=64, kv_tile=256)
+    assert np.max(np.abs(a - b)) < 2 ** -10 * np.abs(v.astype(float)).max()
+
+
+def test_int8_emulation_constant_v():
+    q, k, _ = make_custom(1, 1, 200, 32, seed=5)
+    v = np.full((1, 1, 200, 32), 1.5, np.float16)
+    o = O.int8_attention(q, k, v, causal=True, sm_scale=0.2, blk_q=64, blk_k=64)
+    assert np.max(np.abs(o - 1.5)) <= 1.5 * 2 ** -10
+
+
+def test_int8_rows_subset_matches_full():
+    q, k, v = make_custom(1, 2, 300, 32, seed=6)
+    full = O.int8_attention(q, k, v, causal=True, sm_scale=0.2, blk_q=128, blk_k=64)
+    rows = np.array([0, 5, 127, 128, 299])
+    sub = O.int8_attention(q, k, v, causal=True, sm_scale=0.2, blk_q=128, blk_k=64, rows=rows)
+    assert np.array_equal(sub, full[:, :, rows])
+
+
+def test_int8_method_accuracy_tiny_workload():
+    # "Approach": the method's bar is cosine similarity above 99.8% against full precision.
+    q, k, v = make_custom(1, 2, 256, 64, seed=0)
+    ex = O.exact_attention(q, k, v, causal=False, sm_scale=0.125)
+    em = O.int8_attention(q, k, v, causal=False, sm_scale=0.125, blk_q=64, blk_k=64)
+    assert O.metrics(em, ex)["cos"] > 0.998
+
+
+def test_smoothing_helps_with_large_k_offsets():
+    # "Measured effects": smoothing K raises accuracy under INT8 quantization.
+    q, k, v = make_custom(1, 2, 512, 64, seed=8, k_offset_std=20.0)
+    ex = O.exact_attention(q, k, v, causal=False, sm_scale=0.125)
+    on = O.metrics(O.int8_attention(q, k, v, causal=False, sm_scale=0.125, blk_q=64, blk_k=64), ex)["cos"]
+    off = O.metrics(O.int8_attention(q, k, v, causal=False, sm_scale=0.125, blk_q=64, blk_k=64, smooth=False), ex)["cos"]
+    assert on > off
+
+
+# ---------------------------------------------------------------------------
+# MX codecs (reading R8)
+# ---------------------------------------------------------------------------
+
+def _e2m1_from_bits(code: int) -> float:
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = (m / 2.0) if e == 0 else 2.0 ** (e - 1) * (1 + m / 2.0)
+    return -mag if s else mag
+
+
+def test_e2m1_table_matches_bit_field_definition():
+    for code in range(8):
+        assert O.E2M1_MAGNITUDES[code] == _e2m1_from_bits(code)
+        assert -O.E2M1_MAGNITUDES[code] == _e2m1_from_bits(code | 8)
+
+
+def test_e2m1_nearest_is_nearest_with_even_ties():
+    ys = np.concatenate([np.arange(0, 8.5, 1 / 64), [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 100.0]])
+    idx = O.e2m1_nearest(ys)
+    grid = [abs(_e2m1_from_bits(c)) for c in range(8)]
+    for y, i in zip(ys.tolist(), idx.tolist()):
+        dists = [abs(y - g) for g in grid]
+        best = min(dists)
+        assert dists[i] == best
+        ties = [c for c in range(8) if dists[c] == best]
+        if len(ties) > 1:
+            assert i % 2 == 0 and i in ties
+
+
+def _floor_log2(x: float) -> int:
+    n, d = Fraction(x).as_integer_ratio()
+    e = n.bit_length() - d.bit_length()
+    return e if Fraction(2) ** e <= Fraction(n, d) else e - 1
+
+
+def test_e8m0_exponent_rule():
+    vals = [1.0, 2.0, 3.99, 4.0, 6.0, 7.9, 0.3, 1e-3, 1e-40, 2.0 ** -126, 3.0e38, 65504.0, 5.9e-8]
+    e = O.e8m0_exponent(np.array(vals))
+    for x, ei in zip(vals, e.tolist()):
+        assert ei == max(-127, min(127, _floor_log2(x) - 2))
+    assert O.e8m0_exponent(np.array([0.0]))[0] == 0
+
+
+def test_mx_roundtrip_of_representable_blocks_and_error_bound():
+    rng = np.random.default_rng(11)
+    mags = rng.integers(0, 8, size=(4, 64))
+    sign = rng.integers(0, 2, size=(4, 64))
+    mags[:, 0] = 7; mags[:, 32] = 6                # block maxima 6 and 4 set the exponent
+    exps = np.array([0, -3, 5, -10])
+    x = (np.where(sign, -1, 1) * O.E2M1_MAGNITUDES[mags] * np.exp2(exps)[:, None]).astype(np.float32)
+    codes, e8, vals = O.mx_quantize(x, axis=1)
+    assert np.array_equal(vals, x.astype(np.float64))
+    assert np.array_equal(e8[:, 0], (exps + 127).astype(np.uint8))
+    # random data: error at most half a grid step, or the saturation gap above 6 * 2^e
+    y = rng.standard_normal((8, 96)).astype(np.float32) * 3
+    codes, e8, vals = O.mx_quantize(y, axis=1)
+    e = e8.astype(np.int64) - 127
+    step = np.repeat(np.exp2(e), 32, axis=1)
+    err = np.abs(vals - y)
+    assert np.all(err <= np.maximum(np.where(np.abs(y) < 2 * step, 0.25, np.where(np.abs(y) < 4 * step, 0.5, 1.0)) * step,
+                                    (np.abs(y) - 6 * step)))
+
+
+def test_mx_sign_bit_follows_the_sign_of_x():
+    x = np.array([[4.0, -0.0, -1e-3, 1e-3] + [0.0] * 28], np.float32)
+    codes, _, _ = O.mx_quantize(x, axis=1)
+    assert codes[0, :4].tolist() == [6, 8, 8, 0]
+
+
+def test_mx_v_blocks_run_along_tokens():
+    v = np.ones((1, 1, 64, 64), np.float16)
+    v[0, 0, 3, 5] = 64.0
+    d = O.quant_mxfp4(v, v, v)
+    vv = d["v_vals"][0, 0]
+    assert vv[0, 5] == 0.0 and vv[40, 5] == 1.0      # same channel: shares the big value's exponent below token 32
+    assert vv[3, 6] == 1.0 and vv[3, 5] == 64.0      # other channels of that token are untouched
+    assert d["v_e8m0"].shape == (1, 1, 2, 64)
+
+
+def test_pack_fp4_low_nibble_first():
+    c = np.array([[1, 2, 15, 0, 8, 7]], np.uint8)
+    assert O.pack_fp4(c).tolist() == [[0x21, 0x0F, 0x78]]
+
+
+def test_mxfp4_emulation_exact_on_representable_inputs():
+    # Q, V exactly representable in MXFP4, K with an exactly zero token mean (pairs +x, -x)
+    # so that smoothing is the identity: without P quantization the emulation must equal
+    # exact attention; with it, stay within P's quantization error.
+    rng = np.random.default_rng(12)
+    N, d = 64, 64
+
+    def grid(shape, axis_len_block):
+        m = rng.integers(0, 7, size=shape)
+        s = rng.integers(0, 2, size=shape)
+        return np.where(s, -1, 1) * O.E2M1_MAGNITUDES[m] * 0.25
+
+    q = grid((1, 1, N, d), 32); q[..., ::32] = 1.5   # block max 1.5 -> exponent -2 keeps values exact
+    half = grid((1, 1, N // 2, d), 32); half[..., ::32] = 1.5
+    k = np.concatenate([half, -half], axis=2)
+    v = grid((1, 1, N, d), 32); v[:, :, ::32, :] = 1.5
+    q, k, v = q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
+    assert np.all(O.k_mean(k) == 0)
+    ex = O.exact_attention(q, k, v, causal=False, sm_scale=0.3)
+    got = O.mxfp4_attention(q, k, v, causal=False, sm_scale=0.3, quantize_p=False)
+    assert np.max(np.abs(got - ex)) < 1e-12
+    gotp = O.mxfp4_attention(q, k, v, causal=False, sm_scale=0.3)
+    assert np.max(np.abs(gotp - ex)) < 0.25 * np.abs(v.astype(float)).max()
+
+
+def test_metrics_definitions():
+    a = np.array([1.0, 2.0, -3.0])
+    m = O.metrics(a, a)
+    assert abs(m["cos"] - 1) < 1e-15 and m["max_abs"] == 0 and m["rmse"] == 0
+    m = O.metrics(-a, a)
+    assert abs(m["cos"] + 1) < 1e-15 and m["rel_l1"] == 2.0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_emulation_equals_exact_attention_on_dequantized_operands(causal):
+    # The only rounding left after dequantization is P -> fp16 (2^-11 relative per weight).
+    q, k, v = make_custom(1, 2, 200, 32, seed=13)
+    d = O.quant_qk_int8(q, k, blk_q=128, blk_k=32)
+    idx = np.arange(200)
+    qh = d["q_codes"].astype(np.float64) * d["q_scales"][:, :, idx // 128, None]
+    kh = d["k_codes"].astype(np.float64) * d["k_scales"][:, :, idx // 32, None]
+    ex = O.exact_attention(qh, kh, v, causal=causal, sm_scale=0.3)
+    got = O.int8_attention(q, k, v, causal=causal, sm_scale=0.3, blk_q=128, blk_k=32)
+    vmax = np.abs(v.astype(float)).max()
+    assert np.max(np.abs(got - ex)) < 2 ** -10 * vmax
+    assert np.max(np.abs(got - ex)) > 1e-6       # the fp16 rounding of P is really applied
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mxfp4_emulation_equals_exact_attention_on_decoded_operands(causal):
+    q, k, v = make_custom(1, 2, 160, 64, seed=14)
+    d = O.quant_mxfp4(q, k, v)
+    ex = O.exact_attention(d["q_vals"], d["k_vals"], d["v_vals"], causal=causal, sm_scale=0.125)
+    got = O.mxfp4_attention(q, k, v, causal=causal, sm_scale=0.125, quantize_p=False)
+    assert np.max(np.abs(got - ex)) < 1e-12
+    gotp = O.mxfp4_attention(q, k, v, causal=causal, sm_scale=0.125)
+    assert 0 < np.max(np.abs(gotp - ex)) < 0.5
+
+
+def test_oracle_regression_fixture():
+    # tests/golden/tiny_oracle.json was written by tests/golden/make_golden.py (oracle only).
+    import json, os, importlib.util
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    spec = importlib.util.spec_from_file_location("make_golden", os.path.join(here, "make_golden.py"))
+    mg = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mg)
+    with open(os.path.join(here, "tiny_oracle.json")) as f:
+        stored = json.load(f)
+    assert mg.build() == stored

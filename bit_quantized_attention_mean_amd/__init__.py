@@ -1,0 +1,226 @@
+"""Python binding of libsage_attn.so, the gfx950 quantized-attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/sage_attn.h). PyTorch supplies device memory
+(tensors, the workspace) and the current HIP stream. If the library is not
+built, importing this package raises ImportError; there is no fallback path.
+
+Functions carry the C names:
+  sage_attn_fwd(q, k, v, ...)          -> out
+  sage_attn_prepare / sage_attn_compute  (the two phases of sage_attn_fwd)
+  sage_attn_workspace_size(B, H, N, d, mode)
+  sage_quant_qk(q, k, blk_q, blk_k, flags)  -> dict of codes/scales/mean
+  sage_quant_mxfp4(q, k, v, flags)         -> dict of packed codes/exponents
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "SAGE_MODE_INT8_Q128_K64", "SAGE_MODE_INT8_Q64_K64", "SAGE_MODE_MXFP4", "SAGE_MODE_INT8_PER_TOKEN",
+    "SAGE_FLAG_NO_SMOOTH", "SageError", "LIB_PATH", "lib",
+    "sage_attn_fwd", "sage_attn_prepare", "sage_attn_compute", "sage_attn_workspace_size",
+    "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_status_string", "sage_last_error",
+    "EXPORTED_SYMBOLS",
+]
+
+SAGE_MODE_INT8_Q128_K64 = 0
+SAGE_MODE_INT8_Q64_K64 = 1
+SAGE_MODE_MXFP4 = 2
+SAGE_MODE_INT8_PER_TOKEN = 3
+SAGE_FLAG_NO_SMOOTH = 0x100
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_attn.so")
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "sage_status_string": (ctypes.c_char_p, [_i]),
+    "sage_last_error": (ctypes.c_char_p, []),
+    "sage_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "sage_quant_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "sage_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "sage_attn_prepare": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "sage_attn_compute": (_i, [_vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "sage_quant_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sage_quant_mxfp4": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+
+def _load():
+    # PyTorch ships its own HIP runtime (libamdhip64.so, SONAME libamdhip64.so.7).
+    # Loading torch first makes the library bind to that same runtime by SONAME,
+    # so torch's streams and allocations are valid handles for it; loading the
+    # library first would bring in a second runtime from /opt/rocm.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_quantized_attention_mean_amd.build`")
+    so = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(so, name)
+        fn.restype = res
+        fn.argtypes = args
+    return so
+
+
+lib = _load()
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sage_status_string(status)}: {sage_last_error()}")
+
+
+def sage_status_string(status: int) -> str:
+    return lib.sage_status_string(status).decode()
+
+
+def sage_last_error() -> str:
+    return lib.sage_last_error().decode()
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise SageError(rc, where)
+
+
+def sage_attn_workspace_size(B: int, H: int, N: int, d: int, mode: int = 0) -> int:
+    return int(lib.sage_attn_workspace_size(B, H, N, d, mode))
+
+
+def sage_quant_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(lib.sage_quant_workspace_size(B, H, N, d))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _shape4(q):
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    return tuple(int(x) for x in q.shape)
+
+
+def make_workspace(B, H, N, d, mode=0, device=None):
+    """A device workspace tensor (uint8) large enough for sage_attn_fwd."""
+    torch = _torch()
+    n = sage_attn_workspace_size(B, H, N, d, mode)
+    if n == 0:
+        raise ValueError("invalid problem size or mode")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def sage_attn_fwd(q, k, v, out=None, *, causal=False, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64,
+                  workspace=None, stream=None):
+    """out[B,H,N,d] fp16 = quantized attention of fp16 q, k, v [B,H,N,d]."""
+    torch = _torch()
+    B, H, N, d = _shape4(q)
+    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
+        raise ValueError("q, k, v must have the same shape")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = make_workspace(B, H, N, d, mode, q.device)
+    rc = lib.sage_attn_fwd(_dev_ptr(q, "q", torch.float16), _dev_ptr(k, "k", torch.float16),
+                           _dev_ptr(v, "v", torch.float16), _dev_ptr(out, "out", torch.float16),
+                           B, H, N, d, int(bool(causal)), float(sm_scale), int(mode),
+                           _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                           _stream(stream))
+    _check(rc, "sage_attn_fwd")
+    return out
+
+
+def sage_attn_prepare(q, k, v, workspace, *, mode=SAGE_MODE_INT8_Q128_K64, stream=None):
+    torch = _torch()
+    B, H, N, d = _shape4(q)
+    rc = lib.sage_attn_prepare(_dev_ptr(q, "q", torch.float16), _dev_ptr(k, "k", torch.float16),
+                               _dev_ptr(v, "v", torch.float16), B, H, N, d, int(mode),
+                               _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    _check(rc, "sage_attn_prepare")
+
+
+def sage_attn_compute(out, workspace, *, causal=False, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64, stream=None):
+    torch = _torch()
+    B, H, N, d = _shape4(out)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    rc = lib.sage_attn_compute(_dev_ptr(out, "out", torch.float16), B, H, N, d, int(bool(causal)),
+                               float(sm_scale), int(mode), _dev_ptr(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "sage_attn_compute")
+    return out
+
+
+def sage_quant_qk(q, k, *, blk_q=128, blk_k=64, flags=0, stream=None):
+    """INT8 codes and scales of Q and the mean-smoothed K (plus the K mean)."""
+    torch = _torch()
+    B, H, N, d = _shape4(q)
+    dev = q.device
+    res = {
+        "q_codes": torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+        "k_codes": torch.empty((B, H, N, d), dtype=torch.int8, device=dev),
+        "q_scales": torch.empty((B, H, -(-N // blk_q)), dtype=torch.float32, device=dev),
+        "k_scales": torch.empty((B, H, -(-N // blk_k)), dtype=torch.float32, device=dev),
+        "k_mean": torch.empty((B, H, d), dtype=torch.float32, device=dev),
+    }
+    ws = torch.empty(max(1, sage_quant_workspace_size(B, H, N, d)), dtype=torch.uint8, device=dev)
+    rc = lib.sage_quant_qk(_dev_ptr(q, "q", torch.float16), _dev_ptr(k, "k", torch.float16), B, H, N, d,
+                           int(blk_q), int(blk_k), int(flags),
+                           _dev_ptr(res["q_codes"], "q_codes"), _dev_ptr(res["q_scales"], "q_scales"),
+                           _dev_ptr(res["k_codes"], "k_codes"), _dev_ptr(res["k_scales"], "k_scales"),
+                           _dev_ptr(res["k_mean"], "k_mean"), _dev_ptr(ws, "workspace"), ws.numel(),
+                           _stream(stream))
+    _check(rc, "sage_quant_qk")
+    return res
+
+
+def sage_quant_mxfp4(q, k, v, *, flags=0, stream=None):
+    """MXFP4 codes (packed, low nibble first) and E8M0 exponents of Q, K_s and V^T."""
+    torch = _torch()
+    B, H, N, d = _shape4(q)
+    dev = q.device
+    Nv = -(-N // 32) * 32
+    u8 = torch.uint8
+    res = {
+        "q_fp4": torch.empty((B, H, N, d // 2), dtype=u8, device=dev),
+        "q_e8m0": torch.empty((B, H, N, d // 32), dtype=u8, device=dev),
+        "k_fp4": torch.empty((B, H, N, d // 2), dtype=u8, device=dev),
+        "k_e8m0": torch.empty((B, H, N, d // 32), dtype=u8, device=dev),
+        "vt_fp4": torch.empty((B, H, d, Nv // 2), dtype=u8, device=dev),
+        "vt_e8m0": torch.empty((B, H, d, Nv // 32), dtype=u8, device=dev),
+        "k_mean": torch.empty((B, H, d), dtype=torch.float32, device=dev),
+    }
+    ws = torch.empty(max(1, sage_quant_workspace_size(B, H, N, d)), dtype=u8, device=dev)
+    rc = lib.sage_quant_mxfp4(_dev_ptr(q, "q", torch.float16), _dev_ptr(k, "k", torch.float16),
+                              _dev_ptr(v, "v", torch.float16), B, H, N, d, int(flags),
+                              *(_dev_ptr(res[n], n) for n in ("q_fp4", "q_e8m0", "k_fp4", "k_e8m0", "vt_fp4", "vt_e8m0")),
+                              _dev_ptr(res["k_mean"], "k_mean"), _dev_ptr(ws, "workspace"), ws.numel(),
+                              _stream(stream))
+    _check(rc, "sage_quant_mxfp4")
+    return res

@@ -1,0 +1,312 @@
+// C ABI of the quantized-attention library (declared in include/sage_attn.h):
+// argument validation, workspace sizing, device check and kernel dispatch.
+// Every argument is validated before the first HIP runtime call, so argument
+// errors are reported identically on hosts without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "sage_attn.h"
+#include "sage_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr int kMaxN = 1 << 22;
+
+int check_dims(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return fail(SAGE_ERR_INVALID_ARG, "B, H and N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if (N > kMaxN) return fail(SAGE_ERR_INVALID_ARG, "N = %d exceeds the supported maximum %d", N, kMaxN);
+  if (d != 64 && d != 128) return fail(SAGE_ERR_UNSUPPORTED, "head dim d = %d is not supported (64 or 128)", d);
+  const long long bh = static_cast<long long>(B) * H;
+  if (bh > (1LL << 24)) return fail(SAGE_ERR_INVALID_ARG, "B*H = %lld is too large", bh);
+  // the largest grid is B*H*Npad/128 workgroups and the largest tensor B*H*Npad*d bytes*2
+  const long long rows = bh * sage::round_up(N, sage::kRowPad);
+  if (rows / sage::kQTile > 0x7fffffffLL || rows > (1LL << 40) / d)
+    return fail(SAGE_ERR_INVALID_ARG, "problem too large (B*H*N = %lld)", bh * N);
+  return SAGE_OK;
+}
+
+int check_ptr(const void* p, const char* name, size_t align) {
+  if (!p) return fail(SAGE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % align) return fail(SAGE_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return SAGE_OK;
+}
+
+int check_mode(int mode, bool attention) {
+  if (mode & ~(SAGE_MODE_MASK | SAGE_FLAG_NO_SMOOTH)) return fail(SAGE_ERR_UNSUPPORTED, "unknown flag bits in mode 0x%x", mode);
+  const int lo = mode & SAGE_MODE_MASK;
+  if (lo > SAGE_MODE_INT8_PER_TOKEN) return fail(SAGE_ERR_UNSUPPORTED, "unknown mode %d", lo);
+  (void)attention;
+  return SAGE_OK;
+}
+
+// Device check: a HIP device must be current and be gfx950. Cached per device.
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = -1;
+  int count = 0;
+  const hipError_t ce = hipGetDeviceCount(&count);
+  if (ce != hipSuccess || count < 1) {
+    (void)hipGetLastError();
+    return fail(SAGE_ERR_NO_DEVICE, "no HIP device is visible (hipGetDeviceCount: %s, count %d)",
+                hipGetErrorString(ce), count);
+  }
+  const hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(SAGE_ERR_NO_DEVICE, "no current HIP device (hipGetDevice: %s)", hipGetErrorString(de));
+  }
+  if (dev < 64) {
+    const int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (st == 1) return SAGE_OK;
+    if (st == 2) return fail(SAGE_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SAGE_ERR_HIP, "hipGetDeviceProperties failed on device %d", dev);
+  }
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  if (!ok) return fail(SAGE_ERR_UNSUPPORTED, "device %d is %s, the kernels are built for gfx950", dev, prop.gcnArchName);
+  return SAGE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SAGE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return SAGE_OK;
+}
+
+#define SAGE_TRY(expr)              \
+  do {                              \
+    const int rc_ = (expr);         \
+    if (rc_ != SAGE_OK) return rc_; \
+  } while (0)
+
+unsigned char* at(void* base, size_t off) { return static_cast<unsigned char*>(base) + off; }
+const unsigned char* at(const void* base, size_t off) { return static_cast<const unsigned char*>(base) + off; }
+
+int validate_attn(int B, int H, int N, int d, int mode, const void* ws, size_t ws_bytes) {
+  SAGE_TRY(check_dims(B, H, N, d));
+  SAGE_TRY(check_mode(mode, true));
+  SAGE_TRY(check_ptr(ws, "workspace", 256));
+  const sage::Layout L = sage::make_layout(static_cast<long long>(B) * H, N, d, mode & SAGE_MODE_MASK, true);
+  if (ws_bytes < L.total)
+    return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, L.total);
+  return SAGE_OK;
+}
+
+int check_scale(float sm_scale) {
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  return SAGE_OK;
+}
+
+int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d, int mode,
+               void* ws, hipStream_t s) {
+  const int BH = B * H;
+  const int lo = mode & SAGE_MODE_MASK;
+  const bool smooth = !(mode & SAGE_FLAG_NO_SMOOTH);
+  const sage::Layout L = sage::make_layout(BH, N, d, lo, true);
+  (void)hipGetLastError();
+  float* mu = reinterpret_cast<float*>(at(ws, L.kmean));
+  if (smooth)
+    SAGE_TRY(hip_status(sage::launch_kmean(k, reinterpret_cast<long long*>(at(ws, L.ksum)), mu, nullptr, BH, N, d,
+                                           L.chunk, L.nchunk, s), "K mean kernels"));
+  if (lo == SAGE_MODE_MXFP4) {
+    sage::MxRowJob jq, jk;
+    jq.src = q; jq.fp4 = at(ws, L.q_fp4); jq.e8 = at(ws, L.q_e8); jq.mu = nullptr; jq.rows = L.Npad;
+    jk.src = k; jk.fp4 = at(ws, L.k_fp4); jk.e8 = at(ws, L.k_e8); jk.mu = smooth ? mu : nullptr; jk.rows = L.Npad;
+    SAGE_TRY(hip_status(sage::launch_mx_rows(jq, jk, BH, N, d, s), "MXFP4 Q/K quantization kernel"));
+    SAGE_TRY(hip_status(sage::launch_mx_vt(v, at(ws, L.vt_fp4), at(ws, L.vt_e8), BH, N, L.Npad, d, s),
+                        "MXFP4 V quantization kernel"));
+    return SAGE_OK;
+  }
+  const int blk_q = lo == SAGE_MODE_INT8_Q128_K64 ? 128 : (lo == SAGE_MODE_INT8_Q64_K64 ? 64 : 1);
+  const int blk_k = lo == SAGE_MODE_INT8_PER_TOKEN ? 1 : 64;
+  sage::Int8Job jq, jk;
+  jq.src = q; jq.codes = reinterpret_cast<int8_t*>(at(ws, L.q_codes)); jq.scales = reinterpret_cast<float*>(at(ws, L.q_scales));
+  jq.mu = nullptr; jq.blk = blk_q; jq.code_rows = L.Npad; jq.nscale = L.Npad / blk_q; jq.ntile = L.Npad / sage::kQTile;
+  jk.src = k; jk.codes = reinterpret_cast<int8_t*>(at(ws, L.k_codes)); jk.scales = reinterpret_cast<float*>(at(ws, L.k_scales));
+  jk.mu = smooth ? mu : nullptr; jk.blk = blk_k; jk.code_rows = L.Npad; jk.nscale = L.Npad / blk_k; jk.ntile = L.Npad / sage::kQTile;
+  SAGE_TRY(hip_status(sage::launch_int8_quant(jq, jk, BH, N, d, s), "INT8 quantization kernel"));
+  SAGE_TRY(hip_status(sage::launch_v_transpose(v, at(ws, L.vt), BH, N, L.Npad, d, s), "V transpose kernel"));
+  return SAGE_OK;
+}
+
+int do_compute(void* out, int B, int H, int N, int d, int causal, float sm_scale, int mode, const void* ws,
+               hipStream_t s) {
+  const int BH = B * H;
+  const int lo = mode & SAGE_MODE_MASK;
+  const sage::Layout L = sage::make_layout(BH, N, d, lo, true);
+  sage::AttnArgs a;
+  a.BH = BH; a.N = N; a.Npad = L.Npad; a.d = d; a.causal = causal != 0;
+  a.sl2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);  // sm_scale * log2(e)
+  a.mode = lo; a.out = out;
+  (void)hipGetLastError();
+  if (lo == SAGE_MODE_MXFP4)
+    return hip_status(sage::launch_attn_mxfp4(a, at(ws, L.q_fp4), at(ws, L.q_e8), at(ws, L.k_fp4), at(ws, L.k_e8),
+                                              at(ws, L.vt_fp4), at(ws, L.vt_e8), s), "MXFP4 attention kernel");
+  return hip_status(sage::launch_attn_int8(a, reinterpret_cast<const int8_t*>(at(ws, L.q_codes)),
+                                           reinterpret_cast<const int8_t*>(at(ws, L.k_codes)), at(ws, L.vt),
+                                           reinterpret_cast<const float*>(at(ws, L.q_scales)),
+                                           reinterpret_cast<const float*>(at(ws, L.k_scales)), s),
+                    "INT8 attention kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sage_status_string(int status) {
+  switch (status) {
+    case SAGE_OK: return "SAGE_OK";
+    case SAGE_ERR_INVALID_ARG: return "SAGE_ERR_INVALID_ARG";
+    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED";
+    case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE";
+    case SAGE_ERR_NO_DEVICE: return "SAGE_ERR_NO_DEVICE";
+    case SAGE_ERR_HIP: return "SAGE_ERR_HIP";
+    default: return "SAGE_ERR_UNKNOWN";
+  }
+}
+
+const char* sage_last_error(void) { return g_err; }
+
+size_t sage_attn_workspace_size(int B, int H, int N, int d, int mode) {
+  if (check_dims(B, H, N, d) != SAGE_OK || check_mode(mode, true) != SAGE_OK) return 0;
+  return sage::make_layout(static_cast<long long>(B) * H, N, d, mode & SAGE_MODE_MASK, true).total;
+}
+
+size_t sage_quant_workspace_size(int B, int H, int N, int d) {
+  if (check_dims(B, H, N, d) != SAGE_OK) return 0;
+  return sage::make_layout(static_cast<long long>(B) * H, N, d, 0, false).total;
+}
+
+int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d, int mode,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_ptr(q, "q", 16));
+  SAGE_TRY(check_ptr(k, "k", 16));
+  SAGE_TRY(check_ptr(v, "v", 16));
+  SAGE_TRY(validate_attn(B, H, N, d, mode, workspace, workspace_bytes));
+  SAGE_TRY(check_device());
+  return do_prepare(q, k, v, B, H, N, d, mode, workspace, static_cast<hipStream_t>(stream));
+}
+
+int sage_attn_compute(void* out, int B, int H, int N, int d, int causal, float sm_scale, int mode,
+                      const void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_ptr(out, "out", 16));
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  SAGE_TRY(check_scale(sm_scale));
+  SAGE_TRY(validate_attn(B, H, N, d, mode, workspace, workspace_bytes));
+  SAGE_TRY(check_device());
+  return do_compute(out, B, H, N, d, causal, sm_scale, mode, workspace, static_cast<hipStream_t>(stream));
+}
+
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                  int causal, float sm_scale, int mode, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_ptr(q, "q", 16));
+  SAGE_TRY(check_ptr(k, "k", 16));
+  SAGE_TRY(check_ptr(v, "v", 16));
+  SAGE_TRY(check_ptr(out, "out", 16));
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  SAGE_TRY(check_scale(sm_scale));
+  SAGE_TRY(validate_attn(B, H, N, d, mode, workspace, workspace_bytes));
+  SAGE_TRY(check_device());
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, workspace, s));
+  return do_compute(out, B, H, N, d, causal, sm_scale, mode, workspace, s);
+}
+
+int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, int blk_q, int blk_k, int flags,
+                  int8_t* q_codes, float* q_scales, int8_t* k_codes, float* k_scales, float* k_mean,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_dims(B, H, N, d));
+  SAGE_TRY(check_ptr(q, "q", 16));
+  SAGE_TRY(check_ptr(k, "k", 16));
+  SAGE_TRY(check_ptr(q_codes, "q_codes", 16));
+  SAGE_TRY(check_ptr(k_codes, "k_codes", 16));
+  SAGE_TRY(check_ptr(q_scales, "q_scales", 4));
+  SAGE_TRY(check_ptr(k_scales, "k_scales", 4));
+  if (k_mean) SAGE_TRY(check_ptr(k_mean, "k_mean", 4));
+  auto blk_ok = [](int b) { return b == 1 || b == 16 || b == 32 || b == 64 || b == 128; };
+  if (!blk_ok(blk_q) || !blk_ok(blk_k))
+    return fail(SAGE_ERR_UNSUPPORTED, "block sizes must be 1, 16, 32, 64 or 128 (got %d, %d)", blk_q, blk_k);
+  if (flags & ~SAGE_FLAG_NO_SMOOTH) return fail(SAGE_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  SAGE_TRY(check_ptr(workspace, "workspace", 256));
+  const int BH = B * H;
+  const sage::Layout L = sage::make_layout(BH, N, d, 0, false);
+  if (workspace_bytes < L.total)
+    return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+  SAGE_TRY(check_device());
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool smooth = !(flags & SAGE_FLAG_NO_SMOOTH);
+  (void)hipGetLastError();
+  float* mu = reinterpret_cast<float*>(at(workspace, L.kmean));
+  if (smooth)
+    SAGE_TRY(hip_status(sage::launch_kmean(k, reinterpret_cast<long long*>(at(workspace, L.ksum)), mu, k_mean, BH, N,
+                                           d, L.chunk, L.nchunk, s), "K mean kernels"));
+  const int ntile = (N + sage::kQTile - 1) / sage::kQTile;
+  sage::Int8Job jq, jk;
+  jq.src = q; jq.codes = q_codes; jq.scales = q_scales; jq.mu = nullptr; jq.blk = blk_q; jq.code_rows = N;
+  jq.nscale = (N + blk_q - 1) / blk_q; jq.ntile = ntile;
+  jk.src = k; jk.codes = k_codes; jk.scales = k_scales; jk.mu = smooth ? mu : nullptr; jk.blk = blk_k; jk.code_rows = N;
+  jk.nscale = (N + blk_k - 1) / blk_k; jk.ntile = ntile;
+  return hip_status(sage::launch_int8_quant(jq, jk, BH, N, d, s), "INT8 quantization kernel");
+}
+
+int sage_quant_mxfp4(const void* q, const void* k, const void* v, int B, int H, int N, int d, int flags,
+                     uint8_t* q_fp4, uint8_t* q_e8m0, uint8_t* k_fp4, uint8_t* k_e8m0, uint8_t* vt_fp4,
+                     uint8_t* vt_e8m0, float* k_mean, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_dims(B, H, N, d));
+  SAGE_TRY(check_ptr(q, "q", 16));
+  SAGE_TRY(check_ptr(k, "k", 16));
+  SAGE_TRY(check_ptr(v, "v", 16));
+  SAGE_TRY(check_ptr(q_fp4, "q_fp4", 16));
+  SAGE_TRY(check_ptr(k_fp4, "k_fp4", 16));
+  SAGE_TRY(check_ptr(vt_fp4, "vt_fp4", 16));
+  SAGE_TRY(check_ptr(q_e8m0, "q_e8m0", 1));
+  SAGE_TRY(check_ptr(k_e8m0, "k_e8m0", 1));
+  SAGE_TRY(check_ptr(vt_e8m0, "vt_e8m0", 1));
+  if (k_mean) SAGE_TRY(check_ptr(k_mean, "k_mean", 4));
+  if (flags & ~SAGE_FLAG_NO_SMOOTH) return fail(SAGE_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  SAGE_TRY(check_ptr(workspace, "workspace", 256));
+  const int BH = B * H;
+  const sage::Layout L = sage::make_layout(BH, N, d, 0, false);
+  if (workspace_bytes < L.total)
+    return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+  SAGE_TRY(check_device());
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool smooth = !(flags & SAGE_FLAG_NO_SMOOTH);
+  (void)hipGetLastError();
+  float* mu = reinterpret_cast<float*>(at(workspace, L.kmean));
+  if (smooth)
+    SAGE_TRY(hip_status(sage::launch_kmean(k, reinterpret_cast<long long*>(at(workspace, L.ksum)), mu, k_mean, BH, N,
+                                           d, L.chunk, L.nchunk, s), "K mean kernels"));
+  sage::MxRowJob jq, jk;
+  jq.src = q; jq.fp4 = q_fp4; jq.e8 = q_e8m0; jq.mu = nullptr; jq.rows = N;
+  jk.src = k; jk.fp4 = k_fp4; jk.e8 = k_e8m0; jk.mu = smooth ? mu : nullptr; jk.rows = N;
+  SAGE_TRY(hip_status(sage::launch_mx_rows(jq, jk, BH, N, d, s), "MXFP4 Q/K quantization kernel"));
+  const int Nv = sage::round_up(N, 32);
+  return hip_status(sage::launch_mx_vt(v, vt_fp4, vt_e8m0, BH, N, Nv, d, s), "MXFP4 V quantization kernel");
+}
+
+}  // extern "C"

@@ -1,0 +1,291 @@
+// Fused microscaled-FP4 attention kernel for gfx950 (CDNA4).
+//
+// The SageAttention3 abstract's idea (attention with microscaled FP4
+// operands on FP4 matrix units) on CDNA4's block-scaled MFMA
+// v_mfma_scale_f32_32x32x64_f8f6f4: Q, the mean-smoothed K, V and the softmax
+// P are E2M1 with one E8M0 exponent per 32 elements of the contraction
+// dimension (d for Q K^T, keys for P V), accumulation in FP32.
+//
+// Same decomposition as the INT8 kernel: 4 waves x 32 query rows per
+// workgroup, 64-key tiles in LDS (double-buffered), scores computed as
+// S^T = K Q^T so each lane owns one query column; the permuted K row
+// placement leaves lane group g holding keys g*32 .. g*32+31 of the tile,
+// which is exactly one MX block of P for the B operand of O^T = V^T P^T. P is
+// therefore quantized in registers: block max (in-lane), shared exponent
+// e = floor(log2 max) - 2, and v_cvt_scalef32_pk_fp4_f32 (RNE, saturating)
+// for the E2M1 codes.
+#include "sage_internal.h"
+
+#include <math.h>
+
+namespace sage {
+
+namespace {
+
+__device__ __forceinline__ int lds_row_of_key4(int k) {
+  const int g = k >> 5, t = (k >> 4) & 1, i = k & 15;
+  return t * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+}
+
+__device__ __forceinline__ float pair_max4(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum4(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void map_workgroup4(int bid, int BH, int nqt, bool causal, int& bh, int& qt) {
+  if (BH % 8 == 0) {
+    const int x = bid & 7, r = bid >> 3, hpx = BH >> 3;
+    if (causal) {
+      bh = x * hpx + r % hpx;
+      qt = nqt - 1 - r / hpx;
+    } else {
+      bh = x * hpx + r / nqt;
+      qt = r % nqt;
+    }
+  } else {
+    bh = bid / nqt;
+    qt = bid % nqt;
+    if (causal) qt = nqt - 1 - qt;
+  }
+}
+
+// 32x32x64 FP4 x FP4 block-scaled MFMA; the scale byte is byte 0 of sa / sb.
+__device__ __forceinline__ v16f mfma_fp4(const v4i a, const v4i b, unsigned sa, unsigned sb, v16f c) {
+  const v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, static_cast<int>(sa), 0,
+                                                          static_cast<int>(sb));
+}
+
+}  // namespace
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
+    const uint8_t* __restrict__ q4, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k4,
+    const uint8_t* __restrict__ ke, const uint8_t* __restrict__ v4, const uint8_t* __restrict__ ve,
+    _Float16* __restrict__ out, int N, int Npad, float sl2, int BH) {
+  constexpr int NC = D / 64;         // 64-channel steps of the score contraction
+  constexpr int NE = D / 32;         // exponent bytes per Q / K row
+  constexpr int NT = D / 32;         // 32-row tiles of O^T
+  constexpr int KROW = D / 2 + 16;   // LDS bytes per K row
+  constexpr int VROW = 32 + 16;      // LDS bytes per V^T row (64 keys)
+  constexpr int KT_BYTES = kKTile * KROW;
+  constexpr int KS_BYTES = kKTile * 4;
+  constexpr int VT_BYTES = D * VROW;
+  constexpr int VS_BYTES = D * 4;
+  constexpr int BUF = KT_BYTES + KS_BYTES + VT_BYTES + VS_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+
+  const int nqt = Npad / kQTile;
+  int bh, qt;
+  map_workgroup4(blockIdx.x, BH, nqt, CAUSAL, bh, qt);
+  const int q0 = qt * kQTile;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int qrow = q0 + wave * 32 + l32;
+  const size_t row_q = static_cast<size_t>(bh) * Npad + qrow;
+
+  v4i qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const v4i*>(q4 + row_q * (D / 2) + c * 32 + g * 16);
+  unsigned qsw;  // exponent bytes of this query row, shifted so block c*2+g sits at byte 2c
+  if (NE == 4) qsw = *reinterpret_cast<const unsigned*>(qe + row_q * 4);
+  else qsw = *reinterpret_cast<const uint16_t*>(qe + row_q * 2);
+  qsw >>= 8 * g;
+
+  int nkt = (N + kKTile - 1) / kKTile;
+  if (CAUSAL) nkt = min(nkt, (q0 + kQTile) / kKTile);
+
+  const uint8_t* kb4 = k4 + static_cast<size_t>(bh) * Npad * (D / 2);
+  const uint8_t* kbe = ke + static_cast<size_t>(bh) * Npad * NE;
+  const uint8_t* vb4 = v4 + static_cast<size_t>(bh) * D * (Npad / 2);
+  const uint8_t* vbe = ve + static_cast<size_t>(bh) * D * (Npad / 32);
+
+  // staging registers: one 16-byte K chunk, one K exponent word, one 16-byte V^T chunk, one V^T exponent pair
+  unsigned kr[4], vr[4];
+  unsigned ksr = 0, vsr = 0;
+  constexpr int KCHUNKS = kKTile * D / 32;  // 16-byte chunks per K tile (256 or 128)
+  constexpr int VCHUNKS = D * 2;            // 16-byte chunks per V^T tile (256 or 128)
+#define SAGE_GLOAD4(J_)                                                                              \
+  do {                                                                                               \
+    if (tid < KCHUNKS) {                                                                             \
+      const int row_ = tid / (D / 32), col_ = tid % (D / 32);                                        \
+      const uint4 t_ = *reinterpret_cast<const uint4*>(kb4 + static_cast<size_t>((J_) * kKTile + row_) * (D / 2) + \
+                                                       col_ * 16);                                   \
+      kr[0] = t_.x; kr[1] = t_.y; kr[2] = t_.z; kr[3] = t_.w;                                        \
+    }                                                                                                \
+    if (tid < kKTile) {                                                                              \
+      const size_t r_ = static_cast<size_t>((J_) * kKTile + tid);                                    \
+      ksr = (NE == 4) ? *reinterpret_cast<const unsigned*>(kbe + r_ * 4)                             \
+                      : static_cast<unsigned>(*reinterpret_cast<const uint16_t*>(kbe + r_ * 2));     \
+    }                                                                                                \
+    if (tid < VCHUNKS) {                                                                             \
+      const int row_ = tid >> 1, col_ = tid & 1;                                                     \
+      const uint4 t_ = *reinterpret_cast<const uint4*>(vb4 + static_cast<size_t>(row_) * (Npad / 2) + \
+                                                       (J_) * 32 + col_ * 16);                       \
+      vr[0] = t_.x; vr[1] = t_.y; vr[2] = t_.z; vr[3] = t_.w;                                        \
+    }                                                                                                \
+    if (tid < D)                                                                                     \
+      vsr = *reinterpret_cast<const uint16_t*>(vbe + static_cast<size_t>(tid) * (Npad / 32) + (J_) * 2); \
+  } while (0)
+#define SAGE_SWRITE4(BUF_)                                                                           \
+  do {                                                                                               \
+    unsigned char* kt_ = smem + (BUF_) * BUF;                                                        \
+    unsigned char* ks_ = kt_ + KT_BYTES;                                                             \
+    unsigned char* vl_ = ks_ + KS_BYTES;                                                             \
+    unsigned char* vs_ = vl_ + VT_BYTES;                                                             \
+    if (tid < KCHUNKS) {                                                                             \
+      const int row_ = tid / (D / 32), col_ = tid % (D / 32);                                        \
+      *reinterpret_cast<uint4*>(kt_ + lds_row_of_key4(row_) * KROW + col_ * 16) =                    \
+          make_uint4(kr[0], kr[1], kr[2], kr[3]);                                                    \
+    }                                                                                                \
+    if (tid < kKTile) *reinterpret_cast<unsigned*>(ks_ + lds_row_of_key4(tid) * 4) = ksr;            \
+    if (tid < VCHUNKS) {                                                                             \
+      const int row_ = tid >> 1, col_ = tid & 1;                                                     \
+      *reinterpret_cast<uint4*>(vl_ + row_ * VROW + col_ * 16) = make_uint4(vr[0], vr[1], vr[2], vr[3]); \
+    }                                                                                                \
+    if (tid < D) *reinterpret_cast<unsigned*>(vs_ + tid * 4) = vsr;                                  \
+  } while (0)
+
+  v16f o[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[c][i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  SAGE_GLOAD4(0);
+  SAGE_SWRITE4(0);
+  __syncthreads();
+
+  for (int j = 0; j < nkt; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nkt) SAGE_GLOAD4(j + 1);
+    const unsigned char* kt = smem + buf * BUF;
+    const unsigned char* ksl = kt + KT_BYTES;
+    const unsigned char* vl = ksl + KS_BYTES;
+    const unsigned char* vsl = vl + VT_BYTES;
+
+    // S^T = K_s Q^T on the block-scaled FP4 MFMA (scores come out dequantized)
+    v16f s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
+      const int krow = t * 32 + l32;
+      const unsigned ksw = *reinterpret_cast<const unsigned*>(ksl + krow * 4) >> (8 * g);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const v4i a = *reinterpret_cast<const v4i*>(kt + krow * KROW + c * 32 + g * 16);
+        s[t] = mfma_fp4(a, qf[c], ksw >> (16 * c), qsw >> (16 * c), s[t]);
+      }
+    }
+
+    float p[32];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[t * 16 + i] = s[t][i] * sl2;
+    const bool diag = CAUSAL && (j * kKTile + kKTile - 1 > q0 + wave * 32);
+    const bool tail = (j * kKTile + kKTile > N);
+    if (diag || tail) {
+      const int kb = j * kKTile + g * 32;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int key = kb + e;
+        if ((CAUSAL && key > qrow) || key >= N) p[e] = -INFINITY;
+      }
+    }
+
+    float mx = p[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, p[e]);
+    mx = pair_max4(mx);
+    const float mnew = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    float rs = 0.f, pmax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(p[e] - mnew);
+      rs += p[e];
+      pmax = fmaxf(pmax, p[e]);
+    }
+    l = l * alpha + rs;  // the row sum uses the unquantized P
+    m = mnew;
+
+    // MX-quantize this lane's 32 P values (one block of 32 keys).
+    // e = floor(log2 pmax) - 2, floored at -126 (blocks below 2^-124 are negligible).
+    unsigned pe8 = 127;
+    float pscale = 1.f;
+    if (pmax > 0.f) {
+      const int E = static_cast<int>(__float_as_uint(pmax) >> 23);
+      const int e = max(E - 129, -126);
+      pe8 = static_cast<unsigned>(e + 127);
+      pscale = __uint_as_float(pe8 << 23);
+    }
+    v4i pq;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      unsigned r = 0;
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 0], p[8 * w + 1], pscale, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 2], p[8 * w + 3], pscale, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 4], p[8 * w + 5], pscale, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 6], p[8 * w + 7], pscale, 3);
+      pq[w] = static_cast<int>(r);
+    }
+
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[c][i] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+      const int vrow = dt * 32 + l32;
+      const v4i a = *reinterpret_cast<const v4i*>(vl + vrow * VROW + g * 16);
+      const unsigned vsw = *reinterpret_cast<const unsigned*>(vsl + vrow * 4) >> (8 * g);
+      o[dt] = mfma_fp4(a, pq, vsw, pe8, o[dt]);
+    }
+
+    if (j + 1 < nkt) SAGE_SWRITE4(buf ^ 1);
+    __syncthreads();
+  }
+#undef SAGE_GLOAD4
+#undef SAGE_SWRITE4
+
+  const float inv = 1.f / pair_sum4(l);
+  if (qrow < N) {
+    _Float16* orow = out + (static_cast<size_t>(bh) * N + qrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v4h h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(o[dt][r * 4 + i] * inv);
+        *reinterpret_cast<v4h*>(orow + dt * 32 + r * 8 + g * 4) = h;
+      }
+  }
+}
+
+hipError_t launch_attn_mxfp4(const AttnArgs& a, const uint8_t* q4, const uint8_t* qe,
+                             const uint8_t* k4, const uint8_t* ke, const uint8_t* v4,
+                             const uint8_t* ve, hipStream_t s) {
+  const int nqt = a.Npad / kQTile;
+  const dim3 grid(a.BH * nqt), block(256);
+  auto* o = static_cast<_Float16*>(a.out);
+  if (a.d == 128) {
+    if (a.causal) attn_mxfp4_kernel<128, true><<<grid, block, 0, s>>>(q4, qe, k4, ke, v4, ve, o, a.N, a.Npad, a.sl2, a.BH);
+    else attn_mxfp4_kernel<128, false><<<grid, block, 0, s>>>(q4, qe, k4, ke, v4, ve, o, a.N, a.Npad, a.sl2, a.BH);
+  } else {
+    if (a.causal) attn_mxfp4_kernel<64, true><<<grid, block, 0, s>>>(q4, qe, k4, ke, v4, ve, o, a.N, a.Npad, a.sl2, a.BH);
+    else attn_mxfp4_kernel<64, false><<<grid, block, 0, s>>>(q4, qe, k4, ke, v4, ve, o, a.N, a.Npad, a.sl2, a.BH);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sage

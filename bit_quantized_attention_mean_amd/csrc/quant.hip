@@ -1,0 +1,385 @@
+// Quantization kernels for gfx950: the K channel mean, per-block INT8 codes,
+// the transposed fp16 V used by the INT8 attention kernel, and MXFP4
+// (E2M1 + E8M0) codes. All of them are HBM-streaming kernels: 16-byte
+// coalesced loads and stores, one pass over each input.
+//
+// Method (SageAttention page, "Approach"): subtract the mean of K across
+// tokens (softmax is unchanged because every score row shifts by q.mu), then
+// quantize Q and the smoothed K to INT8 with per-block or per-token scales.
+// MXFP4 (SageAttention3 abstract; the MX format of its reference list):
+// 32 elements share one power-of-two scale, elements are E2M1.
+#include "sage_internal.h"
+
+namespace sage {
+
+// ---------------------------------------------------------------------------
+// K channel mean: exact and order-independent. Every fp16 value is an integer
+// multiple of 2^-24, so K * 2^24 is an integer below 2^41 and sums exactly in
+// int64. mu = fp32(fp64(sum) * 2^-24 / N): one correctly rounded fp64
+// division and one RNE conversion, identical however the sum was split.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ long long f16_to_fixed24(unsigned h) {
+  const unsigned e = (h >> 10) & 31u, m = h & 1023u;
+  const long long mag = e ? (static_cast<long long>(m | 1024u) << (e - 1)) : static_cast<long long>(m);
+  return (h & 0x8000u) ? -mag : mag;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void ksum_partial_kernel(const uint16_t* __restrict__ k,
+                                                           long long* __restrict__ part, int N,
+                                                           int chunk, int nchunk) {
+  constexpr int TPR = D / 8;      // threads per token row, 8 channels (16 bytes) each
+  constexpr int RPP = 256 / TPR;  // token rows per pass
+  __shared__ long long red[256][9];
+  const int bh = blockIdx.x / nchunk, ci = blockIdx.x % nchunk;
+  const int tid = threadIdx.x, cg = tid % TPR;
+  const int n0 = ci * chunk, n1 = min(N, n0 + chunk);
+  const uint16_t* src = k + static_cast<size_t>(bh) * N * D + cg * 8;
+  long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int n = n0 + tid / TPR; n < n1; n += RPP) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(n) * D);
+    const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += f16_to_fixed24(w[j] & 0xffffu);
+      acc[2 * j + 1] += f16_to_fixed24(w[j] >> 16);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[tid][j] = acc[j];
+  __syncthreads();
+  if (tid < D) {
+    const int g = tid / 8, j = tid % 8;
+    long long s = 0;
+    for (int r = 0; r < RPP; ++r) s += red[r * TPR + g][j];
+    part[(static_cast<size_t>(bh) * nchunk + ci) * D + tid] = s;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void kmean_kernel(const long long* __restrict__ part,
+                                                    float* __restrict__ mu_ws,
+                                                    float* __restrict__ mu_out, int N, int nchunk) {
+  constexpr int G = 256 / D;  // chunk groups reduced in parallel
+  __shared__ long long red[256];
+  const int bh = blockIdx.x, c = threadIdx.x % D, grp = threadIdx.x / D;
+  long long s = 0;
+  for (int i = grp; i < nchunk; i += G) s += part[(static_cast<size_t>(bh) * nchunk + i) * D + c];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    long long t = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) t += red[g * D + c];  // integer: order is irrelevant
+    const float mu = static_cast<float>((static_cast<double>(t) * 0x1p-24) / static_cast<double>(N));
+    mu_ws[static_cast<size_t>(bh) * D + c] = mu;
+    if (mu_out) mu_out[static_cast<size_t>(bh) * D + c] = mu;
+  }
+}
+
+hipError_t launch_kmean(const void* k, long long* ksum, float* kmean_ws, float* kmean_out, int BH,
+                        int N, int d, int chunk, int nchunk, hipStream_t s) {
+  const auto* kk = static_cast<const uint16_t*>(k);
+  if (d == 128) {
+    ksum_partial_kernel<128><<<BH * nchunk, 256, 0, s>>>(kk, ksum, N, chunk, nchunk);
+    kmean_kernel<128><<<BH, 256, 0, s>>>(ksum, kmean_ws, kmean_out, N, nchunk);
+  } else {
+    ksum_partial_kernel<64><<<BH * nchunk, 256, 0, s>>>(kk, ksum, N, chunk, nchunk);
+    kmean_kernel<64><<<BH, 256, 0, s>>>(ksum, kmean_ws, kmean_out, N, nchunk);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-block INT8 quantization. A workgroup owns 128 token rows of one head.
+// Per block of `blk` rows: a = max|x|, s = fp32(a / 127) (IEEE division),
+// code = rint(fp32(x / s)) (ties to even); a = 0 gives s = 0 and zero codes.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void unpack8(const uint4 raw, float* x) {
+  const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j] & 0xffffu)));
+    x[2 * j + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j] >> 16)));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void int8_quant_kernel(Int8Job j0, Int8Job j1, int N) {
+  constexpr int TPR = D / 8;         // threads per row
+  constexpr int RPP = 256 / TPR;     // rows per pass
+  constexpr int NP = kQTile / RPP;   // passes per 128-row tile
+  __shared__ float rmax[kQTile];
+  __shared__ float bmax[kQTile];
+  const Int8Job J = blockIdx.y ? j1 : j0;
+  const int bh = blockIdx.x / J.ntile, tile = blockIdx.x % J.ntile;
+  const int tid = threadIdx.x, cg = tid % TPR, rl = tid / TPR;
+  const int row0 = tile * kQTile;
+  const uint16_t* src = static_cast<const uint16_t*>(J.src) + static_cast<size_t>(bh) * N * D + cg * 8;
+
+  float mu[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (J.mu) {
+    const float4* m4 = reinterpret_cast<const float4*>(J.mu + static_cast<size_t>(bh) * D + cg * 8);
+    const float4 a = m4[0], b = m4[1];
+    mu[0] = a.x; mu[1] = a.y; mu[2] = a.z; mu[3] = a.w;
+    mu[4] = b.x; mu[5] = b.y; mu[6] = b.z; mu[7] = b.w;
+  }
+
+  float x[NP][8];
+  float lm[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int row = row0 + p * RPP + rl;
+    if (row < N) {
+      unpack8(*reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * D), x[p]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[p][e] = x[p][e] - mu[e];  // fp32 RNE subtraction (mu = 0 if off)
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[p][e] = 0.f;
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[p][e]));
+    // max over the TPR consecutive lanes that share this row
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    lm[p] = m;
+  }
+
+  const int blk = J.blk;
+  float s[NP];
+  if (blk == 1) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) s[p] = lm[p] / 127.0f;
+  } else {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (cg == 0) rmax[p * RPP + rl] = lm[p];
+    __syncthreads();
+    const int nb = kQTile / blk;
+    if (tid < nb) {
+      float m = 0.f;
+      for (int r = 0; r < blk; ++r) m = fmaxf(m, rmax[tid * blk + r]);
+      bmax[tid] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NP; ++p) s[p] = bmax[(p * RPP + rl) / blk] / 127.0f;
+  }
+
+  // codes
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int row = row0 + p * RPP + rl;
+    if (row < J.code_rows) {
+      unsigned lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int c = 0;
+        if (s[p] > 0.f) {
+          const float qv = __builtin_rintf(x[p][e] / s[p]);  // IEEE division, ties-to-even rounding
+          c = static_cast<int>(fminf(fmaxf(qv, -127.f), 127.f));
+        }
+        const unsigned b = static_cast<unsigned>(c) & 0xffu;
+        if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
+      }
+      *reinterpret_cast<uint2*>(J.codes + (static_cast<size_t>(bh) * J.code_rows + row) * D + cg * 8) =
+          make_uint2(lo, hi);
+    }
+  }
+
+  // scales
+  if (blk == 1) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int row = row0 + p * RPP + rl;
+      if (cg == 0 && row < J.nscale) J.scales[static_cast<size_t>(bh) * J.nscale + row] = s[p];
+    }
+  } else {
+    const int nb = kQTile / blk;
+    const int bi = tile * nb + tid;
+    if (tid < nb && bi < J.nscale) J.scales[static_cast<size_t>(bh) * J.nscale + bi] = bmax[tid] / 127.0f;
+  }
+}
+
+hipError_t launch_int8_quant(const Int8Job& j0, const Int8Job& j1, int BH, int N, int d, hipStream_t s) {
+  // Both jobs cover the same rows per head, so they share the tile count.
+  dim3 grid(BH * j0.ntile, 2);
+  if (d == 128) int8_quant_kernel<128><<<grid, 256, 0, s>>>(j0, j1, N);
+  else int8_quant_kernel<64><<<grid, 256, 0, s>>>(j0, j1, N);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// V transpose for the INT8 path: V^T [BH, d, Npad] fp16, tokens >= N zeroed.
+// The P.V matrix op consumes V with keys along the contraction; storing it
+// transposed makes every operand fetch one 16-byte LDS read.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v,
+                                                          uint16_t* __restrict__ vt, int N, int Npad) {
+  constexpr int TT = 64;  // tokens per tile
+  __shared__ uint16_t t[TT][D + 8];
+  const int ntile = Npad / TT;
+  const int bh = blockIdx.x / ntile, tb = blockIdx.x % ntile;
+  const int tid = threadIdx.x;
+  const uint16_t* src = v + static_cast<size_t>(bh) * N * D;
+  constexpr int CPR = D / 8;  // 16-byte chunks per token row
+#pragma unroll
+  for (int u = 0; u < TT * CPR / 256; ++u) {
+    const int i = tid + 256 * u, r = i / CPR, c8 = i % CPR;
+    const int n = tb * TT + r;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (n < N) val = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(n) * D + c8 * 8);
+    *reinterpret_cast<uint4*>(&t[r][c8 * 8]) = val;
+  }
+  __syncthreads();
+  uint16_t* dst = vt + static_cast<size_t>(bh) * D * Npad + tb * TT;
+#pragma unroll
+  for (int u = 0; u < D * (TT / 8) / 256; ++u) {
+    const int i = tid + 256 * u, dd = i / (TT / 8), n8 = i % (TT / 8);
+    unsigned w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = static_cast<unsigned>(t[n8 * 8 + 2 * j][dd]) | (static_cast<unsigned>(t[n8 * 8 + 2 * j + 1][dd]) << 16);
+    *reinterpret_cast<uint4*>(dst + static_cast<size_t>(dd) * Npad + n8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+hipError_t launch_v_transpose(const void* v, void* vt, int BH, int N, int Npad, int d, hipStream_t s) {
+  const int grid = BH * (Npad / 64);
+  if (d == 128)
+    v_transpose_kernel<128><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), N, Npad);
+  else
+    v_transpose_kernel<64><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), N, Npad);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4: per 32-element block, e = floor(log2 max|x|) - 2 clamped to
+// [-127, 127] (0 for an all-zero block), E8M0 byte e + 127, and every element
+// the E2M1 value nearest to x * 2^-e with ties to the even code, saturating at
+// 6. The E2M1 magnitudes are 0, .5, 1, 1.5, 2, 3, 4, 6; their midpoints .25,
+// .75, 1.25, 1.75, 2.5, 3.5, 5 go down at even-below (.25, 1.25, 2.5, 5) and
+// up at odd-below (.75, 1.75, 3.5), hence the mix of > and >= below.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const int E = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);  // amax >= 0
+  const int e = E - 129;  // floor(log2 a) - 2 for a normal a
+  return e < -127 ? -127 : e;
+}
+
+__device__ __forceinline__ unsigned e2m1_code(float x, int e) {
+  const float y = ldexpf(fabsf(x), -e);  // exact power-of-two scaling
+  const unsigned c = static_cast<unsigned>(y > 0.25f) + static_cast<unsigned>(y >= 0.75f) +
+                     static_cast<unsigned>(y > 1.25f) + static_cast<unsigned>(y >= 1.75f) +
+                     static_cast<unsigned>(y > 2.5f) + static_cast<unsigned>(y >= 3.5f) +
+                     static_cast<unsigned>(y > 5.0f);
+  return c | ((__float_as_uint(x) >> 28) & 8u);  // sign bit of x
+}
+
+// Quantizes 32 floats: 16 packed bytes (element 2i in the low nibble) + exponent byte.
+__device__ __forceinline__ uint4 mx_block(const float* x, unsigned& e8) {
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));
+  const int e = mx_exponent(a);
+  e8 = static_cast<unsigned>(e + 127);
+  unsigned w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i / 8] |= e2m1_code(x[i], e) << (4 * (i % 8));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void mx_rows_kernel(MxRowJob j0, MxRowJob j1, int BH, int N) {
+  constexpr int NB = D / 32;  // blocks per row
+  const MxRowJob J = blockIdx.y ? j1 : j0;
+  const long long gb = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const long long per_head = static_cast<long long>(J.rows) * NB;
+  if (gb >= per_head * BH) return;
+  const int bh = static_cast<int>(gb / per_head);
+  const int rem = static_cast<int>(gb % per_head);
+  const int row = rem / NB, db = rem % NB;
+  float x[32];
+  if (row < N) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(J.src) +
+                                                    (static_cast<size_t>(bh) * N + row) * D + db * 32);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) unpack8(p[u], x + 8 * u);
+    if (J.mu) {
+      const float* m = J.mu + static_cast<size_t>(bh) * D + db * 32;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = x[i] - m[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.f;
+  }
+  unsigned e8;
+  const uint4 packed = mx_block(x, e8);
+  const size_t r = static_cast<size_t>(bh) * J.rows + row;
+  *reinterpret_cast<uint4*>(J.fp4 + r * (D / 2) + db * 16) = packed;
+  J.e8[r * NB + db] = static_cast<uint8_t>(e8);
+}
+
+hipError_t launch_mx_rows(const MxRowJob& j0, const MxRowJob& j1, int BH, int N, int d, hipStream_t s) {
+  const long long nblk = static_cast<long long>(BH) * j0.rows * (d / 32);
+  dim3 grid(static_cast<unsigned>((nblk + 255) / 256), 2);
+  if (d == 128) mx_rows_kernel<128><<<grid, 256, 0, s>>>(j0, j1, BH, N);
+  else mx_rows_kernel<64><<<grid, 256, 0, s>>>(j0, j1, BH, N);
+  return hipGetLastError();
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void mx_vt_kernel(const uint16_t* __restrict__ v, uint8_t* __restrict__ fp4,
+                                                    uint8_t* __restrict__ e8, int N, int Nv) {
+  constexpr int TT = 256 * 32 / D;  // tokens per tile: every thread owns one (channel, 32-token block)
+  constexpr int CPR = D / 8;
+  __shared__ uint16_t t[TT][D + 2];
+  const int ntile = (Nv + TT - 1) / TT;
+  const int bh = blockIdx.x / ntile, tb = blockIdx.x % ntile;
+  const int tid = threadIdx.x;
+  const uint16_t* src = v + static_cast<size_t>(bh) * N * D;
+#pragma unroll
+  for (int u = 0; u < TT * CPR / 256; ++u) {
+    const int i = tid + 256 * u, r = i / CPR, c8 = i % CPR;
+    const int n = tb * TT + r;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (n < N) val = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(n) * D + c8 * 8);
+    const unsigned w[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[r][c8 * 8 + 2 * j] = static_cast<uint16_t>(w[j] & 0xffffu);
+      t[r][c8 * 8 + 2 * j + 1] = static_cast<uint16_t>(w[j] >> 16);
+    }
+  }
+  __syncthreads();
+  const int c = tid % D, b = tid / D;
+  const int n0 = tb * TT + b * 32;
+  if (n0 >= Nv) return;
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = static_cast<float>(__builtin_bit_cast(_Float16, t[b * 32 + i][c]));
+  unsigned eb;
+  const uint4 packed = mx_block(x, eb);
+  const size_t rowc = static_cast<size_t>(bh) * D + c;
+  *reinterpret_cast<uint4*>(fp4 + rowc * (Nv / 2) + n0 / 2) = packed;
+  e8[rowc * (Nv / 32) + n0 / 32] = static_cast<uint8_t>(eb);
+}
+
+hipError_t launch_mx_vt(const void* v, uint8_t* fp4, uint8_t* e8, int BH, int N, int Nv, int d, hipStream_t s) {
+  const int TT = 256 * 32 / d;
+  const int grid = BH * ((Nv + TT - 1) / TT);
+  if (d == 128) mx_vt_kernel<128><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp4, e8, N, Nv);
+  else mx_vt_kernel<64><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp4, e8, N, Nv);
+  return hipGetLastError();
+}
+
+}  // namespace sage

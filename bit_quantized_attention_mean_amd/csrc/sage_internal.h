@@ -1,0 +1,141 @@
+// Internal declarations of the gfx950 quantized-attention library: vector
+// types, the private workspace layout and the kernel launchers. Not part of
+// the public C ABI (include/sage_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+// Query rows per attention workgroup and keys per key tile. Every per-head
+// row count in the workspace is padded to a multiple of kRowPad, with zero
+// rows, so the attention kernel's tile loads never need bounds checks.
+constexpr int kQTile = 128;
+constexpr int kKTile = 64;
+constexpr int kRowPad = 128;
+
+inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Tokens per partial-sum chunk of the K column sum: at least 256 and large
+// enough that no head has more than 64 chunks.
+inline int ksum_chunk(int N) {
+  int c = round_up((N + 63) / 64, 64);
+  return c < 256 ? 256 : c;
+}
+
+// Byte offsets of the regions of a workspace. All offsets are 256-aligned.
+struct Layout {
+  int Npad = 0;      // rows per head of every padded operand
+  int nchunk = 0;    // K column-sum chunks per head
+  int chunk = 0;     // tokens per chunk
+  size_t ksum = 0;   // int64 [BH, nchunk, d] partial column sums
+  size_t kmean = 0;  // fp32 [BH, d]
+  // INT8 modes
+  size_t q_codes = 0, k_codes = 0;    // int8 [BH, Npad, d]
+  size_t q_scales = 0, k_scales = 0;  // fp32 [BH, Npad] (enough for any block size)
+  size_t vt = 0;                      // fp16 [BH, d, Npad] (V transposed, zero-padded)
+  // MXFP4 mode
+  size_t q_fp4 = 0, k_fp4 = 0;    // uint8 [BH, Npad, d/2]
+  size_t q_e8 = 0, k_e8 = 0;      // uint8 [BH, Npad, d/32]
+  size_t vt_fp4 = 0, vt_e8 = 0;   // uint8 [BH, d, Npad/2], [BH, d, Npad/32]
+  size_t total = 0;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// mode_lo: SAGE_MODE_* without flags; attention=false gives the layout of the
+// standalone quantization entry points (column sums and mean only).
+inline Layout make_layout(long long BH, int N, int d, int mode_lo, bool attention) {
+  Layout L;
+  L.Npad = round_up(N, kRowPad);
+  L.chunk = ksum_chunk(N);
+  L.nchunk = (N + L.chunk - 1) / L.chunk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+  L.ksum = take(size_t(BH) * L.nchunk * d * 8);
+  L.kmean = take(size_t(BH) * d * 4);
+  if (attention) {
+    const size_t rows = size_t(BH) * L.Npad;
+    if (mode_lo == 2) {
+      L.q_fp4 = take(rows * d / 2);
+      L.k_fp4 = take(rows * d / 2);
+      L.q_e8 = take(rows * d / 32);
+      L.k_e8 = take(rows * d / 32);
+      L.vt_fp4 = take(rows * d / 2);
+      L.vt_e8 = take(rows * d / 32);
+    } else {
+      L.q_codes = take(rows * d);
+      L.k_codes = take(rows * d);
+      L.q_scales = take(rows * 4);
+      L.k_scales = take(rows * 4);
+      L.vt = take(rows * d * 2);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (return the hipError_t of the launch). All take B*H as BH.
+// ---------------------------------------------------------------------------
+
+// K column sums (exact int64 fixed point) and the per-channel mean.
+hipError_t launch_kmean(const void* k, long long* ksum, float* kmean_ws, float* kmean_out, int BH,
+                        int N, int d, int chunk, int nchunk, hipStream_t s);
+
+// One INT8 quantization job: `src` fp16 [BH, N, d] -> codes [BH, code_rows, d],
+// scales [BH, nscale]; rows in [N, code_rows) are written as zero codes.
+struct Int8Job {
+  const void* src = nullptr;
+  int8_t* codes = nullptr;
+  float* scales = nullptr;
+  const float* mu = nullptr;  // [BH, d] subtracted when non-null
+  int blk = 64;
+  int code_rows = 0;
+  int nscale = 0;
+  int ntile = 0;  // 128-row tiles per head to process
+};
+hipError_t launch_int8_quant(const Int8Job& j0, const Int8Job& j1, int BH, int N, int d, hipStream_t s);
+
+// fp16 V [BH, N, d] -> V^T [BH, d, Npad] with zero-padded tokens.
+hipError_t launch_v_transpose(const void* v, void* vt, int BH, int N, int Npad, int d, hipStream_t s);
+
+// MXFP4 quantization along channels: src fp16 [BH, N, d] -> fp4 [BH, rows, d/2],
+// e8 [BH, rows, d/32]; rows in [N, rows) get zero codes and exponent byte 127.
+struct MxRowJob {
+  const void* src = nullptr;
+  uint8_t* fp4 = nullptr;
+  uint8_t* e8 = nullptr;
+  const float* mu = nullptr;
+  int rows = 0;
+};
+hipError_t launch_mx_rows(const MxRowJob& j0, const MxRowJob& j1, int BH, int N, int d, hipStream_t s);
+
+// MXFP4 quantization of V along tokens: -> fp4 [BH, d, Nv/2], e8 [BH, d, Nv/32]
+// (Nv a multiple of 32, tokens >= N are zeros).
+hipError_t launch_mx_vt(const void* v, uint8_t* fp4, uint8_t* e8, int BH, int N, int Nv, int d, hipStream_t s);
+
+// Fused attention from a prepared workspace.
+struct AttnArgs {
+  int BH = 0, N = 0, Npad = 0, d = 0;
+  bool causal = false;
+  float sl2 = 0.f;  // sm_scale * log2(e)
+  int mode = 0;     // SAGE_MODE_* (no flags)
+  void* out = nullptr;
+};
+hipError_t launch_attn_int8(const AttnArgs& a, const int8_t* qc, const int8_t* kc, const void* vt,
+                            const float* qs, const float* ks, hipStream_t s);
+hipError_t launch_attn_mxfp4(const AttnArgs& a, const uint8_t* q4, const uint8_t* qe,
+                             const uint8_t* k4, const uint8_t* ke, const uint8_t* v4,
+                             const uint8_t* ve, hipStream_t s);
+
+}  // namespace sage

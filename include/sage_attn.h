@@ -1,0 +1,159 @@
+/*
+ * sage_attn.h -- C ABI of the MI355X (gfx950) quantized-attention library.
+ *
+ * The library computes the forward pass that the SageAttention page
+ * ("SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
+ * Acceleration", atlas.scime.ai summary, sections "Approach" and the summary
+ * paragraph) describes as a plug-and-play replacement for attention: Q, K, V
+ * in, O out. INT8 path: subtract the per-channel mean of K over tokens,
+ * quantize Q and K to INT8 with per-block float scales, QK^T with integer
+ * accumulation, dequantize, online softmax (FlashAttention-2 style, the page's
+ * "Experimental setup: builds on"), P.V in FP16. MXFP4 path: the microscaled
+ * FP4 idea of "SageAttention3: Microscaling FP4 Attention for Inference and
+ * An Exploration of 8-Bit Training" (abstract), using E2M1 elements with one
+ * E8M0 scale per 32 elements (the MX format its reference list names).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, C-contiguous [B, H, N, d] (batch, head, token,
+ *     channel) unless stated otherwise. fp16 means IEEE binary16.
+ *   - Pointers named q, k, v, out, *_codes, *_scales, *_fp4, *_e8m0, k_mean
+ *     and workspace are DEVICE pointers on the current HIP device. q, k, v,
+ *     out and workspace must be 16-byte aligned; workspace 256-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream). All
+ *     work is enqueued on it; the library never synchronizes, allocates or
+ *     frees device memory. Results are valid once the stream reaches them.
+ *   - The caller owns every buffer. The library keeps no state besides a
+ *     per-device architecture check and a thread-local error message, so calls
+ *     are re-entrant; calls that share a workspace must be stream-ordered.
+ *   - Supported head dims d: 64 and 128. 1 <= N <= 4194304. B, H >= 1.
+ *   - Every argument check happens before the first HIP call, so every error
+ *     except SAGE_ERR_HIP and SAGE_ERR_NO_DEVICE is reported on a host with no
+ *     GPU. Errors return a negative sage_status_t and set sage_last_error();
+ *     no exception crosses the ABI and the library never aborts.
+ */
+#ifndef SAGE_ATTN_H
+#define SAGE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sage_status {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size, non-finite scale */
+  SAGE_ERR_UNSUPPORTED = -2,  /* d, mode or block size not supported; device is not gfx950 */
+  SAGE_ERR_WORKSPACE = -3,    /* workspace smaller than the *_workspace_size() query */
+  SAGE_ERR_NO_DEVICE = -4,    /* no HIP device is visible */
+  SAGE_ERR_HIP = -5           /* a HIP launch or runtime call failed */
+} sage_status_t;
+
+/* Modes (low byte of `mode`). */
+#define SAGE_MODE_INT8_Q128_K64 0  /* INT8 Q,K; Q scale blocks of 128 tokens, K blocks of 64 */
+#define SAGE_MODE_INT8_Q64_K64 1   /* INT8 Q,K; Q and K scale blocks of 64 tokens            */
+#define SAGE_MODE_MXFP4 2          /* MXFP4 Q, K_s, V and P, E8M0 scale per 32 elements      */
+#define SAGE_MODE_INT8_PER_TOKEN 3 /* INT8 Q,K with one scale per token (blocks of 1)        */
+#define SAGE_MODE_MASK 0xff
+
+/* Flags OR-ed into `mode` (or passed as `flags`). */
+#define SAGE_FLAG_NO_SMOOTH 0x100  /* skip the K mean subtraction (ablation only) */
+
+/* Human-readable name of a status code; never NULL. */
+const char* sage_status_string(int status);
+
+/* Detail text of the last error raised on the calling thread ("" if none). */
+const char* sage_last_error(void);
+
+/*
+ * Bytes of device workspace sage_attn_fwd / sage_attn_prepare /
+ * sage_attn_compute need for this problem (0 if the arguments are invalid).
+ * The workspace holds the quantized operands between the two phases.
+ */
+size_t sage_attn_workspace_size(int B, int H, int N, int d, int mode);
+
+/*
+ * Full forward pass: out = attention(q, k, v) computed by the quantized
+ * method of `mode` (SageAttention page, "Approach"; SageAttention3 abstract
+ * for SAGE_MODE_MXFP4). Equivalent to sage_attn_prepare followed by
+ * sage_attn_compute on the same stream and workspace.
+ *   q, k, v  fp16 [B, H, N, d] device, read only.
+ *   out      fp16 [B, H, N, d] device, written (may not alias q, k, v).
+ *   causal   0: no mask; 1: key j is hidden from query i when j > i.
+ *   sm_scale softmax temperature applied to QK^T; finite and > 0
+ *            (the usual value is 1/sqrt(d)).
+ *   mode     SAGE_MODE_* | SAGE_FLAG_*.
+ *   workspace, workspace_bytes  scratch of at least sage_attn_workspace_size().
+ * Returns SAGE_OK or a negative sage_status_t; on error nothing is enqueued
+ * (except after SAGE_ERR_HIP, where earlier kernels of the call may run).
+ */
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
+                  int d, int causal, float sm_scale, int mode, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * First phase of sage_attn_fwd: the K channel mean and the quantization of
+ * Q, K (and V's layout, or its MXFP4 codes) into `workspace`. The steps are
+ * those of sage_quant_qk / sage_quant_mxfp4; the workspace layout is private.
+ */
+int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                      int mode, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Second phase of sage_attn_fwd: the fused attention kernel (quantized QK^T,
+ * dequantization, online softmax, P.V, normalization) reading the operands a
+ * previous sage_attn_prepare with the same B, H, N, d and mode left in
+ * `workspace`, writing fp16 `out` [B, H, N, d]. Arguments as for sage_attn_fwd.
+ */
+int sage_attn_compute(void* out, int B, int H, int N, int d, int causal, float sm_scale,
+                      int mode, const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace sage_quant_qk and sage_quant_mxfp4 need. */
+size_t sage_quant_workspace_size(int B, int H, int N, int d);
+
+/*
+ * INT8 quantization of Q and the mean-smoothed K (SageAttention page,
+ * "Approach": subtract the mean of K across tokens, then INT8 with per-block
+ * or per-token scales).
+ *   q, k       fp16 [B, H, N, d] device.
+ *   blk_q, blk_k  tokens per scale block: 1 (per token), 16, 32, 64 or 128.
+ *   flags      0 or SAGE_FLAG_NO_SMOOTH.
+ *   q_codes, k_codes   int8 [B, H, N, d] device, written.
+ *   q_scales   fp32 [B, H, ceil(N/blk_q)] device, written.
+ *   k_scales   fp32 [B, H, ceil(N/blk_k)] device, written.
+ *   k_mean     fp32 [B, H, d] device, written; may be NULL.
+ * Definitions (bit-exact):
+ *   mu[b,h,c] = fp32( fp64(sum_n K[b,h,n,c] * 2^24 as an exact int64) * 2^-24 / N ).
+ *   K_s = fp32(K) - mu (fp32 subtraction); with SAGE_FLAG_NO_SMOOTH, K_s = fp32(K).
+ *   per block: a = max |x|, s = fp32(a / 127) (correctly rounded division),
+ *   code = round_half_even(fp32(x / s)) in [-127, 127]; a = 0 gives s = 0, codes 0.
+ */
+int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, int blk_q, int blk_k,
+                  int flags, int8_t* q_codes, float* q_scales, int8_t* k_codes, float* k_scales,
+                  float* k_mean, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * MXFP4 quantization of Q, the mean-smoothed K and V (SageAttention3 abstract;
+ * MX format: 32 elements share one E8M0 exponent).
+ *   q_fp4, k_fp4   uint8 [B, H, N, d/2]: E2M1 codes, element 2i in the low nibble.
+ *   q_e8m0, k_e8m0 uint8 [B, H, N, d/32]: blocks of 32 channels.
+ *   vt_fp4   uint8 [B, H, d, Nv/2], Nv = N rounded up to a multiple of 32:
+ *            V transposed, blocks of 32 tokens per channel, zero-padded.
+ *   vt_e8m0  uint8 [B, H, d, Nv/32].
+ *   k_mean   fp32 [B, H, d] or NULL. flags: 0 or SAGE_FLAG_NO_SMOOTH.
+ * Definitions (bit-exact): a = max |x| over the block; e = floor(log2 a) - 2
+ * clamped to [-127, 127] (e = 0 when a = 0); E8M0 byte = e + 127; element =
+ * E2M1 value nearest to x * 2^-e (ties to the even code, saturating at 6),
+ * sign bit = sign bit of x.
+ */
+int sage_quant_mxfp4(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                     int flags, uint8_t* q_fp4, uint8_t* q_e8m0, uint8_t* k_fp4, uint8_t* k_e8m0,
+                     uint8_t* vt_fp4, uint8_t* vt_e8m0, float* k_mean, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_ATTN_H */

@@ -1,0 +1,103 @@
+"""C ABI contract, checked on the CPU: the library loads, exports every function
+include/sage_attn.h declares, and rejects every invalid argument before any HIP
+call (so the same errors come back on a host without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage_attn.h")
+
+sa = pytest.importorskip("bit_quantized_attention_mean_amd")
+lib = sa.lib
+
+OK, INVALID, UNSUP, WS, NODEV, HIP = 0, -1, -2, -3, -4, -5
+A16 = 0x10000          # a 16/256-aligned fake address; never dereferenced in these tests
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(sa.EXPORTED_SYMBOLS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_cover_every_code():
+    names = {c: sa.sage_status_string(c) for c in (OK, INVALID, UNSUP, WS, NODEV, HIP)}
+    assert names[OK] == "SAGE_OK" and names[HIP] == "SAGE_ERR_HIP"
+    assert len(set(names.values())) == 6
+    assert sa.sage_status_string(-99) == "SAGE_ERR_UNKNOWN"
+
+
+def test_workspace_sizes():
+    assert sa.sage_attn_workspace_size(1, 2, 256, 64, 0) > 0
+    assert sa.sage_attn_workspace_size(0, 2, 256, 64, 0) == 0
+    assert sa.sage_attn_workspace_size(1, 2, 256, 96, 0) == 0
+    assert sa.sage_attn_workspace_size(1, 2, 256, 64, 7) == 0
+    small = sa.sage_attn_workspace_size(1, 2, 256, 128, 0)
+    big = sa.sage_attn_workspace_size(1, 2, 4096, 128, 0)
+    assert big > small
+    # INT8: codes (2 B/elem) + V^T (2 B/elem) dominate; MXFP4: ~1.6 B/elem
+    n = 4 * 32 * 4096 * 128
+    assert 4 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 0) < 4.2 * n
+    assert 1.5 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 2) < 1.8 * n
+    assert sa.sage_quant_workspace_size(1, 2, 256, 64) > 0
+
+
+def _fwd(q=A16, k=A16, v=A16, out=A16, B=1, H=2, N=256, d=64, causal=0, scale=0.125, mode=0, ws=A16, wsb=None):
+    if wsb is None:
+        wsb = sa.sage_attn_workspace_size(B, H, N, d, mode) or 1 << 20
+    return lib.sage_attn_fwd(q, k, v, out, B, H, N, d, causal, scale, mode, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(out=None), INVALID),
+    (dict(q=A16 + 8), INVALID), (dict(out=A16 + 2), INVALID), (dict(ws=A16 + 16), INVALID),
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID), (dict(N=(1 << 22) + 1), INVALID),
+    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(mode=9), UNSUP), (dict(mode=0x200), UNSUP),
+    (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(causal=2), INVALID), (dict(wsb=1024), WS),
+])
+def test_fwd_rejects_invalid_arguments_before_touching_the_gpu(kw, code):
+    assert _fwd(**kw) == code
+    assert sa.sage_last_error() != ""
+
+
+def test_prepare_compute_and_quant_validation():
+    ws = sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
+    assert lib.sage_attn_prepare(None, A16, A16, 1, 2, 256, 64, 0, A16, ws, None) == INVALID
+    assert lib.sage_attn_prepare(A16, A16, A16, 1, 2, 256, 64, 0, A16, 10, None) == WS
+    assert lib.sage_attn_compute(A16, 1, 2, 256, 64, 0, 0.0, 0, A16, ws, None) == INVALID
+    assert lib.sage_attn_compute(A16, 1, 2, 256, 48, 0, 0.1, 0, A16, ws, None) == UNSUP
+    qw = sa.sage_quant_workspace_size(1, 2, 256, 64)
+    assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 48, 64, 0, A16, A16, A16, A16, None, A16, qw, None) == UNSUP
+    assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 4, A16, A16, A16, A16, None, A16, qw, None) == UNSUP
+    assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 0, None, A16, A16, A16, None, A16, qw, None) == INVALID
+    assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 0, A16, A16, A16, A16, None, A16, 8, None) == WS
+    assert lib.sage_quant_mxfp4(A16, A16, A16, 1, 2, 256, 64, 0, A16, A16, A16, A16, A16 + 4, A16, None, A16, qw,
+                                None) == INVALID
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers must never reach a real GPU")
+def test_valid_arguments_without_a_device_report_no_device():
+    assert _fwd() == NODEV
+    assert "device" in sa.sage_last_error()
+    qw = sa.sage_quant_workspace_size(1, 2, 256, 64)
+    assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 0, A16, A16, A16, A16, None, A16, qw, None) == NODEV

@@ -1,0 +1,157 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Quantization outputs (K mean, INT8 codes and scales, MXFP4 codes and
+exponents) must match bit for bit; attention outputs must be within
+2e-3 + half an fp16 ulp of the quantization-emulating oracle, element by
+element. Inputs are seeded synthetic tensors (synthetic.make_custom).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from synthetic import make_custom
+from _parity import assert_output_parity, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_attention_mean_amd as m
+    return m
+
+
+def _dev(*arrs):
+    return [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in arrs]
+
+
+QUANT_CASES = [
+    # B, H, N, d, blk_q, blk_k, flags, dist
+    (1, 2, 256, 64, 64, 64, 0, "normal"),
+    (2, 3, 1000, 128, 128, 64, 0, "normal"),
+    (1, 2, 777, 64, 128, 64, 0, "student_t"),
+    (1, 1, 1, 128, 128, 64, 0, "normal"),
+    (1, 2, 63, 64, 64, 64, 0, "normal"),
+    (1, 2, 65, 128, 16, 32, 0, "normal"),
+    (1, 2, 300, 128, 1, 1, 0, "normal"),
+    (1, 2, 300, 64, 128, 64, 0x100, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"-b{c[4]}-{c[5]}-f{c[6]}")
+def test_int8_quant_bitexact(sa, case):
+    B, H, N, d, bq, bk, flags, dist = case
+    say("int8 quant", case)
+    q, k, _ = make_custom(B, H, N, d, seed=N + d, dist=dist)
+    ref = O.quant_qk_int8(q, k, blk_q=bq, blk_k=bk, smooth=not flags)
+    qd, kd = _dev(q, k)
+    got = sa.sage_quant_qk(qd, kd, blk_q=bq, blk_k=bk, flags=flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(got["q_codes"].cpu().numpy(), ref["q_codes"])
+    assert np.array_equal(got["k_codes"].cpu().numpy(), ref["k_codes"])
+    assert np.array_equal(got["q_scales"].cpu().numpy().view(np.uint32), ref["q_scales"].view(np.uint32))
+    assert np.array_equal(got["k_scales"].cpu().numpy().view(np.uint32), ref["k_scales"].view(np.uint32))
+    if not flags:
+        assert np.array_equal(got["k_mean"].cpu().numpy().view(np.uint32), ref["k_mean"].view(np.uint32))
+
+
+MX_CASES = [(1, 2, 256, 64, 0), (2, 2, 1000, 128, 0), (1, 1, 33, 128, 0), (1, 2, 96, 64, 0x100)]
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_mxfp4_quant_bitexact(sa, case):
+    B, H, N, d, flags = case
+    say("mxfp4 quant", case)
+    q, k, v = make_custom(B, H, N, d, seed=7 * N + d)
+    ref = O.quant_mxfp4(q, k, v, smooth=not flags)
+    qd, kd, vd = _dev(q, k, v)
+    got = sa.sage_quant_mxfp4(qd, kd, vd, flags=flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(got["q_fp4"].cpu().numpy(), O.pack_fp4(ref["q_codes"]))
+    assert np.array_equal(got["k_fp4"].cpu().numpy(), O.pack_fp4(ref["k_codes"]))
+    assert np.array_equal(got["q_e8m0"].cpu().numpy(), ref["q_e8m0"])
+    assert np.array_equal(got["k_e8m0"].cpu().numpy(), ref["k_e8m0"])
+    Nv = -(-N // 32) * 32
+    vcodes = np.zeros((B, H, Nv, d), np.uint8)
+    vcodes[:, :, :N] = ref["v_codes"]
+    assert np.array_equal(got["vt_fp4"].cpu().numpy(), O.pack_fp4(np.swapaxes(vcodes, 2, 3)))
+    assert np.array_equal(got["vt_e8m0"].cpu().numpy(), np.swapaxes(ref["v_e8m0"], 2, 3))
+
+
+ATTN_CASES = [
+    # B, H, N, d, causal, mode, dist
+    (1, 2, 256, 64, False, 1, "normal"),       # the tiny workload's shape
+    (1, 2, 1000, 128, False, 0, "normal"),
+    (1, 2, 1000, 128, True, 0, "normal"),
+    (2, 2, 777, 64, False, 0, "student_t"),
+    (1, 2, 777, 64, True, 1, "normal"),
+    (1, 1, 1, 128, False, 0, "normal"),
+    (1, 1, 1, 64, True, 0, "normal"),
+    (1, 2, 300, 128, False, 3, "normal"),      # per-token scales
+    (1, 2, 300, 64, True, 3, "normal"),
+]
+
+
+def _int8_blocks(mode):
+    return {0: (128, 64), 1: (64, 64), 3: (1, 1)}[mode]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"-c{int(c[4])}-m{c[5]}")
+def test_int8_attention_matches_oracle(sa, case):
+    B, H, N, d, causal, mode, dist = case
+    say("int8 attention", case)
+    q, k, v = make_custom(B, H, N, d, seed=3 * N + d + mode, dist=dist)
+    sm = 1.0 / np.sqrt(d)
+    bq, bk = _int8_blocks(mode)
+    ref = O.int8_attention(q, k, v, causal=causal, sm_scale=sm, blk_q=bq, blk_k=bk)
+    qd, kd, vd = _dev(q, k, v)
+    out = sa.sage_attn_fwd(qd, kd, vd, causal=causal, sm_scale=sm, mode=mode)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = assert_output_parity(got, ref, what=f"int8 {case}")
+    ex = O.exact_attention(q, k, v, causal=causal, sm_scale=sm)
+    say(f"  max err vs oracle {err:.2e}; cos vs fp64 gpu {O.metrics(got, ex)['cos']:.6f} "
+        f"oracle {O.metrics(ref, ex)['cos']:.6f}")
+
+
+MXATTN_CASES = [
+    (1, 2, 256, 64, False),
+    (1, 2, 1000, 128, False),
+    (1, 2, 1000, 128, True),
+    (1, 2, 333, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", MXATTN_CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"-c{int(c[4])}")
+def test_mxfp4_attention_matches_oracle(sa, case):
+    B, H, N, d, causal = case
+    say("mxfp4 attention", case)
+    q, k, v = make_custom(B, H, N, d, seed=5 * N + d)
+    sm = 1.0 / np.sqrt(d)
+    ref = O.mxfp4_attention(q, k, v, causal=causal, sm_scale=sm)
+    qd, kd, vd = _dev(q, k, v)
+    out = sa.sage_attn_fwd(qd, kd, vd, causal=causal, sm_scale=sm, mode=2)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = assert_output_parity(got, ref, what=f"mxfp4 {case}")
+    ex = O.exact_attention(q, k, v, causal=causal, sm_scale=sm)
+    say(f"  max err vs oracle {err:.2e}; cos vs fp64 gpu {O.metrics(got, ex)['cos']:.6f} "
+        f"oracle {O.metrics(ref, ex)['cos']:.6f}")
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_prepare_compute_equals_fwd_and_is_deterministic(sa, mode):
+    say("determinism mode", mode)
+    q, k, v = make_custom(1, 2, 700, 128, seed=11)
+    qd, kd, vd = _dev(q, k, v)
+    a = sa.sage_attn_fwd(qd, kd, vd, causal=True, mode=mode)
+    b = sa.sage_attn_fwd(qd, kd, vd, causal=True, mode=mode)
+    ws = sa.make_workspace(1, 2, 700, 128, mode)
+    c = torch.empty_like(qd)
+    sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode)
+    sa.sage_attn_compute(c, ws, causal=True, mode=mode)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)

@@ -1,0 +1,199 @@
+"""Throughput bench of the quantized-attention forward pass on one MI355X.
+
+A step is one sage_attn_fwd call (K mean, quantization of Q and K, V layout or
+V quantization, fused attention kernel) over one synthetic workload whose
+inputs are already resident in HBM. `value` is attention TOPS: 4*B*H*N^2*d
+per step (halved when causal) divided by the step time.
+
+Default workload: LLM prefill, B=4, H=32, N=4096, d=128, non-causal, INT8
+Q/K with Q scale blocks of 128 tokens and K blocks of 64, FP16 P.V.
+--workload picks another: n16k (B=1, H=32, N=16384, d=128, the kernel
+throughput target shape), long_causal, video_dit, mxfp4, tiny.
+
+Also on the JSON line:
+  roofline      the fused attention kernel alone (sage_attn_compute), timed
+                with HIP events on the stream it runs on, against the dense
+                MFMA peak of its input type (INT8, or MXFP4); `traffic` comes
+                from committed rocprofv3 counter summaries taken on the
+                current kernel source, else null.
+  cpu_baseline  the CPU oracle (oracle.int8_attention / mxfp4_attention in
+                float64) timed on a bounded sample of the same workload
+                (whole heads) on one host thread.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published dense MFMA peaks (TOPS) and HBM bandwidth (GB/s)
+PEAK = {"int8": 5000.0, "fp16": 2500.0, "mxfp4": 10100.0}
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(name: str) -> str:
+    path = os.path.join(ROOT, "bit_quantized_attention_mean_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(tag: str, source: str):
+    """HBM bytes per launch from profiles/<tag>_traffic.json, if taken on this kernel source."""
+    path = os.path.join(PROFILES, f"{tag}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != kernel_source_hash(source):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def timed(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def cpu_baseline(name: str, budget_s: float = 12.0):
+    """The oracle on whole heads of the workload until ~budget_s of CPU time (1 thread)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from synthetic import WORKLOADS, make_inputs
+
+    w = WORKLOADS[name]
+    ops = 0.0
+    t_total = 0.0
+    heads = 0
+    with threadpool_limits(limits=1):
+        while t_total < budget_s and heads < w.B * w.H:
+            q, k, v = make_inputs(name, B=1, H=1, seed=1000 + heads)   # one head, same recipe
+            t0 = time.perf_counter()
+            if w.mode == "mxfp4":
+                O.mxfp4_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale)
+            else:
+                bq = 128 if w.mode == "int8_q128_k64" else 64
+                O.int8_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, blk_q=bq, blk_k=64)
+            t_total += time.perf_counter() - t0
+            ops += 4.0 * w.N * w.N * w.d / (2 if w.causal else 1)
+            heads += 1
+    return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{heads} whole head(s) of the {name} workload (N={w.N}, d={w.d}): "
+                      f"quantization + tiled fp64 emulation, {t_total:.1f} s on 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the whole hot path runs on a single MI355X "
+              f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_attention_mean_amd as sa
+    from synthetic import WORKLOADS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    mode = {"int8_q128_k64": 0, "int8_q64_k64": 1, "mxfp4": 2}[w.mode]
+    t0 = time.perf_counter()
+    q, k, v = make_inputs(w.name)
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    del q, k, v
+    ws = sa.make_workspace(w.B, w.H, w.N, w.d, mode, dev)
+    out = torch.empty_like(qd)
+    log(f"[bench] {w.name}: inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    # whole step
+    step = lambda: sa.sage_attn_fwd(qd, kd, vd, out, causal=w.causal, sm_scale=w.sm_scale, mode=mode, workspace=ws)
+    ms_step, wall_step = timed(step, args.steps, args.warmup, torch)
+    # the two phases separately
+    prep = lambda: sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode)
+    ms_prep, _ = timed(prep, args.steps, args.warmup, torch)
+    comp = lambda: sa.sage_attn_compute(out, ws, causal=w.causal, sm_scale=w.sm_scale, mode=mode)
+    ms_attn, _ = timed(comp, args.steps, args.warmup, torch)
+    log(f"[bench] {w.name}: step {ms_step:.4f} ms (wall {wall_step:.4f}), attention kernel {ms_attn:.4f} ms, "
+        f"quantization phase {ms_prep:.4f} ms")
+
+    ops = w.attention_ops()
+    tops_step = ops / (ms_step * 1e-3) / 1e12
+    tops_attn = ops / (ms_attn * 1e-3) / 1e12
+    n_el = w.B * w.H * w.N * w.d
+    if mode == 2:
+        # read K (mean), Q, K, V (2 B each); write packed codes (0.5 B) + exponents (1/32 B) x3
+        quant_bytes = n_el * 8 + 3 * n_el * (0.5 + 1 / 32)
+        peak, kernel, src = PEAK["mxfp4"], f"attn_mxfp4_kernel<{w.d},{str(w.causal).lower()}>", "attn_mxfp4.hip"
+    else:
+        # read K (mean), Q, K, V (2 B each); write Q/K codes (1 B each) and V^T (2 B)
+        quant_bytes = n_el * 8 + n_el * 4
+        peak, kernel, src = PEAK["int8"], f"attn_int8_kernel<{w.d},{str(w.causal).lower()},false>", "attn_int8.hip"
+    roofline = {"bound": "mfma", "achieved": round(tops_attn, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tops_attn / peak, 4), "traffic": load_traffic(f"{src[:-4]}_{w.name}", src),
+                "kernel": kernel, "kernel_ms": round(ms_attn, 4)}
+    if mode != 2:
+        roofline["mixed_int8_fp16_peak"] = round(2 / (1 / PEAK["int8"] + 1 / PEAK["fp16"]), 1)
+    del qd, kd, vd, ws, out
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w.name)
+        log(f"[bench] cpu oracle: {cpu['value']:.3e} TOPS")
+
+    line = {
+        "metric": "attention TOPS (4*B*H*N^2*d per step / step time, halved if causal)",
+        "value": round(tops_step, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4" if mode == 2 else "int8+f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "mode": w.mode, "global_batch": w.B, "seq_len": w.N},
+        "attn_kernel_ms": round(ms_attn, 4),
+        "attn_kernel_tops": round(tops_attn, 2),
+        "quant_phase_ms": round(ms_prep, 4),
+        "quant_phase_gbs": round(quant_bytes / (ms_prep * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

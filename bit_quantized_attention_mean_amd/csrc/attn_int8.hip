@@ -27,11 +27,20 @@
 //     masking runs only on tiles that cross the diagonal or the ragged tail.
 #include "sage_internal.h"
 
+#include <limits.h>
 #include <math.h>
 
 namespace sage {
 
 namespace {
+
+// The softmax reference max of a row moves only when a tile's row max exceeds
+// it by more than this (log2 units), so P <= 2^8 and the O rescale is skipped
+// on most tiles; the result is the same softmax, rounded at a different point.
+constexpr float kRefSlack = 8.0f;
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+constexpr v2h kOnes2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 
 // LDS row (0..63) holding key k of a 64-key tile. Row t*32 + r feeds row r of
 // score MFMA t; its accumulator register i of lane group g is row
@@ -45,6 +54,10 @@ __device__ __forceinline__ int lds_row_of_key(int k) {
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int pair_max_i(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+  return max(static_cast<int>(r[0]), static_cast<int>(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -75,26 +88,30 @@ __device__ __forceinline__ void map_workgroup(int bid, int BH, int nqt, bool cau
 }  // namespace
 
 template <int D, bool CAUSAL, bool PERTOK>
-__global__ __launch_bounds__(256, 2) void attn_int8_kernel(
+__global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     const int8_t* __restrict__ qc, const int8_t* __restrict__ kc, const _Float16* __restrict__ vt,
     const float* __restrict__ qs, const float* __restrict__ ks, _Float16* __restrict__ out, int N,
     int Npad, int qblk, float sl2, int BH) {
-  constexpr int NC = D / 32;            // 32-channel chunks of the score contraction
-  constexpr int KROW = D + 16;          // LDS bytes per K row (16 bytes of padding)
-  constexpr int VROW = kKTile * 2 + 16; // LDS bytes per V^T row
+  constexpr int NC = D / 32;             // 32-channel chunks of the score contraction
+  constexpr int KROW = D + 16;           // LDS bytes per K row (16 bytes of padding)
+  constexpr int VROW = kKTile * 2 + 16;  // LDS bytes per V^T row
   constexpr int KT_BYTES = kKTile * KROW;
   constexpr int VT_BYTES = D * VROW;
-  constexpr int BUF = KT_BYTES + VT_BYTES;
-  constexpr int KCH = kKTile * D / 16 / 256;  // 16-byte K chunks per thread per tile
-  constexpr int VCH = D * 8 / 256;            // 16-byte V^T chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+  constexpr int KB0 = 0, KB1 = KT_BYTES, VB0 = 2 * KT_BYTES, VB1 = 2 * KT_BYTES + VT_BYTES;
+  constexpr int KCHN = kKTile * D / 16;  // 16-byte chunks of a K tile
+  constexpr int VCHN = D * 8;            // 16-byte chunks of a V^T tile
+  constexpr int VPT = (VCHN + 511) / 512;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KT_BYTES + 2 * VT_BYTES];
 
-  const int nqt = Npad / kQTile;
+  const int nqt = Npad / kWGQ;
   int bh, qt;
   map_workgroup(blockIdx.x, BH, nqt, CAUSAL, bh, qt);
-  const int q0 = qt * kQTile;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const int qrow = q0 + wave * 32 + l32;
+  const int q0 = qt * kWGQ;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;                     // 0 or 1: which half of the ping-pong
+  const int wrow0 = q0 + grp * 128 + (wave & 3) * 32;   // first query row of this wave
+  const int qrow = wrow0 + l32;
 
   // Q codes of this lane's query: the B operand of the score MFMAs, kept in registers.
   v4i qf[NC];
@@ -105,155 +122,265 @@ __global__ __launch_bounds__(256, 2) void attn_int8_kernel(
   }
   // Q scale: one per block of qblk rows (a wave never straddles two), or per row.
   const int nqs = Npad / qblk;
-  const float sq = qs[static_cast<size_t>(bh) * nqs + (PERTOK ? qrow : (q0 + wave * 32) / qblk)];
+  const float sq = qs[static_cast<size_t>(bh) * nqs + (PERTOK ? qrow : wrow0 / qblk)];
   // K scale: one per 64-key block (= one key tile), or one per key.
   const int nks = PERTOK ? Npad : Npad / kKTile;
   const float* ksh = ks + static_cast<size_t>(bh) * nks;
 
   int nkt = (N + kKTile - 1) / kKTile;
-  if (CAUSAL) nkt = min(nkt, (q0 + kQTile) / kKTile);
+  if (CAUSAL) nkt = min(nkt, (q0 + kWGQ) / kKTile);
 
   const int8_t* kbase = kc + static_cast<size_t>(bh) * Npad * D;
   const _Float16* vbase = vt + static_cast<size_t>(bh) * D * Npad;
-  // Global -> register staging of one key tile (K codes and V^T), then
-  // register -> LDS. The K rows go to their permuted LDS rows. (Arrays of
-  // scalars, not of uint4, so the compiler keeps them in registers.)
-  unsigned kr[4 * KCH], vr[4 * VCH];
-#define SAGE_GLOAD(J_)                                                                               \
-  do {                                                                                               \
-    _Pragma("unroll") for (int u = 0; u < KCH; ++u) {                                                \
-      const int i_ = tid + 256 * u, row_ = i_ / (D / 16), col_ = i_ % (D / 16);                      \
-      const uint4 t_ = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>((J_) * kKTile + row_) * D + \
-                                                       col_ * 16);                                   \
-      kr[4 * u] = t_.x; kr[4 * u + 1] = t_.y; kr[4 * u + 2] = t_.z; kr[4 * u + 3] = t_.w;           \
-    }                                                                                                \
-    _Pragma("unroll") for (int u = 0; u < VCH; ++u) {                                                \
-      const int i_ = tid + 256 * u, row_ = i_ >> 3, col_ = i_ & 7;                                   \
-      const uint4 t_ = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(row_) * Npad +    \
-                                                       (J_) * kKTile + col_ * 8);                    \
-      vr[4 * u] = t_.x; vr[4 * u + 1] = t_.y; vr[4 * u + 2] = t_.z; vr[4 * u + 3] = t_.w;           \
-    }                                                                                                \
-  } while (0)
-#define SAGE_SWRITE(BUF_)                                                                            \
-  do {                                                                                               \
-    unsigned char* kt_ = smem + (BUF_) * BUF;                                                        \
-    unsigned char* vl_ = kt_ + KT_BYTES;                                                             \
-    _Pragma("unroll") for (int u = 0; u < KCH; ++u) {                                                \
-      const int i_ = tid + 256 * u, row_ = i_ / (D / 16), col_ = i_ % (D / 16);                      \
-      *reinterpret_cast<uint4*>(kt_ + lds_row_of_key(row_) * KROW + col_ * 16) =                     \
-          make_uint4(kr[4 * u], kr[4 * u + 1], kr[4 * u + 2], kr[4 * u + 3]);                        \
-    }                                                                                                \
-    _Pragma("unroll") for (int u = 0; u < VCH; ++u) {                                                \
-      const int i_ = tid + 256 * u, row_ = i_ >> 3, col_ = i_ & 7;                                   \
-      *reinterpret_cast<uint4*>(vl_ + row_ * VROW + col_ * 16) =                                     \
-          make_uint4(vr[4 * u], vr[4 * u + 1], vr[4 * u + 2], vr[4 * u + 3]);                        \
-    }                                                                                                \
-  } while (0)
+
+  // Loading: every thread moves at most one 16-byte K chunk and VPT V^T chunks
+  // per tile, global -> registers at the start of a period, registers -> LDS
+  // at its end. K rows go to their permuted LDS rows.
+  const bool kload = tid < KCHN;
+  int kg = 0, kl = 0;
+  {
+    const int row = tid / (D / 16), col = tid % (D / 16);
+    kg = row * D + col * 16;
+    kl = lds_row_of_key(row) * KROW + col * 16;
+  }
+  int vg[VPT], vls[VPT];
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int i = tid + 512 * u, row = i >> 3, col = i & 7;
+    vg[u] = row * Npad + col * 8;
+    vls[u] = row * VROW + col * 16;
+  }
+  const bool vload_last = (tid + 512 * (VPT - 1)) < VCHN;
+  unsigned kr[4], vr[4 * VPT];
+  const int ka = l32 * KROW + g * 16;   // score A operand: K row l32 of each 32-key half
+  const int va = l32 * VROW + g * 64;   // P.V A operand: V^T row l32 of each 32-channel tile
 
   v16f o[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[c][i] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f, alpha = 1.f;
+  v16i s[2];
+  v8h pf[4];
 
-  SAGE_GLOAD(0);
-  SAGE_SWRITE(0);
-  __syncthreads();
-
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkt) SAGE_GLOAD(j + 1);
-    const unsigned char* kt = smem + buf * BUF;
-    const unsigned char* vl = kt + KT_BYTES;
-
-    // S^T = K Q^T for keys j*64 .. j*64+63 (two 32-key halves t)
-    v16i s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[t][i] = 0;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const v4i a = *reinterpret_cast<const v4i*>(kt + (t * 32 + l32) * KROW + c * 32 + g * 16);
-        s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[c], s[t], 0, 0, 0);
-      }
-    }
-
-    // dequantize into base-2 logits; p[t*16+i] is key j*64 + g*32 + t*16 + i
-    float p[32];
-    if (PERTOK) {
-      const float sc = sq * sl2;
-      const float4* k4 = reinterpret_cast<const float4*>(ksh + j * kKTile + g * 32);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float4 kk = k4[u];
-        const int e = 4 * u;
-        p[e] = static_cast<float>(s[e >> 4][e & 15]) * sc * kk.x;
-        p[e + 1] = static_cast<float>(s[(e + 1) >> 4][(e + 1) & 15]) * sc * kk.y;
-        p[e + 2] = static_cast<float>(s[(e + 2) >> 4][(e + 2) & 15]) * sc * kk.z;
-        p[e + 3] = static_cast<float>(s[(e + 3) >> 4][(e + 3) & 15]) * sc * kk.w;
-      }
-    } else {
-      const float sc = sq * ksh[j] * sl2;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p[t * 16 + i] = static_cast<float>(s[t][i]) * sc;
-    }
-    const bool diag = CAUSAL && (j * kKTile + kKTile - 1 > q0 + wave * 32);
-    const bool tail = (j * kKTile + kKTile > N);
-    if (diag || tail) {
-      const int kb = j * kKTile + g * 32;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int key = kb + e;
-        if ((CAUSAL && key > qrow) || key >= N) p[e] = -INFINITY;
-      }
-    }
-
-    // online softmax (base 2)
-    float mx = p[0];
-#pragma unroll
-    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, p[e]);
-    mx = pair_max(mx);
-    const float mnew = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    float rs = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(p[e] - mnew);
-      rs += p[e];
-    }
-    l = l * alpha + rs;
-    m = mnew;
-
-    // P -> fp16 (RNE); pf[c] holds keys g*32 + c*8 .. +7
-    v8h pf[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[c][e] = static_cast<_Float16>(p[c * 8 + e]);
-
-    // O^T = alpha * O^T + V^T P^T
-    if (__ballot(alpha != 1.f)) {  // wave-uniform: skip when no row max moved
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[c][i] *= alpha;
-    }
-#pragma unroll
-    for (int dt = 0; dt < NC; ++dt) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const v8h a = *reinterpret_cast<const v8h*>(vl + (dt * 32 + l32) * VROW + (g * 32 + c * 8) * 2);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[c], o[dt], 0, 0, 0);
-      }
-    }
-
-    if (j + 1 < nkt) SAGE_SWRITE(buf ^ 1);
-    __syncthreads();
+#define SAGE_LOAD_K(J_)                                                                          \
+  if (kload) {                                                                                   \
+    const uint4 t_ = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(J_) * kKTile * D + kg); \
+    kr[0] = t_.x; kr[1] = t_.y; kr[2] = t_.z; kr[3] = t_.w;                                      \
   }
+#define SAGE_LOAD_V(J_)                                                                          \
+  _Pragma("unroll") for (int u = 0; u < VPT; ++u) {                                              \
+    if (u < VPT - 1 || vload_last) {                                                             \
+      const uint4 t_ = *reinterpret_cast<const uint4*>(vbase + (J_) * kKTile + vg[u]);           \
+      vr[4 * u] = t_.x; vr[4 * u + 1] = t_.y; vr[4 * u + 2] = t_.z; vr[4 * u + 3] = t_.w;       \
+    }                                                                                            \
+  }
+#define SAGE_STORE_K(KB_)                                                                        \
+  if (kload) *reinterpret_cast<uint4*>(smem + (KB_) + kl) = make_uint4(kr[0], kr[1], kr[2], kr[3]);
+#define SAGE_STORE_V(VB_)                                                                        \
+  _Pragma("unroll") for (int u = 0; u < VPT; ++u) {                                              \
+    if (u < VPT - 1 || vload_last)                                                               \
+      *reinterpret_cast<uint4*>(smem + (VB_) + vls[u]) =                                         \
+          make_uint4(vr[4 * u], vr[4 * u + 1], vr[4 * u + 2], vr[4 * u + 3]);                    \
+  }
+
+  // S^T = K Q^T for key tile J_ from the K buffer KB_ (INT8 MFMA, exact int32).
+  // All eight K operands are read up front so the matrix ops issue back to back.
+#define SAGE_SCORES(KB_)                                                                         \
+  do {                                                                                           \
+    v4i ka_[2 * NC];                                                                             \
+    _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
+      _Pragma("unroll") for (int c = 0; c < NC; ++c)                                             \
+        ka_[t * NC + c] = *reinterpret_cast<const v4i*>(smem + (KB_) + ka + t * 32 * KROW + c * 32); \
+    _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                              \
+      _Pragma("unroll") for (int i = 0; i < 16; ++i) s[t][i] = 0;                                \
+      _Pragma("unroll") for (int c = 0; c < NC; ++c)                                             \
+        s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka_[t * NC + c], qf[c], s[t], 0, 0, 0);    \
+    }                                                                                            \
+    /* issue order: 4 LDS reads ahead, then one read per matrix op */                           \
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);                                           \
+    _Pragma("unroll") for (int u = 0; u < 2 * NC - 4; ++u) {                                     \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);                                         \
+    }                                                                                            \
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);                                           \
+  } while (0)
+
+  // O^T = alpha * O^T + V^T P^T from the V buffer VB_ (FP16 MFMA, FP32
+  // accumulation). The rescale by the last softmax's alpha is done here, in the
+  // matrix phase, so the softmax phase never touches the O registers.
+#define SAGE_PV(VB_)                                                                             \
+  do {                                                                                           \
+    if (__ballot(alpha != 1.f)) {                                                                \
+      _Pragma("unroll") for (int c = 0; c < NC; ++c)                                             \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) o[c][i] *= alpha;                         \
+    }                                                                                            \
+    v8h va_[2][4];                                                                               \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                \
+      va_[0][c] = *reinterpret_cast<const v8h*>(smem + (VB_) + va + c * 16);                     \
+    _Pragma("unroll") for (int dt = 0; dt < NC; ++dt) {                                          \
+      if (dt + 1 < NC) {                                                                         \
+        _Pragma("unroll") for (int c = 0; c < 4; ++c)                                            \
+          va_[(dt + 1) & 1][c] =                                                                 \
+              *reinterpret_cast<const v8h*>(smem + (VB_) + va + (dt + 1) * 32 * VROW + c * 16);  \
+      }                                                                                          \
+      _Pragma("unroll") for (int c = 0; c < 4; ++c)                                              \
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va_[dt & 1][c], pf[c], o[dt], 0, 0, 0);   \
+    }                                                                                            \
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);                                           \
+    _Pragma("unroll") for (int u = 0; u < 4 * NC - 4; ++u) {                                     \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);                                         \
+    }                                                                                            \
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);                                           \
+  } while (0)
+
+  // Softmax of key tile J_ on the scores in s: dequantize to base-2 logits,
+  // mask, move the reference max if needed (rescaling l now and O in the next
+  // P.V), P = exp2(S - m), row sum, P -> fp16 in pf (keys g*32 + c*8 .. +7 in pf[c]).
+#define SAGE_SOFTMAX(J_)                                                                         \
+  do {                                                                                           \
+    const int j_ = (J_);                                                                         \
+    const bool masked_ = (CAUSAL && (j_ * kKTile + kKTile - 1 > wrow0)) || (j_ * kKTile + kKTile > N); \
+    const int kb_ = j_ * kKTile + g * 32;                                                        \
+    float p[32];                                                                                 \
+    float mt_, mnew_;                                                                            \
+    bool need_;                                                                                  \
+    if (PERTOK) {                                                                                \
+      const float scq_ = sq * sl2;                                                               \
+      const float4* k4_ = reinterpret_cast<const float4*>(ksh + kb_);                            \
+      _Pragma("unroll") for (int u = 0; u < 8; ++u) {                                            \
+        const float4 kk_ = k4_[u];                                                               \
+        const float kv_[4] = {kk_.x, kk_.y, kk_.z, kk_.w};                                       \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                          \
+          const int e = 4 * u + r;                                                               \
+          p[e] = static_cast<float>(s[e >> 4][e & 15]) * scq_ * kv_[r];                          \
+        }                                                                                        \
+      }                                                                                          \
+      if (masked_) {                                                                             \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
+          const int key = kb_ + e;                                                               \
+          if ((CAUSAL && key > qrow) || key >= N) p[e] = -INFINITY;                              \
+        }                                                                                        \
+      }                                                                                          \
+      float mx_ = p[0];                                                                          \
+      _Pragma("unroll") for (int e = 1; e < 32; ++e) mx_ = fmaxf(mx_, p[e]);                     \
+      mt_ = pair_max(mx_);                                                                       \
+      need_ = mt_ > m + kRefSlack;                                                               \
+      mnew_ = need_ ? mt_ : m;                                                                   \
+      _Pragma("unroll") for (int e = 0; e < 32; ++e) p[e] = __builtin_amdgcn_exp2f(p[e] - mnew_); \
+    } else {                                                                                     \
+      /* one scale per (query block, key tile): the max of the integer scores, */               \
+      /* scaled once, is the max of the dequantized scores (the scale is >= 0) */               \
+      const float sc_ = sq * ksh[j_] * sl2;                                                      \
+      if (masked_) {                                                                             \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
+          const int key = kb_ + e;                                                               \
+          if ((CAUSAL && key > qrow) || key >= N) s[e >> 4][e & 15] = INT_MIN;                   \
+        }                                                                                        \
+        int mi_ = s[0][0];                                                                       \
+        _Pragma("unroll") for (int e = 1; e < 32; ++e) mi_ = max(mi_, s[e >> 4][e & 15]);        \
+        mi_ = pair_max_i(mi_);                                                                   \
+        mt_ = (mi_ == INT_MIN) ? -INFINITY : static_cast<float>(mi_) * sc_;                      \
+        need_ = mt_ > m + kRefSlack;                                                             \
+        mnew_ = need_ ? mt_ : m;                                                                 \
+        const float nm_ = -mnew_;                                                                \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
+          const float x_ = __builtin_fmaf(static_cast<float>(s[e >> 4][e & 15]), sc_, nm_);     \
+          p[e] = (s[e >> 4][e & 15] == INT_MIN) ? 0.f : __builtin_amdgcn_exp2f(x_);             \
+        }                                                                                        \
+      } else {                                                                                   \
+        int mi_ = s[0][0];                                                                       \
+        _Pragma("unroll") for (int e = 1; e < 32; ++e) mi_ = max(mi_, s[e >> 4][e & 15]);        \
+        mi_ = pair_max_i(mi_);                                                                   \
+        mt_ = static_cast<float>(mi_) * sc_;                                                     \
+        need_ = mt_ > m + kRefSlack;                                                             \
+        mnew_ = need_ ? mt_ : m;                                                                 \
+        const float nm_ = -mnew_;                                                                \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e)                                           \
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[e >> 4][e & 15]), sc_, nm_)); \
+      }                                                                                          \
+    }                                                                                            \
+    const float alpha_ = need_ ? __builtin_amdgcn_exp2f(m - mnew_) : 1.f;                       \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) pf[c][e] = static_cast<_Float16>(p[c * 8 + e]); \
+    /* row sum of the fp16 P that multiplies V: two products per v_dot2_f32_f16 */              \
+    float rs0_ = 0.f, rs1_ = 0.f;                                                                \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                \
+      _Pragma("unroll") for (int e = 0; e < 8; e += 4) {                                         \
+        rs0_ = __builtin_amdgcn_fdot2(v2h{pf[c][e], pf[c][e + 1]}, kOnes2, rs0_, false);        \
+        rs1_ = __builtin_amdgcn_fdot2(v2h{pf[c][e + 2], pf[c][e + 3]}, kOnes2, rs1_, false);    \
+      }                                                                                          \
+    l = l * alpha_ + (rs0_ + rs1_);                                                              \
+    m = mnew_;                                                                                   \
+    alpha = alpha_;                                                                              \
+  } while (0)
+
+  // One period of the ping-pong. Key tile jp_ is in K buffer KB_, tile jp_-1
+  // in V buffer VBP_ (buffer offsets are per-period values; every LDS access
+  // is a per-period base plus an immediate). Phase A: group 0 runs its matrix
+  // ops (P.V of tile jp_-1, scores of tile jp_) while group 1 runs its softmax
+  // of tile jp_-1; phase B swaps the roles. Tiles jp_+1 (K, clamped to the
+  // last tile) and jp_ (V) are staged meanwhile into the free buffers KBN_ and
+  // VBC_. The first (jp_ = 0) and last (jp_ = nkt) periods are peeled, so the
+  // steady-state loop has no conditional work and no register copies.
+#define SAGE_PHASE_MATRIX(HAS_PV_, HAS_K_, KB_, VBP_)                                                     \
+  __builtin_amdgcn_s_setprio(1);                                                                 \
+  if (HAS_PV_) { SAGE_PV(VBP_); }                                                                \
+  __builtin_amdgcn_sched_barrier(0);                                                             \
+  if (HAS_K_) { SAGE_SCORES(KB_); }                                                              \
+  __builtin_amdgcn_s_setprio(0);
+#define SAGE_PERIOD(J_, KB_, KBN_, VBC_, VBP_, FIRST_, LAST_)                                    \
+  do {                                                                                           \
+    const int jp_ = (J_);                                                                        \
+    if (!(LAST_)) {                                                                              \
+      SAGE_LOAD_K(min(jp_ + 1, nkt - 1))                                                         \
+      SAGE_LOAD_V(jp_)                                                                           \
+    }                                                                                            \
+    if (grp == 0) {                                                                              \
+      SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), KB_, VBP_)                                          \
+    } else if (!(FIRST_)) {                                                                      \
+      SAGE_SOFTMAX(jp_ - 1);                                                                     \
+    }                                                                                            \
+    __syncthreads();                                                                             \
+    if (grp == 1) {                                                                              \
+      SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), KB_, VBP_)                                          \
+    } else if (!(LAST_)) {                                                                       \
+      SAGE_SOFTMAX(jp_);                                                                         \
+    }                                                                                            \
+    if (!(LAST_)) {                                                                              \
+      SAGE_STORE_K(KBN_)                                                                         \
+      SAGE_STORE_V(VBC_)                                                                         \
+    }                                                                                            \
+    __syncthreads();                                                                             \
+  } while (0)
+
+  SAGE_LOAD_K(0)
+  SAGE_STORE_K(KB0)
+  // Drain every outstanding load here (Q fragments included): otherwise the
+  // counter-based waits inside the loop cannot tell the Q loads are done and
+  // wait on the tile prefetch before each period's score MFMAs.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  SAGE_PERIOD(0, KB0, KB1, VB0, VB1, true, false);
+  for (int jt = 1; jt < nkt; ++jt) {
+    const int odd = jt & 1;
+    SAGE_PERIOD(jt, odd ? KB1 : KB0, odd ? KB0 : KB1, odd ? VB1 : VB0, odd ? VB0 : VB1, false, false);
+  }
+  {
+    const int odd = nkt & 1;
+    SAGE_PERIOD(nkt, odd ? KB1 : KB0, odd ? KB0 : KB1, odd ? VB1 : VB0, odd ? VB0 : VB1, false, true);
+  }
+#undef SAGE_PHASE_MATRIX
+#undef SAGE_PERIOD
+#undef SAGE_SOFTMAX
+#undef SAGE_PV
+#undef SAGE_SCORES
+#undef SAGE_STORE_V
+#undef SAGE_STORE_K
+#undef SAGE_LOAD_V
+#undef SAGE_LOAD_K
 
   // epilogue: O = O^T / l, rows >= N are padding and are not stored
   const float inv = 1.f / pair_sum(l);
@@ -271,13 +398,10 @@ __global__ __launch_bounds__(256, 2) void attn_int8_kernel(
   }
 }
 
-#undef SAGE_GLOAD
-#undef SAGE_SWRITE
-
 hipError_t launch_attn_int8(const AttnArgs& a, const int8_t* qc, const int8_t* kc, const void* vt,
                             const float* qs, const float* ks, hipStream_t s) {
-  const int nqt = a.Npad / kQTile;
-  const dim3 grid(a.BH * nqt), block(256);
+  const int nqt = a.Npad / kWGQ;
+  const dim3 grid(a.BH * nqt), block(512);
   const int qblk = (a.mode == 0) ? 128 : (a.mode == 1 ? 64 : 1);
   const bool pt = (a.mode == 3);
   const auto* v = static_cast<const _Float16*>(vt);

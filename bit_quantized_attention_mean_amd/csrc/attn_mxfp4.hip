@@ -22,6 +22,9 @@ namespace sage {
 
 namespace {
 
+// Reference-max slack of the online softmax (log2 units), as in the INT8 kernel.
+constexpr float kRefSlack4 = 8.0f;
+
 __device__ __forceinline__ int lds_row_of_key4(int k) {
   const int g = k >> 5, t = (k >> 4) & 1, i = k & 15;
   return t * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
@@ -204,8 +207,9 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
 #pragma unroll
     for (int e = 1; e < 32; ++e) mx = fmaxf(mx, p[e]);
     mx = pair_max4(mx);
-    const float mnew = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    const bool need = mx > m + kRefSlack4;
+    const float mnew = need ? mx : m;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
     float rs = 0.f, pmax = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
       pq[w] = static_cast<int>(r);
     }
 
-    if (__ballot(alpha != 1.f)) {
+    if (__ballot(need)) {
 #pragma unroll
       for (int c = 0; c < NT; ++c)
 #pragma unroll

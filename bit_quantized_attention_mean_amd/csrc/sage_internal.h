@@ -16,12 +16,14 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
-// Query rows per attention workgroup and keys per key tile. Every per-head
-// row count in the workspace is padded to a multiple of kRowPad, with zero
-// rows, so the attention kernel's tile loads never need bounds checks.
+// Rows per quantization tile (and per MXFP4 attention workgroup), query rows
+// per INT8 attention workgroup, and keys per key tile. Every per-head row
+// count in the workspace is padded to a multiple of kRowPad, with zero rows,
+// so the attention kernels' tile loads never need bounds checks.
 constexpr int kQTile = 128;
+constexpr int kWGQ = 256;
 constexpr int kKTile = 64;
-constexpr int kRowPad = 128;
+constexpr int kRowPad = 256;
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 

@@ -41,9 +41,15 @@ Readings where the pages are silent (each also listed in the design doc):
   R4 INT8 code: rint_half_even(fp32(x / s)), clamp [-127, 127]; a = 0 gives
      s = 0 and all codes 0.
   R5 sm_scale is applied at dequantization, not folded into Q.
-  R6 online softmax over key tiles of `kv_tile` keys in ascending order; P is
-     formed against the running max; P16 = fp16_RNE(P); the row sum l uses the
-     unrounded P; O accumulates P16 . V.
+  R6 online softmax over key tiles of `kv_tile` keys in ascending order. P is
+     formed against a per-row reference max m that follows the running max
+     lazily: m moves to the tile's row max only when that exceeds m by more
+     than `ref_slack` (in log2 units; 8 by default, 0 = the plain running max),
+     so P <= 2^8. Any reference point gives the same softmax; this one only
+     fixes where P is rounded. P16 = fp16_RNE(P); O accumulates P16 . V and
+     the row sum l accumulates the same P16 (so O is an exact weighted mean of
+     V rows up to accumulation rounding). In the MXFP4 path l sums the
+     unquantized P.
   R7 causal: key j is masked for query i when j > i (N_q = N_k).
   R8 MX blocks: 32 contiguous elements along the contraction dimension (d for
      Q and K_s; tokens, per channel, for V; keys, per query row inside a key
@@ -169,42 +175,49 @@ def quant_qk_int8(q16, k16, *, blk_q: int, blk_k: int, smooth: bool = True):
     return dict(q_codes=qc, q_scales=qs, k_codes=kc, k_scales=kscl, k_mean=mu)
 
 
-def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, valid=None):
+REF_SLACK = 8.0   # log2 units by which the tile max may exceed the reference max (reading R6)
+
+
+def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, ref_slack: float = REF_SLACK,
+                      sum_rounded: bool = False):
     """FlashAttention-2 style online softmax and P.V over key tiles ([SA-Setup]).
 
     S: float64 scores [R, N] (already scaled, -inf where masked).
     V: float64 values [N, d] (already in the precision P.V consumes).
     round_p(P_tile) -> the P that multiplies V (fp16 RNE for the INT8 path, the
     MX-quantized P for the FP4 path, identity for an exact run).
-    Reading R6: ascending tiles, P against the running max, l from unrounded P.
-    Returns O [R, d] float64.
+    Reading R6: ascending tiles, P against the lazily updated reference max;
+    l sums round_p(P) if sum_rounded else P. Returns O [R, d] float64.
     """
     R, N = S.shape
     d = V.shape[1]
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     O = np.zeros((R, d))
+    slack = ref_slack * math.log(2.0)
     for t0 in range(0, N, kv_tile):
         St = S[:, t0:t0 + kv_tile]
         with np.errstate(invalid="ignore"):
-            m_new = np.maximum(m, St.max(axis=1))
+            tmax = St.max(axis=1)
+            m_new = np.where(tmax > m + slack, tmax, m)
             # factor for what was accumulated under the old max (0 before any valid key)
             alpha = np.where(np.isneginf(m_new), 0.0, np.exp(m - m_new))
             P = np.where(np.isneginf(St), 0.0, np.exp(St - m_new[:, None]))
-        l = l * alpha + P.sum(axis=1)
-        O = O * alpha[:, None] + round_p(P) @ V[t0:t0 + kv_tile]
+        Pr = round_p(P)
+        l = l * alpha + (Pr if sum_rounded else P).sum(axis=1)
+        O = O * alpha[:, None] + Pr @ V[t0:t0 + kv_tile]
         m = m_new
     return O / l[:, None]
 
 
 def int8_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, blk_k: int,
                    kv_tile: int = 64, smooth: bool = True, rows=None, quantize: bool = True,
-                   quant=None):
+                   quant=None, ref_slack: float = REF_SLACK):
     """Emulated INT8 SageAttention forward ([SA-Approach], [SA-Summary]), float64 out.
 
     Steps: mu and K_s (R1, R2); per-block INT8 codes of Q and K_s (R3, R4);
     S_int = codes_q . codes_k^T exactly; S = S_int * s_q * s_k * sm_scale (R5);
-    causal mask (R7); online softmax with fp16 P and fp16 V (R6).
+    causal mask (R7); online softmax with fp16 P and fp16 V, l from the fp16 P (R6).
     quantize=False replaces every code by the unquantized value (scale 1) and
     P16 by P: the same tiled arithmetic then reduces to exact attention.
     `quant` may pass a precomputed quant_qk_int8 result.
@@ -233,7 +246,8 @@ def int8_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, 
                 S = (as_f64(q16[b, h, rows]) @ ks[b, h].astype(np.float64).T) * sm_scale
             if causal:
                 S[_causal_mask(rows, keys)] = -np.inf
-            out[b, h] = online_softmax_pv(S, as_f64(v16[b, h]), kv_tile=kv_tile, round_p=round16)
+            out[b, h] = online_softmax_pv(S, as_f64(v16[b, h]), kv_tile=kv_tile, round_p=round16,
+                                          ref_slack=ref_slack, sum_rounded=True)
     return out
 
 
@@ -324,7 +338,8 @@ def quant_mxfp4(q16, k16, v16, *, smooth: bool = True):
 
 
 def mxfp4_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: int = 64,
-                    smooth: bool = True, rows=None, quant=None, quantize_p: bool = True):
+                    smooth: bool = True, rows=None, quant=None, quantize_p: bool = True,
+                    ref_slack: float = REF_SLACK):
     """Emulated microscaled-FP4 attention ([SA3-Abstract] with the MX format, reading R8).
 
     Q, K_s, V and the softmax P are MXFP4; the scores are the exact products of
@@ -351,7 +366,8 @@ def mxfp4_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: in
             S = (qd["q_vals"][b, h, rows] @ qd["k_vals"][b, h].T) * sm_scale
             if causal:
                 S[_causal_mask(rows, keys)] = -np.inf
-            out[b, h] = online_softmax_pv(S, qd["v_vals"][b, h], kv_tile=kv_tile, round_p=round_p)
+            out[b, h] = online_softmax_pv(S, qd["v_vals"][b, h], kv_tile=kv_tile, round_p=round_p,
+                                          ref_slack=ref_slack)
     return out
 
 

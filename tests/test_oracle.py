@@ -241,10 +241,11 @@ def test_int8_emulation_tiling_changes_only_fp16_rounding():
 
 
 def test_int8_emulation_constant_v():
+    # l sums the same fp16 P that weights V, so a constant V comes back exactly
     q, k, _ = make_custom(1, 1, 200, 32, seed=5)
     v = np.full((1, 1, 200, 32), 1.5, np.float16)
     o = O.int8_attention(q, k, v, causal=True, sm_scale=0.2, blk_q=64, blk_k=64)
-    assert np.max(np.abs(o - 1.5)) <= 1.5 * 2 ** -10
+    assert np.max(np.abs(o - 1.5)) <= 1e-14
 
 
 def test_int8_rows_subset_matches_full():
@@ -425,3 +426,22 @@ def test_oracle_regression_fixture():
     with open(os.path.join(here, "tiny_oracle.json")) as f:
         stored = json.load(f)
     assert mg.build() == stored
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_max_slack_only_moves_rounding(causal):
+    # Softmax is invariant to the reference point: without P rounding, any slack gives the
+    # same output; with fp16 P, the slack only changes where P is rounded.
+    q, k, v = make_custom(1, 2, 300, 32, seed=21)
+    a = O.int8_attention(q, k, v, causal=causal, sm_scale=0.3, blk_q=64, blk_k=64, quantize=False, ref_slack=0.0)
+    b = O.int8_attention(q, k, v, causal=causal, sm_scale=0.3, blk_q=64, blk_k=64, quantize=False, ref_slack=8.0)
+    assert np.max(np.abs(a - b)) < 1e-12
+    c = O.int8_attention(q, k, v, causal=causal, sm_scale=0.3, blk_q=64, blk_k=64, ref_slack=0.0)
+    e = O.int8_attention(q, k, v, causal=causal, sm_scale=0.3, blk_q=64, blk_k=64, ref_slack=8.0)
+    assert 0 < np.max(np.abs(c - e)) < 2 ** -10 * np.abs(v.astype(float)).max()
+    # with slack 8 the reference max lags the running max by at most 8 (log2 units): P <= 2^8
+    S = np.array([[0.0, 1.0, 2.0, 3.0], [0.0, 0.0, 0.0, 10.0]]) * np.log(2.0)
+    V = np.eye(4)
+    seen = []
+    O.online_softmax_pv(S, V, kv_tile=1, round_p=lambda P: (seen.append(P.max()), P)[1], ref_slack=8.0)
+    assert abs(max(seen) - 8.0) < 1e-12   # row 0: the reference stays at 0 while the max climbs to 3

@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the whole hot path runs on a single MI355X "
@@ -117,6 +119,18 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        # A plain copy of 1 GiB (read 1 GiB, write 1 GiB per launch): the reference
+        # against which rocprofv3's FETCH_SIZE / WRITE_SIZE are scaled to bytes.
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}), flush=True)
+        return
 
     import bit_quantized_attention_mean_amd as sa
     from synthetic import WORKLOADS, make_inputs

@@ -7,22 +7,28 @@
 // setup: builds on FlashAttention-2 ... online softmax").
 //
 // Work decomposition
-//   * one workgroup = 4 waves = 128 query rows of one head; wave w owns rows
-//     q0 + 32w .. q0 + 32w + 31; key tiles of 64 keys are staged in LDS
-//     (double-buffered) and shared by the 4 waves.
+//   * one workgroup = 8 waves = 256 query rows of one head, in two groups of
+//     4 waves (128 rows each; one Q scale block). Waves w and w + 4 share a
+//     SIMD. The groups alternate phases ("ping-pong"): while one group runs
+//     its matrix ops for a key tile (P.V of the previous tile, then the scores
+//     of this one), the other runs its softmax on the VALU; a workgroup
+//     barrier separates the phases. 64-key tiles of K and V^T are staged in
+//     LDS (double-buffered) and shared by all 8 waves.
 //   * scores are computed transposed, S^T = K Q^T, on v_mfma_i32_32x32x32_i8:
 //     in the 32x32 accumulator layout every lane owns one query column
 //     (lane % 32) and 16 key rows, so the row max and row sum of the softmax
 //     are in-lane reductions plus one swap between lanes l and l + 32.
 //   * K rows are placed in LDS in a permuted order so that, after the score
 //     MFMA, lane group g = lane / 32 holds exactly keys g*32 .. g*32+31 of the
-//     tile, in order. Those fp32 values, rounded to fp16, are already the
-//     B operand of O^T = V^T P^T on v_mfma_f32_32x32x16_f16: no shuffle and no
-//     LDS round trip for P.
+//     tile, in order. Those values, rounded to fp16, are already the B operand
+//     of O^T = V^T P^T on v_mfma_f32_32x32x16_f16: no shuffle and no LDS round
+//     trip for P.
 //   * O^T accumulates in fp32 (CDNA4's FP16 matrix op accumulates in FP32; the
 //     page reports no accuracy difference between FP16 and FP32 accumulators).
-//   * softmax in base 2: the dequantization scale s_q * s_k * sm_scale * log2(e)
-//     is one fp32 multiply per score; P = exp2(S - m) on v_exp_f32.
+//   * softmax in base 2: the row max is taken on the integer scores, then one
+//     fma per score applies s_q * s_k * sm_scale * log2(e) and subtracts the
+//     reference max; P = exp2(.) on v_exp_f32; the reference max moves lazily
+//     (see kRefSlack); the row sum adds the fp16 P pairwise on v_dot2_f32_f16.
 //   * causal: key tiles wholly above the workgroup's last query are skipped;
 //     masking runs only on tiles that cross the diagonal or the ragged tail.
 #include "sage_internal.h"
@@ -364,10 +370,12 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   SAGE_PERIOD(0, KB0, KB1, VB0, VB1, true, false);
-  for (int jt = 1; jt < nkt; ++jt) {
-    const int odd = jt & 1;
-    SAGE_PERIOD(jt, odd ? KB1 : KB0, odd ? KB0 : KB1, odd ? VB1 : VB0, odd ? VB0 : VB1, false, false);
+  int jt = 1;
+  for (; jt + 1 < nkt; jt += 2) {
+    SAGE_PERIOD(jt, KB1, KB0, VB1, VB0, false, false);
+    SAGE_PERIOD(jt + 1, KB0, KB1, VB0, VB1, false, false);
   }
+  if (jt < nkt) SAGE_PERIOD(jt, KB1, KB0, VB1, VB0, false, false);
   {
     const int odd = nkt & 1;
     SAGE_PERIOD(nkt, odd ? KB1 : KB0, odd ? KB0 : KB1, odd ? VB1 : VB0, odd ? VB0 : VB1, false, true);

@@ -1,0 +1,95 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+Per workload: the whole quantization (K mean, codes, scales / MX codes and
+exponents) is compared with the oracle bit for bit over every element; the
+attention output is compared element by element on sampled query rows of two
+heads (first and last), which the oracle computes from that head alone (every
+quantity is per head). Rows: the first and last 64 (the ragged tail) and random
+rows in between.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from synthetic import WORKLOADS, make_inputs
+from _parity import assert_output_parity, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+MODES = {"int8_q128_k64": 0, "int8_q64_k64": 1, "mxfp4": 2}
+
+
+@pytest.fixture(scope="module")
+def sa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_attention_mean_amd as m
+    return m
+
+
+def _rows(N, rng, n=256):
+    fixed = np.unique(np.concatenate([np.arange(min(64, N)), np.arange(max(0, N - 64), N)]))
+    rest = np.setdiff1d(np.arange(N), fixed)
+    extra = rng.choice(rest, size=min(len(rest), n - len(fixed)), replace=False)
+    return np.sort(np.concatenate([fixed, extra])).astype(np.int64)
+
+
+@pytest.mark.parametrize("name", ["prefill", "long_causal", "video_dit", "n16k", "mxfp4"])
+def test_full_size_workload(sa, name):
+    w = WORKLOADS[name]
+    mode = MODES[w.mode]
+    say(f"full-size {name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} mode={w.mode}")
+    q, k, v = make_inputs(name)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+
+    # quantization: INT8 every element; MXFP4 every element of six sampled heads
+    # (quantization is per head; the oracle's brute-force E2M1 search over all
+    # 128 Mi elements per tensor would take minutes)
+    if mode == 2:
+        got = sa.sage_quant_mxfp4(qd, kd, vd)
+        torch.cuda.synchronize()
+        got = {key: val.cpu().numpy() for key, val in got.items()}
+        for (b, h) in [(0, 0), (0, w.H - 1), (1, 7), (2, 16), (w.B - 1, 3), (w.B - 1, w.H - 1)]:
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            ref = O.quant_mxfp4(q[sl], k[sl], v[sl])
+            assert np.array_equal(got["q_fp4"][sl], O.pack_fp4(ref["q_codes"]))
+            assert np.array_equal(got["k_fp4"][sl], O.pack_fp4(ref["k_codes"]))
+            assert np.array_equal(got["q_e8m0"][sl], ref["q_e8m0"])
+            assert np.array_equal(got["k_e8m0"][sl], ref["k_e8m0"])
+            assert np.array_equal(got["vt_e8m0"][sl], np.swapaxes(ref["v_e8m0"], 2, 3))
+            assert np.array_equal(got["vt_fp4"][sl], O.pack_fp4(np.swapaxes(ref["v_codes"], 2, 3)))
+            assert np.array_equal(got["k_mean"][sl], ref["k_mean"])
+        del ref
+    else:
+        bq = 128 if mode == 0 else 64
+        got = sa.sage_quant_qk(qd, kd, blk_q=bq, blk_k=64)
+        torch.cuda.synchronize()
+        ref = O.quant_qk_int8(q, k, blk_q=bq, blk_k=64)
+        assert np.array_equal(got["k_mean"].cpu().numpy().view(np.uint32), ref["k_mean"].view(np.uint32))
+        assert np.array_equal(got["q_scales"].cpu().numpy().view(np.uint32), ref["q_scales"].view(np.uint32))
+        assert np.array_equal(got["k_scales"].cpu().numpy().view(np.uint32), ref["k_scales"].view(np.uint32))
+        assert np.array_equal(got["q_codes"].cpu().numpy(), ref["q_codes"])
+        assert np.array_equal(got["k_codes"].cpu().numpy(), ref["k_codes"])
+        del ref
+    del got
+    say(f"  quantization bit-exact")
+
+    # attention, as bench.py runs it (workspace + current stream)
+    ws = sa.make_workspace(w.B, w.H, w.N, w.d, mode)
+    out = torch.empty_like(qd)
+    sa.sage_attn_fwd(qd, kd, vd, out, causal=w.causal, sm_scale=w.sm_scale, mode=mode, workspace=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(99)
+    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+        rows = _rows(w.N, rng)
+        qs, ks, vs = (x[b:b + 1, h:h + 1] for x in (q, k, v))
+        if mode == 2:
+            ref = O.mxfp4_attention(qs, ks, vs, causal=w.causal, sm_scale=w.sm_scale, rows=rows)
+        else:
+            bq = 128 if mode == 0 else 64
+            ref = O.int8_attention(qs, ks, vs, causal=w.causal, sm_scale=w.sm_scale, blk_q=bq, blk_k=64, rows=rows)
+        err = assert_output_parity(got[b, h, rows], ref[0, 0], what=f"{name} head ({b},{h})")
+        say(f"  head ({b},{h}): {rows.size} rows, max |gpu - oracle| = {err:.2e}")

@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--mode", default=None, choices=["int8_q128_k64", "int8_q64_k64", "int8_per_token", "mxfp4"],
+                    help="override the workload's quantization mode (ablations)")
+    ap.add_argument("--no-smooth", action="store_true", help="skip the K mean subtraction (ablation)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
@@ -138,22 +141,25 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload]
-    mode = {"int8_q128_k64": 0, "int8_q64_k64": 1, "mxfp4": 2}[w.mode]
+    mode_name = args.mode or w.mode
+    mode = {"int8_q128_k64": 0, "int8_q64_k64": 1, "mxfp4": 2, "int8_per_token": 3}[mode_name]
+    flags = sa.SAGE_FLAG_NO_SMOOTH if args.no_smooth else 0
     t0 = time.perf_counter()
     q, k, v = make_inputs(w.name)
     qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
     del q, k, v
-    ws = sa.make_workspace(w.B, w.H, w.N, w.d, mode, dev)
+    ws = sa.make_workspace(w.B, w.H, w.N, w.d, mode | flags, dev)
     out = torch.empty_like(qd)
     log(f"[bench] {w.name}: inputs ready in {time.perf_counter() - t0:.1f} s")
 
     # whole step
-    step = lambda: sa.sage_attn_fwd(qd, kd, vd, out, causal=w.causal, sm_scale=w.sm_scale, mode=mode, workspace=ws)
+    step = lambda: sa.sage_attn_fwd(qd, kd, vd, out, causal=w.causal, sm_scale=w.sm_scale, mode=mode | flags,
+                                    workspace=ws)
     ms_step, wall_step = timed(step, args.steps, args.warmup, torch)
     # the two phases separately
-    prep = lambda: sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode)
+    prep = lambda: sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode | flags)
     ms_prep, _ = timed(prep, args.steps, args.warmup, torch)
-    comp = lambda: sa.sage_attn_compute(out, ws, causal=w.causal, sm_scale=w.sm_scale, mode=mode)
+    comp = lambda: sa.sage_attn_compute(out, ws, causal=w.causal, sm_scale=w.sm_scale, mode=mode | flags)
     ms_attn, _ = timed(comp, args.steps, args.warmup, torch)
     log(f"[bench] {w.name}: step {ms_step:.4f} ms (wall {wall_step:.4f}), attention kernel {ms_attn:.4f} ms, "
         f"quantization phase {ms_prep:.4f} ms")
@@ -169,9 +175,11 @@ def main():
     else:
         # read K (mean), Q, K, V (2 B each); write Q/K codes (1 B each) and V^T (2 B)
         quant_bytes = n_el * 8 + n_el * 4
-        peak, kernel, src = PEAK["int8"], f"attn_int8_kernel<{w.d},{str(w.causal).lower()},false>", "attn_int8.hip"
+        peak, src = PEAK["int8"], "attn_int8.hip"
+        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},{str(mode == 3).lower()}>"
     roofline = {"bound": "mfma", "achieved": round(tops_attn, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(tops_attn / peak, 4), "traffic": load_traffic(f"{src[:-4]}_{w.name}", src),
+                "frac": round(tops_attn / peak, 4),
+                "traffic": load_traffic(f"{src[:-4]}_{w.name}", src) if (mode_name == w.mode and not flags) else None,
                 "kernel": kernel, "kernel_ms": round(ms_attn, 4)}
     if mode != 2:
         roofline["mixed_int8_fp16_peak"] = round(2 / (1 / PEAK["int8"] + 1 / PEAK["fp16"]), 1)
@@ -198,7 +206,7 @@ def main():
         "dtype": "mxfp4" if mode == 2 else "int8+f16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "mode": w.mode, "global_batch": w.B, "seq_len": w.N},
+                   "mode": mode_name, "k_smoothing": not args.no_smooth, "global_batch": w.B, "seq_len": w.N},
         "attn_kernel_ms": round(ms_attn, 4),
         "attn_kernel_tops": round(tops_attn, 2),
         "quant_phase_ms": round(ms_prep, 4),

@@ -159,33 +159,69 @@ __global__ __launch_bounds__(256) void int8_quant_kernel(Int8Job j0, Int8Job j1,
     for (int p = 0; p < NP; ++p)
       if (cg == 0) rmax[p * RPP + rl] = lm[p];
     __syncthreads();
-    const int nb = kQTile / blk;
-    if (tid < nb) {
-      float m = 0.f;
-      for (int r = 0; r < blk; ++r) m = fmaxf(m, rmax[tid * blk + r]);
-      bmax[tid] = m;
+    // block maxima by one wave: lane i holds rows i and i + 64, then a
+    // butterfly over the lanes of each block (blk is a power of two)
+    if (tid < 64) {
+      float m0 = rmax[tid], m1 = rmax[tid + 64];
+      if (blk >= 128) m0 = m1 = fmaxf(m0, m1);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        if (off < blk) {
+          m0 = fmaxf(m0, __shfl_xor(m0, off, 64));
+          m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
+        }
+      }
+      if (tid % blk == 0) {
+        bmax[tid / blk] = m0;
+        if (blk < 128) bmax[(tid + 64) / blk] = m1;
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < NP; ++p) s[p] = bmax[(p * RPP + rl) / blk] / 127.0f;
   }
 
-  // codes
+  // codes. fp32(x / s) is formed without a division per element: with
+  // y = fp32(1 / s) (one IEEE division per row) and q0 = fp32(x * y), the
+  // remainder x - q0 * s is exact in one fma and q0 + r * y rounded once is the
+  // correctly rounded quotient (Markstein's correction step; its preconditions
+  // hold here: y is the rounded reciprocal of s, q0 is within one ulp, the
+  // quotient is at most 127 in magnitude, and with s >= 2^-60 every x whose
+  // code can be nonzero is far above the subnormal range, so the remainder is
+  // exact). Smaller scales take the plain division; s = 0 means an all-zero
+  // block and zero codes.
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int row = row0 + p * RPP + rl;
     if (row < J.code_rows) {
-      unsigned lo = 0, hi = 0;
+      const float sp = s[p];
+      // t = fp32(q + 1.5 * 2^23) rounds q to the nearest integer, ties to even
+      // (the sum lies in [2^23, 2^24), whose ulp is 1, and 1.5 * 2^23 is even),
+      // and the low byte of its bits is that integer as a two's complement
+      // int8. |q| <= 127 needs no clamp: q = x / s with |x| <= a and
+      // s = fp32(a / 127), so |q| <= 127 * (1 + 2^-24).
+      constexpr float kRound = 12582912.0f;
+      float t[8];
+      if (sp >= 0x1p-60f) {
+        const float y = 1.0f / sp;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int c = 0;
-        if (s[p] > 0.f) {
-          const float qv = __builtin_rintf(x[p][e] / s[p]);  // IEEE division, ties-to-even rounding
-          c = static_cast<int>(fminf(fmaxf(qv, -127.f), 127.f));
+        for (int e = 0; e < 8; ++e) {
+          const float q0 = x[p][e] * y;
+          const float r = __builtin_fmaf(-q0, sp, x[p][e]);
+          t[e] = __builtin_fmaf(r, y, q0) + kRound;
         }
-        const unsigned b = static_cast<unsigned>(c) & 0xffu;
-        if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (sp > 0.f ? x[p][e] / sp : 0.f) + kRound;
       }
+      unsigned w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = __float_as_uint(t[e]);
+      // byte e of the 8-byte code group = low byte of w[e]
+      const unsigned lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w[3], w[2], 0x04000c0cu),
+                                                __builtin_amdgcn_perm(w[1], w[0], 0x0c0c0400u), 0x07060100u);
+      const unsigned hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w[7], w[6], 0x04000c0cu),
+                                                __builtin_amdgcn_perm(w[5], w[4], 0x0c0c0400u), 0x07060100u);
       *reinterpret_cast<uint2*>(J.codes + (static_cast<size_t>(bh) * J.code_rows + row) * D + cg * 8) =
           make_uint2(lo, hi);
     }

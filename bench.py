@@ -16,6 +16,9 @@ Also on the JSON line:
                 MFMA peak of its input type (INT8, or MXFP4); `traffic` comes
                 from committed rocprofv3 counter summaries taken on the
                 current kernel source, else null.
+  torch_sdpa_fp16  PyTorch's fused FP16 scaled_dot_product_attention on the
+                same inputs (context for the quantized path's speedup; not
+                vs_baseline).
   cpu_baseline  the CPU oracle (oracle.int8_attention / mxfp4_attention in
                 float64) timed on a bounded sample of the same workload
                 (whole heads) on one host thread.
@@ -75,7 +78,7 @@ def timed(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def cpu_baseline(name: str, budget_s: float = 12.0):
+def cpu_baseline(name: str, mode_name: str, budget_s: float = 12.0):
     """The oracle on whole heads of the workload until ~budget_s of CPU time (1 thread)."""
     from threadpoolctl import threadpool_limits
 
@@ -90,11 +93,13 @@ def cpu_baseline(name: str, budget_s: float = 12.0):
         while t_total < budget_s and heads < w.B * w.H:
             q, k, v = make_inputs(name, B=1, H=1, seed=1000 + heads)   # one head, same recipe
             t0 = time.perf_counter()
-            if w.mode == "mxfp4":
+            if mode_name == "mxfp4":
                 O.mxfp4_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale)
+            elif mode_name == "fp16":
+                O.fp16_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale)
             else:
-                bq = 128 if w.mode == "int8_q128_k64" else 64
-                O.int8_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, blk_q=bq, blk_k=64)
+                bq, bk = {"int8_q128_k64": (128, 64), "int8_q64_k64": (64, 64), "int8_per_token": (1, 1)}[mode_name]
+                O.int8_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, blk_q=bq, blk_k=bk)
             t_total += time.perf_counter() - t0
             ops += 4.0 * w.N * w.N * w.d / (2 if w.causal else 1)
             heads += 1
@@ -110,8 +115,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--mode", default=None, choices=["int8_q128_k64", "int8_q64_k64", "int8_per_token", "mxfp4"],
-                    help="override the workload's quantization mode (ablations)")
+    ap.add_argument("--no-sdpa", action="store_true", help="skip timing torch's FP16 SDPA for context")
+    ap.add_argument("--mode", default=None,
+                    choices=["int8_q128_k64", "int8_q64_k64", "int8_per_token", "mxfp4", "fp16"],
+                    help="override the workload's quantization mode (ablations; fp16 = unquantized baseline)")
     ap.add_argument("--no-smooth", action="store_true", help="skip the K mean subtraction (ablation)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
@@ -142,7 +149,7 @@ def main():
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload]
     mode_name = args.mode or w.mode
-    mode = {"int8_q128_k64": 0, "int8_q64_k64": 1, "mxfp4": 2, "int8_per_token": 3}[mode_name]
+    mode = {"int8_q128_k64": 0, "int8_q64_k64": 1, "mxfp4": 2, "int8_per_token": 3, "fp16": 4}[mode_name]
     flags = sa.SAGE_FLAG_NO_SMOOTH if args.no_smooth else 0
     t0 = time.perf_counter()
     q, k, v = make_inputs(w.name)
@@ -159,7 +166,7 @@ def main():
     # the two phases separately
     prep = lambda: sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode | flags)
     ms_prep, _ = timed(prep, args.steps, args.warmup, torch)
-    comp = lambda: sa.sage_attn_compute(out, ws, causal=w.causal, sm_scale=w.sm_scale, mode=mode | flags)
+    comp = lambda: sa.sage_attn_compute(out, ws, causal=w.causal, sm_scale=w.sm_scale, mode=mode | flags, q=qd, k=kd)
     ms_attn, _ = timed(comp, args.steps, args.warmup, torch)
     log(f"[bench] {w.name}: step {ms_step:.4f} ms (wall {wall_step:.4f}), attention kernel {ms_attn:.4f} ms, "
         f"quantization phase {ms_prep:.4f} ms")
@@ -172,24 +179,39 @@ def main():
         # read K (mean), Q, K, V (2 B each); write packed codes (0.5 B) + exponents (1/32 B) x3
         quant_bytes = n_el * 8 + 3 * n_el * (0.5 + 1 / 32)
         peak, kernel, src = PEAK["mxfp4"], f"attn_mxfp4_kernel<{w.d},{str(w.causal).lower()}>", "attn_mxfp4.hip"
+    elif mode == 4:
+        # unquantized baseline: only V -> V^T (read 2 B, write 2 B)
+        quant_bytes = n_el * 4
+        peak, src = PEAK["fp16"], "attn_int8.hip"
+        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},2>"
     else:
         # read K (mean), Q, K, V (2 B each); write Q/K codes (1 B each) and V^T (2 B)
         quant_bytes = n_el * 8 + n_el * 4
         peak, src = PEAK["int8"], "attn_int8.hip"
-        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},{str(mode == 3).lower()}>"
+        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},{1 if mode == 3 else 0}>"
     roofline = {"bound": "mfma", "achieved": round(tops_attn, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tops_attn / peak, 4),
                 "traffic": load_traffic(f"{src[:-4]}_{w.name}", src) if (mode_name == w.mode and not flags) else None,
                 "kernel": kernel, "kernel_ms": round(ms_attn, 4)}
-    if mode != 2:
+    if mode in (0, 1, 3):
         roofline["mixed_int8_fp16_peak"] = round(2 / (1 / PEAK["int8"] + 1 / PEAK["fp16"]), 1)
+    # context: PyTorch's own fused FP16 attention (scaled_dot_product_attention,
+    # the flash backend of this ROCm build) on the same resident inputs
+    sdpa = None
+    if not args.no_sdpa:
+        import torch.nn.functional as F
+        sdpa_fn = lambda: F.scaled_dot_product_attention(qd, kd, vd, is_causal=w.causal, scale=w.sm_scale)
+        ms_sdpa, _ = timed(sdpa_fn, max(5, args.steps // 5), 3, torch)
+        sdpa = {"ms": round(ms_sdpa, 4), "tflops": round(ops / (ms_sdpa * 1e-3) / 1e12, 2),
+                "step_speedup": round(ms_sdpa / ms_step, 3), "kernel_speedup": round(ms_sdpa / ms_attn, 3)}
+        log(f"[bench] torch SDPA fp16: {ms_sdpa:.4f} ms; this step is {ms_sdpa / ms_step:.2f}x faster")
     del qd, kd, vd, ws, out
     torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(w.name)
+        cpu = cpu_baseline(w.name, mode_name)
         log(f"[bench] cpu oracle: {cpu['value']:.3e} TOPS")
 
     line = {
@@ -203,7 +225,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4" if mode == 2 else "int8+f16",
+        "dtype": {2: "mxfp4", 4: "f16"}.get(mode, "int8+f16"),
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "mode": mode_name, "k_smoothing": not args.no_smooth, "global_batch": w.B, "seq_len": w.N},
@@ -213,6 +235,7 @@ def main():
         "quant_phase_gbs": round(quant_bytes / (ms_prep * 1e-3) / 1e9, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "torch_sdpa_fp16": sdpa,
     }
     print(json.dumps(line), flush=True)
 

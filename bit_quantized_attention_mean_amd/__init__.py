@@ -20,6 +20,7 @@ import os
 
 __all__ = [
     "SAGE_MODE_INT8_Q128_K64", "SAGE_MODE_INT8_Q64_K64", "SAGE_MODE_MXFP4", "SAGE_MODE_INT8_PER_TOKEN",
+    "SAGE_MODE_FP16",
     "SAGE_FLAG_NO_SMOOTH", "SageError", "LIB_PATH", "lib",
     "sage_attn_fwd", "sage_attn_prepare", "sage_attn_compute", "sage_attn_workspace_size",
     "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_status_string", "sage_last_error",
@@ -30,6 +31,7 @@ SAGE_MODE_INT8_Q128_K64 = 0
 SAGE_MODE_INT8_Q64_K64 = 1
 SAGE_MODE_MXFP4 = 2
 SAGE_MODE_INT8_PER_TOKEN = 3
+SAGE_MODE_FP16 = 4
 SAGE_FLAG_NO_SMOOTH = 0x100
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_attn.so")
@@ -42,7 +44,7 @@ _SIGS = {
     "sage_quant_workspace_size": (_sz, [_i, _i, _i, _i]),
     "sage_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "sage_attn_prepare": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
-    "sage_attn_compute": (_i, [_vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "sage_attn_compute": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "sage_quant_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sage_quant_mxfp4": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -165,12 +167,19 @@ def sage_attn_prepare(q, k, v, workspace, *, mode=SAGE_MODE_INT8_Q128_K64, strea
     _check(rc, "sage_attn_prepare")
 
 
-def sage_attn_compute(out, workspace, *, causal=False, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64, stream=None):
+def sage_attn_compute(out, workspace, *, causal=False, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64, q=None, k=None,
+                      stream=None):
+    """Attention from a prepared workspace. q, k (the tensors given to prepare) are needed by SAGE_MODE_FP16 only."""
     torch = _torch()
     B, H, N, d = _shape4(out)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
-    rc = lib.sage_attn_compute(_dev_ptr(out, "out", torch.float16), B, H, N, d, int(bool(causal)),
+    for t, name in ((q, "q"), (k, "k")):
+        if t is not None and tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{name} and out must have the same shape")
+    qp = None if q is None else _dev_ptr(q, "q", torch.float16)
+    kp = None if k is None else _dev_ptr(k, "k", torch.float16)
+    rc = lib.sage_attn_compute(qp, kp, _dev_ptr(out, "out", torch.float16), B, H, N, d, int(bool(causal)),
                                float(sm_scale), int(mode), _dev_ptr(workspace, "workspace"),
                                workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "sage_attn_compute")

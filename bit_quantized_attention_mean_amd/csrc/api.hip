@@ -48,7 +48,7 @@ int check_ptr(const void* p, const char* name, size_t align) {
 int check_mode(int mode, bool attention) {
   if (mode & ~(SAGE_MODE_MASK | SAGE_FLAG_NO_SMOOTH)) return fail(SAGE_ERR_UNSUPPORTED, "unknown flag bits in mode 0x%x", mode);
   const int lo = mode & SAGE_MODE_MASK;
-  if (lo > SAGE_MODE_INT8_PER_TOKEN) return fail(SAGE_ERR_UNSUPPORTED, "unknown mode %d", lo);
+  if (lo > SAGE_MODE_FP16) return fail(SAGE_ERR_UNSUPPORTED, "unknown mode %d", lo);
   (void)attention;
   return SAGE_OK;
 }
@@ -123,6 +123,8 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
   const sage::Layout L = sage::make_layout(BH, N, d, lo, true);
   (void)hipGetLastError();
   float* mu = reinterpret_cast<float*>(at(ws, L.kmean));
+  if (lo == SAGE_MODE_FP16)  // unquantized baseline: only the V^T layout (smoothing would be a no-op)
+    return hip_status(sage::launch_v_transpose(v, at(ws, L.vt), BH, N, L.Npad, d, s), "V transpose kernel");
   if (smooth)
     SAGE_TRY(hip_status(sage::launch_kmean(k, reinterpret_cast<long long*>(at(ws, L.ksum)), mu, nullptr, BH, N, d,
                                            L.chunk, L.nchunk, s), "K mean kernels"));
@@ -147,8 +149,8 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
   return SAGE_OK;
 }
 
-int do_compute(void* out, int B, int H, int N, int d, int causal, float sm_scale, int mode, const void* ws,
-               hipStream_t s) {
+int do_compute(const void* q, const void* k, void* out, int B, int H, int N, int d, int causal, float sm_scale,
+               int mode, const void* ws, hipStream_t s) {
   const int BH = B * H;
   const int lo = mode & SAGE_MODE_MASK;
   const sage::Layout L = sage::make_layout(BH, N, d, lo, true);
@@ -160,8 +162,9 @@ int do_compute(void* out, int B, int H, int N, int d, int causal, float sm_scale
   if (lo == SAGE_MODE_MXFP4)
     return hip_status(sage::launch_attn_mxfp4(a, at(ws, L.q_fp4), at(ws, L.q_e8), at(ws, L.k_fp4), at(ws, L.k_e8),
                                               at(ws, L.vt_fp4), at(ws, L.vt_e8), s), "MXFP4 attention kernel");
-  return hip_status(sage::launch_attn_int8(a, reinterpret_cast<const int8_t*>(at(ws, L.q_codes)),
-                                           reinterpret_cast<const int8_t*>(at(ws, L.k_codes)), at(ws, L.vt),
+  if (lo == SAGE_MODE_FP16)
+    return hip_status(sage::launch_attn_int8(a, q, k, at(ws, L.vt), nullptr, nullptr, s), "FP16 attention kernel");
+  return hip_status(sage::launch_attn_int8(a, at(ws, L.q_codes), at(ws, L.k_codes), at(ws, L.vt),
                                            reinterpret_cast<const float*>(at(ws, L.q_scales)),
                                            reinterpret_cast<const float*>(at(ws, L.k_scales)), s),
                     "INT8 attention kernel");
@@ -206,15 +209,19 @@ int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H,
   return do_prepare(q, k, v, B, H, N, d, mode, workspace, static_cast<hipStream_t>(stream));
 }
 
-int sage_attn_compute(void* out, int B, int H, int N, int d, int causal, float sm_scale, int mode,
-                      const void* workspace, size_t workspace_bytes, void* stream) {
+int sage_attn_compute(const void* q, const void* k, void* out, int B, int H, int N, int d, int causal,
+                      float sm_scale, int mode, const void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
+  if ((mode & SAGE_MODE_MASK) == SAGE_MODE_FP16) {
+    SAGE_TRY(check_ptr(q, "q", 16));
+    SAGE_TRY(check_ptr(k, "k", 16));
+  }
   SAGE_TRY(check_ptr(out, "out", 16));
   if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
   SAGE_TRY(check_scale(sm_scale));
   SAGE_TRY(validate_attn(B, H, N, d, mode, workspace, workspace_bytes));
   SAGE_TRY(check_device());
-  return do_compute(out, B, H, N, d, causal, sm_scale, mode, workspace, static_cast<hipStream_t>(stream));
+  return do_compute(q, k, out, B, H, N, d, causal, sm_scale, mode, workspace, static_cast<hipStream_t>(stream));
 }
 
 int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
@@ -231,7 +238,7 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
   SAGE_TRY(check_device());
   const hipStream_t s = static_cast<hipStream_t>(stream);
   SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, workspace, s));
-  return do_compute(out, B, H, N, d, causal, sm_scale, mode, workspace, s);
+  return do_compute(q, k, out, B, H, N, d, causal, sm_scale, mode, workspace, s);
 }
 
 int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, int blk_q, int blk_k, int flags,

@@ -93,18 +93,28 @@ __device__ __forceinline__ void map_workgroup(int bid, int BH, int nqt, bool cau
 
 }  // namespace
 
-template <int D, bool CAUSAL, bool PERTOK>
+// Score variants of the kernel: INT8 codes with one scale per (query block,
+// key tile), INT8 codes with per-token scales, or unquantized fp16 Q and K on
+// the FP16 matrix op (the FlashAttention-style baseline of the same design).
+constexpr int kScoresInt8Block = 0, kScoresInt8Token = 1, kScoresF16 = 2;
+
+template <int D, bool CAUSAL, int SM>
 __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
-    const int8_t* __restrict__ qc, const int8_t* __restrict__ kc, const _Float16* __restrict__ vt,
+    const void* __restrict__ qsrc, const void* __restrict__ ksrc, const _Float16* __restrict__ vt,
     const float* __restrict__ qs, const float* __restrict__ ks, _Float16* __restrict__ out, int N,
     int Npad, int qblk, float sl2, int BH) {
-  constexpr int NC = D / 32;             // 32-channel chunks of the score contraction
-  constexpr int KROW = D + 16;           // LDS bytes per K row (16 bytes of padding)
+  constexpr bool PERTOK = SM == kScoresInt8Token;
+  constexpr bool F16 = SM == kScoresF16;
+  constexpr int EB = F16 ? 2 : 1;        // bytes per Q / K element
+  constexpr int NC = D / 32;             // 32-channel tiles of O^T
+  constexpr int NQF = F16 ? D / 16 : D / 32;  // score matrix ops per 32 keys (16 bytes of Q each)
+  constexpr int KROW = D * EB + 16;      // LDS bytes per K row (16 bytes of padding)
   constexpr int VROW = kKTile * 2 + 16;  // LDS bytes per V^T row
   constexpr int KT_BYTES = kKTile * KROW;
   constexpr int VT_BYTES = D * VROW;
   constexpr int KB0 = 0, KB1 = KT_BYTES, VB0 = 2 * KT_BYTES, VB1 = 2 * KT_BYTES + VT_BYTES;
-  constexpr int KCHN = kKTile * D / 16;  // 16-byte chunks of a K tile
+  constexpr int KCHN = kKTile * D * EB / 16;  // 16-byte chunks of a K tile
+  constexpr int KPT = (KCHN + 511) / 512;
   constexpr int VCHN = D * 8;            // 16-byte chunks of a V^T tile
   constexpr int VPT = (VCHN + 511) / 512;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KT_BYTES + 2 * VT_BYTES];
@@ -119,35 +129,55 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   const int wrow0 = q0 + grp * 128 + (wave & 3) * 32;   // first query row of this wave
   const int qrow = wrow0 + l32;
 
-  // Q codes of this lane's query: the B operand of the score MFMAs, kept in registers.
-  v4i qf[NC];
-  {
-    const int8_t* qp = qc + (static_cast<size_t>(bh) * Npad + qrow) * D + g * 16;
+  // Q of this lane's query (16 bytes per score matrix op: 16 INT8 codes, or
+  // 8 fp16 values): the B operand of the score MFMAs, kept in registers. The
+  // INT8 codes are zero-padded to Npad rows; fp16 Q is read as given, with
+  // zeros for rows >= N.
+  v4i qf[NQF];
+  if (F16) {
+    const bool live = qrow < N;
+    const unsigned char* qp = static_cast<const unsigned char*>(qsrc) +
+                              (static_cast<size_t>(bh) * N + (live ? qrow : 0)) * D * 2 + g * 16;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const v4i*>(qp + c * 32);
+    for (int c = 0; c < NQF; ++c) {
+      qf[c] = v4i{0, 0, 0, 0};
+      if (live) qf[c] = *reinterpret_cast<const v4i*>(qp + c * 32);
+    }
+  } else {
+    const int8_t* qp = static_cast<const int8_t*>(qsrc) + (static_cast<size_t>(bh) * Npad + qrow) * D + g * 16;
+#pragma unroll
+    for (int c = 0; c < NQF; ++c) qf[c] = *reinterpret_cast<const v4i*>(qp + c * 32);
   }
   // Q scale: one per block of qblk rows (a wave never straddles two), or per row.
-  const int nqs = Npad / qblk;
-  const float sq = qs[static_cast<size_t>(bh) * nqs + (PERTOK ? qrow : wrow0 / qblk)];
   // K scale: one per 64-key block (= one key tile), or one per key.
-  const int nks = PERTOK ? Npad : Npad / kKTile;
-  const float* ksh = ks + static_cast<size_t>(bh) * nks;
+  float sq = 1.f;
+  const float* ksh = nullptr;
+  if (!F16) {
+    const int nqs = Npad / qblk;
+    sq = qs[static_cast<size_t>(bh) * nqs + (PERTOK ? qrow : wrow0 / qblk)];
+    const int nks = PERTOK ? Npad : Npad / kKTile;
+    ksh = ks + static_cast<size_t>(bh) * nks;
+  }
 
   int nkt = (N + kKTile - 1) / kKTile;
   if (CAUSAL) nkt = min(nkt, (q0 + kWGQ) / kKTile);
 
-  const int8_t* kbase = kc + static_cast<size_t>(bh) * Npad * D;
+  // K: INT8 codes zero-padded to Npad rows, or fp16 K as given ([N, d] per head).
+  const unsigned char* kbase = static_cast<const unsigned char*>(ksrc) +
+                               static_cast<size_t>(bh) * (F16 ? N : Npad) * D * EB;
   const _Float16* vbase = vt + static_cast<size_t>(bh) * D * Npad;
 
-  // Loading: every thread moves at most one 16-byte K chunk and VPT V^T chunks
+  // Loading: every thread moves at most KPT 16-byte K chunks and VPT V^T chunks
   // per tile, global -> registers at the start of a period, registers -> LDS
   // at its end. K rows go to their permuted LDS rows.
-  const bool kload = tid < KCHN;
-  int kg = 0, kl = 0;
-  {
-    const int row = tid / (D / 16), col = tid % (D / 16);
-    kg = row * D + col * 16;
-    kl = lds_row_of_key(row) * KROW + col * 16;
+  const bool kload_last = (tid + 512 * (KPT - 1)) < KCHN;
+  int kg[KPT], kl[KPT], krw[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int i = tid + 512 * u, row = i / (D * EB / 16), col = i % (D * EB / 16);
+    kg[u] = row * D * EB + col * 16;
+    kl[u] = lds_row_of_key(row) * KROW + col * 16;
+    krw[u] = row;
   }
   int vg[VPT], vls[VPT];
 #pragma unroll
@@ -157,7 +187,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     vls[u] = row * VROW + col * 16;
   }
   const bool vload_last = (tid + 512 * (VPT - 1)) < VCHN;
-  unsigned kr[4], vr[4 * VPT];
+  unsigned kr[4 * KPT], vr[4 * VPT];
   const int ka = l32 * KROW + g * 16;   // score A operand: K row l32 of each 32-key half
   const int va = l32 * VROW + g * 64;   // P.V A operand: V^T row l32 of each 32-channel tile
 
@@ -171,9 +201,14 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   v8h pf[4];
 
 #define SAGE_LOAD_K(J_)                                                                          \
-  if (kload) {                                                                                   \
-    const uint4 t_ = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(J_) * kKTile * D + kg); \
-    kr[0] = t_.x; kr[1] = t_.y; kr[2] = t_.z; kr[3] = t_.w;                                      \
+  _Pragma("unroll") for (int u = 0; u < KPT; ++u) {                                              \
+    if (u < KPT - 1 || kload_last) {                                                             \
+      uint4 t_ = make_uint4(0, 0, 0, 0);                                                         \
+      /* INT8 codes are padded; fp16 K rows >= N read as zeros (their scores are masked) */     \
+      if (!F16 || (J_) * kKTile + krw[u] < N)                                                    \
+        t_ = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(J_) * kKTile * D * EB + kg[u]); \
+      kr[4 * u] = t_.x; kr[4 * u + 1] = t_.y; kr[4 * u + 2] = t_.z; kr[4 * u + 3] = t_.w;       \
+    }                                                                                            \
   }
 #define SAGE_LOAD_V(J_)                                                                          \
   _Pragma("unroll") for (int u = 0; u < VPT; ++u) {                                              \
@@ -183,7 +218,11 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     }                                                                                            \
   }
 #define SAGE_STORE_K(KB_)                                                                        \
-  if (kload) *reinterpret_cast<uint4*>(smem + (KB_) + kl) = make_uint4(kr[0], kr[1], kr[2], kr[3]);
+  _Pragma("unroll") for (int u = 0; u < KPT; ++u) {                                              \
+    if (u < KPT - 1 || kload_last)                                                               \
+      *reinterpret_cast<uint4*>(smem + (KB_) + kl[u]) =                                          \
+          make_uint4(kr[4 * u], kr[4 * u + 1], kr[4 * u + 2], kr[4 * u + 3]);                    \
+  }
 #define SAGE_STORE_V(VB_)                                                                        \
   _Pragma("unroll") for (int u = 0; u < VPT; ++u) {                                              \
     if (u < VPT - 1 || vload_last)                                                               \
@@ -191,22 +230,31 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
           make_uint4(vr[4 * u], vr[4 * u + 1], vr[4 * u + 2], vr[4 * u + 3]);                    \
   }
 
-  // S^T = K Q^T for key tile J_ from the K buffer KB_ (INT8 MFMA, exact int32).
-  // All eight K operands are read up front so the matrix ops issue back to back.
+  // S^T = K Q^T for key tile J_ from the K buffer KB_: INT8 MFMA (exact int32)
+  // or, for fp16 Q and K, the FP16 MFMA (fp32 accumulation; the fp32 bits are
+  // kept in the same registers). Both read 16 bytes of K per lane and matrix op
+  // at the same LDS offsets. All K operands are read up front so the matrix ops
+  // issue back to back.
 #define SAGE_SCORES(KB_)                                                                         \
   do {                                                                                           \
-    v4i ka_[2 * NC];                                                                             \
+    v4i ka_[2 * NQF];                                                                            \
     _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
-      _Pragma("unroll") for (int c = 0; c < NC; ++c)                                             \
-        ka_[t * NC + c] = *reinterpret_cast<const v4i*>(smem + (KB_) + ka + t * 32 * KROW + c * 32); \
+      _Pragma("unroll") for (int c = 0; c < NQF; ++c)                                            \
+        ka_[t * NQF + c] = *reinterpret_cast<const v4i*>(smem + (KB_) + ka + t * 32 * KROW + c * 32); \
     _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                              \
       _Pragma("unroll") for (int i = 0; i < 16; ++i) s[t][i] = 0;                                \
-      _Pragma("unroll") for (int c = 0; c < NC; ++c)                                             \
-        s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka_[t * NC + c], qf[c], s[t], 0, 0, 0);    \
+      _Pragma("unroll") for (int c = 0; c < NQF; ++c) {                                          \
+        if (F16)                                                                                 \
+          s[t] = __builtin_bit_cast(v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(                \
+                     __builtin_bit_cast(v8h, ka_[t * NQF + c]), __builtin_bit_cast(v8h, qf[c]),  \
+                     __builtin_bit_cast(v16f, s[t]), 0, 0, 0));                                  \
+        else                                                                                     \
+          s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka_[t * NQF + c], qf[c], s[t], 0, 0, 0); \
+      }                                                                                          \
     }                                                                                            \
     /* issue order: 4 LDS reads ahead, then one read per matrix op */                           \
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);                                           \
-    _Pragma("unroll") for (int u = 0; u < 2 * NC - 4; ++u) {                                     \
+    _Pragma("unroll") for (int u = 0; u < 2 * NQF - 4; ++u) {                                    \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);                                         \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);                                         \
     }                                                                                            \
@@ -276,6 +324,32 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
       need_ = mt_ > m + kRefSlack;                                                               \
       mnew_ = need_ ? mt_ : m;                                                                   \
       _Pragma("unroll") for (int e = 0; e < 32; ++e) p[e] = __builtin_amdgcn_exp2f(p[e] - mnew_); \
+    } else if (F16) {                                                                            \
+      /* fp32 scores (bits in s): the max is taken before the sm_scale * log2(e) */             \
+      /* factor, which is > 0, and the factor is applied in the fma */                          \
+      const float sc_ = sl2;                                                                     \
+      if (masked_) {                                                                             \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
+          const int key = kb_ + e;                                                               \
+          if ((CAUSAL && key > qrow) || key >= N) s[e >> 4][e & 15] = __float_as_int(-INFINITY); \
+        }                                                                                        \
+      }                                                                                          \
+      float mx_ = __int_as_float(s[0][0]);                                                       \
+      _Pragma("unroll") for (int e = 1; e < 32; ++e) mx_ = fmaxf(mx_, __int_as_float(s[e >> 4][e & 15])); \
+      mx_ = pair_max(mx_);                                                                       \
+      mt_ = (mx_ == -INFINITY) ? -INFINITY : mx_ * sc_;                                          \
+      need_ = mt_ > m + kRefSlack;                                                               \
+      mnew_ = need_ ? mt_ : m;                                                                   \
+      const float nm_ = -mnew_;                                                                  \
+      if (masked_) {                                                                             \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
+          const float x_ = __int_as_float(s[e >> 4][e & 15]);                                    \
+          p[e] = (x_ == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x_, sc_, nm_)); \
+        }                                                                                        \
+      } else {                                                                                   \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e)                                           \
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[e >> 4][e & 15]), sc_, nm_)); \
+      }                                                                                          \
     } else {                                                                                     \
       /* one scale per (query block, key tile): the max of the integer scores, */               \
       /* scaled once, is the max of the dequantized scores (the scale is >= 0) */               \
@@ -406,23 +480,28 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   }
 }
 
-hipError_t launch_attn_int8(const AttnArgs& a, const int8_t* qc, const int8_t* kc, const void* vt,
+hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, const void* vt,
                             const float* qs, const float* ks, hipStream_t s) {
   const int nqt = a.Npad / kWGQ;
   const dim3 grid(a.BH * nqt), block(512);
   const int qblk = (a.mode == 0) ? 128 : (a.mode == 1 ? 64 : 1);
-  const bool pt = (a.mode == 3);
+  const int sm = a.mode == 3 ? kScoresInt8Token : (a.mode == 4 ? kScoresF16 : kScoresInt8Block);
   const auto* v = static_cast<const _Float16*>(vt);
   auto* o = static_cast<_Float16*>(a.out);
-#define SAGE_LAUNCH(D_, C_, P_) \
-  attn_int8_kernel<D_, C_, P_><<<grid, block, 0, s>>>(qc, kc, v, qs, ks, o, a.N, a.Npad, qblk, a.sl2, a.BH)
+#define SAGE_LAUNCH(D_, C_, S_) \
+  attn_int8_kernel<D_, C_, S_><<<grid, block, 0, s>>>(q, k, v, qs, ks, o, a.N, a.Npad, qblk, a.sl2, a.BH)
+#define SAGE_LAUNCH_SM(D_, C_)                                               \
+  do {                                                                       \
+    if (sm == kScoresInt8Token) SAGE_LAUNCH(D_, C_, kScoresInt8Token);       \
+    else if (sm == kScoresF16) SAGE_LAUNCH(D_, C_, kScoresF16);              \
+    else SAGE_LAUNCH(D_, C_, kScoresInt8Block);                              \
+  } while (0)
   if (a.d == 128) {
-    if (a.causal) { if (pt) SAGE_LAUNCH(128, true, true); else SAGE_LAUNCH(128, true, false); }
-    else { if (pt) SAGE_LAUNCH(128, false, true); else SAGE_LAUNCH(128, false, false); }
+    if (a.causal) SAGE_LAUNCH_SM(128, true); else SAGE_LAUNCH_SM(128, false);
   } else {
-    if (a.causal) { if (pt) SAGE_LAUNCH(64, true, true); else SAGE_LAUNCH(64, true, false); }
-    else { if (pt) SAGE_LAUNCH(64, false, true); else SAGE_LAUNCH(64, false, false); }
+    if (a.causal) SAGE_LAUNCH_SM(64, true); else SAGE_LAUNCH_SM(64, false);
   }
+#undef SAGE_LAUNCH_SM
 #undef SAGE_LAUNCH
   return hipGetLastError();
 }

@@ -74,6 +74,8 @@ inline Layout make_layout(long long BH, int N, int d, int mode_lo, bool attentio
       L.k_e8 = take(rows * d / 32);
       L.vt_fp4 = take(rows * d / 2);
       L.vt_e8 = take(rows * d / 32);
+    } else if (mode_lo == 4) {  // SAGE_MODE_FP16: V^T only
+      L.vt = take(rows * d * 2);
     } else {
       L.q_codes = take(rows * d);
       L.k_codes = take(rows * d);
@@ -134,7 +136,9 @@ struct AttnArgs {
   int mode = 0;     // SAGE_MODE_* (no flags)
   void* out = nullptr;
 };
-hipError_t launch_attn_int8(const AttnArgs& a, const int8_t* qc, const int8_t* kc, const void* vt,
+// q, k: INT8 codes (padded to Npad rows) with scales qs, ks; or, for
+// SAGE_MODE_FP16, the caller's fp16 Q and K [BH, N, d] (qs, ks unused).
+hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, const void* vt,
                             const float* qs, const float* ks, hipStream_t s);
 hipError_t launch_attn_mxfp4(const AttnArgs& a, const uint8_t* q4, const uint8_t* qe,
                              const uint8_t* k4, const uint8_t* ke, const uint8_t* v4,

@@ -55,6 +55,9 @@ typedef enum sage_status {
 #define SAGE_MODE_INT8_Q64_K64 1   /* INT8 Q,K; Q and K scale blocks of 64 tokens            */
 #define SAGE_MODE_MXFP4 2          /* MXFP4 Q, K_s, V and P, E8M0 scale per 32 elements      */
 #define SAGE_MODE_INT8_PER_TOKEN 3 /* INT8 Q,K with one scale per token (blocks of 1)        */
+#define SAGE_MODE_FP16 4           /* no quantization: fp16 Q K^T on the FP16 matrix op, same */
+                                   /* online softmax and fp16 P.V (FlashAttention-style        */
+                                   /* baseline of the same kernel; reads q, k when computing)  */
 #define SAGE_MODE_MASK 0xff
 
 /* Flags OR-ed into `mode` (or passed as `flags`). */
@@ -105,9 +108,13 @@ int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H,
  * dequantization, online softmax, P.V, normalization) reading the operands a
  * previous sage_attn_prepare with the same B, H, N, d and mode left in
  * `workspace`, writing fp16 `out` [B, H, N, d]. Arguments as for sage_attn_fwd.
+ *   q, k  the fp16 tensors given to sage_attn_prepare. Only SAGE_MODE_FP16
+ *         reads them here (the quantized modes read their codes from the
+ *         workspace and accept NULL).
  */
-int sage_attn_compute(void* out, int B, int H, int N, int d, int causal, float sm_scale,
-                      int mode, const void* workspace, size_t workspace_bytes, void* stream);
+int sage_attn_compute(const void* q, const void* k, void* out, int B, int H, int N, int d,
+                      int causal, float sm_scale, int mode, const void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace sage_quant_qk and sage_quant_mxfp4 need. */
 size_t sage_quant_workspace_size(int B, int H, int N, int d);

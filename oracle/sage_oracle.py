@@ -251,6 +251,32 @@ def int8_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, 
     return out
 
 
+def fp16_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: int = 64, rows=None,
+                   ref_slack: float = REF_SLACK):
+    """Unquantized FlashAttention-style forward, the baseline the method is
+    measured against ([SA-Setup]: the kernels build on FlashAttention-2's
+    tiled online softmax; [SA-Summary]: the speedup is quoted over it).
+
+    S = (Q K^T) * sm_scale from the fp16 inputs, exactly (float64); causal mask
+    (R7); the same tiled online softmax as the INT8 path (R6) with fp16 P and
+    fp16 V, l summing the fp16 P. No quantization, no smoothing.
+    Returns float64 [B, H, len(rows), d].
+    """
+    B, H, N, d = q16.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    keys = np.arange(N)
+    round16 = lambda P: P.astype(np.float16).astype(np.float64)
+    out = np.empty((B, H, rows.size, d))
+    for b in range(B):
+        for h in range(H):
+            S = (as_f64(q16[b, h, rows]) @ as_f64(k16[b, h]).T) * sm_scale
+            if causal:
+                S[_causal_mask(rows, keys)] = -np.inf
+            out[b, h] = online_softmax_pv(S, as_f64(v16[b, h]), kv_tile=kv_tile, round_p=round16,
+                                          ref_slack=ref_slack, sum_rounded=True)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # (c3) Microscaled FP4 path: [SA3-Abstract] and the MX format it builds on.
 # ---------------------------------------------------------------------------

@@ -50,6 +50,9 @@ def test_workspace_sizes():
     n = 4 * 32 * 4096 * 128
     assert 4 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 0) < 4.2 * n
     assert 1.5 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 2) < 1.8 * n
+    # FP16 baseline: only V^T (2 B/elem)
+    assert 2 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 4) < 2.1 * n
+    assert sa.sage_attn_workspace_size(1, 2, 256, 64, 5) == 0
     assert sa.sage_quant_workspace_size(1, 2, 256, 64) > 0
 
 
@@ -76,8 +79,13 @@ def test_prepare_compute_and_quant_validation():
     ws = sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
     assert lib.sage_attn_prepare(None, A16, A16, 1, 2, 256, 64, 0, A16, ws, None) == INVALID
     assert lib.sage_attn_prepare(A16, A16, A16, 1, 2, 256, 64, 0, A16, 10, None) == WS
-    assert lib.sage_attn_compute(A16, 1, 2, 256, 64, 0, 0.0, 0, A16, ws, None) == INVALID
-    assert lib.sage_attn_compute(A16, 1, 2, 256, 48, 0, 0.1, 0, A16, ws, None) == UNSUP
+    assert lib.sage_attn_compute(None, None, A16, 1, 2, 256, 64, 0, 0.0, 0, A16, ws, None) == INVALID
+    assert lib.sage_attn_compute(None, None, A16, 1, 2, 256, 48, 0, 0.1, 0, A16, ws, None) == UNSUP
+    # the unquantized baseline reads q and k in the attention phase
+    ws4 = sa.sage_attn_workspace_size(1, 2, 256, 64, 4)
+    assert lib.sage_attn_compute(None, A16, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
+    assert lib.sage_attn_compute(A16, A16 + 2, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
+    assert lib.sage_attn_compute(A16, A16, A16, 1, 2, 256, 64, 0, 0.1, 5, A16, ws4, None) == UNSUP
     qw = sa.sage_quant_workspace_size(1, 2, 256, 64)
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 48, 64, 0, A16, A16, A16, A16, None, A16, qw, None) == UNSUP
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 4, A16, A16, A16, A16, None, A16, qw, None) == UNSUP

@@ -117,6 +117,31 @@ def test_int8_attention_matches_oracle(sa, case):
         f"oracle {O.metrics(ref, ex)['cos']:.6f}")
 
 
+F16_CASES = [
+    # B, H, N, d, causal, dist: the unquantized FP16 baseline of the same kernel
+    (1, 2, 256, 64, False, "normal"),
+    (1, 2, 1000, 128, False, "normal"),
+    (1, 2, 1000, 128, True, "normal"),
+    (2, 1, 777, 64, True, "student_t"),
+    (1, 1, 1, 128, False, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", F16_CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"-c{int(c[4])}")
+def test_fp16_baseline_attention_matches_oracle(sa, case):
+    B, H, N, d, causal, dist = case
+    say("fp16 baseline attention", case)
+    q, k, v = make_custom(B, H, N, d, seed=11 * N + d, dist=dist)
+    sm = 1.0 / np.sqrt(d)
+    ref = O.fp16_attention(q, k, v, causal=causal, sm_scale=sm)
+    qd, kd, vd = _dev(q, k, v)
+    out = sa.sage_attn_fwd(qd, kd, vd, causal=causal, sm_scale=sm, mode=sa.SAGE_MODE_FP16)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = assert_output_parity(got, ref, what=f"fp16 {case}")
+    say(f"  max err vs oracle {err:.2e}")
+
+
 MXATTN_CASES = [
     (1, 2, 256, 64, False),
     (1, 2, 1000, 128, False),
@@ -142,7 +167,7 @@ def test_mxfp4_attention_matches_oracle(sa, case):
         f"oracle {O.metrics(ref, ex)['cos']:.6f}")
 
 
-@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("mode", [0, 2, 4])
 def test_prepare_compute_equals_fwd_and_is_deterministic(sa, mode):
     say("determinism mode", mode)
     q, k, v = make_custom(1, 2, 700, 128, seed=11)
@@ -152,6 +177,6 @@ def test_prepare_compute_equals_fwd_and_is_deterministic(sa, mode):
     ws = sa.make_workspace(1, 2, 700, 128, mode)
     c = torch.empty_like(qd)
     sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode)
-    sa.sage_attn_compute(c, ws, causal=True, mode=mode)
+    sa.sage_attn_compute(c, ws, causal=True, mode=mode, q=qd, k=kd)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)

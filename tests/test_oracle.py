@@ -248,6 +248,29 @@ def test_int8_emulation_constant_v():
     assert np.max(np.abs(o - 1.5)) <= 1e-14
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_baseline_is_exact_attention_up_to_p16_rounding(causal):
+    # unquantized baseline: the only rounding on the way is P -> fp16
+    # (relative error <= 2^-11 per weight), so O moves by at most ~2^-10 max|V|
+    q, k, v = make_custom(1, 2, 300, 32, seed=12, k_offset_std=2.0)
+    ex = O.exact_attention(q, k, v, causal=causal, sm_scale=0.3)
+    got = O.fp16_attention(q, k, v, causal=causal, sm_scale=0.3)
+    err = np.max(np.abs(got - ex))
+    assert err <= 2 ** -10 * np.abs(v.astype(float)).max()
+    assert err > 0  # P really is rounded
+
+
+def test_fp16_baseline_constant_v_and_row_subsets():
+    q, k, _ = make_custom(1, 1, 200, 32, seed=13)
+    v = np.full((1, 1, 200, 32), -2.25, np.float16)
+    o = O.fp16_attention(q, k, v, causal=True, sm_scale=0.2)
+    assert np.max(np.abs(o + 2.25)) <= 1e-14
+    q, k, v = make_custom(1, 2, 190, 32, seed=14)
+    full = O.fp16_attention(q, k, v, causal=True, sm_scale=0.2)
+    rows = np.array([0, 63, 64, 189])
+    assert np.array_equal(O.fp16_attention(q, k, v, causal=True, sm_scale=0.2, rows=rows), full[:, :, rows])
+
+
 def test_int8_rows_subset_matches_full():
     q, k, v = make_custom(1, 2, 300, 32, seed=6)
     full = O.int8_attention(q, k, v, causal=True, sm_scale=0.2, blk_q=128, blk_k=64)

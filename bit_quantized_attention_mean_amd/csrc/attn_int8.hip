@@ -56,6 +56,28 @@ __device__ __forceinline__ int lds_row_of_key(int k) {
   return t * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
 }
 
+// Max of the 32 scores a lane holds, as four independent chains of eight.
+__device__ __forceinline__ int max32_i(const v16i& a, const v16i& b) {
+  int c0 = max(a[0], a[1]), c1 = max(a[8], a[9]), c2 = max(b[0], b[1]), c3 = max(b[8], b[9]);
+#pragma unroll
+  for (int i = 2; i < 8; ++i) {
+    c0 = max(c0, a[i]); c1 = max(c1, a[8 + i]); c2 = max(c2, b[i]); c3 = max(c3, b[8 + i]);
+  }
+  return max(max(c0, c1), max(c2, c3));
+}
+__device__ __forceinline__ float max32_f(const v16i& a, const v16i& b) {
+  float c0 = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+  float c1 = fmaxf(__int_as_float(a[8]), __int_as_float(a[9]));
+  float c2 = fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+  float c3 = fmaxf(__int_as_float(b[8]), __int_as_float(b[9]));
+#pragma unroll
+  for (int i = 2; i < 8; ++i) {
+    c0 = fmaxf(c0, __int_as_float(a[i])); c1 = fmaxf(c1, __int_as_float(a[8 + i]));
+    c2 = fmaxf(c2, __int_as_float(b[i])); c3 = fmaxf(c3, __int_as_float(b[8 + i]));
+  }
+  return fmaxf(fmaxf(c0, c1), fmaxf(c2, c3));
+}
+
 // Combines a per-lane value with the one in lane l ^ 32 (same query column).
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -292,8 +314,112 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
 
   // Softmax of key tile J_ on the scores in s: dequantize to base-2 logits,
   // mask, move the reference max if needed (rescaling l now and O in the next
-  // P.V), P = exp2(S - m), row sum, P -> fp16 in pf (keys g*32 + c*8 .. +7 in pf[c]).
-#define SAGE_SOFTMAX(J_)                                                                         \
+  // P.V), P = exp2(S - m), row sum, P -> fp16 in pf (keys g*32 + c*8 .. +7 in
+  // pf[c]). Two forms of the same arithmetic: SAGE_SOFTMAX_ILP works in place
+  // on the 32 score registers (fp32 bits replace the integers) with a tree row
+  // max, which measured faster where many tiles need masking (causal);
+  // SAGE_SOFTMAX_SEQ, a plain per-score sequence, measured faster on unmasked
+  // tiles, so non-causal launches use it.
+#define SAGE_SOFTMAX_ILP(J_)                                                                         \
+  do {                                                                                           \
+    const int j_ = (J_);                                                                         \
+    const bool masked_ = (CAUSAL && (j_ * kKTile + kKTile - 1 > wrow0)) || (j_ * kKTile + kKTile > N); \
+    const int kb_ = j_ * kKTile + g * 32;                                                        \
+    float mt_, mnew_;                                                                            \
+    bool need_;                                                                                  \
+    if (PERTOK) {                                                                                \
+      /* per-token dequantization to fp32 logits, in place */                                    \
+      const float scq_ = sq * sl2;                                                               \
+      const float4* k4_ = reinterpret_cast<const float4*>(ksh + kb_);                            \
+      _Pragma("unroll") for (int u = 0; u < 8; ++u) {                                            \
+        const float4 kk_ = k4_[u];                                                               \
+        const float kv_[4] = {kk_.x, kk_.y, kk_.z, kk_.w};                                       \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                          \
+          const int e = 4 * u + r;                                                               \
+          s[e >> 4][e & 15] = __float_as_int(static_cast<float>(s[e >> 4][e & 15]) * scq_ * kv_[r]); \
+        }                                                                                        \
+      }                                                                                          \
+      if (masked_) {                                                                             \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
+          const int key = kb_ + e;                                                               \
+          if ((CAUSAL && key > qrow) || key >= N) s[e >> 4][e & 15] = __float_as_int(-INFINITY); \
+        }                                                                                        \
+      }                                                                                          \
+      mt_ = pair_max(max32_f(s[0], s[1]));                                                       \
+      need_ = mt_ > m + kRefSlack;                                                               \
+      mnew_ = need_ ? mt_ : m;                                                                   \
+      /* exp2(-inf - finite) = 0 for masked keys */                                              \
+      _Pragma("unroll") for (int e = 0; e < 32; ++e)                                             \
+        s[e >> 4][e & 15] = __float_as_int(__builtin_amdgcn_exp2f(__int_as_float(s[e >> 4][e & 15]) - mnew_)); \
+    } else if (F16) {                                                                            \
+      /* fp32 scores (bits in s): the max is taken before the sm_scale * log2(e) */             \
+      /* factor, which is > 0, and the factor is applied in the fma */                          \
+      const float sc_ = sl2;                                                                     \
+      if (masked_) {                                                                             \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
+          const int key = kb_ + e;                                                               \
+          if ((CAUSAL && key > qrow) || key >= N) s[e >> 4][e & 15] = __float_as_int(-INFINITY); \
+        }                                                                                        \
+      }                                                                                          \
+      const float mx_ = pair_max(max32_f(s[0], s[1]));                                           \
+      mt_ = (mx_ == -INFINITY) ? -INFINITY : mx_ * sc_;                                          \
+      need_ = mt_ > m + kRefSlack;                                                               \
+      mnew_ = need_ ? mt_ : m;                                                                   \
+      const float nm_ = -mnew_;                                                                  \
+      if (masked_) {                                                                             \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
+          const float x_ = __int_as_float(s[e >> 4][e & 15]);                                    \
+          s[e >> 4][e & 15] = __float_as_int(                                                    \
+              (x_ == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x_, sc_, nm_)));   \
+        }                                                                                        \
+      } else {                                                                                   \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e)                                           \
+          s[e >> 4][e & 15] = __float_as_int(                                                    \
+              __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[e >> 4][e & 15]), sc_, nm_))); \
+      }                                                                                          \
+    } else {                                                                                     \
+      /* one scale per (query block, key tile): the max of the integer scores, */               \
+      /* scaled once, is the max of the dequantized scores (the scale is >= 0) */               \
+      const float sc_ = sq * ksh[j_] * sl2;                                                      \
+      if (masked_) {                                                                             \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
+          const int key = kb_ + e;                                                               \
+          if ((CAUSAL && key > qrow) || key >= N) s[e >> 4][e & 15] = INT_MIN;                   \
+        }                                                                                        \
+      }                                                                                          \
+      const int mi_ = pair_max_i(max32_i(s[0], s[1]));                                           \
+      mt_ = (mi_ == INT_MIN) ? -INFINITY : static_cast<float>(mi_) * sc_;                        \
+      need_ = mt_ > m + kRefSlack;                                                               \
+      mnew_ = need_ ? mt_ : m;                                                                   \
+      const float nm_ = -mnew_;                                                                  \
+      if (masked_) {                                                                             \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
+          const int si_ = s[e >> 4][e & 15];                                                     \
+          const float x_ = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(si_), sc_, nm_)); \
+          s[e >> 4][e & 15] = __float_as_int(si_ == INT_MIN ? 0.f : x_);                         \
+        }                                                                                        \
+      } else {                                                                                   \
+        _Pragma("unroll") for (int e = 0; e < 32; ++e)                                           \
+          s[e >> 4][e & 15] = __float_as_int(                                                    \
+              __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[e >> 4][e & 15]), sc_, nm_))); \
+      }                                                                                          \
+    }                                                                                            \
+    const float alpha_ = need_ ? __builtin_amdgcn_exp2f(m - mnew_) : 1.f;                       \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e)                                              \
+        pf[c][e] = static_cast<_Float16>(__int_as_float(s[(c * 8 + e) >> 4][(c * 8 + e) & 15])); \
+    /* row sum of the fp16 P that multiplies V: two products per v_dot2_f32_f16, */             \
+    /* four independent partial sums */                                                          \
+    float rs_[4] = {0.f, 0.f, 0.f, 0.f};                                                         \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                \
+      _Pragma("unroll") for (int e = 0; e < 8; e += 2)                                           \
+        rs_[e >> 1] = __builtin_amdgcn_fdot2(v2h{pf[c][e], pf[c][e + 1]}, kOnes2, rs_[e >> 1], false); \
+    l = l * alpha_ + ((rs_[0] + rs_[1]) + (rs_[2] + rs_[3]));                                    \
+    m = mnew_;                                                                                   \
+    alpha = alpha_;                                                                              \
+  } while (0)
+
+#define SAGE_SOFTMAX_SEQ(J_)                                                                         \
   do {                                                                                           \
     const int j_ = (J_);                                                                         \
     const bool masked_ = (CAUSAL && (j_ * kKTile + kKTile - 1 > wrow0)) || (j_ * kKTile + kKTile > N); \
@@ -397,6 +523,11 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     alpha = alpha_;                                                                              \
   } while (0)
 
+#define SAGE_SOFTMAX(J_)                                                                         \
+  do {                                                                                           \
+    if (CAUSAL) { SAGE_SOFTMAX_ILP(J_); } else { SAGE_SOFTMAX_SEQ(J_); }                         \
+  } while (0)
+
   // One period of the ping-pong. Key tile jp_ is in K buffer KB_, tile jp_-1
   // in V buffer VBP_ (buffer offsets are per-period values; every LDS access
   // is a per-period base plus an immediate). Phase A: group 0 runs its matrix
@@ -457,6 +588,8 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
 #undef SAGE_PHASE_MATRIX
 #undef SAGE_PERIOD
 #undef SAGE_SOFTMAX
+#undef SAGE_SOFTMAX_ILP
+#undef SAGE_SOFTMAX_SEQ
 #undef SAGE_PV
 #undef SAGE_SCORES
 #undef SAGE_STORE_V

@@ -107,34 +107,35 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
   const uint8_t* vb4 = v4 + static_cast<size_t>(bh) * D * (Npad / 2);
   const uint8_t* vbe = ve + static_cast<size_t>(bh) * D * (Npad / 32);
 
-  // staging registers: one 16-byte K chunk, one K exponent word, one 16-byte V^T chunk, one V^T exponent pair
-  unsigned kr[4], vr[4];
-  unsigned ksr = 0, vsr = 0;
+  // staging registers, two sets (tiles are loaded two iterations ahead): one
+  // 16-byte K chunk, one K exponent word, one 16-byte V^T chunk, one V^T exponent pair
+  unsigned kr[2][4], vr[2][4];
+  unsigned ksr[2] = {0, 0}, vsr[2] = {0, 0};
   constexpr int KCHUNKS = kKTile * D / 32;  // 16-byte chunks per K tile (256 or 128)
   constexpr int VCHUNKS = D * 2;            // 16-byte chunks per V^T tile (256 or 128)
-#define SAGE_GLOAD4(J_)                                                                              \
+#define SAGE_GLOAD4(J_, S_)                                                                          \
   do {                                                                                               \
     if (tid < KCHUNKS) {                                                                             \
       const int row_ = tid / (D / 32), col_ = tid % (D / 32);                                        \
       const uint4 t_ = *reinterpret_cast<const uint4*>(kb4 + static_cast<size_t>((J_) * kKTile + row_) * (D / 2) + \
                                                        col_ * 16);                                   \
-      kr[0] = t_.x; kr[1] = t_.y; kr[2] = t_.z; kr[3] = t_.w;                                        \
+      kr[S_][0] = t_.x; kr[S_][1] = t_.y; kr[S_][2] = t_.z; kr[S_][3] = t_.w;                        \
     }                                                                                                \
     if (tid < kKTile) {                                                                              \
       const size_t r_ = static_cast<size_t>((J_) * kKTile + tid);                                    \
-      ksr = (NE == 4) ? *reinterpret_cast<const unsigned*>(kbe + r_ * 4)                             \
+      ksr[S_] = (NE == 4) ? *reinterpret_cast<const unsigned*>(kbe + r_ * 4)                         \
                       : static_cast<unsigned>(*reinterpret_cast<const uint16_t*>(kbe + r_ * 2));     \
     }                                                                                                \
     if (tid < VCHUNKS) {                                                                             \
       const int row_ = tid >> 1, col_ = tid & 1;                                                     \
       const uint4 t_ = *reinterpret_cast<const uint4*>(vb4 + static_cast<size_t>(row_) * (Npad / 2) + \
                                                        (J_) * 32 + col_ * 16);                       \
-      vr[0] = t_.x; vr[1] = t_.y; vr[2] = t_.z; vr[3] = t_.w;                                        \
+      vr[S_][0] = t_.x; vr[S_][1] = t_.y; vr[S_][2] = t_.z; vr[S_][3] = t_.w;                        \
     }                                                                                                \
     if (tid < D)                                                                                     \
-      vsr = *reinterpret_cast<const uint16_t*>(vbe + static_cast<size_t>(tid) * (Npad / 32) + (J_) * 2); \
+      vsr[S_] = *reinterpret_cast<const uint16_t*>(vbe + static_cast<size_t>(tid) * (Npad / 32) + (J_) * 2); \
   } while (0)
-#define SAGE_SWRITE4(BUF_)                                                                           \
+#define SAGE_SWRITE4(BUF_, S_)                                                                       \
   do {                                                                                               \
     unsigned char* kt_ = smem + (BUF_) * BUF;                                                        \
     unsigned char* ks_ = kt_ + KT_BYTES;                                                             \
@@ -143,14 +144,15 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
     if (tid < KCHUNKS) {                                                                             \
       const int row_ = tid / (D / 32), col_ = tid % (D / 32);                                        \
       *reinterpret_cast<uint4*>(kt_ + lds_row_of_key4(row_) * KROW + col_ * 16) =                    \
-          make_uint4(kr[0], kr[1], kr[2], kr[3]);                                                    \
+          make_uint4(kr[S_][0], kr[S_][1], kr[S_][2], kr[S_][3]);                                    \
     }                                                                                                \
-    if (tid < kKTile) *reinterpret_cast<unsigned*>(ks_ + lds_row_of_key4(tid) * 4) = ksr;            \
+    if (tid < kKTile) *reinterpret_cast<unsigned*>(ks_ + lds_row_of_key4(tid) * 4) = ksr[S_];        \
     if (tid < VCHUNKS) {                                                                             \
       const int row_ = tid >> 1, col_ = tid & 1;                                                     \
-      *reinterpret_cast<uint4*>(vl_ + row_ * VROW + col_ * 16) = make_uint4(vr[0], vr[1], vr[2], vr[3]); \
+      *reinterpret_cast<uint4*>(vl_ + row_ * VROW + col_ * 16) =                                     \
+          make_uint4(vr[S_][0], vr[S_][1], vr[S_][2], vr[S_][3]);                                    \
     }                                                                                                \
-    if (tid < D) *reinterpret_cast<unsigned*>(vs_ + tid * 4) = vsr;                                  \
+    if (tid < D) *reinterpret_cast<unsigned*>(vs_ + tid * 4) = vsr[S_];                              \
   } while (0)
 
   v16f o[NT];
@@ -160,104 +162,120 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
     for (int i = 0; i < 16; ++i) o[c][i] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  SAGE_GLOAD4(0);
-  SAGE_SWRITE4(0);
+  // One key tile (J_) from LDS buffer BUF_: scores, softmax, P quantization, P.V.
+#define SAGE_TILE4(J_, BUF_)                                                                         \
+  do {                                                                                               \
+    const int j = (J_);                                                                              \
+    const int buf = (BUF_);                                                                          \
+    const unsigned char* kt = smem + buf * BUF;                                                     \
+    const unsigned char* ksl = kt + KT_BYTES;                                                       \
+    const unsigned char* vl = ksl + KS_BYTES;                                                       \
+    const unsigned char* vsl = vl + VT_BYTES;                                                       \
+                                                                                                    \
+    /* S^T = K_s Q^T on the block-scaled FP4 MFMA (scores come out dequantized) */                  \
+    v16f s[2];                                                                                      \
+_Pragma("unroll")                                                                                   \
+    for (int t = 0; t < 2; ++t) {                                                                   \
+_Pragma("unroll")                                                                                   \
+      for (int i = 0; i < 16; ++i) s[t][i] = 0.f;                                                   \
+      const int krow = t * 32 + l32;                                                                \
+      const unsigned ksw = *reinterpret_cast<const unsigned*>(ksl + krow * 4) >> (8 * g);           \
+_Pragma("unroll")                                                                                   \
+      for (int c = 0; c < NC; ++c) {                                                                \
+        const v4i a = *reinterpret_cast<const v4i*>(kt + krow * KROW + c * 32 + g * 16);            \
+        s[t] = mfma_fp4(a, qf[c], ksw >> (16 * c), qsw >> (16 * c), s[t]);                          \
+      }                                                                                             \
+    }                                                                                               \
+                                                                                                    \
+    float p[32];                                                                                    \
+_Pragma("unroll")                                                                                   \
+    for (int t = 0; t < 2; ++t)                                                                     \
+_Pragma("unroll")                                                                                   \
+      for (int i = 0; i < 16; ++i) p[t * 16 + i] = s[t][i] * sl2;                                   \
+    const bool diag = CAUSAL && (j * kKTile + kKTile - 1 > q0 + wave * 32);                         \
+    const bool tail = (j * kKTile + kKTile > N);                                                    \
+    if (diag || tail) {                                                                             \
+      const int kb = j * kKTile + g * 32;                                                           \
+_Pragma("unroll")                                                                                   \
+      for (int e = 0; e < 32; ++e) {                                                                \
+        const int key = kb + e;                                                                     \
+        if ((CAUSAL && key > qrow) || key >= N) p[e] = -INFINITY;                                   \
+      }                                                                                             \
+    }                                                                                               \
+                                                                                                    \
+    float mx = p[0];                                                                                \
+_Pragma("unroll")                                                                                   \
+    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, p[e]);                                              \
+    mx = pair_max4(mx);                                                                             \
+    const bool need = mx > m + kRefSlack4;                                                          \
+    const float mnew = need ? mx : m;                                                               \
+    const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;                              \
+    float rs = 0.f, pmax = 0.f;                                                                     \
+_Pragma("unroll")                                                                                   \
+    for (int e = 0; e < 32; ++e) {                                                                  \
+      p[e] = __builtin_amdgcn_exp2f(p[e] - mnew);                                                   \
+      rs += p[e];                                                                                   \
+      pmax = fmaxf(pmax, p[e]);                                                                     \
+    }                                                                                               \
+    l = l * alpha + rs;  /* the row sum uses the unquantized P */                                   \
+    m = mnew;                                                                                       \
+                                                                                                    \
+    /* MX-quantize this lane's 32 P values (one block of 32 keys). */                               \
+    /* e = floor(log2 pmax) - 2, floored at -126 (blocks below 2^-124 are negligible). */           \
+    unsigned pe8 = 127;                                                                             \
+    float pscale = 1.f;                                                                             \
+    if (pmax > 0.f) {                                                                               \
+      const int E = static_cast<int>(__float_as_uint(pmax) >> 23);                                  \
+      const int e = max(E - 129, -126);                                                             \
+      pe8 = static_cast<unsigned>(e + 127);                                                         \
+      pscale = __uint_as_float(pe8 << 23);                                                          \
+    }                                                                                               \
+    v4i pq;                                                                                         \
+_Pragma("unroll")                                                                                   \
+    for (int w = 0; w < 4; ++w) {                                                                   \
+      unsigned r = 0;                                                                               \
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 0], p[8 * w + 1], pscale, 0);       \
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 2], p[8 * w + 3], pscale, 1);       \
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 4], p[8 * w + 5], pscale, 2);       \
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 6], p[8 * w + 7], pscale, 3);       \
+      pq[w] = static_cast<int>(r);                                                                  \
+    }                                                                                               \
+                                                                                                    \
+    if (__ballot(need)) {                                                                           \
+_Pragma("unroll")                                                                                   \
+      for (int c = 0; c < NT; ++c)                                                                  \
+_Pragma("unroll")                                                                                   \
+        for (int i = 0; i < 16; ++i) o[c][i] *= alpha;                                              \
+    }                                                                                               \
+_Pragma("unroll")                                                                                   \
+    for (int dt = 0; dt < NT; ++dt) {                                                               \
+      const int vrow = dt * 32 + l32;                                                               \
+      const v4i a = *reinterpret_cast<const v4i*>(vl + vrow * VROW + g * 16);                       \
+      const unsigned vsw = *reinterpret_cast<const unsigned*>(vsl + vrow * 4) >> (8 * g);           \
+      o[dt] = mfma_fp4(a, pq, vsw, pe8, o[dt]);                                                     \
+    }                                                                                               \
+  } while (0)
+
+  // Tiles are loaded into registers two iterations ahead (two staging sets)
+  // and stored to LDS one iteration ahead (two LDS buffers), so a tile's
+  // global loads have a whole iteration to arrive before they are stored.
+  SAGE_GLOAD4(0, 0);
+  SAGE_SWRITE4(0, 0);
+  if (nkt > 1) SAGE_GLOAD4(1, 1);
   __syncthreads();
-
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkt) SAGE_GLOAD4(j + 1);
-    const unsigned char* kt = smem + buf * BUF;
-    const unsigned char* ksl = kt + KT_BYTES;
-    const unsigned char* vl = ksl + KS_BYTES;
-    const unsigned char* vsl = vl + VT_BYTES;
-
-    // S^T = K_s Q^T on the block-scaled FP4 MFMA (scores come out dequantized)
-    v16f s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
-      const int krow = t * 32 + l32;
-      const unsigned ksw = *reinterpret_cast<const unsigned*>(ksl + krow * 4) >> (8 * g);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const v4i a = *reinterpret_cast<const v4i*>(kt + krow * KROW + c * 32 + g * 16);
-        s[t] = mfma_fp4(a, qf[c], ksw >> (16 * c), qsw >> (16 * c), s[t]);
-      }
-    }
-
-    float p[32];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[t * 16 + i] = s[t][i] * sl2;
-    const bool diag = CAUSAL && (j * kKTile + kKTile - 1 > q0 + wave * 32);
-    const bool tail = (j * kKTile + kKTile > N);
-    if (diag || tail) {
-      const int kb = j * kKTile + g * 32;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int key = kb + e;
-        if ((CAUSAL && key > qrow) || key >= N) p[e] = -INFINITY;
-      }
-    }
-
-    float mx = p[0];
-#pragma unroll
-    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, p[e]);
-    mx = pair_max4(mx);
-    const bool need = mx > m + kRefSlack4;
-    const float mnew = need ? mx : m;
-    const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
-    float rs = 0.f, pmax = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(p[e] - mnew);
-      rs += p[e];
-      pmax = fmaxf(pmax, p[e]);
-    }
-    l = l * alpha + rs;  // the row sum uses the unquantized P
-    m = mnew;
-
-    // MX-quantize this lane's 32 P values (one block of 32 keys).
-    // e = floor(log2 pmax) - 2, floored at -126 (blocks below 2^-124 are negligible).
-    unsigned pe8 = 127;
-    float pscale = 1.f;
-    if (pmax > 0.f) {
-      const int E = static_cast<int>(__float_as_uint(pmax) >> 23);
-      const int e = max(E - 129, -126);
-      pe8 = static_cast<unsigned>(e + 127);
-      pscale = __uint_as_float(pe8 << 23);
-    }
-    v4i pq;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      unsigned r = 0;
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 0], p[8 * w + 1], pscale, 0);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 2], p[8 * w + 3], pscale, 1);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 4], p[8 * w + 5], pscale, 2);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 6], p[8 * w + 7], pscale, 3);
-      pq[w] = static_cast<int>(r);
-    }
-
-    if (__ballot(need)) {
-#pragma unroll
-      for (int c = 0; c < NT; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[c][i] *= alpha;
-    }
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt) {
-      const int vrow = dt * 32 + l32;
-      const v4i a = *reinterpret_cast<const v4i*>(vl + vrow * VROW + g * 16);
-      const unsigned vsw = *reinterpret_cast<const unsigned*>(vsl + vrow * 4) >> (8 * g);
-      o[dt] = mfma_fp4(a, pq, vsw, pe8, o[dt]);
-    }
-
-    if (j + 1 < nkt) SAGE_SWRITE4(buf ^ 1);
+  int j2 = 0;
+  for (; j2 + 1 < nkt; j2 += 2) {
+    if (j2 + 2 < nkt) SAGE_GLOAD4(j2 + 2, 0);
+    SAGE_TILE4(j2, 0);
+    SAGE_SWRITE4(1, 1);
+    __syncthreads();
+    if (j2 + 3 < nkt) SAGE_GLOAD4(j2 + 3, 1);
+    SAGE_TILE4(j2 + 1, 1);
+    if (j2 + 2 < nkt) SAGE_SWRITE4(0, 0);
     __syncthreads();
   }
+  if (j2 < nkt) SAGE_TILE4(j2, 0);
+#undef SAGE_TILE4
 #undef SAGE_GLOAD4
 #undef SAGE_SWRITE4
 

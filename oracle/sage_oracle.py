@@ -57,6 +57,10 @@ Readings where the pages are silent (each also listed in the design doc):
      a = 0 gives e = 0 and all codes 0. Element code = nearest E2M1 value to
      x * 2^-e, ties to the even code index, saturating at +-6; the sign bit is
      the sign bit of x. Packing: element 2k in the low nibble of byte k.
+  R13 MX-FP8 variant for P and V (not on the pages; the accuracy variant of
+     the FP4 path): the same blocks as R8, e = floor(log2 a) - 8 (E4M3's largest
+     binade is 2^8), element = nearest E4M3 value to x * 2^-e, ties to the even
+     code, saturating at 448; Q and K_s stay MXFP4.
 """
 from __future__ import annotations
 
@@ -348,42 +352,114 @@ def pack_fp4(codes: np.ndarray) -> np.ndarray:
     return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 
 
-def quant_mxfp4(q16, k16, v16, *, smooth: bool = True):
+# MX-FP8 (E4M3 elements, E8M0 block exponent): the accuracy variant for P and V
+# (reading R13). E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits;
+# exponent field 0 is subnormal (m * 2^-9); code 0x7F (and 0xFF) is NaN, so the
+# largest magnitude is 0x7E = 448 = 1.75 * 2^8.
+E4M3_MAX = 448.0
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """Decode E4M3 bytes to float64 (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ef = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(ef == 0, m * 2.0 ** -9, (8.0 + m) * np.exp2(ef.astype(np.float64) - 10.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def e4m3_nearest(y: np.ndarray) -> np.ndarray:
+    """Code (0..0x7E) of the E4M3 magnitude nearest to y >= 0, ties to the even
+    code, saturating at 448.
+
+    In the binade [2^e, 2^(e+1)) (e clamped to [-6, 8]; below 2^-6 the subnormal
+    spacing 2^-9 continues) the representable magnitudes are multiples of
+    2^(e-3), so the nearest one is q * 2^(e-3) with q = round-half-even(y / 2^(e-3))
+    (q = 8 + mantissa, or the subnormal mantissa; q even <=> code even).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    _, ex = np.frexp(np.where(y > 0, y, 1.0))
+    e = np.clip(ex.astype(np.int64) - 1, -6, 8)
+    step = np.exp2((e - 3).astype(np.float64))
+    q = np.round(y / step)                         # numpy rounds halves to even; y/step is exact
+    val = np.minimum(q * step, E4M3_MAX)
+    # encode val (a representable magnitude) as a code
+    _, vx = np.frexp(np.where(val > 0, val, 1.0))
+    ve = vx.astype(np.int64) - 1
+    normal = val >= 2.0 ** -6
+    ef = np.where(normal, ve + 7, 0)
+    mant = np.where(normal, val / np.exp2(ve.astype(np.float64)) * 8 - 8, val * 2.0 ** 9)
+    return np.where(y > 0, ef * 8 + np.round(mant).astype(np.int64), 0).astype(np.int64)
+
+
+def mx_quantize_fp8(x: np.ndarray, axis: int):
+    """MX-FP8 quantization of x in blocks of 32 along `axis` (zero-padded at the
+    end): e = floor(log2 amax) - 8 clamped to [-127, 127] (0 for an all-zero
+    block), element = nearest E4M3 to x * 2^-e, ties to even, saturating at 448,
+    sign bit = sign bit of x. Returns (codes uint8, e8m0 uint8, values float64)
+    like mx_quantize."""
+    x = np.moveaxis(np.asarray(x, dtype=np.float64), axis, -1)
+    n = x.shape[-1]
+    nblk = -(-n // MX_BLOCK)
+    pad = nblk * MX_BLOCK - n
+    if pad:
+        x = np.concatenate([x, np.zeros(x.shape[:-1] + (pad,))], axis=-1)
+    xb = x.reshape(x.shape[:-1] + (nblk, MX_BLOCK))
+    amax = np.abs(xb).max(axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    e = np.where(amax > 0, np.clip(ex.astype(np.int64) - 1 - 8, -127, 127), 0)
+    y = np.abs(xb) * np.exp2(-e.astype(np.float64))[..., None]
+    mag = e4m3_nearest(y)
+    sign = np.signbit(xb)
+    codes = (mag + 0x80 * sign).astype(np.uint8)
+    vals = np.where(sign, -1.0, 1.0) * e4m3_value(mag) * np.exp2(e.astype(np.float64))[..., None]
+    codes = codes.reshape(x.shape)[..., :n]
+    vals = vals.reshape(x.shape)[..., :n]
+    e8 = (e + 127).astype(np.uint8)
+    return np.moveaxis(codes, -1, axis), np.moveaxis(e8, -1, axis), np.moveaxis(vals, -1, axis)
+
+
+def quant_mxfp4(q16, k16, v16, *, smooth: bool = True, v_fp8: bool = False):
     """MX quantization of Q (along d), K_s (along d) and V (along tokens, per channel).
 
-    Returns dict with codes/e8m0/values for q, k, v; v arrays are in [B, H, N, d]
-    orientation (blocks run along N). k_mean is None with smoothing off.
+    V is MXFP4, or MX-FP8 with v_fp8 (R13). Returns dict with codes/e8m0/values
+    for q, k, v; v arrays are in [B, H, N, d] orientation (blocks run along N).
+    k_mean is None with smoothing off.
     """
     mu = k_mean(k16) if smooth else None
     ks = smooth_k(k16, mu)
     qc, qe, qv = mx_quantize(np.asarray(q16).astype(np.float32), axis=3)
     kc, ke, kv = mx_quantize(ks, axis=3)
-    vc, ve, vv = mx_quantize(np.asarray(v16).astype(np.float32), axis=2)
+    vq = mx_quantize_fp8 if v_fp8 else mx_quantize
+    vc, ve, vv = vq(np.asarray(v16).astype(np.float32), axis=2)
     return dict(q_codes=qc, q_e8m0=qe, q_vals=qv, k_codes=kc, k_e8m0=ke, k_vals=kv,
                 v_codes=vc, v_e8m0=ve, v_vals=vv, k_mean=mu)
 
 
 def mxfp4_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: int = 64,
                     smooth: bool = True, rows=None, quant=None, quantize_p: bool = True,
-                    ref_slack: float = REF_SLACK):
+                    ref_slack: float = REF_SLACK, pv_fp8: bool = False):
     """Emulated microscaled-FP4 attention ([SA3-Abstract] with the MX format, reading R8).
 
-    Q, K_s, V and the softmax P are MXFP4; the scores are the exact products of
-    the decoded values (what an FP32-accumulating block-scaled matrix unit
-    computes up to accumulation rounding); online softmax as in the INT8 path
-    with the MX-quantized P in place of P16. Returns float64 [B, H, len(rows), d].
+    Q, K_s, V and the softmax P are MXFP4 (with pv_fp8, P and V are MX-FP8
+    instead, reading R13); the scores are the exact products of the decoded
+    values (what an FP32-accumulating block-scaled matrix unit computes up to
+    accumulation rounding); online softmax as in the INT8 path with the
+    MX-quantized P in place of P16. Returns float64 [B, H, len(rows), d].
     """
     B, H, N, d = q16.shape
     if kv_tile % MX_BLOCK:
         raise ValueError("kv_tile must be a multiple of 32")
     rows = np.arange(N) if rows is None else np.asarray(rows)
     keys = np.arange(N)
-    qd = quant if quant is not None else quant_mxfp4(q16, k16, v16, smooth=smooth)
+    qd = quant if quant is not None else quant_mxfp4(q16, k16, v16, smooth=smooth, v_fp8=pv_fp8)
     out = np.empty((B, H, rows.size, d))
+    pq = mx_quantize_fp8 if pv_fp8 else mx_quantize
     if quantize_p:
         def round_p(P):
-            # blocks of 32 keys inside the tile; a short tail tile is zero-padded by mx_quantize
-            return mx_quantize(P, axis=1)[2]
+            # blocks of 32 keys inside the tile; a short tail tile is zero-padded by the quantizer
+            return pq(P, axis=1)[2]
     else:
         def round_p(P):
             return P

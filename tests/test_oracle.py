@@ -375,6 +375,74 @@ def test_mx_v_blocks_run_along_tokens():
     assert d["v_e8m0"].shape == (1, 1, 2, 64)
 
 
+# --- MX-FP8 variant for P and V (reading R13): pinned to torch's float8_e4m3fn ---
+
+def test_e4m3_decode_matches_torch_float8():
+    codes = np.arange(256)
+    ours = O.e4m3_value(codes)
+    ref = torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[~np.isnan(ours)], ref[~np.isnan(ref)])
+    assert np.nanmax(ours) == 448.0 and ours[1] == 2.0 ** -9
+
+
+def test_e4m3_nearest_matches_torch_cast_including_ties():
+    rng = np.random.default_rng(21)
+    y = np.abs(rng.standard_normal(50000)) * np.exp2(rng.integers(-12, 9, 50000))
+    # exact midpoints between neighbouring magnitudes: ties go to the even code
+    mags = O.e4m3_value(np.arange(0x7F))
+    mids = (mags[:-1] + mags[1:]) / 2
+    y = np.concatenate([np.minimum(y, 448.0), mids, mags]).astype(np.float32).astype(np.float64)
+    ours = O.e4m3_nearest(y)
+    ref = torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    assert np.array_equal(ours, ref)
+    assert np.all(ours[len(y) - 2 * 0x7F + 1:len(y) - 0x7F] % 2 == 0)   # every midpoint lands on an even code
+
+
+def test_e4m3_saturates_at_448():
+    assert O.e4m3_nearest(np.array([448.0, 460.0, 1e6])).tolist() == [0x7E] * 3
+
+
+def test_mx_fp8_block_rule_and_roundtrip():
+    rng = np.random.default_rng(22)
+    codes = rng.integers(0, 0x7F, size=(3, 64))
+    codes[:, 0] = 0x7E; codes[:, 32] = 0x70          # block maxima 448 = 1.75 * 2^8 and 256 = 2^8
+    exps = np.array([0, -7, 4])
+    x = (O.e4m3_value(codes) * np.where(rng.integers(0, 2, (3, 64)), -1, 1) * np.exp2(exps)[:, None]).astype(np.float32)
+    c, e8, vals = O.mx_quantize_fp8(x, axis=1)
+    assert np.array_equal(vals, x.astype(np.float64))          # representable blocks come back exactly
+    assert np.array_equal(e8[:, 0], (exps + 127).astype(np.uint8))   # floor(log2 448 * 2^e) - 8 = e
+    assert np.array_equal(e8[:, 1], (exps + 127).astype(np.uint8))
+    z = np.zeros((1, 32), np.float32)
+    c, e8, vals = O.mx_quantize_fp8(z, axis=1)
+    assert e8[0, 0] == 127 and not c.any() and not vals.any()
+    # random data: relative error at most 2^-4 between the block's subnormal range
+    # and 448 * 2^e; above that (the block max can reach 512 * 2^e) elements saturate
+    y = (rng.standard_normal((16, 64)) * 3).astype(np.float32)
+    _, e8, vals = O.mx_quantize_fp8(y, axis=1)
+    e = np.repeat(e8.astype(np.int64) - 127, 32, axis=1)
+    top = 448.0 * np.exp2(e.astype(np.float64))
+    mid = (np.abs(y) >= np.exp2(e - 6.0)) & (np.abs(y) <= top)
+    assert np.all(np.abs(vals - y)[mid] <= np.abs(y)[mid] * 2.0 ** -4)
+    sat = np.abs(y) > top
+    assert np.array_equal(vals[sat], np.sign(y[sat]) * top[sat])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mxfp4_with_fp8_pv_equals_exact_attention_on_decoded_operands(causal):
+    q, k, v = make_custom(1, 2, 160, 64, seed=15)
+    d = O.quant_mxfp4(q, k, v, v_fp8=True)
+    ex = O.exact_attention(d["q_vals"], d["k_vals"], d["v_vals"], causal=causal, sm_scale=0.125)
+    got = O.mxfp4_attention(q, k, v, causal=causal, sm_scale=0.125, quantize_p=False, pv_fp8=True)
+    assert np.max(np.abs(got - ex)) < 1e-12
+    # FP8 P moves O far less than FP4 P does
+    e8p = np.max(np.abs(O.mxfp4_attention(q, k, v, causal=causal, sm_scale=0.125, pv_fp8=True) - ex))
+    d4 = O.quant_mxfp4(q, k, v)
+    ex4 = O.exact_attention(d4["q_vals"], d4["k_vals"], d4["v_vals"], causal=causal, sm_scale=0.125)
+    e4p = np.max(np.abs(O.mxfp4_attention(q, k, v, causal=causal, sm_scale=0.125) - ex4))
+    assert 0 < e8p < e4p
+
+
 def test_pack_fp4_low_nibble_first():
     c = np.array([[1, 2, 15, 0, 8, 7]], np.uint8)
     assert O.pack_fp4(c).tolist() == [[0x21, 0x0F, 0x78]]

@@ -35,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # MI355X published dense MFMA peaks (TOPS) and HBM bandwidth (GB/s)
-PEAK = {"int8": 5000.0, "fp16": 2500.0, "mxfp4": 10100.0}
+PEAK = {"int8": 5000.0, "fp16": 2500.0, "mxfp4": 10100.0, "fp8": 5000.0}
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -93,8 +93,8 @@ def cpu_baseline(name: str, mode_name: str, budget_s: float = 12.0):
         while t_total < budget_s and heads < w.B * w.H:
             q, k, v = make_inputs(name, B=1, H=1, seed=1000 + heads)   # one head, same recipe
             t0 = time.perf_counter()
-            if mode_name == "mxfp4":
-                O.mxfp4_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale)
+            if mode_name in ("mxfp4", "mxfp4_fp8pv"):
+                O.mxfp4_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, pv_fp8=mode_name == "mxfp4_fp8pv")
             elif mode_name == "fp16":
                 O.fp16_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale)
             else:
@@ -117,7 +117,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sdpa", action="store_true", help="skip timing torch's FP16 SDPA for context")
     ap.add_argument("--mode", default=None,
-                    choices=["int8_q128_k64", "int8_q64_k64", "int8_per_token", "mxfp4", "fp16"],
+                    choices=["int8_q128_k64", "int8_q64_k64", "int8_per_token", "mxfp4", "fp16", "mxfp4_fp8pv"],
                     help="override the workload's quantization mode (ablations; fp16 = unquantized baseline)")
     ap.add_argument("--no-smooth", action="store_true", help="skip the K mean subtraction (ablation)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -149,7 +149,8 @@ def main():
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.workload]
     mode_name = args.mode or w.mode
-    mode = {"int8_q128_k64": 0, "int8_q64_k64": 1, "mxfp4": 2, "int8_per_token": 3, "fp16": 4}[mode_name]
+    mode = {"int8_q128_k64": 0, "int8_q64_k64": 1, "mxfp4": 2, "int8_per_token": 3, "fp16": 4,
+            "mxfp4_fp8pv": 5}[mode_name]
     flags = sa.SAGE_FLAG_NO_SMOOTH if args.no_smooth else 0
     t0 = time.perf_counter()
     q, k, v = make_inputs(w.name)
@@ -175,10 +176,14 @@ def main():
     tops_step = ops / (ms_step * 1e-3) / 1e12
     tops_attn = ops / (ms_attn * 1e-3) / 1e12
     n_el = w.B * w.H * w.N * w.d
-    if mode == 2:
-        # read K (mean), Q, K, V (2 B each); write packed codes (0.5 B) + exponents (1/32 B) x3
-        quant_bytes = n_el * 8 + 3 * n_el * (0.5 + 1 / 32)
-        peak, kernel, src = PEAK["mxfp4"], f"attn_mxfp4_kernel<{w.d},{str(w.causal).lower()}>", "attn_mxfp4.hip"
+    if mode in (2, 5):
+        # read K (mean), Q, K, V (2 B each); write packed codes (0.5 B) + exponents (1/32 B)
+        # for Q and K, and for V 0.5 B (E2M1) or 1 B (E4M3) + exponents
+        quant_bytes = n_el * 8 + 2 * n_el * (0.5 + 1 / 32) + n_el * ((1.0 if mode == 5 else 0.5) + 1 / 32)
+        # mode 5: half the work (Q K^T) on FP4, half (P V) on FP8
+        peak = PEAK["mxfp4"] if mode == 2 else round(2 / (1 / PEAK["mxfp4"] + 1 / PEAK["fp8"]), 1)
+        kernel = f"attn_mxfp4_kernel<{w.d},{str(w.causal).lower()},{str(mode == 5).lower()}>"
+        src = "attn_mxfp4.hip"
     elif mode == 4:
         # unquantized baseline: only V -> V^T (read 2 B, write 2 B)
         quant_bytes = n_el * 4
@@ -225,7 +230,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {2: "mxfp4", 4: "f16"}.get(mode, "int8+f16"),
+        "dtype": {2: "mxfp4", 4: "f16", 5: "mxfp4+mxfp8"}.get(mode, "int8+f16"),
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "mode": mode_name, "k_smoothing": not args.no_smooth, "global_batch": w.B, "seq_len": w.N},

@@ -20,8 +20,8 @@ import os
 
 __all__ = [
     "SAGE_MODE_INT8_Q128_K64", "SAGE_MODE_INT8_Q64_K64", "SAGE_MODE_MXFP4", "SAGE_MODE_INT8_PER_TOKEN",
-    "SAGE_MODE_FP16",
-    "SAGE_FLAG_NO_SMOOTH", "SageError", "LIB_PATH", "lib",
+    "SAGE_MODE_FP16", "SAGE_MODE_MXFP4_FP8PV",
+    "SAGE_FLAG_NO_SMOOTH", "SAGE_FLAG_FP8_V", "SageError", "LIB_PATH", "lib",
     "sage_attn_fwd", "sage_attn_prepare", "sage_attn_compute", "sage_attn_workspace_size",
     "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_status_string", "sage_last_error",
     "EXPORTED_SYMBOLS",
@@ -32,7 +32,9 @@ SAGE_MODE_INT8_Q64_K64 = 1
 SAGE_MODE_MXFP4 = 2
 SAGE_MODE_INT8_PER_TOKEN = 3
 SAGE_MODE_FP16 = 4
+SAGE_MODE_MXFP4_FP8PV = 5
 SAGE_FLAG_NO_SMOOTH = 0x100
+SAGE_FLAG_FP8_V = 0x200
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_attn.so")
 
@@ -221,7 +223,7 @@ def sage_quant_mxfp4(q, k, v, *, flags=0, stream=None):
         "q_e8m0": torch.empty((B, H, N, d // 32), dtype=u8, device=dev),
         "k_fp4": torch.empty((B, H, N, d // 2), dtype=u8, device=dev),
         "k_e8m0": torch.empty((B, H, N, d // 32), dtype=u8, device=dev),
-        "vt_fp4": torch.empty((B, H, d, Nv // 2), dtype=u8, device=dev),
+        "vt_fp4": torch.empty((B, H, d, Nv if flags & SAGE_FLAG_FP8_V else Nv // 2), dtype=u8, device=dev),
         "vt_e8m0": torch.empty((B, H, d, Nv // 32), dtype=u8, device=dev),
         "k_mean": torch.empty((B, H, d), dtype=torch.float32, device=dev),
     }

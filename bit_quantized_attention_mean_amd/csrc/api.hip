@@ -48,7 +48,7 @@ int check_ptr(const void* p, const char* name, size_t align) {
 int check_mode(int mode, bool attention) {
   if (mode & ~(SAGE_MODE_MASK | SAGE_FLAG_NO_SMOOTH)) return fail(SAGE_ERR_UNSUPPORTED, "unknown flag bits in mode 0x%x", mode);
   const int lo = mode & SAGE_MODE_MASK;
-  if (lo > SAGE_MODE_FP16) return fail(SAGE_ERR_UNSUPPORTED, "unknown mode %d", lo);
+  if (lo > SAGE_MODE_MXFP4_FP8PV) return fail(SAGE_ERR_UNSUPPORTED, "unknown mode %d", lo);
   (void)attention;
   return SAGE_OK;
 }
@@ -128,13 +128,17 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
   if (smooth)
     SAGE_TRY(hip_status(sage::launch_kmean(k, reinterpret_cast<long long*>(at(ws, L.ksum)), mu, nullptr, BH, N, d,
                                            L.chunk, L.nchunk, s), "K mean kernels"));
-  if (lo == SAGE_MODE_MXFP4) {
+  if (lo == SAGE_MODE_MXFP4 || lo == SAGE_MODE_MXFP4_FP8PV) {
     sage::MxRowJob jq, jk;
     jq.src = q; jq.fp4 = at(ws, L.q_fp4); jq.e8 = at(ws, L.q_e8); jq.mu = nullptr; jq.rows = L.Npad;
     jk.src = k; jk.fp4 = at(ws, L.k_fp4); jk.e8 = at(ws, L.k_e8); jk.mu = smooth ? mu : nullptr; jk.rows = L.Npad;
     SAGE_TRY(hip_status(sage::launch_mx_rows(jq, jk, BH, N, d, s), "MXFP4 Q/K quantization kernel"));
-    SAGE_TRY(hip_status(sage::launch_mx_vt(v, at(ws, L.vt_fp4), at(ws, L.vt_e8), BH, N, L.Npad, d, s),
-                        "MXFP4 V quantization kernel"));
+    if (lo == SAGE_MODE_MXFP4_FP8PV)
+      SAGE_TRY(hip_status(sage::launch_mx_vt8(v, at(ws, L.vt_fp4), at(ws, L.vt_e8), BH, N, L.Npad, d, s),
+                          "MX-FP8 V quantization kernel"));
+    else
+      SAGE_TRY(hip_status(sage::launch_mx_vt(v, at(ws, L.vt_fp4), at(ws, L.vt_e8), BH, N, L.Npad, d, s),
+                          "MXFP4 V quantization kernel"));
     return SAGE_OK;
   }
   const int blk_q = lo == SAGE_MODE_INT8_Q128_K64 ? 128 : (lo == SAGE_MODE_INT8_Q64_K64 ? 64 : 1);
@@ -159,7 +163,7 @@ int do_compute(const void* q, const void* k, void* out, int B, int H, int N, int
   a.sl2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);  // sm_scale * log2(e)
   a.mode = lo; a.out = out;
   (void)hipGetLastError();
-  if (lo == SAGE_MODE_MXFP4)
+  if (lo == SAGE_MODE_MXFP4 || lo == SAGE_MODE_MXFP4_FP8PV)
     return hip_status(sage::launch_attn_mxfp4(a, at(ws, L.q_fp4), at(ws, L.q_e8), at(ws, L.k_fp4), at(ws, L.k_e8),
                                               at(ws, L.vt_fp4), at(ws, L.vt_e8), s), "MXFP4 attention kernel");
   if (lo == SAGE_MODE_FP16)
@@ -294,7 +298,7 @@ int sage_quant_mxfp4(const void* q, const void* k, const void* v, int B, int H, 
   SAGE_TRY(check_ptr(k_e8m0, "k_e8m0", 1));
   SAGE_TRY(check_ptr(vt_e8m0, "vt_e8m0", 1));
   if (k_mean) SAGE_TRY(check_ptr(k_mean, "k_mean", 4));
-  if (flags & ~SAGE_FLAG_NO_SMOOTH) return fail(SAGE_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (flags & ~(SAGE_FLAG_NO_SMOOTH | SAGE_FLAG_FP8_V)) return fail(SAGE_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   SAGE_TRY(check_ptr(workspace, "workspace", 256));
   const int BH = B * H;
   const sage::Layout L = sage::make_layout(BH, N, d, 0, false);
@@ -313,6 +317,8 @@ int sage_quant_mxfp4(const void* q, const void* k, const void* v, int B, int H, 
   jk.src = k; jk.fp4 = k_fp4; jk.e8 = k_e8m0; jk.mu = smooth ? mu : nullptr; jk.rows = N;
   SAGE_TRY(hip_status(sage::launch_mx_rows(jq, jk, BH, N, d, s), "MXFP4 Q/K quantization kernel"));
   const int Nv = sage::round_up(N, 32);
+  if (flags & SAGE_FLAG_FP8_V)
+    return hip_status(sage::launch_mx_vt8(v, vt_fp4, vt_e8m0, BH, N, Nv, d, s), "MX-FP8 V quantization kernel");
   return hip_status(sage::launch_mx_vt(v, vt_fp4, vt_e8m0, BH, N, Nv, d, s), "MXFP4 V quantization kernel");
 }
 

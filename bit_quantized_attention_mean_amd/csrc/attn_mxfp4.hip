@@ -22,6 +22,8 @@ namespace sage {
 
 namespace {
 
+typedef short v2s __attribute__((ext_vector_type(2)));
+
 // Reference-max slack of the online softmax (log2 units), as in the INT8 kernel.
 constexpr float kRefSlack4 = 8.0f;
 
@@ -66,7 +68,12 @@ __device__ __forceinline__ v16f mfma_fp4(const v4i a, const v4i b, unsigned sa, 
 
 }  // namespace
 
-template <int D, bool CAUSAL>
+// PV8: P and V in MX-FP8 (E4M3) instead of MXFP4 (the accuracy variant; Q and
+// K_s stay MXFP4). The P.V matrix op then takes 32 bytes of each operand per
+// lane (format code 0 = E4M3), laid out (measured on the GPU) as keys g*16 ..
+// g*16+15 and 32 + g*16 .. 32+g*16+15 for lane group g, with the block scale
+// of keys 32b .. 32b+31 taken from lane group b.
+template <int D, bool CAUSAL, bool PV8>
 __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
     const uint8_t* __restrict__ q4, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k4,
     const uint8_t* __restrict__ ke, const uint8_t* __restrict__ v4, const uint8_t* __restrict__ ve,
@@ -75,7 +82,8 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
   constexpr int NE = D / 32;         // exponent bytes per Q / K row
   constexpr int NT = D / 32;         // 32-row tiles of O^T
   constexpr int KROW = D / 2 + 16;   // LDS bytes per K row
-  constexpr int VROW = 32 + 16;      // LDS bytes per V^T row (64 keys)
+  constexpr int VTB = PV8 ? 64 : 32;  // bytes of one V^T row per key tile (64 keys)
+  constexpr int VROW = VTB + 16;      // LDS bytes per V^T row
   constexpr int KT_BYTES = kKTile * KROW;
   constexpr int KS_BYTES = kKTile * 4;
   constexpr int VT_BYTES = D * VROW;
@@ -104,15 +112,18 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
 
   const uint8_t* kb4 = k4 + static_cast<size_t>(bh) * Npad * (D / 2);
   const uint8_t* kbe = ke + static_cast<size_t>(bh) * Npad * NE;
-  const uint8_t* vb4 = v4 + static_cast<size_t>(bh) * D * (Npad / 2);
+  const int vrb = PV8 ? Npad : Npad / 2;  // bytes per V^T row in HBM
+  const uint8_t* vb4 = v4 + static_cast<size_t>(bh) * D * vrb;
   const uint8_t* vbe = ve + static_cast<size_t>(bh) * D * (Npad / 32);
 
   // staging registers, two sets (tiles are loaded two iterations ahead): one
   // 16-byte K chunk, one K exponent word, one 16-byte V^T chunk, one V^T exponent pair
-  unsigned kr[2][4], vr[2][4];
-  unsigned ksr[2] = {0, 0}, vsr[2] = {0, 0};
   constexpr int KCHUNKS = kKTile * D / 32;  // 16-byte chunks per K tile (256 or 128)
-  constexpr int VCHUNKS = D * 2;            // 16-byte chunks per V^T tile (256 or 128)
+  constexpr int VCPR = VTB / 16;            // 16-byte chunks per V^T row of a tile
+  constexpr int VCHUNKS = D * VCPR;         // 16-byte chunks per V^T tile
+  constexpr int VPT4 = (VCHUNKS + 255) / 256;
+  unsigned kr[2][4], vr[2][4 * VPT4];
+  unsigned ksr[2] = {0, 0}, vsr[2] = {0, 0};
 #define SAGE_GLOAD4(J_, S_)                                                                          \
   do {                                                                                               \
     if (tid < KCHUNKS) {                                                                             \
@@ -126,11 +137,14 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
       ksr[S_] = (NE == 4) ? *reinterpret_cast<const unsigned*>(kbe + r_ * 4)                         \
                       : static_cast<unsigned>(*reinterpret_cast<const uint16_t*>(kbe + r_ * 2));     \
     }                                                                                                \
-    if (tid < VCHUNKS) {                                                                             \
-      const int row_ = tid >> 1, col_ = tid & 1;                                                     \
-      const uint4 t_ = *reinterpret_cast<const uint4*>(vb4 + static_cast<size_t>(row_) * (Npad / 2) + \
-                                                       (J_) * 32 + col_ * 16);                       \
-      vr[S_][0] = t_.x; vr[S_][1] = t_.y; vr[S_][2] = t_.z; vr[S_][3] = t_.w;                        \
+    _Pragma("unroll") for (int u_ = 0; u_ < VPT4; ++u_) {                                           \
+      const int i_ = tid + 256 * u_;                                                                 \
+      if (i_ < VCHUNKS) {                                                                            \
+        const int row_ = i_ / VCPR, col_ = i_ % VCPR;                                                \
+        const uint4 t_ = *reinterpret_cast<const uint4*>(vb4 + static_cast<size_t>(row_) * vrb +     \
+                                                         (J_) * VTB + col_ * 16);                    \
+        vr[S_][4 * u_] = t_.x; vr[S_][4 * u_ + 1] = t_.y; vr[S_][4 * u_ + 2] = t_.z; vr[S_][4 * u_ + 3] = t_.w; \
+      }                                                                                              \
     }                                                                                                \
     if (tid < D)                                                                                     \
       vsr[S_] = *reinterpret_cast<const uint16_t*>(vbe + static_cast<size_t>(tid) * (Npad / 32) + (J_) * 2); \
@@ -147,10 +161,13 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
           make_uint4(kr[S_][0], kr[S_][1], kr[S_][2], kr[S_][3]);                                    \
     }                                                                                                \
     if (tid < kKTile) *reinterpret_cast<unsigned*>(ks_ + lds_row_of_key4(tid) * 4) = ksr[S_];        \
-    if (tid < VCHUNKS) {                                                                             \
-      const int row_ = tid >> 1, col_ = tid & 1;                                                     \
-      *reinterpret_cast<uint4*>(vl_ + row_ * VROW + col_ * 16) =                                     \
-          make_uint4(vr[S_][0], vr[S_][1], vr[S_][2], vr[S_][3]);                                    \
+    _Pragma("unroll") for (int u_ = 0; u_ < VPT4; ++u_) {                                           \
+      const int i_ = tid + 256 * u_;                                                                 \
+      if (i_ < VCHUNKS) {                                                                            \
+        const int row_ = i_ / VCPR, col_ = i_ % VCPR;                                                \
+        *reinterpret_cast<uint4*>(vl_ + row_ * VROW + col_ * 16) =                                   \
+            make_uint4(vr[S_][4 * u_], vr[S_][4 * u_ + 1], vr[S_][4 * u_ + 2], vr[S_][4 * u_ + 3]);  \
+      }                                                                                              \
     }                                                                                                \
     if (tid < D) *reinterpret_cast<unsigned*>(vs_ + tid * 4) = vsr[S_];                              \
   } while (0)
@@ -220,25 +237,46 @@ _Pragma("unroll")                                                               
     l = l * alpha + rs;  /* the row sum uses the unquantized P */                                   \
     m = mnew;                                                                                       \
                                                                                                     \
-    /* MX-quantize this lane's 32 P values (one block of 32 keys). */                               \
-    /* e = floor(log2 pmax) - 2, floored at -126 (blocks below 2^-124 are negligible). */           \
+    /* MX-quantize this lane's 32 P values (one block of 32 keys): */                              \
+    /* e = floor(log2 pmax) - 2 (E2M1) or - 8 (E4M3), floored at -126 */                            \
+    /* (blocks below 2^-118 are negligible). E4M3 values past 448 saturate */                       \
+    /* (the conversion itself would give NaN). */                                                   \
     unsigned pe8 = 127;                                                                             \
     float pscale = 1.f;                                                                             \
     if (pmax > 0.f) {                                                                               \
       const int E = static_cast<int>(__float_as_uint(pmax) >> 23);                                  \
-      const int e = max(E - 129, -126);                                                             \
+      const int e = max(E - (PV8 ? 135 : 129), -126);                                               \
       pe8 = static_cast<unsigned>(e + 127);                                                         \
       pscale = __uint_as_float(pe8 << 23);                                                          \
     }                                                                                               \
-    v4i pq;                                                                                         \
-_Pragma("unroll")                                                                                   \
-    for (int w = 0; w < 4; ++w) {                                                                   \
-      unsigned r = 0;                                                                               \
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 0], p[8 * w + 1], pscale, 0);       \
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 2], p[8 * w + 3], pscale, 1);       \
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 4], p[8 * w + 5], pscale, 2);       \
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 6], p[8 * w + 7], pscale, 3);       \
-      pq[w] = static_cast<int>(r);                                                                  \
+    v8i pq;                                                                                         \
+    if (PV8) {                                                                                      \
+      const float plim = 448.f * pscale;                                                            \
+      _Pragma("unroll") for (int w = 0; w < 8; ++w) {                                               \
+        v2s r = {0, 0};                                                                             \
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(p[4 * w], plim), fminf(p[4 * w + 1], plim), pscale, false); \
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(p[4 * w + 2], plim), fminf(p[4 * w + 3], plim), pscale, true); \
+        pq[w] = __builtin_bit_cast(int, r);                                                         \
+      }                                                                                             \
+      /* the FP8 operand of the matrix op takes keys g*16 .. +15 in bytes 0-15 and */               \
+      /* 32 + g*16 .. +15 in bytes 16-31 (the block scale of keys 32b .. 32b+31 */                 \
+      /* comes from lane group b): swap keys 16-31 of group 0 with 32-47 of group 1 */              \
+      _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                               \
+        const auto x_ = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(pq[w]),              \
+                                                         static_cast<unsigned>(pq[4 + w]), false, false); \
+        pq[w] = static_cast<int>(x_[0]);                                                            \
+        pq[4 + w] = static_cast<int>(x_[1]);                                                        \
+      }                                                                                             \
+    } else {                                                                                        \
+      _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                               \
+        unsigned r = 0;                                                                             \
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 0], p[8 * w + 1], pscale, 0);     \
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 2], p[8 * w + 3], pscale, 1);     \
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 4], p[8 * w + 5], pscale, 2);     \
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 6], p[8 * w + 7], pscale, 3);     \
+        pq[w] = static_cast<int>(r);                                                                \
+      }                                                                                             \
+      pq[4] = pq[5] = pq[6] = pq[7] = 0;                                                            \
     }                                                                                               \
                                                                                                     \
     if (__ballot(need)) {                                                                           \
@@ -250,9 +288,19 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                   \
     for (int dt = 0; dt < NT; ++dt) {                                                               \
       const int vrow = dt * 32 + l32;                                                               \
-      const v4i a = *reinterpret_cast<const v4i*>(vl + vrow * VROW + g * 16);                       \
       const unsigned vsw = *reinterpret_cast<const unsigned*>(vsl + vrow * 4) >> (8 * g);           \
-      o[dt] = mfma_fp4(a, pq, vsw, pe8, o[dt]);                                                     \
+      if (PV8) {                                                                                    \
+        /* keys g*16 .. +15 and 32 + g*16 .. +15 of the tile (see the P swap) */                    \
+        const v4i a0 = *reinterpret_cast<const v4i*>(vl + vrow * VROW + g * 16);                    \
+        const v4i a1 = *reinterpret_cast<const v4i*>(vl + vrow * VROW + 32 + g * 16);               \
+        const v8i a8 = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};                    \
+        o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, pq, o[dt], 0, 0, 0,            \
+                                                                static_cast<int>(vsw), 0,           \
+                                                                static_cast<int>(pe8));             \
+      } else {                                                                                      \
+        const v4i a = *reinterpret_cast<const v4i*>(vl + vrow * VROW + g * 16);                     \
+        o[dt] = mfma_fp4(a, v4i{pq[0], pq[1], pq[2], pq[3]}, vsw, pe8, o[dt]);                      \
+      }                                                                                             \
     }                                                                                               \
   } while (0)
 
@@ -300,13 +348,21 @@ hipError_t launch_attn_mxfp4(const AttnArgs& a, const uint8_t* q4, const uint8_t
   const int nqt = a.Npad / kQTile;
   const dim3 grid(a.BH * nqt), block(256);
   auto* o = static_cast<_Float16*>(a.out);
+  const bool pv8 = (a.mode == 5);
+#define SAGE_LAUNCH4(D_, C_, P_) \
+  attn_mxfp4_kernel<D_, C_, P_><<<grid, block, 0, s>>>(q4, qe, k4, ke, v4, ve, o, a.N, a.Npad, a.sl2, a.BH)
+#define SAGE_LAUNCH4_PV(D_, C_)                         \
+  do {                                                  \
+    if (pv8) SAGE_LAUNCH4(D_, C_, true);                \
+    else SAGE_LAUNCH4(D_, C_, false);                   \
+  } while (0)
   if (a.d == 128) {
-    if (a.causal) attn_mxfp4_kernel<128, true><<<grid, block, 0, s>>>(q4, qe, k4, ke, v4, ve, o, a.N, a.Npad, a.sl2, a.BH);
-    else attn_mxfp4_kernel<128, false><<<grid, block, 0, s>>>(q4, qe, k4, ke, v4, ve, o, a.N, a.Npad, a.sl2, a.BH);
+    if (a.causal) SAGE_LAUNCH4_PV(128, true); else SAGE_LAUNCH4_PV(128, false);
   } else {
-    if (a.causal) attn_mxfp4_kernel<64, true><<<grid, block, 0, s>>>(q4, qe, k4, ke, v4, ve, o, a.N, a.Npad, a.sl2, a.BH);
-    else attn_mxfp4_kernel<64, false><<<grid, block, 0, s>>>(q4, qe, k4, ke, v4, ve, o, a.N, a.Npad, a.sl2, a.BH);
+    if (a.causal) SAGE_LAUNCH4_PV(64, true); else SAGE_LAUNCH4_PV(64, false);
   }
+#undef SAGE_LAUNCH4_PV
+#undef SAGE_LAUNCH4
   return hipGetLastError();
 }
 

@@ -410,6 +410,95 @@ __global__ __launch_bounds__(256) void mx_vt_kernel(const uint16_t* __restrict__
   e8[rowc * (Nv / 32) + n0 / 32] = static_cast<uint8_t>(eb);
 }
 
+// ---------------------------------------------------------------------------
+// MX-FP8 (E4M3 elements) for V, the accuracy variant of the FP4 path: per
+// block of 32 tokens of one channel, e = floor(log2 max|x|) - 8 clamped to
+// [-127, 127] (0 for an all-zero block), element = nearest E4M3 value to
+// x * 2^-e with ties to even, saturating at 448. The rounding is the hardware
+// conversion (v_cvt_scalef32_pk_fp8_f32: divides by the power-of-two scale,
+// rounds to nearest even); it turns values past 448 into NaN, so they are
+// clamped to +-448 * 2^e first.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int mx_exponent8(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const int E = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);
+  const int e = E - 135;  // floor(log2 a) - 8 for a normal a
+  return e < -127 ? -127 : e;
+}
+
+typedef short v2s_t __attribute__((ext_vector_type(2)));
+
+// 32 floats -> 32 E4M3 bytes (element i in byte i) + exponent byte.
+__device__ __forceinline__ void mx_block8(const float* x, uint4& lo, uint4& hi, unsigned& e8) {
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));
+  const int e = mx_exponent8(a);
+  e8 = static_cast<unsigned>(e + 127);
+  const float scale = ldexpf(1.f, e);
+  const float lim = 448.f * scale;
+  unsigned w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    v2s_t r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(fmaxf(x[4 * k], -lim), lim),
+                                                 fminf(fmaxf(x[4 * k + 1], -lim), lim), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(fmaxf(x[4 * k + 2], -lim), lim),
+                                                 fminf(fmaxf(x[4 * k + 3], -lim), lim), scale, true);
+    w[k] = __builtin_bit_cast(unsigned, r);
+  }
+  lo = make_uint4(w[0], w[1], w[2], w[3]);
+  hi = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void mx_vt8_kernel(const uint16_t* __restrict__ v, uint8_t* __restrict__ fp8,
+                                                     uint8_t* __restrict__ e8, int N, int Nv) {
+  constexpr int TT = 256 * 32 / D;  // tokens per tile: every thread owns one (channel, 32-token block)
+  constexpr int CPR = D / 8;
+  __shared__ uint16_t t[TT][D + 2];
+  const int ntile = (Nv + TT - 1) / TT;
+  const int bh = blockIdx.x / ntile, tb = blockIdx.x % ntile;
+  const int tid = threadIdx.x;
+  const uint16_t* src = v + static_cast<size_t>(bh) * N * D;
+#pragma unroll
+  for (int u = 0; u < TT * CPR / 256; ++u) {
+    const int i = tid + 256 * u, r = i / CPR, c8 = i % CPR;
+    const int n = tb * TT + r;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (n < N) val = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(n) * D + c8 * 8);
+    const unsigned w[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[r][c8 * 8 + 2 * j] = static_cast<uint16_t>(w[j] & 0xffffu);
+      t[r][c8 * 8 + 2 * j + 1] = static_cast<uint16_t>(w[j] >> 16);
+    }
+  }
+  __syncthreads();
+  const int c = tid % D, b = tid / D;
+  const int n0 = tb * TT + b * 32;
+  if (n0 >= Nv) return;
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = static_cast<float>(__builtin_bit_cast(_Float16, t[b * 32 + i][c]));
+  unsigned eb;
+  uint4 lo, hi;
+  mx_block8(x, lo, hi, eb);
+  const size_t rowc = static_cast<size_t>(bh) * D + c;
+  *reinterpret_cast<uint4*>(fp8 + rowc * Nv + n0) = lo;
+  *reinterpret_cast<uint4*>(fp8 + rowc * Nv + n0 + 16) = hi;
+  e8[rowc * (Nv / 32) + n0 / 32] = static_cast<uint8_t>(eb);
+}
+
+hipError_t launch_mx_vt8(const void* v, uint8_t* fp8, uint8_t* e8, int BH, int N, int Nv, int d, hipStream_t s) {
+  const int TT = 256 * 32 / d;
+  const int grid = BH * ((Nv + TT - 1) / TT);
+  if (d == 128) mx_vt8_kernel<128><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp8, e8, N, Nv);
+  else mx_vt8_kernel<64><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp8, e8, N, Nv);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_vt(const void* v, uint8_t* fp4, uint8_t* e8, int BH, int N, int Nv, int d, hipStream_t s) {
   const int TT = 256 * 32 / d;
   const int grid = BH * ((Nv + TT - 1) / TT);

@@ -48,7 +48,7 @@ struct Layout {
   // MXFP4 mode
   size_t q_fp4 = 0, k_fp4 = 0;    // uint8 [BH, Npad, d/2]
   size_t q_e8 = 0, k_e8 = 0;      // uint8 [BH, Npad, d/32]
-  size_t vt_fp4 = 0, vt_e8 = 0;   // uint8 [BH, d, Npad/2], [BH, d, Npad/32]
+  size_t vt_fp4 = 0, vt_e8 = 0;   // uint8 [BH, d, Npad/2] (E4M3 variant: [BH, d, Npad]), [BH, d, Npad/32]
   size_t total = 0;
 };
 
@@ -67,12 +67,12 @@ inline Layout make_layout(long long BH, int N, int d, int mode_lo, bool attentio
   L.kmean = take(size_t(BH) * d * 4);
   if (attention) {
     const size_t rows = size_t(BH) * L.Npad;
-    if (mode_lo == 2) {
+    if (mode_lo == 2 || mode_lo == 5) {
       L.q_fp4 = take(rows * d / 2);
       L.k_fp4 = take(rows * d / 2);
       L.q_e8 = take(rows * d / 32);
       L.k_e8 = take(rows * d / 32);
-      L.vt_fp4 = take(rows * d / 2);
+      L.vt_fp4 = take(mode_lo == 5 ? rows * d : rows * d / 2);  // V^T codes: E2M1 (packed) or E4M3
       L.vt_e8 = take(rows * d / 32);
     } else if (mode_lo == 4) {  // SAGE_MODE_FP16: V^T only
       L.vt = take(rows * d * 2);
@@ -127,6 +127,8 @@ hipError_t launch_mx_rows(const MxRowJob& j0, const MxRowJob& j1, int BH, int N,
 // MXFP4 quantization of V along tokens: -> fp4 [BH, d, Nv/2], e8 [BH, d, Nv/32]
 // (Nv a multiple of 32, tokens >= N are zeros).
 hipError_t launch_mx_vt(const void* v, uint8_t* fp4, uint8_t* e8, int BH, int N, int Nv, int d, hipStream_t s);
+// The same with MX-FP8 (E4M3, one byte per element) codes: fp8 [BH, d, Nv].
+hipError_t launch_mx_vt8(const void* v, uint8_t* fp8, uint8_t* e8, int BH, int N, int Nv, int d, hipStream_t s);
 
 // Fused attention from a prepared workspace.
 struct AttnArgs {
@@ -140,6 +142,8 @@ struct AttnArgs {
 // SAGE_MODE_FP16, the caller's fp16 Q and K [BH, N, d] (qs, ks unused).
 hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, const void* vt,
                             const float* qs, const float* ks, hipStream_t s);
+// v4 holds E2M1 V^T codes, or E4M3 ones for SAGE_MODE_MXFP4_FP8PV (a.mode 5,
+// where P is quantized to MX-FP8 as well).
 hipError_t launch_attn_mxfp4(const AttnArgs& a, const uint8_t* q4, const uint8_t* qe,
                              const uint8_t* k4, const uint8_t* ke, const uint8_t* v4,
                              const uint8_t* ve, hipStream_t s);

@@ -58,10 +58,13 @@ typedef enum sage_status {
 #define SAGE_MODE_FP16 4           /* no quantization: fp16 Q K^T on the FP16 matrix op, same */
                                    /* online softmax and fp16 P.V (FlashAttention-style        */
                                    /* baseline of the same kernel; reads q, k when computing)  */
+#define SAGE_MODE_MXFP4_FP8PV 5    /* MXFP4 Q, K_s; P and V in MX-FP8 (E4M3 + E8M0 per 32):   */
+                                   /* the accuracy variant of SAGE_MODE_MXFP4                 */
 #define SAGE_MODE_MASK 0xff
 
 /* Flags OR-ed into `mode` (or passed as `flags`). */
 #define SAGE_FLAG_NO_SMOOTH 0x100  /* skip the K mean subtraction (ablation only) */
+#define SAGE_FLAG_FP8_V 0x200      /* sage_quant_mxfp4 only: V in MX-FP8 (E4M3) codes */
 
 /* Human-readable name of a status code; never NULL. */
 const char* sage_status_string(int status);
@@ -147,12 +150,16 @@ int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, int 
  *   q_e8m0, k_e8m0 uint8 [B, H, N, d/32]: blocks of 32 channels.
  *   vt_fp4   uint8 [B, H, d, Nv/2], Nv = N rounded up to a multiple of 32:
  *            V transposed, blocks of 32 tokens per channel, zero-padded.
+ *            With SAGE_FLAG_FP8_V: uint8 [B, H, d, Nv] E4M3 codes (one per byte).
  *   vt_e8m0  uint8 [B, H, d, Nv/32].
- *   k_mean   fp32 [B, H, d] or NULL. flags: 0 or SAGE_FLAG_NO_SMOOTH.
+ *   k_mean   fp32 [B, H, d] or NULL.
+ *   flags    0, SAGE_FLAG_NO_SMOOTH and/or SAGE_FLAG_FP8_V.
  * Definitions (bit-exact): a = max |x| over the block; e = floor(log2 a) - 2
  * clamped to [-127, 127] (e = 0 when a = 0); E8M0 byte = e + 127; element =
  * E2M1 value nearest to x * 2^-e (ties to the even code, saturating at 6),
- * sign bit = sign bit of x.
+ * sign bit = sign bit of x. MX-FP8 (V with SAGE_FLAG_FP8_V): e = floor(log2 a)
+ * - 8, element = E4M3 value nearest to x * 2^-e (ties to the even code,
+ * saturating at 448).
  */
 int sage_quant_mxfp4(const void* q, const void* k, const void* v, int B, int H, int N, int d,
                      int flags, uint8_t* q_fp4, uint8_t* q_e8m0, uint8_t* k_fp4, uint8_t* k_e8m0,

@@ -5,7 +5,8 @@ quantization-emulating oracle with fp64 exact attention (cosine similarity,
 relative L1, RMSE, max abs) for the INT8 per-block path as configured, and the
 ablations the SageAttention page's "Measured effects" table reports the
 direction of: no K smoothing, and per-token scales (blocks of 1 token).
-MXFP4 runs the microscaled-FP4 emulation. Test infrastructure: the numbers
+MXFP4 runs the microscaled-FP4 emulation (and its variant with MX-FP8 P and
+V). Test infrastructure: the numbers
 describe the method (what any faithful kernel computes), not a kernel.
 Usage: python oracle/method_accuracy.py [workload ...] > table.md
 """
@@ -50,7 +51,10 @@ def main(names):
                 variants = {"MXFP4 (Q, K_s, V, P)": O.mxfp4_attention(qs, ks, vs, causal=w.causal,
                                                                       sm_scale=w.sm_scale, rows=rows),
                             "MXFP4, no K smoothing": O.mxfp4_attention(qs, ks, vs, causal=w.causal,
-                                                                       sm_scale=w.sm_scale, rows=rows, smooth=False)}
+                                                                       sm_scale=w.sm_scale, rows=rows, smooth=False),
+                            "MXFP4 Q, K_s; MX-FP8 P, V": O.mxfp4_attention(qs, ks, vs, causal=w.causal,
+                                                                          sm_scale=w.sm_scale, rows=rows,
+                                                                          pv_fp8=True)}
             else:
                 bq = 128 if w.mode == "int8_q128_k64" else 64
                 variants = {

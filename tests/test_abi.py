@@ -50,9 +50,11 @@ def test_workspace_sizes():
     n = 4 * 32 * 4096 * 128
     assert 4 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 0) < 4.2 * n
     assert 1.5 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 2) < 1.8 * n
-    # FP16 baseline: only V^T (2 B/elem)
+    # FP16 baseline: only V^T (2 B/elem); MXFP4 with MX-FP8 V: ~2.1 B/elem
     assert 2 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 4) < 2.1 * n
-    assert sa.sage_attn_workspace_size(1, 2, 256, 64, 5) == 0
+    assert 2 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 5) < 2.3 * n
+    assert sa.sage_attn_workspace_size(1, 2, 256, 64, 6) == 0
+    assert sa.sage_attn_workspace_size(1, 2, 256, 64, 0x200 | 2) == 0   # the V-format flag is quantization-only
     assert sa.sage_quant_workspace_size(1, 2, 256, 64) > 0
 
 
@@ -85,7 +87,7 @@ def test_prepare_compute_and_quant_validation():
     ws4 = sa.sage_attn_workspace_size(1, 2, 256, 64, 4)
     assert lib.sage_attn_compute(None, A16, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
     assert lib.sage_attn_compute(A16, A16 + 2, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
-    assert lib.sage_attn_compute(A16, A16, A16, 1, 2, 256, 64, 0, 0.1, 5, A16, ws4, None) == UNSUP
+    assert lib.sage_attn_compute(A16, A16, A16, 1, 2, 256, 64, 0, 0.1, 6, A16, ws4, None) == UNSUP
     qw = sa.sage_quant_workspace_size(1, 2, 256, 64)
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 48, 64, 0, A16, A16, A16, A16, None, A16, qw, None) == UNSUP
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 4, A16, A16, A16, A16, None, A16, qw, None) == UNSUP

@@ -58,15 +58,17 @@ def test_int8_quant_bitexact(sa, case):
         assert np.array_equal(got["k_mean"].cpu().numpy().view(np.uint32), ref["k_mean"].view(np.uint32))
 
 
-MX_CASES = [(1, 2, 256, 64, 0), (2, 2, 1000, 128, 0), (1, 1, 33, 128, 0), (1, 2, 96, 64, 0x100)]
+MX_CASES = [(1, 2, 256, 64, 0), (2, 2, 1000, 128, 0), (1, 1, 33, 128, 0), (1, 2, 96, 64, 0x100),
+            (1, 2, 300, 128, 0x200), (1, 1, 33, 64, 0x300)]   # 0x200: V in MX-FP8 (E4M3)
 
 
 @pytest.mark.parametrize("case", MX_CASES, ids=lambda c: "x".join(map(str, c)))
 def test_mxfp4_quant_bitexact(sa, case):
     B, H, N, d, flags = case
     say("mxfp4 quant", case)
+    fp8v = bool(flags & 0x200)
     q, k, v = make_custom(B, H, N, d, seed=7 * N + d)
-    ref = O.quant_mxfp4(q, k, v, smooth=not flags)
+    ref = O.quant_mxfp4(q, k, v, smooth=not (flags & 0x100), v_fp8=fp8v)
     qd, kd, vd = _dev(q, k, v)
     got = sa.sage_quant_mxfp4(qd, kd, vd, flags=flags)
     torch.cuda.synchronize()
@@ -77,7 +79,8 @@ def test_mxfp4_quant_bitexact(sa, case):
     Nv = -(-N // 32) * 32
     vcodes = np.zeros((B, H, Nv, d), np.uint8)
     vcodes[:, :, :N] = ref["v_codes"]
-    assert np.array_equal(got["vt_fp4"].cpu().numpy(), O.pack_fp4(np.swapaxes(vcodes, 2, 3)))
+    vt = np.swapaxes(vcodes, 2, 3)
+    assert np.array_equal(got["vt_fp4"].cpu().numpy(), vt if fp8v else O.pack_fp4(vt))
     assert np.array_equal(got["vt_e8m0"].cpu().numpy(), np.swapaxes(ref["v_e8m0"], 2, 3))
 
 
@@ -150,6 +153,31 @@ MXATTN_CASES = [
 ]
 
 
+MX8ATTN_CASES = [
+    (1, 2, 256, 64, False),
+    (1, 2, 1000, 128, False),
+    (1, 2, 777, 128, True),
+    (1, 1, 1, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", MX8ATTN_CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"-c{int(c[4])}")
+def test_mxfp4_fp8pv_attention_matches_oracle(sa, case):
+    B, H, N, d, causal = case
+    say("mxfp4 + fp8 P,V attention", case)
+    q, k, v = make_custom(B, H, N, d, seed=13 * N + d)
+    sm = 1.0 / np.sqrt(d)
+    ref = O.mxfp4_attention(q, k, v, causal=causal, sm_scale=sm, pv_fp8=True)
+    qd, kd, vd = _dev(q, k, v)
+    out = sa.sage_attn_fwd(qd, kd, vd, causal=causal, sm_scale=sm, mode=sa.SAGE_MODE_MXFP4_FP8PV)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = assert_output_parity(got, ref, what=f"mxfp4-fp8pv {case}")
+    ex = O.exact_attention(q, k, v, causal=causal, sm_scale=sm)
+    say(f"  max err vs oracle {err:.2e}; cos vs fp64 gpu {O.metrics(got, ex)['cos']:.6f} "
+        f"oracle {O.metrics(ref, ex)['cos']:.6f}")
+
+
 @pytest.mark.parametrize("case", MXATTN_CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"-c{int(c[4])}")
 def test_mxfp4_attention_matches_oracle(sa, case):
     B, H, N, d, causal = case
@@ -167,7 +195,7 @@ def test_mxfp4_attention_matches_oracle(sa, case):
         f"oracle {O.metrics(ref, ex)['cos']:.6f}")
 
 
-@pytest.mark.parametrize("mode", [0, 2, 4])
+@pytest.mark.parametrize("mode", [0, 2, 4, 5])
 def test_prepare_compute_equals_fwd_and_is_deterministic(sa, mode):
     say("determinism mode", mode)
     q, k, v = make_custom(1, 2, 700, 128, seed=11)

@@ -4,7 +4,8 @@ For each workload, on sampled heads and query rows, compares the
 quantization-emulating oracle with fp64 exact attention (cosine similarity,
 relative L1, RMSE, max abs) for the INT8 per-block path as configured, and the
 ablations the SageAttention page's "Measured effects" table reports the
-direction of: no K smoothing, and per-token scales (blocks of 1 token).
+direction of: no K smoothing, per-token scales (blocks of 1 token), and INT8
+P and V (per-block and per-token Q, K).
 MXFP4 runs the microscaled-FP4 emulation (and its variant with MX-FP8 P and
 V). Test infrastructure: the numbers
 describe the method (what any faithful kernel computes), not a kernel.
@@ -65,6 +66,12 @@ def main(names):
                                                                        rows=rows, smooth=False),
                     "INT8 per-token": O.int8_attention(qs, ks, vs, causal=w.causal, sm_scale=w.sm_scale,
                                                        blk_q=1, blk_k=1, rows=rows),
+                    "INT8 per-block, INT8 P and V": O.int8_pv_attention(qs, ks, vs, causal=w.causal,
+                                                                        sm_scale=w.sm_scale, blk_q=bq, blk_k=64,
+                                                                        rows=rows),
+                    "INT8 per-token, INT8 P and V": O.int8_pv_attention(qs, ks, vs, causal=w.causal,
+                                                                        sm_scale=w.sm_scale, blk_q=1, blk_k=1,
+                                                                        rows=rows),
                 }
             for key, val in variants.items():
                 results.setdefault(key, []).append((val, ex))

@@ -57,6 +57,13 @@ Readings where the pages are silent (each also listed in the design doc):
      a = 0 gives e = 0 and all codes 0. Element code = nearest E2M1 value to
      x * 2^-e, ties to the even code index, saturating at +-6; the sign bit is
      the sign bit of x. Packing: element 2k in the low nibble of byte k.
+  R14 INT8 P and V (the "Quantize P,V to INT8" ablation of [SA-Effects];
+     the page gives no granularity): V gets one scale per (head, channel) over
+     all tokens, with the R3/R4 rules (a = max|V|, s = fp32(a / 127), code =
+     rint_half_even(fp32(V / s))); P is formed against the plain running max
+     (slack 0), so 0 <= P <= 1, and quantized with the fixed scale 1/127:
+     code = rint_half_even(127 P). l sums the quantized P, O accumulates the
+     quantized P times the dequantized V.
   R13 MX-FP8 variant for P and V (not on the pages; the accuracy variant of
      the FP4 path): the same blocks as R8, e = floor(log2 a) - 8 (E4M3's largest
      binade is 2^8), element = nearest E4M3 value to x * 2^-e, ties to the even
@@ -252,6 +259,56 @@ def int8_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, 
                 S[_causal_mask(rows, keys)] = -np.inf
             out[b, h] = online_softmax_pv(S, as_f64(v16[b, h]), kv_tile=kv_tile, round_p=round16,
                                           ref_slack=ref_slack, sum_rounded=True)
+    return out
+
+
+def int8_quant_v_channels(v16):
+    """INT8 codes of V with one scale per (b, h, channel) over all tokens (reading R14).
+
+    a = max over tokens of |V|, s = fp32(a / 127) (correctly rounded), code =
+    rint_half_even(fp32(V / s)) in [-127, 127]; a = 0 gives s = 0 and codes 0.
+    Returns (codes int8 [B, H, N, d], scales float32 [B, H, d]).
+    """
+    v32 = np.asarray(v16).astype(np.float32)
+    amax = np.abs(v32).max(axis=2)                               # [B, H, d], exact
+    scales = (amax / np.float32(127.0)).astype(np.float32)       # fp32 division, correctly rounded
+    safe = np.where(scales > 0, scales, np.float32(1.0)).astype(np.float32)
+    codes = np.clip(np.rint(v32 / safe[:, :, None, :]), -127, 127)   # fp32 division, ties to even
+    codes = np.where((scales > 0)[:, :, None, :], codes, 0.0).astype(np.int8)
+    return codes, scales
+
+
+def int8_pv_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, blk_k: int,
+                      kv_tile: int = 64, smooth: bool = True, rows=None, quant=None):
+    """The INT8 P,V variant ([SA-Effects]: "Quantize P,V to INT8 rather than
+    retaining FP16"; [SA-Approach]: the faster kernel chosen per layer where
+    cosine similarity stays above 99.8%), float64 out.
+
+    Q and K_s as in int8_attention (R1-R5; blk_q = blk_k = 1 is the per-token
+    form). V: per-channel INT8 (R14). Online softmax against the plain running
+    max (R6 with slack 0), P quantized to rint(127 P) / 127 (R14); l sums the
+    quantized P; O accumulates quantized P times dequantized V.
+    Returns float64 [B, H, len(rows), d].
+    """
+    B, H, N, d = q16.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    keys = np.arange(N)
+    qd = quant if quant is not None else quant_qk_int8(q16, k16, blk_q=blk_q, blk_k=blk_k, smooth=smooth)
+    vc, vs = int8_quant_v_channels(v16)
+    round127 = lambda P: np.rint(127.0 * P) / 127.0
+    out = np.empty((B, H, rows.size, d))
+    for b in range(B):
+        for h in range(H):
+            cq = qd["q_codes"][b, h, rows].astype(np.float64)
+            ck = qd["k_codes"][b, h].astype(np.float64)
+            sq = qd["q_scales"][b, h][rows // blk_q].astype(np.float64)
+            sk = qd["k_scales"][b, h][keys // blk_k].astype(np.float64)
+            S = (cq @ ck.T) * sq[:, None] * sk[None, :] * sm_scale
+            if causal:
+                S[_causal_mask(rows, keys)] = -np.inf
+            Vh = vc[b, h].astype(np.float64) * vs[b, h].astype(np.float64)[None, :]
+            out[b, h] = online_softmax_pv(S, Vh, kv_tile=kv_tile, round_p=round127, ref_slack=0.0,
+                                          sum_rounded=True)
     return out
 
 

@@ -536,3 +536,174 @@ def test_reference_max_slack_only_moves_rounding(causal):
     seen = []
     O.online_softmax_pv(S, V, kv_tile=1, round_p=lambda P: (seen.append(P.max()), P)[1], ref_slack=8.0)
     assert abs(max(seen) - 8.0) < 1e-12   # row 0: the reference stays at 0 while the max climbs to 3
+
+
+# ---------------------------------------------------------------------------
+# INT8 P and V variant (reading R14)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N", [1, 37, 130])
+def test_int8_v_channel_codes_exact(N):
+    v = (RNG.standard_normal((1, 2, N, 6)) * 3.0).astype(np.float16)
+    v[0, 1, :, 4] = 0                                    # an all-zero channel: scale 0, codes 0
+    codes, scales = O.int8_quant_v_channels(v)
+    assert codes.shape == v.shape and scales.shape == (1, 2, 6)
+    for h in range(2):
+        for c in range(6):
+            col = v[0, h, :, c].astype(np.float32)
+            a = Fraction(float(np.abs(col).max()))
+            s = _f32_round(a / 127)
+            assert Fraction(float(scales[0, h, c])) == s
+            if s == 0:
+                assert np.all(codes[0, h, :, c] == 0)
+                continue
+            for n in range(N):
+                want = _round_half_even(_f32_round(Fraction(float(col[n])) / s))
+                assert int(codes[0, h, n, c]) == want
+            assert abs(int(codes[0, h, int(np.argmax(np.abs(col))), c])) == 127
+
+
+def _int8_pv_direct(q, k, v, *, causal, sm_scale, blk):
+    """Brute-force loops for the INT8 P,V variant when the softmax reference is the
+    row max over all keys: P = exp(S - max), weight = round_half_even(127 P),
+    O = sum(weight * V_hat) / sum(weight). Codes come from the (separately pinned)
+    quantizers; scores, weights and sums are plain Python."""
+    d = O.quant_qk_int8(q, k, blk_q=blk, blk_k=blk)
+    vc, vs = O.int8_quant_v_channels(v)
+    _, H, N, D = q.shape
+    out = np.zeros((1, H, N, D))
+    for h in range(H):
+        for i in range(N):
+            S = []
+            for j in range(N):
+                if causal and j > i:
+                    continue
+                dot = sum(int(d["q_codes"][0, h, i, c]) * int(d["k_codes"][0, h, j, c]) for c in range(D))
+                S.append((j, dot * float(d["q_scales"][0, h, i // blk]) * float(d["k_scales"][0, h, j // blk]) * sm_scale))
+            mx = max(s for _, s in S)
+            w = [(j, round(127.0 * math.exp(s - mx))) for j, s in S]
+            tot = sum(x for _, x in w)
+            for c in range(D):
+                out[0, h, i, c] = sum(x * int(vc[0, h, j, c]) * float(vs[0, h, c]) for j, x in w) / tot
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_pv_single_tile_matches_direct_loops(causal):
+    # one key tile: the running max is the row max, so the online form is the direct formula
+    q, k, v = make_custom(1, 2, 50, 8, seed=31)
+    got = O.int8_pv_attention(q, k, v, causal=causal, sm_scale=0.4, blk_q=64, blk_k=64)
+    want = _int8_pv_direct(q, k, v, causal=causal, sm_scale=0.4, blk=64)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_int8_pv_max_in_first_tile_matches_direct_loops():
+    # Key 0 dominates every row, so the running max never moves after the first tile and the
+    # four tiles (last one ragged) must add up to the direct formula.
+    rng = np.random.default_rng(32)
+    q = (np.abs(rng.standard_normal((1, 1, 200, 8))) + 0.5).astype(np.float16)
+    k = (rng.standard_normal((1, 1, 200, 8)) * 0.3).astype(np.float16)
+    k[0, 0, 0] = 4.0
+    v = rng.standard_normal((1, 1, 200, 8)).astype(np.float16)
+    got = O.int8_pv_attention(q, k, v, causal=False, sm_scale=0.5, blk_q=1, blk_k=1, smooth=False)
+    dq = O.quant_qk_int8(q, k, blk_q=1, blk_k=1, smooth=False)
+    S0 = (dq["q_codes"][0, 0].astype(float) @ dq["k_codes"][0, 0].astype(float).T) * dq["q_scales"][0, 0][:, None] \
+        * dq["k_scales"][0, 0][None, :]
+    assert np.all(np.argmax(S0, axis=1) == 0)
+    want = _int8_pv_direct_nosmooth(q, k, v, sm_scale=0.5)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def _int8_pv_direct_nosmooth(q, k, v, *, sm_scale):
+    d = O.quant_qk_int8(q, k, blk_q=1, blk_k=1, smooth=False)
+    vc, vs = O.int8_quant_v_channels(v)
+    _, _, N, D = q.shape
+    out = np.zeros((1, 1, N, D))
+    for i in range(N):
+        S = [sum(int(d["q_codes"][0, 0, i, c]) * int(d["k_codes"][0, 0, j, c]) for c in range(D))
+             * float(d["q_scales"][0, 0, i]) * float(d["k_scales"][0, 0, j]) * sm_scale for j in range(N)]
+        mx = max(S)
+        w = [round(127.0 * math.exp(s - mx)) for s in S]
+        for c in range(D):
+            out[0, 0, i, c] = sum(w[j] * int(vc[0, 0, j, c]) * float(vs[0, 0, c]) for j in range(N)) / sum(w)
+    return out
+
+
+def test_int8_pv_running_max_moves_the_weights():
+    # When the max moves, earlier tiles keep the weights they were given against the old max
+    # (then rescaled by exp(m_old - m_new)). Scores 0 then 3 (natural log units), one key per tile:
+    # tile 0 weight round(127) = 127, tile 1 weight 127 and tile 0 becomes 127 e^-3.
+    S = np.array([[0.0, 3.0]])
+    V = np.array([[1.0], [0.0]])
+    got = O.online_softmax_pv(S, V, kv_tile=1, round_p=lambda P: np.rint(127.0 * P) / 127.0, ref_slack=0.0,
+                              sum_rounded=True)
+    w0 = 127 * math.exp(-3.0)
+    assert abs(got[0, 0] - w0 / (w0 + 127)) < 1e-15
+    # single-tile form of the same row: weights against the final max, round(127 e^-3) = 6
+    one = O.online_softmax_pv(S, V, kv_tile=2, round_p=lambda P: np.rint(127.0 * P) / 127.0, ref_slack=0.0,
+                              sum_rounded=True)
+    assert abs(one[0, 0] - 6 / 133) < 1e-15
+
+
+def test_int8_pv_constant_v_and_weights_in_range():
+    q, k, _ = make_custom(1, 1, 200, 32, seed=33)
+    v = np.full((1, 1, 200, 32), 1.5, np.float16)
+    _, vs = O.int8_quant_v_channels(v)
+    o = O.int8_pv_attention(q, k, v, causal=True, sm_scale=0.2, blk_q=64, blk_k=64)
+    # l sums the same quantized P that weights V: a constant channel comes back as its
+    # dequantized value 127 * s
+    assert np.max(np.abs(o - 127.0 * vs[0, 0, 0].astype(np.float64))) <= 1e-14
+    seen = []
+    S = np.array([[0.0, -0.001, -5.0, -0.5, 2.0, 1.9999]])
+    O.online_softmax_pv(S, np.ones((6, 1)), kv_tile=2,
+                        round_p=lambda P: (seen.append(np.rint(127.0 * P)), np.rint(127.0 * P) / 127.0)[1],
+                        ref_slack=0.0, sum_rounded=True)
+    w = np.concatenate(seen, axis=1)
+    assert w.min() >= 0 and w.max() == 127 and np.all(w == np.rint(w))
+
+
+def test_int8_pv_is_less_accurate_than_fp16_pv():
+    # "Measured effects": quantizing P and V to INT8 lowers cosine similarity (99.94% -> 99.70%
+    # across real-model layers); the direction holds on the synthetic prefill-like data.
+    q, k, v = make_custom(1, 2, 512, 64, seed=34, k_offset_std=3.0)
+    ex = O.exact_attention(q, k, v, causal=False, sm_scale=0.125)
+    fp16pv = O.metrics(O.int8_attention(q, k, v, causal=False, sm_scale=0.125, blk_q=128, blk_k=64), ex)["cos"]
+    int8pv = O.metrics(O.int8_pv_attention(q, k, v, causal=False, sm_scale=0.125, blk_q=128, blk_k=64), ex)["cos"]
+    assert int8pv < fp16pv
+    assert int8pv > 0.99
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_pv_multi_tile_matches_python_loops(causal):
+    # Three 64-key tiles (the last ragged) on data whose row max moves between tiles: a
+    # pure-Python running-max loop with integer weights round(127 exp(S - m)), the earlier
+    # partial sums rescaled by exp(m_old - m_new) when m moves.
+    q, k, v = make_custom(1, 1, 150, 8, seed=35, k_offset_std=1.0)
+    got = O.int8_pv_attention(q, k, v, causal=causal, sm_scale=0.6, blk_q=64, blk_k=64)
+    d = O.quant_qk_int8(q, k, blk_q=64, blk_k=64)
+    vc, vs = O.int8_quant_v_channels(v)
+    N, D = 150, 8
+    moved = 0
+    for i in range(N):
+        m, lsum, acc = -math.inf, 0.0, [0.0] * D
+        for t0 in range(0, N, 64):
+            keys = [j for j in range(t0, min(t0 + 64, N)) if not (causal and j > i)]
+            if not keys:
+                continue
+            S = {j: sum(int(d["q_codes"][0, 0, i, c]) * int(d["k_codes"][0, 0, j, c]) for c in range(D))
+                 * float(d["q_scales"][0, 0, i // 64]) * float(d["k_scales"][0, 0, j // 64]) * 0.6 for j in keys}
+            mt = max(S.values())
+            if mt > m:
+                f = math.exp(m - mt) if m > -math.inf else 0.0
+                lsum, acc = lsum * f, [a * f for a in acc]
+                moved += m > -math.inf
+                m = mt
+            for j in keys:
+                w = round(127.0 * math.exp(S[j] - m))
+                assert 0 <= w <= 127
+                lsum += w
+                for c in range(D):
+                    acc[c] += w * int(vc[0, 0, j, c]) * float(vs[0, 0, c])
+        want = [a / lsum for a in acc]
+        assert max(abs(got[0, 0, i, c] - want[c]) for c in range(D)) < 1e-12
+    assert moved > 10      # the case really exercises a moving max

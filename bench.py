@@ -97,6 +97,9 @@ def cpu_baseline(name: str, mode_name: str, budget_s: float = 12.0):
                 O.mxfp4_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, pv_fp8=mode_name == "mxfp4_fp8pv")
             elif mode_name == "fp16":
                 O.fp16_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale)
+            elif mode_name in ("int8_pv", "int8_pv_per_token"):
+                b = 1 if mode_name == "int8_pv_per_token" else None
+                O.int8_pv_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, blk_q=b or 128, blk_k=b or 64)
             else:
                 bq, bk = {"int8_q128_k64": (128, 64), "int8_q64_k64": (64, 64), "int8_per_token": (1, 1)}[mode_name]
                 O.int8_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, blk_q=bq, blk_k=bk)
@@ -117,8 +120,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sdpa", action="store_true", help="skip timing torch's FP16 SDPA for context")
     ap.add_argument("--mode", default=None,
-                    choices=["int8_q128_k64", "int8_q64_k64", "int8_per_token", "mxfp4", "fp16", "mxfp4_fp8pv"],
-                    help="override the workload's quantization mode (ablations; fp16 = unquantized baseline)")
+                    choices=["int8_q128_k64", "int8_q64_k64", "int8_per_token", "mxfp4", "fp16", "mxfp4_fp8pv",
+                             "int8_pv", "int8_pv_per_token"],
+                    help="override the workload's quantization mode (ablations; fp16 = unquantized baseline; "
+                         "int8_pv* = P and V in INT8 as well)")
     ap.add_argument("--no-smooth", action="store_true", help="skip the K mean subtraction (ablation)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
@@ -150,7 +155,7 @@ def main():
     w = WORKLOADS[args.workload]
     mode_name = args.mode or w.mode
     mode = {"int8_q128_k64": 0, "int8_q64_k64": 1, "mxfp4": 2, "int8_per_token": 3, "fp16": 4,
-            "mxfp4_fp8pv": 5}[mode_name]
+            "mxfp4_fp8pv": 5, "int8_pv": 6, "int8_pv_per_token": 7}[mode_name]
     flags = sa.SAGE_FLAG_NO_SMOOTH if args.no_smooth else 0
     t0 = time.perf_counter()
     q, k, v = make_inputs(w.name)
@@ -188,12 +193,17 @@ def main():
         # unquantized baseline: only V -> V^T (read 2 B, write 2 B)
         quant_bytes = n_el * 4
         peak, src = PEAK["fp16"], "attn_int8.hip"
-        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},2>"
+        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},2,false>"
+    elif mode in (6, 7):
+        # read K (mean), Q, K, V (channel maxima), V (codes) (2 B each); write Q/K/V^T codes (1 B each)
+        quant_bytes = n_el * 10 + n_el * 3
+        peak, src = PEAK["int8"], "attn_int8.hip"
+        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},{1 if mode == 7 else 0},true>"
     else:
         # read K (mean), Q, K, V (2 B each); write Q/K codes (1 B each) and V^T (2 B)
         quant_bytes = n_el * 8 + n_el * 4
         peak, src = PEAK["int8"], "attn_int8.hip"
-        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},{1 if mode == 3 else 0}>"
+        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},{1 if mode == 3 else 0},false>"
     roofline = {"bound": "mfma", "achieved": round(tops_attn, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tops_attn / peak, 4),
                 "traffic": load_traffic(f"{src[:-4]}_{w.name}", src) if (mode_name == w.mode and not flags) else None,
@@ -230,7 +240,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {2: "mxfp4", 4: "f16", 5: "mxfp4+mxfp8"}.get(mode, "int8+f16"),
+        "dtype": {2: "mxfp4", 4: "f16", 5: "mxfp4+mxfp8", 6: "int8", 7: "int8"}.get(mode, "int8+f16"),
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "mode": mode_name, "k_smoothing": not args.no_smooth, "global_batch": w.B, "seq_len": w.N},

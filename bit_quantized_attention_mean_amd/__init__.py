@@ -11,6 +11,7 @@ Functions carry the C names:
   sage_attn_workspace_size(B, H, N, d, mode)
   sage_quant_qk(q, k, blk_q, blk_k, flags)  -> dict of codes/scales/mean
   sage_quant_mxfp4(q, k, v, flags)         -> dict of packed codes/exponents
+  sage_quant_v_int8(v)                     -> dict of V^T codes and channel scales
 """
 from __future__ import annotations
 
@@ -20,10 +21,10 @@ import os
 
 __all__ = [
     "SAGE_MODE_INT8_Q128_K64", "SAGE_MODE_INT8_Q64_K64", "SAGE_MODE_MXFP4", "SAGE_MODE_INT8_PER_TOKEN",
-    "SAGE_MODE_FP16", "SAGE_MODE_MXFP4_FP8PV",
+    "SAGE_MODE_FP16", "SAGE_MODE_MXFP4_FP8PV", "SAGE_MODE_INT8_PV", "SAGE_MODE_INT8_PV_PER_TOKEN",
     "SAGE_FLAG_NO_SMOOTH", "SAGE_FLAG_FP8_V", "SageError", "LIB_PATH", "lib",
     "sage_attn_fwd", "sage_attn_prepare", "sage_attn_compute", "sage_attn_workspace_size",
-    "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_status_string", "sage_last_error",
+    "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_quant_v_int8", "sage_status_string", "sage_last_error",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -33,6 +34,8 @@ SAGE_MODE_MXFP4 = 2
 SAGE_MODE_INT8_PER_TOKEN = 3
 SAGE_MODE_FP16 = 4
 SAGE_MODE_MXFP4_FP8PV = 5
+SAGE_MODE_INT8_PV = 6
+SAGE_MODE_INT8_PV_PER_TOKEN = 7
 SAGE_FLAG_NO_SMOOTH = 0x100
 SAGE_FLAG_FP8_V = 0x200
 
@@ -49,6 +52,7 @@ _SIGS = {
     "sage_attn_compute": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "sage_quant_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sage_quant_mxfp4": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sage_quant_v_int8": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -60,7 +64,7 @@ def _load():
     # library first would bring in a second runtime from /opt/rocm.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_quantized_attention_mean_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python bit_quantized_attention_mean_amd/build.py` (or __graft_entry__.build())")
     so = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGS.items():
         fn = getattr(so, name)
@@ -234,4 +238,22 @@ def sage_quant_mxfp4(q, k, v, *, flags=0, stream=None):
                               _dev_ptr(res["k_mean"], "k_mean"), _dev_ptr(ws, "workspace"), ws.numel(),
                               _stream(stream))
     _check(rc, "sage_quant_mxfp4")
+    return res
+
+
+def sage_quant_v_int8(v, *, stream=None):
+    """Per-channel INT8 codes of V, transposed ([B, H, d, Nv], Nv = N rounded up to 16), and the scales."""
+    torch = _torch()
+    B, H, N, d = _shape4(v)
+    dev = v.device
+    Nv = -(-N // 16) * 16
+    res = {
+        "vt_codes": torch.empty((B, H, d, Nv), dtype=torch.int8, device=dev),
+        "v_scales": torch.empty((B, H, d), dtype=torch.float32, device=dev),
+    }
+    ws = torch.empty(max(1, sage_quant_workspace_size(B, H, N, d)), dtype=torch.uint8, device=dev)
+    rc = lib.sage_quant_v_int8(_dev_ptr(v, "v", torch.float16), B, H, N, d, _dev_ptr(res["vt_codes"], "vt_codes"),
+                               _dev_ptr(res["v_scales"], "v_scales"), _dev_ptr(ws, "workspace"), ws.numel(),
+                               _stream(stream))
+    _check(rc, "sage_quant_v_int8")
     return res

@@ -3,7 +3,8 @@
 Every .hip file under csrc/ is compiled to an object in _build/ (in parallel),
 then linked into bit_quantized_attention_mean_amd/libsage_attn.so. The library
 is replaced atomically, so a failed build leaves the previous one in place.
-Run: python -m bit_quantized_attention_mean_amd.build
+Run: python bit_quantized_attention_mean_amd/build.py (by path: importing it
+through the package would first load the library it is about to build).
 """
 from __future__ import annotations
 

@@ -25,6 +25,8 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr int kMaxN = 1 << 22;
+// INT8 P.V: the int32 P.V sums are at most 127 * 127 * N and must stay below 2^31.
+constexpr int kMaxNPv8 = 1 << 17;
 
 int check_dims(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return fail(SAGE_ERR_INVALID_ARG, "B, H and N must be >= 1 (got %d, %d, %d)", B, H, N);
@@ -48,7 +50,7 @@ int check_ptr(const void* p, const char* name, size_t align) {
 int check_mode(int mode, bool attention) {
   if (mode & ~(SAGE_MODE_MASK | SAGE_FLAG_NO_SMOOTH)) return fail(SAGE_ERR_UNSUPPORTED, "unknown flag bits in mode 0x%x", mode);
   const int lo = mode & SAGE_MODE_MASK;
-  if (lo > SAGE_MODE_MXFP4_FP8PV) return fail(SAGE_ERR_UNSUPPORTED, "unknown mode %d", lo);
+  if (lo > SAGE_MODE_INT8_PV_PER_TOKEN) return fail(SAGE_ERR_UNSUPPORTED, "unknown mode %d", lo);
   (void)attention;
   return SAGE_OK;
 }
@@ -103,6 +105,8 @@ const unsigned char* at(const void* base, size_t off) { return static_cast<const
 int validate_attn(int B, int H, int N, int d, int mode, const void* ws, size_t ws_bytes) {
   SAGE_TRY(check_dims(B, H, N, d));
   SAGE_TRY(check_mode(mode, true));
+  if (sage::mode_pv_int8(mode & SAGE_MODE_MASK) && N > kMaxNPv8)
+    return fail(SAGE_ERR_UNSUPPORTED, "N = %d exceeds %d, the limit of the INT8 P.V modes", N, kMaxNPv8);
   SAGE_TRY(check_ptr(ws, "workspace", 256));
   const sage::Layout L = sage::make_layout(static_cast<long long>(B) * H, N, d, mode & SAGE_MODE_MASK, true);
   if (ws_bytes < L.total)
@@ -141,14 +145,20 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
                           "MXFP4 V quantization kernel"));
     return SAGE_OK;
   }
-  const int blk_q = lo == SAGE_MODE_INT8_Q128_K64 ? 128 : (lo == SAGE_MODE_INT8_Q64_K64 ? 64 : 1);
-  const int blk_k = lo == SAGE_MODE_INT8_PER_TOKEN ? 1 : 64;
+  const bool per_token = lo == SAGE_MODE_INT8_PER_TOKEN || lo == SAGE_MODE_INT8_PV_PER_TOKEN;
+  const int blk_q = per_token ? 1 : (lo == SAGE_MODE_INT8_Q64_K64 ? 64 : 128);
+  const int blk_k = per_token ? 1 : 64;
   sage::Int8Job jq, jk;
   jq.src = q; jq.codes = reinterpret_cast<int8_t*>(at(ws, L.q_codes)); jq.scales = reinterpret_cast<float*>(at(ws, L.q_scales));
   jq.mu = nullptr; jq.blk = blk_q; jq.code_rows = L.Npad; jq.nscale = L.Npad / blk_q; jq.ntile = L.Npad / sage::kQTile;
   jk.src = k; jk.codes = reinterpret_cast<int8_t*>(at(ws, L.k_codes)); jk.scales = reinterpret_cast<float*>(at(ws, L.k_scales));
   jk.mu = smooth ? mu : nullptr; jk.blk = blk_k; jk.code_rows = L.Npad; jk.nscale = L.Npad / blk_k; jk.ntile = L.Npad / sage::kQTile;
   SAGE_TRY(hip_status(sage::launch_int8_quant(jq, jk, BH, N, d, s), "INT8 quantization kernel"));
+  if (sage::mode_pv_int8(lo))
+    return hip_status(sage::launch_v_int8(v, reinterpret_cast<unsigned*>(at(ws, L.vmax)),
+                                          reinterpret_cast<int8_t*>(at(ws, L.vt)),
+                                          reinterpret_cast<float*>(at(ws, L.vscale)), BH, N, L.Npad, d, L.chunk,
+                                          L.nchunk, s), "INT8 V quantization kernels");
   SAGE_TRY(hip_status(sage::launch_v_transpose(v, at(ws, L.vt), BH, N, L.Npad, d, s), "V transpose kernel"));
   return SAGE_OK;
 }
@@ -167,10 +177,13 @@ int do_compute(const void* q, const void* k, void* out, int B, int H, int N, int
     return hip_status(sage::launch_attn_mxfp4(a, at(ws, L.q_fp4), at(ws, L.q_e8), at(ws, L.k_fp4), at(ws, L.k_e8),
                                               at(ws, L.vt_fp4), at(ws, L.vt_e8), s), "MXFP4 attention kernel");
   if (lo == SAGE_MODE_FP16)
-    return hip_status(sage::launch_attn_int8(a, q, k, at(ws, L.vt), nullptr, nullptr, s), "FP16 attention kernel");
+    return hip_status(sage::launch_attn_int8(a, q, k, at(ws, L.vt), nullptr, nullptr, nullptr, s),
+                      "FP16 attention kernel");
   return hip_status(sage::launch_attn_int8(a, at(ws, L.q_codes), at(ws, L.k_codes), at(ws, L.vt),
                                            reinterpret_cast<const float*>(at(ws, L.q_scales)),
-                                           reinterpret_cast<const float*>(at(ws, L.k_scales)), s),
+                                           reinterpret_cast<const float*>(at(ws, L.k_scales)),
+                                           sage::mode_pv_int8(lo) ? reinterpret_cast<const float*>(at(ws, L.vscale))
+                                                                  : nullptr, s),
                     "INT8 attention kernel");
 }
 
@@ -194,6 +207,7 @@ const char* sage_last_error(void) { return g_err; }
 
 size_t sage_attn_workspace_size(int B, int H, int N, int d, int mode) {
   if (check_dims(B, H, N, d) != SAGE_OK || check_mode(mode, true) != SAGE_OK) return 0;
+  if (sage::mode_pv_int8(mode & SAGE_MODE_MASK) && N > kMaxNPv8) return 0;
   return sage::make_layout(static_cast<long long>(B) * H, N, d, mode & SAGE_MODE_MASK, true).total;
 }
 
@@ -320,6 +334,26 @@ int sage_quant_mxfp4(const void* q, const void* k, const void* v, int B, int H, 
   if (flags & SAGE_FLAG_FP8_V)
     return hip_status(sage::launch_mx_vt8(v, vt_fp4, vt_e8m0, BH, N, Nv, d, s), "MX-FP8 V quantization kernel");
   return hip_status(sage::launch_mx_vt(v, vt_fp4, vt_e8m0, BH, N, Nv, d, s), "MXFP4 V quantization kernel");
+}
+
+int sage_quant_v_int8(const void* v, int B, int H, int N, int d, int8_t* vt_codes, float* v_scales,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_dims(B, H, N, d));
+  SAGE_TRY(check_ptr(v, "v", 16));
+  SAGE_TRY(check_ptr(vt_codes, "vt_codes", 16));
+  SAGE_TRY(check_ptr(v_scales, "v_scales", 4));
+  SAGE_TRY(check_ptr(workspace, "workspace", 256));
+  const int BH = B * H;
+  const sage::Layout L = sage::make_layout(BH, N, d, 0, false);
+  if (workspace_bytes < L.total)
+    return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+  SAGE_TRY(check_device());
+  (void)hipGetLastError();
+  return hip_status(sage::launch_v_int8(v, reinterpret_cast<unsigned*>(at(workspace, L.vmax)), vt_codes, v_scales,
+                                        BH, N, sage::round_up(N, 16), d, L.chunk, L.nchunk,
+                                        static_cast<hipStream_t>(stream)),
+                    "INT8 V quantization kernels");
 }
 
 }  // extern "C"

@@ -31,6 +31,16 @@
 //     (see kRefSlack); the row sum adds the fp16 P pairwise on v_dot2_f32_f16.
 //   * causal: key tiles wholly above the workgroup's last query are skipped;
 //     masking runs only on tiles that cross the diagonal or the ragged tail.
+//   * INT8 P.V variant (the page's "Quantize P,V to INT8" ablation, "Measured
+//     effects"; the faster kernel its "Approach" picks per layer where
+//     accuracy allows): V^T arrives as INT8 codes with one scale per channel,
+//     P is formed against the exact running max (so P <= 1) and converted to
+//     the integer round(127 P) in one v_cvt_pk_u8_f32 per value, and O^T
+//     accumulates exactly in int32 on v_mfma_i32_32x32x32_i8 (half the matrix
+//     ops of the FP16 form). There is no INT8 matrix op with a float
+//     accumulator, so when a row max moves the int32 accumulator is rescaled
+//     by alpha through fp32 and rounded back; the row sum adds the integer
+//     weights on v_dot4_i32_i8, and the epilogue applies the channel scales.
 #include "sage_internal.h"
 
 #include <limits.h>
@@ -43,7 +53,11 @@ namespace {
 // The softmax reference max of a row moves only when a tile's row max exceeds
 // it by more than this (log2 units), so P <= 2^8 and the O rescale is skipped
 // on most tiles; the result is the same softmax, rounded at a different point.
+// The INT8 P.V variant needs P <= 1 for its fixed 1/127 scale and follows the
+// running max exactly (slack 0).
 constexpr float kRefSlack = 8.0f;
+// log2(127): exp2(x + log2(127)) = 127 * exp2(x), the integer P weight's scale.
+constexpr float kLog2_127 = 6.98868468677216585f;
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 constexpr v2h kOnes2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
@@ -76,6 +90,12 @@ __device__ __forceinline__ float max32_f(const v16i& a, const v16i& b) {
     c2 = fmaxf(c2, __int_as_float(b[i])); c3 = fmaxf(c3, __int_as_float(b[8 + i]));
   }
   return fmaxf(fmaxf(c0, c1), fmaxf(c2, c3));
+}
+
+// The next float below x (x finite).
+__device__ __forceinline__ float below_ulp(float x) {
+  if (x == 0.f) return -0x1p-149f;
+  return __uint_as_float(__float_as_uint(x) + (x > 0.f ? 0xffffffffu : 1u));
 }
 
 // Combines a per-lane value with the one in lane l ^ 32 (same query column).
@@ -120,24 +140,30 @@ __device__ __forceinline__ void map_workgroup(int bid, int BH, int nqt, bool cau
 // the FP16 matrix op (the FlashAttention-style baseline of the same design).
 constexpr int kScoresInt8Block = 0, kScoresInt8Token = 1, kScoresF16 = 2;
 
-template <int D, bool CAUSAL, int SM>
+template <int D, bool CAUSAL, int SM, bool PV8>
 __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
-    const void* __restrict__ qsrc, const void* __restrict__ ksrc, const _Float16* __restrict__ vt,
-    const float* __restrict__ qs, const float* __restrict__ ks, _Float16* __restrict__ out, int N,
-    int Npad, int qblk, float sl2, int BH) {
+    const void* __restrict__ qsrc, const void* __restrict__ ksrc, const void* __restrict__ vt,
+    const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vsc,
+    _Float16* __restrict__ out, int N, int Npad, int qblk, float sl2, int BH) {
   constexpr bool PERTOK = SM == kScoresInt8Token;
   constexpr bool F16 = SM == kScoresF16;
+  static_assert(!(PV8 && F16), "INT8 P.V goes with INT8 scores");
+  constexpr float SLACK = PV8 ? 0.f : kRefSlack;
+  constexpr float PLOG = PV8 ? kLog2_127 : 0.f;  // P (fp16 form) or 127 P (INT8 form)
   constexpr int EB = F16 ? 2 : 1;        // bytes per Q / K element
   constexpr int NC = D / 32;             // 32-channel tiles of O^T
   constexpr int NQF = F16 ? D / 16 : D / 32;  // score matrix ops per 32 keys (16 bytes of Q each)
   constexpr int KROW = D * EB + 16;      // LDS bytes per K row (16 bytes of padding)
-  constexpr int VROW = kKTile * 2 + 16;  // LDS bytes per V^T row
+  constexpr int VEB = PV8 ? 1 : 2;       // bytes per V element
+  constexpr int VROW = kKTile * VEB + 16;  // LDS bytes per V^T row
   constexpr int KT_BYTES = kKTile * KROW;
   constexpr int VT_BYTES = D * VROW;
   constexpr int KB0 = 0, KB1 = KT_BYTES, VB0 = 2 * KT_BYTES, VB1 = 2 * KT_BYTES + VT_BYTES;
   constexpr int KCHN = kKTile * D * EB / 16;  // 16-byte chunks of a K tile
+  constexpr int RPV = PV8 ? 2 : 4;       // 16-byte V^T reads (= matrix ops) per 32-channel tile
   constexpr int KPT = (KCHN + 511) / 512;
-  constexpr int VCHN = D * 8;            // 16-byte chunks of a V^T tile
+  constexpr int VCPR = kKTile * VEB / 16;  // 16-byte chunks per V^T row
+  constexpr int VCHN = D * VCPR;           // 16-byte chunks of a V^T tile
   constexpr int VPT = (VCHN + 511) / 512;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KT_BYTES + 2 * VT_BYTES];
 
@@ -187,7 +213,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   // K: INT8 codes zero-padded to Npad rows, or fp16 K as given ([N, d] per head).
   const unsigned char* kbase = static_cast<const unsigned char*>(ksrc) +
                                static_cast<size_t>(bh) * (F16 ? N : Npad) * D * EB;
-  const _Float16* vbase = vt + static_cast<size_t>(bh) * D * Npad;
+  const unsigned char* vbase = static_cast<const unsigned char*>(vt) + static_cast<size_t>(bh) * D * Npad * VEB;
 
   // Loading: every thread moves at most KPT 16-byte K chunks and VPT V^T chunks
   // per tile, global -> registers at the start of a period, registers -> LDS
@@ -204,14 +230,14 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   int vg[VPT], vls[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
-    const int i = tid + 512 * u, row = i >> 3, col = i & 7;
-    vg[u] = row * Npad + col * 8;
+    const int i = tid + 512 * u, row = i / VCPR, col = i % VCPR;
+    vg[u] = row * Npad * VEB + col * 16;
     vls[u] = row * VROW + col * 16;
   }
   const bool vload_last = (tid + 512 * (VPT - 1)) < VCHN;
   unsigned kr[4 * KPT], vr[4 * VPT];
   const int ka = l32 * KROW + g * 16;   // score A operand: K row l32 of each 32-key half
-  const int va = l32 * VROW + g * 64;   // P.V A operand: V^T row l32 of each 32-channel tile
+  const int va = l32 * VROW + g * 32 * VEB;   // P.V A operand: V^T row l32 of each 32-channel tile
 
   v16f o[NC];
 #pragma unroll
@@ -220,7 +246,8 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     for (int i = 0; i < 16; ++i) o[c][i] = 0.f;
   float m = -INFINITY, l = 0.f, alpha = 1.f;
   v16i s[2];
-  v8h pf[4];
+  v8h pf[4];   // fp16 P, keys g*32 + c*8 .. +7 in pf[c]
+  v4i pq[2];   // INT8 form: round(127 P), keys g*32 + u*16 .. +15 in pq[u]
 
 #define SAGE_LOAD_K(J_)                                                                          \
   _Pragma("unroll") for (int u = 0; u < KPT; ++u) {                                              \
@@ -235,7 +262,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
 #define SAGE_LOAD_V(J_)                                                                          \
   _Pragma("unroll") for (int u = 0; u < VPT; ++u) {                                              \
     if (u < VPT - 1 || vload_last) {                                                             \
-      const uint4 t_ = *reinterpret_cast<const uint4*>(vbase + (J_) * kKTile + vg[u]);           \
+      const uint4 t_ = *reinterpret_cast<const uint4*>(vbase + (J_) * kKTile * VEB + vg[u]);     \
       vr[4 * u] = t_.x; vr[4 * u + 1] = t_.y; vr[4 * u + 2] = t_.z; vr[4 * u + 3] = t_.w;       \
     }                                                                                            \
   }
@@ -285,31 +312,45 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
 
   // O^T = alpha * O^T + V^T P^T from the V buffer VB_ (FP16 MFMA, FP32
   // accumulation). The rescale by the last softmax's alpha is done here, in the
-  // matrix phase, so the softmax phase never touches the O registers.
+  // matrix phase, so the softmax phase never touches the O registers. In the
+  // INT8 form O^T holds int32 sums (in the same registers): the rescale goes
+  // through fp32 and rounds back to the nearest integer, and each 32-channel
+  // tile takes two INT8 matrix ops (32 keys each) instead of four.
 #define SAGE_PV(VB_)                                                                             \
   do {                                                                                           \
     if (__ballot(alpha != 1.f)) {                                                                \
-      _Pragma("unroll") for (int c = 0; c < NC; ++c)                                             \
-        _Pragma("unroll") for (int i = 0; i < 16; ++i) o[c][i] *= alpha;                         \
+      if (PV8) {                                                                                 \
+        _Pragma("unroll") for (int c = 0; c < NC; ++c)                                           \
+          _Pragma("unroll") for (int i = 0; i < 16; ++i)                                         \
+            o[c][i] = __int_as_float(__float2int_rn(static_cast<float>(__float_as_int(o[c][i])) * alpha)); \
+      } else {                                                                                   \
+        _Pragma("unroll") for (int c = 0; c < NC; ++c)                                           \
+          _Pragma("unroll") for (int i = 0; i < 16; ++i) o[c][i] *= alpha;                       \
+      }                                                                                          \
     }                                                                                            \
-    v8h va_[2][4];                                                                               \
-    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                \
+    v8h va_[2][RPV];                                                                             \
+    _Pragma("unroll") for (int c = 0; c < RPV; ++c)                                              \
       va_[0][c] = *reinterpret_cast<const v8h*>(smem + (VB_) + va + c * 16);                     \
     _Pragma("unroll") for (int dt = 0; dt < NC; ++dt) {                                          \
       if (dt + 1 < NC) {                                                                         \
-        _Pragma("unroll") for (int c = 0; c < 4; ++c)                                            \
+        _Pragma("unroll") for (int c = 0; c < RPV; ++c)                                          \
           va_[(dt + 1) & 1][c] =                                                                 \
               *reinterpret_cast<const v8h*>(smem + (VB_) + va + (dt + 1) * 32 * VROW + c * 16);  \
       }                                                                                          \
-      _Pragma("unroll") for (int c = 0; c < 4; ++c)                                              \
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va_[dt & 1][c], pf[c], o[dt], 0, 0, 0);   \
+      _Pragma("unroll") for (int c = 0; c < RPV; ++c) {                                          \
+        if (PV8)                                                                                 \
+          o[dt] = __builtin_bit_cast(v16f, __builtin_amdgcn_mfma_i32_32x32x32_i8(                \
+                      __builtin_bit_cast(v4i, va_[dt & 1][c]), pq[c], __builtin_bit_cast(v16i, o[dt]), 0, 0, 0)); \
+        else                                                                                     \
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va_[dt & 1][c], pf[c], o[dt], 0, 0, 0); \
+      }                                                                                          \
     }                                                                                            \
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);                                           \
-    _Pragma("unroll") for (int u = 0; u < 4 * NC - 4; ++u) {                                     \
+    __builtin_amdgcn_sched_group_barrier(0x100, RPV, 2);                                         \
+    _Pragma("unroll") for (int u = 0; u < RPV * NC - RPV; ++u) {                                 \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                         \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);                                         \
     }                                                                                            \
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);                                           \
+    __builtin_amdgcn_sched_group_barrier(0x008, RPV, 2);                                         \
   } while (0)
 
   // Softmax of key tile J_ on the scores in s: dequantize to base-2 logits,
@@ -320,6 +361,44 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   // max, which measured faster where many tiles need masking (causal);
   // SAGE_SOFTMAX_SEQ, a plain per-score sequence, measured faster on unmasked
   // tiles, so non-causal launches use it.
+  // INT8 form: the exponent offset nm_ = log2(127) - m is lowered by whole
+  // ulps until the tile's largest exponent Y_ (the same expression the
+  // values use) is at most log2(127), so every weight round(127 P) stays <= 127
+  // whatever the rounding of nm_ and of the row max (the excess is below 1.5
+  // ulps of nm_: two steps suffice).
+#define SAGE_CAP_P8(Y_)                                                                          \
+  do {                                                                                           \
+    if (PV8) {                                                                                   \
+      if ((Y_) > PLOG) nm_ = below_ulp(nm_);                                                     \
+      if ((Y_) > PLOG) nm_ = below_ulp(nm_);                                                     \
+    }                                                                                            \
+  } while (0)
+
+  // INT8 form of P: the 32 values 127 P of this lane (GETP_ reads value E_)
+  // rounded to integers (v_cvt_pk_u8_f32 rounds to nearest even; 0 <= 127 P
+  // <= 127 up to the exp2 rounding) and packed four per word into pq; rsum_
+  // is their sum, four bytes per v_dot4_i32_i8 in two chains.
+#define SAGE_PACK_P8(GETP_)                                                                      \
+  float rsum_;                                                                                   \
+  do {                                                                                           \
+    _Pragma("unroll") for (int w_ = 0; w_ < 8; ++w_) {                                           \
+      unsigned x_ = 0;                                                                           \
+      _Pragma("unroll") for (int b_ = 0; b_ < 4; ++b_) {                                         \
+        const int E_ = 4 * w_ + b_;                                                              \
+        x_ = __builtin_amdgcn_cvt_pk_u8_f32(GETP_, b_, x_);                                      \
+      }                                                                                          \
+      pq[w_ >> 2][w_ & 3] = static_cast<int>(x_);                                                \
+    }                                                                                            \
+    int r0_ = 0, r1_ = 0;                                                                        \
+    _Pragma("unroll") for (int u_ = 0; u_ < 2; ++u_) {                                           \
+      r0_ = __builtin_amdgcn_sdot4(pq[u_][0], 0x01010101, r0_, false);                           \
+      r1_ = __builtin_amdgcn_sdot4(pq[u_][1], 0x01010101, r1_, false);                           \
+      r0_ = __builtin_amdgcn_sdot4(pq[u_][2], 0x01010101, r0_, false);                           \
+      r1_ = __builtin_amdgcn_sdot4(pq[u_][3], 0x01010101, r1_, false);                           \
+    }                                                                                            \
+    rsum_ = static_cast<float>(r0_ + r1_);                                                       \
+  } while (0)
+
 #define SAGE_SOFTMAX_ILP(J_)                                                                         \
   do {                                                                                           \
     const int j_ = (J_);                                                                         \
@@ -346,11 +425,13 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
         }                                                                                        \
       }                                                                                          \
       mt_ = pair_max(max32_f(s[0], s[1]));                                                       \
-      need_ = mt_ > m + kRefSlack;                                                               \
+      need_ = mt_ > m + SLACK;                                                               \
       mnew_ = need_ ? mt_ : m;                                                                   \
       /* exp2(-inf - finite) = 0 for masked keys */                                              \
+      float nm_ = PLOG - mnew_;                                                                  \
+      SAGE_CAP_P8(mt_ + nm_);                                                                    \
       _Pragma("unroll") for (int e = 0; e < 32; ++e)                                             \
-        s[e >> 4][e & 15] = __float_as_int(__builtin_amdgcn_exp2f(__int_as_float(s[e >> 4][e & 15]) - mnew_)); \
+        s[e >> 4][e & 15] = __float_as_int(__builtin_amdgcn_exp2f(__int_as_float(s[e >> 4][e & 15]) + nm_)); \
     } else if (F16) {                                                                            \
       /* fp32 scores (bits in s): the max is taken before the sm_scale * log2(e) */             \
       /* factor, which is > 0, and the factor is applied in the fma */                          \
@@ -363,9 +444,10 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
       }                                                                                          \
       const float mx_ = pair_max(max32_f(s[0], s[1]));                                           \
       mt_ = (mx_ == -INFINITY) ? -INFINITY : mx_ * sc_;                                          \
-      need_ = mt_ > m + kRefSlack;                                                               \
+      need_ = mt_ > m + SLACK;                                                               \
       mnew_ = need_ ? mt_ : m;                                                                   \
-      const float nm_ = -mnew_;                                                                  \
+      float nm_ = PLOG - mnew_;                                                                  \
+      SAGE_CAP_P8(__builtin_fmaf(mx_, sc_, nm_));                                                \
       if (masked_) {                                                                             \
         _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
           const float x_ = __int_as_float(s[e >> 4][e & 15]);                                    \
@@ -389,9 +471,10 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
       }                                                                                          \
       const int mi_ = pair_max_i(max32_i(s[0], s[1]));                                           \
       mt_ = (mi_ == INT_MIN) ? -INFINITY : static_cast<float>(mi_) * sc_;                        \
-      need_ = mt_ > m + kRefSlack;                                                               \
+      need_ = mt_ > m + SLACK;                                                               \
       mnew_ = need_ ? mt_ : m;                                                                   \
-      const float nm_ = -mnew_;                                                                  \
+      float nm_ = PLOG - mnew_;                                                                  \
+      SAGE_CAP_P8(__builtin_fmaf(static_cast<float>(mi_), sc_, nm_));                            \
       if (masked_) {                                                                             \
         _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
           const int si_ = s[e >> 4][e & 15];                                                     \
@@ -405,16 +488,21 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
       }                                                                                          \
     }                                                                                            \
     const float alpha_ = need_ ? __builtin_amdgcn_exp2f(m - mnew_) : 1.f;                       \
-    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                \
-      _Pragma("unroll") for (int e = 0; e < 8; ++e)                                              \
-        pf[c][e] = static_cast<_Float16>(__int_as_float(s[(c * 8 + e) >> 4][(c * 8 + e) & 15])); \
-    /* row sum of the fp16 P that multiplies V: two products per v_dot2_f32_f16, */             \
-    /* four independent partial sums */                                                          \
-    float rs_[4] = {0.f, 0.f, 0.f, 0.f};                                                         \
-    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                \
-      _Pragma("unroll") for (int e = 0; e < 8; e += 2)                                           \
-        rs_[e >> 1] = __builtin_amdgcn_fdot2(v2h{pf[c][e], pf[c][e + 1]}, kOnes2, rs_[e >> 1], false); \
-    l = l * alpha_ + ((rs_[0] + rs_[1]) + (rs_[2] + rs_[3]));                                    \
+    if (PV8) {                                                                                   \
+      SAGE_PACK_P8(__int_as_float(s[(E_) >> 4][(E_) & 15]));                                     \
+      l = l * alpha_ + rsum_;                                                                    \
+    } else {                                                                                     \
+      _Pragma("unroll") for (int c = 0; c < 4; ++c)                                              \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e)                                            \
+          pf[c][e] = static_cast<_Float16>(__int_as_float(s[(c * 8 + e) >> 4][(c * 8 + e) & 15])); \
+      /* row sum of the fp16 P that multiplies V: two products per v_dot2_f32_f16, */           \
+      /* four independent partial sums */                                                        \
+      float rs_[4] = {0.f, 0.f, 0.f, 0.f};                                                       \
+      _Pragma("unroll") for (int c = 0; c < 4; ++c)                                              \
+        _Pragma("unroll") for (int e = 0; e < 8; e += 2)                                         \
+          rs_[e >> 1] = __builtin_amdgcn_fdot2(v2h{pf[c][e], pf[c][e + 1]}, kOnes2, rs_[e >> 1], false); \
+      l = l * alpha_ + ((rs_[0] + rs_[1]) + (rs_[2] + rs_[3]));                                  \
+    }                                                                                            \
     m = mnew_;                                                                                   \
     alpha = alpha_;                                                                              \
   } while (0)
@@ -447,9 +535,11 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
       float mx_ = p[0];                                                                          \
       _Pragma("unroll") for (int e = 1; e < 32; ++e) mx_ = fmaxf(mx_, p[e]);                     \
       mt_ = pair_max(mx_);                                                                       \
-      need_ = mt_ > m + kRefSlack;                                                               \
+      need_ = mt_ > m + SLACK;                                                               \
       mnew_ = need_ ? mt_ : m;                                                                   \
-      _Pragma("unroll") for (int e = 0; e < 32; ++e) p[e] = __builtin_amdgcn_exp2f(p[e] - mnew_); \
+      float nm_ = PLOG - mnew_;                                                                  \
+      SAGE_CAP_P8(mt_ + nm_);                                                                    \
+      _Pragma("unroll") for (int e = 0; e < 32; ++e) p[e] = __builtin_amdgcn_exp2f(p[e] + nm_);  \
     } else if (F16) {                                                                            \
       /* fp32 scores (bits in s): the max is taken before the sm_scale * log2(e) */             \
       /* factor, which is > 0, and the factor is applied in the fma */                          \
@@ -464,9 +554,10 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
       _Pragma("unroll") for (int e = 1; e < 32; ++e) mx_ = fmaxf(mx_, __int_as_float(s[e >> 4][e & 15])); \
       mx_ = pair_max(mx_);                                                                       \
       mt_ = (mx_ == -INFINITY) ? -INFINITY : mx_ * sc_;                                          \
-      need_ = mt_ > m + kRefSlack;                                                               \
+      need_ = mt_ > m + SLACK;                                                               \
       mnew_ = need_ ? mt_ : m;                                                                   \
-      const float nm_ = -mnew_;                                                                  \
+      float nm_ = PLOG - mnew_;                                                                  \
+      SAGE_CAP_P8(__builtin_fmaf(mx_, sc_, nm_));                                                \
       if (masked_) {                                                                             \
         _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
           const float x_ = __int_as_float(s[e >> 4][e & 15]);                                    \
@@ -489,9 +580,10 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
         _Pragma("unroll") for (int e = 1; e < 32; ++e) mi_ = max(mi_, s[e >> 4][e & 15]);        \
         mi_ = pair_max_i(mi_);                                                                   \
         mt_ = (mi_ == INT_MIN) ? -INFINITY : static_cast<float>(mi_) * sc_;                      \
-        need_ = mt_ > m + kRefSlack;                                                             \
+        need_ = mt_ > m + SLACK;                                                             \
         mnew_ = need_ ? mt_ : m;                                                                 \
-        const float nm_ = -mnew_;                                                                \
+        float nm_ = PLOG - mnew_;                                                                \
+        SAGE_CAP_P8(__builtin_fmaf(static_cast<float>(mi_), sc_, nm_));                          \
         _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
           const float x_ = __builtin_fmaf(static_cast<float>(s[e >> 4][e & 15]), sc_, nm_);     \
           p[e] = (s[e >> 4][e & 15] == INT_MIN) ? 0.f : __builtin_amdgcn_exp2f(x_);             \
@@ -501,24 +593,30 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
         _Pragma("unroll") for (int e = 1; e < 32; ++e) mi_ = max(mi_, s[e >> 4][e & 15]);        \
         mi_ = pair_max_i(mi_);                                                                   \
         mt_ = static_cast<float>(mi_) * sc_;                                                     \
-        need_ = mt_ > m + kRefSlack;                                                             \
+        need_ = mt_ > m + SLACK;                                                             \
         mnew_ = need_ ? mt_ : m;                                                                 \
-        const float nm_ = -mnew_;                                                                \
+        float nm_ = PLOG - mnew_;                                                                \
+        SAGE_CAP_P8(__builtin_fmaf(static_cast<float>(mi_), sc_, nm_));                          \
         _Pragma("unroll") for (int e = 0; e < 32; ++e)                                           \
           p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[e >> 4][e & 15]), sc_, nm_)); \
       }                                                                                          \
     }                                                                                            \
     const float alpha_ = need_ ? __builtin_amdgcn_exp2f(m - mnew_) : 1.f;                       \
-    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                \
-      _Pragma("unroll") for (int e = 0; e < 8; ++e) pf[c][e] = static_cast<_Float16>(p[c * 8 + e]); \
-    /* row sum of the fp16 P that multiplies V: two products per v_dot2_f32_f16 */              \
-    float rs0_ = 0.f, rs1_ = 0.f;                                                                \
-    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                \
-      _Pragma("unroll") for (int e = 0; e < 8; e += 4) {                                         \
-        rs0_ = __builtin_amdgcn_fdot2(v2h{pf[c][e], pf[c][e + 1]}, kOnes2, rs0_, false);        \
-        rs1_ = __builtin_amdgcn_fdot2(v2h{pf[c][e + 2], pf[c][e + 3]}, kOnes2, rs1_, false);    \
-      }                                                                                          \
-    l = l * alpha_ + (rs0_ + rs1_);                                                              \
+    if (PV8) {                                                                                   \
+      SAGE_PACK_P8(p[E_]);                                                                       \
+      l = l * alpha_ + rsum_;                                                                    \
+    } else {                                                                                     \
+      _Pragma("unroll") for (int c = 0; c < 4; ++c)                                              \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e) pf[c][e] = static_cast<_Float16>(p[c * 8 + e]); \
+      /* row sum of the fp16 P that multiplies V: two products per v_dot2_f32_f16 */            \
+      float rs0_ = 0.f, rs1_ = 0.f;                                                              \
+      _Pragma("unroll") for (int c = 0; c < 4; ++c)                                              \
+        _Pragma("unroll") for (int e = 0; e < 8; e += 4) {                                       \
+          rs0_ = __builtin_amdgcn_fdot2(v2h{pf[c][e], pf[c][e + 1]}, kOnes2, rs0_, false);      \
+          rs1_ = __builtin_amdgcn_fdot2(v2h{pf[c][e + 2], pf[c][e + 3]}, kOnes2, rs1_, false);  \
+        }                                                                                        \
+      l = l * alpha_ + (rs0_ + rs1_);                                                            \
+    }                                                                                            \
     m = mnew_;                                                                                   \
     alpha = alpha_;                                                                              \
   } while (0)
@@ -590,6 +688,8 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
 #undef SAGE_SOFTMAX
 #undef SAGE_SOFTMAX_ILP
 #undef SAGE_SOFTMAX_SEQ
+#undef SAGE_PACK_P8
+#undef SAGE_CAP_P8
 #undef SAGE_PV
 #undef SAGE_SCORES
 #undef SAGE_STORE_V
@@ -606,28 +706,44 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         v4h h;
+        if (PV8) {
+          // int32 sums of weight * code; channel c's value is code * scale[c]
+          const float4 vs4 = *reinterpret_cast<const float4*>(vsc + static_cast<size_t>(bh) * D + dt * 32 + r * 8 + g * 4);
+          const float vsv[4] = {vs4.x, vs4.y, vs4.z, vs4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(o[dt][r * 4 + i] * inv);
+          for (int i = 0; i < 4; ++i)
+            h[i] = static_cast<_Float16>(static_cast<float>(__float_as_int(o[dt][r * 4 + i])) * (vsv[i] * inv));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(o[dt][r * 4 + i] * inv);
+        }
         *reinterpret_cast<v4h*>(orow + dt * 32 + r * 8 + g * 4) = h;
       }
   }
 }
 
 hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, const void* vt,
-                            const float* qs, const float* ks, hipStream_t s) {
+                            const float* qs, const float* ks, const float* vs, hipStream_t s) {
   const int nqt = a.Npad / kWGQ;
   const dim3 grid(a.BH * nqt), block(512);
-  const int qblk = (a.mode == 0) ? 128 : (a.mode == 1 ? 64 : 1);
-  const int sm = a.mode == 3 ? kScoresInt8Token : (a.mode == 4 ? kScoresF16 : kScoresInt8Block);
-  const auto* v = static_cast<const _Float16*>(vt);
+  // modes: 0 Q128/K64, 1 Q64/K64, 3 per token, 4 FP16, 6 Q128/K64 + INT8 P.V, 7 per token + INT8 P.V
+  const bool tok = a.mode == 3 || a.mode == 7;
+  const int qblk = tok ? 1 : (a.mode == 1 ? 64 : 128);
+  const int sm = tok ? kScoresInt8Token : (a.mode == 4 ? kScoresF16 : kScoresInt8Block);
+  const bool pv8 = mode_pv_int8(a.mode);
   auto* o = static_cast<_Float16*>(a.out);
-#define SAGE_LAUNCH(D_, C_, S_) \
-  attn_int8_kernel<D_, C_, S_><<<grid, block, 0, s>>>(q, k, v, qs, ks, o, a.N, a.Npad, qblk, a.sl2, a.BH)
-#define SAGE_LAUNCH_SM(D_, C_)                                               \
-  do {                                                                       \
-    if (sm == kScoresInt8Token) SAGE_LAUNCH(D_, C_, kScoresInt8Token);       \
-    else if (sm == kScoresF16) SAGE_LAUNCH(D_, C_, kScoresF16);              \
-    else SAGE_LAUNCH(D_, C_, kScoresInt8Block);                              \
+#define SAGE_LAUNCH(D_, C_, S_, P_) \
+  attn_int8_kernel<D_, C_, S_, P_><<<grid, block, 0, s>>>(q, k, vt, qs, ks, vs, o, a.N, a.Npad, qblk, a.sl2, a.BH)
+#define SAGE_LAUNCH_SM(D_, C_)                                                    \
+  do {                                                                            \
+    if (sm == kScoresF16) SAGE_LAUNCH(D_, C_, kScoresF16, false);                 \
+    else if (sm == kScoresInt8Token) {                                            \
+      if (pv8) SAGE_LAUNCH(D_, C_, kScoresInt8Token, true);                       \
+      else SAGE_LAUNCH(D_, C_, kScoresInt8Token, false);                          \
+    } else {                                                                      \
+      if (pv8) SAGE_LAUNCH(D_, C_, kScoresInt8Block, true);                       \
+      else SAGE_LAUNCH(D_, C_, kScoresInt8Block, false);                          \
+    }                                                                             \
   } while (0)
   if (a.d == 128) {
     if (a.causal) SAGE_LAUNCH_SM(128, true); else SAGE_LAUNCH_SM(128, false);

@@ -1,5 +1,6 @@
 // Quantization kernels for gfx950: the K channel mean, per-block INT8 codes,
-// the transposed fp16 V used by the INT8 attention kernel, and MXFP4
+// the transposed fp16 V used by the INT8 attention kernel, per-channel INT8 V
+// for its INT8 P.V variant, and MXFP4
 // (E2M1 + E8M0) codes. All of them are HBM-streaming kernels: 16-byte
 // coalesced loads and stores, one pass over each input.
 //
@@ -106,6 +107,38 @@ __device__ __forceinline__ void unpack8(const uint4 raw, float* x) {
   }
 }
 
+// Codes. fp32(x / s) is formed without a division per element: with
+// y = fp32(1 / s) (one IEEE division per scale) and q0 = fp32(x * y), the
+// remainder x - q0 * s is exact in one fma and q0 + r * y rounded once is the
+// correctly rounded quotient (Markstein's correction step; its preconditions
+// hold here: y is the rounded reciprocal of s, q0 is within one ulp, the
+// quotient is at most 127 in magnitude, and with s >= 2^-60 every x whose
+// code can be nonzero is far above the subnormal range, so the remainder is
+// exact). Smaller scales take the plain division; s = 0 means an all-zero
+// block and zero codes.
+// The result is returned as the bits of t = fp32(q + 1.5 * 2^23), which rounds
+// q to the nearest integer, ties to even (the sum lies in [2^23, 2^24), whose
+// ulp is 1, and 1.5 * 2^23 is even): the low byte of t is that integer as a
+// two's complement int8. |q| <= 127 needs no clamp: q = x / s with |x| <= a and
+// s = fp32(a / 127), so |q| <= 127 * (1 + 2^-24).
+constexpr float kMarksteinMinScale = 0x1p-60f;
+
+__device__ __forceinline__ unsigned int8_code_bits(float x, float s, float y) {
+  constexpr float kRound = 12582912.0f;
+  if (s >= kMarksteinMinScale) {
+    const float q0 = x * y;
+    const float r = __builtin_fmaf(-q0, s, x);
+    return __float_as_uint(__builtin_fmaf(r, y, q0) + kRound);
+  }
+  return __float_as_uint((s > 0.f ? x / s : 0.f) + kRound);
+}
+
+// Low bytes of w[0..3] -> one word, byte i = low byte of w[i].
+__device__ __forceinline__ unsigned pack_low_bytes(unsigned w0, unsigned w1, unsigned w2, unsigned w3) {
+  return __builtin_amdgcn_perm(__builtin_amdgcn_perm(w3, w2, 0x04000c0cu),
+                               __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u), 0x07060100u);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void int8_quant_kernel(Int8Job j0, Int8Job j1, int N) {
   constexpr int TPR = D / 8;         // threads per row
@@ -181,49 +214,17 @@ __global__ __launch_bounds__(256) void int8_quant_kernel(Int8Job j0, Int8Job j1,
     for (int p = 0; p < NP; ++p) s[p] = bmax[(p * RPP + rl) / blk] / 127.0f;
   }
 
-  // codes. fp32(x / s) is formed without a division per element: with
-  // y = fp32(1 / s) (one IEEE division per row) and q0 = fp32(x * y), the
-  // remainder x - q0 * s is exact in one fma and q0 + r * y rounded once is the
-  // correctly rounded quotient (Markstein's correction step; its preconditions
-  // hold here: y is the rounded reciprocal of s, q0 is within one ulp, the
-  // quotient is at most 127 in magnitude, and with s >= 2^-60 every x whose
-  // code can be nonzero is far above the subnormal range, so the remainder is
-  // exact). Smaller scales take the plain division; s = 0 means an all-zero
-  // block and zero codes.
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int row = row0 + p * RPP + rl;
     if (row < J.code_rows) {
       const float sp = s[p];
-      // t = fp32(q + 1.5 * 2^23) rounds q to the nearest integer, ties to even
-      // (the sum lies in [2^23, 2^24), whose ulp is 1, and 1.5 * 2^23 is even),
-      // and the low byte of its bits is that integer as a two's complement
-      // int8. |q| <= 127 needs no clamp: q = x / s with |x| <= a and
-      // s = fp32(a / 127), so |q| <= 127 * (1 + 2^-24).
-      constexpr float kRound = 12582912.0f;
-      float t[8];
-      if (sp >= 0x1p-60f) {
-        const float y = 1.0f / sp;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float q0 = x[p][e] * y;
-          const float r = __builtin_fmaf(-q0, sp, x[p][e]);
-          t[e] = __builtin_fmaf(r, y, q0) + kRound;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = (sp > 0.f ? x[p][e] / sp : 0.f) + kRound;
-      }
+      const float y = sp >= kMarksteinMinScale ? 1.0f / sp : 0.f;
       unsigned w[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = __float_as_uint(t[e]);
-      // byte e of the 8-byte code group = low byte of w[e]
-      const unsigned lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w[3], w[2], 0x04000c0cu),
-                                                __builtin_amdgcn_perm(w[1], w[0], 0x0c0c0400u), 0x07060100u);
-      const unsigned hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w[7], w[6], 0x04000c0cu),
-                                                __builtin_amdgcn_perm(w[5], w[4], 0x0c0c0400u), 0x07060100u);
+      for (int e = 0; e < 8; ++e) w[e] = int8_code_bits(x[p][e], sp, y);
       *reinterpret_cast<uint2*>(J.codes + (static_cast<size_t>(bh) * J.code_rows + row) * D + cg * 8) =
-          make_uint2(lo, hi);
+          make_uint2(pack_low_bytes(w[0], w[1], w[2], w[3]), pack_low_bytes(w[4], w[5], w[6], w[7]));
     }
   }
 
@@ -292,6 +293,110 @@ hipError_t launch_v_transpose(const void* v, void* vt, int BH, int N, int Npad, 
     v_transpose_kernel<128><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), N, Npad);
   else
     v_transpose_kernel<64><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), N, Npad);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// INT8 V for the INT8 P.V variant: one scale per (head, channel) over all
+// tokens, a = max|V|, s = fp32(a / 127) (IEEE division), code =
+// rint(fp32(V / s)) (ties to even), with the per-block rules above. Pass 1
+// takes the channel maxima of chunks of tokens; pass 2 finishes the maxima,
+// writes the scales and the codes transposed, V^T [BH, d, ldv] int8 with
+// tokens >= N zero. |V| is compared on the fp16 bit patterns with the sign
+// cleared, which orders finite values like their magnitudes.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void vmax_partial_kernel(const uint16_t* __restrict__ v,
+                                                           unsigned* __restrict__ part, int N,
+                                                           int chunk, int nchunk) {
+  constexpr int TPR = D / 8;      // threads per token row, 8 channels (16 bytes) each
+  constexpr int RPP = 256 / TPR;  // token rows per pass
+  __shared__ unsigned red[256][9];
+  const int bh = blockIdx.x / nchunk, ci = blockIdx.x % nchunk;
+  const int tid = threadIdx.x, cg = tid % TPR;
+  const int n0 = ci * chunk, n1 = min(N, n0 + chunk);
+  const uint16_t* src = v + static_cast<size_t>(bh) * N * D + cg * 8;
+  unsigned acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int n = n0 + tid / TPR; n < n1; n += RPP) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(n) * D);
+    const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] = max(acc[2 * j], w[j] & 0x7fffu);
+      acc[2 * j + 1] = max(acc[2 * j + 1], (w[j] >> 16) & 0x7fffu);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[tid][j] = acc[j];
+  __syncthreads();
+  if (tid < D) {
+    const int g = tid / 8, j = tid % 8;
+    unsigned m = 0;
+    for (int r = 0; r < RPP; ++r) m = max(m, red[r * TPR + g][j]);
+    part[(static_cast<size_t>(bh) * nchunk + ci) * D + tid] = m;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void v_int8_kernel(const uint16_t* __restrict__ v,
+                                                     const unsigned* __restrict__ part,
+                                                     int8_t* __restrict__ codes, float* __restrict__ scales,
+                                                     int N, int nchunk, int ldv) {
+  constexpr int TT = 64;      // tokens per tile
+  constexpr int CPR = D / 8;  // 16-byte chunks per token row
+  __shared__ uint16_t t[TT][D + 8];
+  __shared__ float sc[D];
+  const int ntile = (ldv + TT - 1) / TT;
+  const int bh = blockIdx.x / ntile, tb = blockIdx.x % ntile;
+  const int tid = threadIdx.x;
+  if (tid < D) {
+    unsigned m = 0;
+    for (int i = 0; i < nchunk; ++i) m = max(m, part[(static_cast<size_t>(bh) * nchunk + i) * D + tid]);
+    const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(m)));
+    const float s = a / 127.0f;
+    sc[tid] = s;
+    if (tb == 0) scales[static_cast<size_t>(bh) * D + tid] = s;
+  }
+  const uint16_t* src = v + static_cast<size_t>(bh) * N * D;
+#pragma unroll
+  for (int u = 0; u < TT * CPR / 256; ++u) {
+    const int i = tid + 256 * u, r = i / CPR, c8 = i % CPR;
+    const int n = tb * TT + r;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (n < N) val = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(n) * D + c8 * 8);
+    *reinterpret_cast<uint4*>(&t[r][c8 * 8]) = val;
+  }
+  __syncthreads();
+  // every thread writes 16 consecutive tokens of one channel per pass
+#pragma unroll
+  for (int u = 0; u < D * (TT / 16) / 256; ++u) {
+    const int i = tid + 256 * u, dd = i / (TT / 16), n16 = i % (TT / 16);
+    const int n0 = tb * TT + n16 * 16;
+    if (n0 >= ldv) continue;
+    const float s = sc[dd];
+    const float y = s >= kMarksteinMinScale ? 1.0f / s : 0.f;
+    unsigned w[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      w[j] = int8_code_bits(static_cast<float>(__builtin_bit_cast(_Float16, t[n16 * 16 + j][dd])), s, y);
+    *reinterpret_cast<uint4*>(codes + (static_cast<size_t>(bh) * D + dd) * ldv + n0) =
+        make_uint4(pack_low_bytes(w[0], w[1], w[2], w[3]), pack_low_bytes(w[4], w[5], w[6], w[7]),
+                   pack_low_bytes(w[8], w[9], w[10], w[11]), pack_low_bytes(w[12], w[13], w[14], w[15]));
+  }
+}
+
+hipError_t launch_v_int8(const void* v, unsigned* part, int8_t* codes, float* scales, int BH, int N, int ldv,
+                         int d, int chunk, int nchunk, hipStream_t s) {
+  const auto* vv = static_cast<const uint16_t*>(v);
+  const int grid = BH * ((ldv + 63) / 64);
+  if (d == 128) {
+    vmax_partial_kernel<128><<<BH * nchunk, 256, 0, s>>>(vv, part, N, chunk, nchunk);
+    v_int8_kernel<128><<<grid, 256, 0, s>>>(vv, part, codes, scales, N, nchunk, ldv);
+  } else {
+    vmax_partial_kernel<64><<<BH * nchunk, 256, 0, s>>>(vv, part, N, chunk, nchunk);
+    v_int8_kernel<64><<<grid, 256, 0, s>>>(vv, part, codes, scales, N, nchunk, ldv);
+  }
   return hipGetLastError();
 }
 

@@ -44,7 +44,9 @@ struct Layout {
   // INT8 modes
   size_t q_codes = 0, k_codes = 0;    // int8 [BH, Npad, d]
   size_t q_scales = 0, k_scales = 0;  // fp32 [BH, Npad] (enough for any block size)
-  size_t vt = 0;                      // fp16 [BH, d, Npad] (V transposed, zero-padded)
+  size_t vt = 0;                      // V^T [BH, d, Npad], zero-padded: fp16, or int8 codes (INT8 P.V)
+  size_t vscale = 0;                  // fp32 [BH, d] per-channel V scales (INT8 P.V)
+  size_t vmax = 0;                    // uint32 [BH, nchunk, d] partial channel maxima of |V|
   // MXFP4 mode
   size_t q_fp4 = 0, k_fp4 = 0;    // uint8 [BH, Npad, d/2]
   size_t q_e8 = 0, k_e8 = 0;      // uint8 [BH, Npad, d/32]
@@ -53,6 +55,9 @@ struct Layout {
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Modes whose P.V runs in INT8 (SAGE_MODE_INT8_PV, SAGE_MODE_INT8_PV_PER_TOKEN).
+inline bool mode_pv_int8(int mode_lo) { return mode_lo == 6 || mode_lo == 7; }
 
 // mode_lo: SAGE_MODE_* without flags; attention=false gives the layout of the
 // standalone quantization entry points (column sums and mean only).
@@ -77,12 +82,19 @@ inline Layout make_layout(long long BH, int N, int d, int mode_lo, bool attentio
     } else if (mode_lo == 4) {  // SAGE_MODE_FP16: V^T only
       L.vt = take(rows * d * 2);
     } else {
+      const bool pv8 = mode_pv_int8(mode_lo);
       L.q_codes = take(rows * d);
       L.k_codes = take(rows * d);
       L.q_scales = take(rows * 4);
       L.k_scales = take(rows * 4);
-      L.vt = take(rows * d * 2);
+      L.vt = take(rows * d * (pv8 ? 1 : 2));
+      if (pv8) {
+        L.vscale = take(size_t(BH) * d * 4);
+        L.vmax = take(size_t(BH) * L.nchunk * d * 4);
+      }
     }
+  } else {
+    L.vmax = take(size_t(BH) * L.nchunk * d * 4);  // for sage_quant_v_int8
   }
   L.total = off;
   return L;
@@ -113,6 +125,12 @@ hipError_t launch_int8_quant(const Int8Job& j0, const Int8Job& j1, int BH, int N
 // fp16 V [BH, N, d] -> V^T [BH, d, Npad] with zero-padded tokens.
 hipError_t launch_v_transpose(const void* v, void* vt, int BH, int N, int Npad, int d, hipStream_t s);
 
+// Per-channel INT8 V: channel maxima over chunks of `chunk` tokens into part
+// [BH, nchunk, d], then scales [BH, d] and codes V^T [BH, d, ldv] (ldv a
+// multiple of 16, tokens >= N zero).
+hipError_t launch_v_int8(const void* v, unsigned* part, int8_t* codes, float* scales, int BH, int N, int ldv,
+                         int d, int chunk, int nchunk, hipStream_t s);
+
 // MXFP4 quantization along channels: src fp16 [BH, N, d] -> fp4 [BH, rows, d/2],
 // e8 [BH, rows, d/32]; rows in [N, rows) get zero codes and exponent byte 127.
 struct MxRowJob {
@@ -140,8 +158,10 @@ struct AttnArgs {
 };
 // q, k: INT8 codes (padded to Npad rows) with scales qs, ks; or, for
 // SAGE_MODE_FP16, the caller's fp16 Q and K [BH, N, d] (qs, ks unused).
+// vt: fp16 V^T, or for the INT8 P.V modes int8 V^T codes with per-channel
+// scales vs [BH, d] (unused otherwise).
 hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, const void* vt,
-                            const float* qs, const float* ks, hipStream_t s);
+                            const float* qs, const float* ks, const float* vs, hipStream_t s);
 // v4 holds E2M1 V^T codes, or E4M3 ones for SAGE_MODE_MXFP4_FP8PV (a.mode 5,
 // where P is quantized to MX-FP8 as well).
 hipError_t launch_attn_mxfp4(const AttnArgs& a, const uint8_t* q4, const uint8_t* qe,

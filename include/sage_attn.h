@@ -12,6 +12,13 @@
  * FP4 idea of "SageAttention3: Microscaling FP4 Attention for Inference and
  * An Exploration of 8-Bit Training" (abstract), using E2M1 elements with one
  * E8M0 scale per 32 elements (the MX format its reference list names).
+ * INT8 P.V variants (modes 6, 7): the page's "Measured effects" ablation that
+ * quantizes P and V to INT8 as well ("Quantize P,V to INT8 rather than
+ * retaining FP16"), the faster kernel its "Approach" selects per layer where
+ * cosine similarity stays above 99.8%: V with one scale per (head, channel)
+ * over all tokens, P = exp(S - running row max) in [0, 1] as the integer
+ * weight round(127 P), P.V accumulated exactly in int32, the row sum from the
+ * same integer weights.
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, C-contiguous [B, H, N, d] (batch, head, token,
@@ -60,6 +67,10 @@ typedef enum sage_status {
                                    /* baseline of the same kernel; reads q, k when computing)  */
 #define SAGE_MODE_MXFP4_FP8PV 5    /* MXFP4 Q, K_s; P and V in MX-FP8 (E4M3 + E8M0 per 32):   */
                                    /* the accuracy variant of SAGE_MODE_MXFP4                 */
+#define SAGE_MODE_INT8_PV 6        /* as SAGE_MODE_INT8_Q128_K64, with P and V in INT8 as well */
+                                   /* (P.V on the INT8 matrix op; N <= 131072)                */
+#define SAGE_MODE_INT8_PV_PER_TOKEN 7 /* as SAGE_MODE_INT8_PER_TOKEN, with P and V in INT8   */
+                                   /* (N <= 131072)                                           */
 #define SAGE_MODE_MASK 0xff
 
 /* Flags OR-ed into `mode` (or passed as `flags`). */
@@ -119,7 +130,8 @@ int sage_attn_compute(const void* q, const void* k, void* out, int B, int H, int
                       int causal, float sm_scale, int mode, const void* workspace,
                       size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace sage_quant_qk and sage_quant_mxfp4 need. */
+/* Bytes of device workspace sage_quant_qk, sage_quant_mxfp4 and
+ * sage_quant_v_int8 need. */
 size_t sage_quant_workspace_size(int B, int H, int N, int d);
 
 /*
@@ -165,6 +177,22 @@ int sage_quant_mxfp4(const void* q, const void* k, const void* v, int B, int H, 
                      int flags, uint8_t* q_fp4, uint8_t* q_e8m0, uint8_t* k_fp4, uint8_t* k_e8m0,
                      uint8_t* vt_fp4, uint8_t* vt_e8m0, float* k_mean, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * Per-channel INT8 quantization of V, the V operand of the INT8 P.V modes
+ * (SageAttention page, "Measured effects": P and V quantized to INT8; the
+ * page gives no granularity, and one scale per channel is constant along the
+ * contraction over tokens).
+ *   v          fp16 [B, H, N, d] device.
+ *   vt_codes   int8 [B, H, d, Nv] device, written: V transposed, Nv = N rounded
+ *              up to a multiple of 16, tokens >= N zero.
+ *   v_scales   fp32 [B, H, d] device, written.
+ * Definitions (bit-exact): a = max over tokens of |V[b,h,:,c]| (V finite),
+ * s = fp32(a / 127) (correctly rounded), code = round_half_even(fp32(V / s))
+ * in [-127, 127]; a = 0 gives s = 0 and zero codes.
+ */
+int sage_quant_v_int8(const void* v, int B, int H, int N, int d, int8_t* vt_codes, float* v_scales,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

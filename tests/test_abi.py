@@ -42,7 +42,7 @@ def test_workspace_sizes():
     assert sa.sage_attn_workspace_size(1, 2, 256, 64, 0) > 0
     assert sa.sage_attn_workspace_size(0, 2, 256, 64, 0) == 0
     assert sa.sage_attn_workspace_size(1, 2, 256, 96, 0) == 0
-    assert sa.sage_attn_workspace_size(1, 2, 256, 64, 7) == 0
+    assert sa.sage_attn_workspace_size(1, 2, 256, 64, 8) == 0
     small = sa.sage_attn_workspace_size(1, 2, 256, 128, 0)
     big = sa.sage_attn_workspace_size(1, 2, 4096, 128, 0)
     assert big > small
@@ -53,7 +53,11 @@ def test_workspace_sizes():
     # FP16 baseline: only V^T (2 B/elem); MXFP4 with MX-FP8 V: ~2.1 B/elem
     assert 2 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 4) < 2.1 * n
     assert 2 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 5) < 2.3 * n
-    assert sa.sage_attn_workspace_size(1, 2, 256, 64, 6) == 0
+    # INT8 P.V: Q, K codes (2 B/elem) + INT8 V^T (1 B/elem)
+    for mode in (6, 7):
+        assert 3 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, mode) < 3.2 * n
+    assert sa.sage_attn_workspace_size(1, 2, (1 << 17) + 1, 64, 6) == 0     # int32 P.V sums bound N
+    assert sa.sage_attn_workspace_size(1, 2, (1 << 17) + 1, 64, 0) > 0
     assert sa.sage_attn_workspace_size(1, 2, 256, 64, 0x200 | 2) == 0   # the V-format flag is quantization-only
     assert sa.sage_quant_workspace_size(1, 2, 256, 64) > 0
 
@@ -68,7 +72,8 @@ def _fwd(q=A16, k=A16, v=A16, out=A16, B=1, H=2, N=256, d=64, causal=0, scale=0.
     (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(out=None), INVALID),
     (dict(q=A16 + 8), INVALID), (dict(out=A16 + 2), INVALID), (dict(ws=A16 + 16), INVALID),
     (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID), (dict(N=(1 << 22) + 1), INVALID),
-    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(mode=9), UNSUP), (dict(mode=0x200), UNSUP),
+    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(mode=9), UNSUP), (dict(mode=8), UNSUP),
+    (dict(mode=0x200), UNSUP), (dict(mode=6, N=(1 << 17) + 1), UNSUP), (dict(mode=7 | 0x100, N=(1 << 17) + 1), UNSUP),
     (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(scale=-1.0), INVALID), (dict(causal=2), INVALID), (dict(wsb=1024), WS),
 ])
@@ -87,7 +92,12 @@ def test_prepare_compute_and_quant_validation():
     ws4 = sa.sage_attn_workspace_size(1, 2, 256, 64, 4)
     assert lib.sage_attn_compute(None, A16, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
     assert lib.sage_attn_compute(A16, A16 + 2, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
-    assert lib.sage_attn_compute(A16, A16, A16, 1, 2, 256, 64, 0, 0.1, 6, A16, ws4, None) == UNSUP
+    assert lib.sage_attn_compute(A16, A16, A16, 1, 2, 256, 64, 0, 0.1, 8, A16, ws4, None) == UNSUP
+    # the INT8 P.V workspace also holds INT8 V^T and its channel scales
+    ws0 = sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
+    ws6 = sa.sage_attn_workspace_size(1, 2, 256, 64, 6)
+    assert ws6 != ws0
+    assert lib.sage_attn_compute(None, None, A16, 1, 2, 256, 64, 0, 0.1, 6, A16, ws6 - 1, None) == WS
     qw = sa.sage_quant_workspace_size(1, 2, 256, 64)
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 48, 64, 0, A16, A16, A16, A16, None, A16, qw, None) == UNSUP
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 4, A16, A16, A16, A16, None, A16, qw, None) == UNSUP
@@ -95,6 +105,11 @@ def test_prepare_compute_and_quant_validation():
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 0, A16, A16, A16, A16, None, A16, 8, None) == WS
     assert lib.sage_quant_mxfp4(A16, A16, A16, 1, 2, 256, 64, 0, A16, A16, A16, A16, A16 + 4, A16, None, A16, qw,
                                 None) == INVALID
+    assert lib.sage_quant_v_int8(None, 1, 2, 256, 64, A16, A16, A16, qw, None) == INVALID
+    assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16 + 8, A16, A16, qw, None) == INVALID
+    assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16, A16 + 2, A16, qw, None) == INVALID
+    assert lib.sage_quant_v_int8(A16, 1, 2, 256, 80, A16, A16, A16, qw, None) == UNSUP
+    assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16, A16, A16, 8, None) == WS
 
 
 def _gpu_visible():
@@ -111,3 +126,5 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert "device" in sa.sage_last_error()
     qw = sa.sage_quant_workspace_size(1, 2, 256, 64)
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 0, A16, A16, A16, A16, None, A16, qw, None) == NODEV
+    assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16, A16, A16, qw, None) == NODEV
+    assert _fwd(mode=6) == NODEV and _fwd(mode=7) == NODEV

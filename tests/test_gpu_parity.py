@@ -195,7 +195,77 @@ def test_mxfp4_attention_matches_oracle(sa, case):
         f"oracle {O.metrics(ref, ex)['cos']:.6f}")
 
 
-@pytest.mark.parametrize("mode", [0, 2, 4, 5])
+VQ_CASES = [(1, 2, 256, 64, "normal"), (2, 3, 1000, 128, "normal"), (1, 2, 777, 64, "student_t"),
+            (1, 1, 1, 128, "normal"), (1, 2, 70, 128, "zero_channel")]
+
+
+@pytest.mark.parametrize("case", VQ_CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"-{c[4]}")
+def test_int8_v_quant_bitexact(sa, case):
+    B, H, N, d, dist = case
+    say("int8 V quant", case)
+    _, _, v = make_custom(B, H, N, d, seed=17 * N + d, dist="normal" if dist == "zero_channel" else dist)
+    if dist == "zero_channel":
+        v[:, :, :, 5] = 0
+    codes, scales = O.int8_quant_v_channels(v)
+    (vd,) = _dev(v)
+    got = sa.sage_quant_v_int8(vd)
+    torch.cuda.synchronize()
+    Nv = -(-N // 16) * 16
+    want = np.zeros((B, H, Nv, d), np.int8)
+    want[:, :, :N] = codes
+    assert np.array_equal(got["vt_codes"].cpu().numpy(), np.swapaxes(want, 2, 3))
+    assert np.array_equal(got["v_scales"].cpu().numpy().view(np.uint32), scales.view(np.uint32))
+
+
+PV8_CASES = [
+    # B, H, N, d, causal, mode (6: per-block Q128/K64, 7: per token), dist
+    (1, 2, 256, 64, False, 6, "normal"),
+    (1, 2, 1000, 128, False, 6, "normal"),
+    (1, 2, 1000, 128, True, 6, "normal"),
+    (2, 2, 777, 64, False, 6, "student_t"),
+    (1, 2, 777, 64, True, 7, "normal"),
+    (1, 2, 300, 128, False, 7, "normal"),
+    (1, 1, 1, 128, False, 6, "normal"),
+    (1, 1, 1, 64, True, 7, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", PV8_CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"-c{int(c[4])}-m{c[5]}")
+def test_int8_pv_attention_matches_oracle(sa, case):
+    B, H, N, d, causal, mode, dist = case
+    say("int8 P,V attention", case)
+    q, k, v = make_custom(B, H, N, d, seed=19 * N + d + mode, dist=dist)
+    sm = 1.0 / np.sqrt(d)
+    blk = 1 if mode == 7 else None
+    ref = O.int8_pv_attention(q, k, v, causal=causal, sm_scale=sm, blk_q=blk or 128, blk_k=blk or 64)
+    qd, kd, vd = _dev(q, k, v)
+    out = sa.sage_attn_fwd(qd, kd, vd, causal=causal, sm_scale=sm, mode=mode)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = assert_output_parity(got, ref, what=f"int8-pv {case}")
+    ex = O.exact_attention(q, k, v, causal=causal, sm_scale=sm)
+    say(f"  max err vs oracle {err:.2e}; cos vs fp64 gpu {O.metrics(got, ex)['cos']:.6f} "
+        f"oracle {O.metrics(ref, ex)['cos']:.6f}")
+
+
+def test_int8_pv_weights_stay_in_range_for_large_logits(sa):
+    # Logits near 10^5 (log2 units): the rounding of the reference max could push
+    # round(127 P) of a row's maximum past 127 (an int8 wrap) without the exponent cap.
+    # Constant V rows per channel make every output equal to the dequantized channel value.
+    say("int8 P,V large logits")
+    rng = np.random.default_rng(41)
+    B, H, N, d = 1, 2, 300, 64
+    q = (rng.standard_normal((B, H, N, d)) * 100).astype(np.float16)
+    k = (rng.standard_normal((B, H, N, d)) * 100).astype(np.float16)
+    v = np.broadcast_to(rng.standard_normal((1, 1, 1, d)).astype(np.float16), (B, H, N, d)).copy()
+    ref = O.int8_pv_attention(q, k, v, causal=False, sm_scale=1.0, blk_q=128, blk_k=64)
+    qd, kd, vd = _dev(q, k, v)
+    out = sa.sage_attn_fwd(qd, kd, vd, causal=False, sm_scale=1.0, mode=sa.SAGE_MODE_INT8_PV)
+    torch.cuda.synchronize()
+    assert_output_parity(out.cpu().numpy(), ref, what="int8-pv large logits")
+
+
+@pytest.mark.parametrize("mode", [0, 2, 4, 5, 6, 7])
 def test_prepare_compute_equals_fwd_and_is_deterministic(sa, mode):
     say("determinism mode", mode)
     q, k, v = make_custom(1, 2, 700, 128, seed=11)

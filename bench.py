@@ -111,6 +111,25 @@ def cpu_baseline(name: str, mode_name: str, budget_s: float = 12.0):
                       f"quantization + tiled fp64 emulation, {t_total:.1f} s on 1 thread"}
 
 
+def select_layers(names, torch, sa):
+    """Each synthetic workload stands for one attention layer: calibrate it with the
+    selector and print one JSON line per layer (measured cos and time per mode)."""
+    from bit_quantized_attention_mean_amd import selector as S
+    from synthetic import WORKLOADS, make_inputs
+
+    for name in names:
+        w = WORKLOADS[name]
+        q, k, v = make_inputs(name)
+        qd, kd, vd = (torch.from_numpy(x).to("cuda:0") for x in (q, k, v))
+        del q, k, v
+        mode, meas = S.calibrate(qd, kd, vd, causal=w.causal, sm_scale=w.sm_scale, reps=10)
+        print(json.dumps({"layer": name, "chosen_mode": mode, "threshold": S.COS_THRESHOLD,
+                          "candidates": [{"mode": m.mode, "cos": round(m.cos, 6), "ms": round(m.ms, 4)}
+                                         for m in meas]}), flush=True)
+        del qd, kd, vd
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +146,9 @@ def main():
     ap.add_argument("--no-smooth", action="store_true", help="skip the K mean subtraction (ablation)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--select", nargs="*", default=None, metavar="WORKLOAD",
+                    help="only run the per-layer kernel selection (cos >= 99.8%% vs the FP16 mode, fastest "
+                         "wins) on the named synthetic workloads (default: all but mxfp4)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the whole hot path runs on a single MI355X "
@@ -149,6 +171,10 @@ def main():
 
     import bit_quantized_attention_mean_amd as sa
     from synthetic import WORKLOADS, make_inputs
+
+    if args.select is not None:
+        select_layers(args.select or ["tiny", "prefill", "long_causal", "video_dit", "n16k"], torch, sa)
+        return
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")

@@ -122,14 +122,16 @@ __device__ __forceinline__ void unpack8(const uint4 raw, float* x) {
 // two's complement int8. |q| <= 127 needs no clamp: q = x / s with |x| <= a and
 // s = fp32(a / 127), so |q| <= 127 * (1 + 2^-24).
 constexpr float kMarksteinMinScale = 0x1p-60f;
+constexpr float kRound = 12582912.0f;
 
+// s >= kMarksteinMinScale, y = fp32(1 / s)
 __device__ __forceinline__ unsigned int8_code_bits(float x, float s, float y) {
-  constexpr float kRound = 12582912.0f;
-  if (s >= kMarksteinMinScale) {
-    const float q0 = x * y;
-    const float r = __builtin_fmaf(-q0, s, x);
-    return __float_as_uint(__builtin_fmaf(r, y, q0) + kRound);
-  }
+  const float q0 = x * y;
+  const float r = __builtin_fmaf(-q0, s, x);
+  return __float_as_uint(__builtin_fmaf(r, y, q0) + kRound);
+}
+// any s >= 0 (the slow path for tiny scales; s = 0 gives code 0)
+__device__ __forceinline__ unsigned int8_code_bits_div(float x, float s) {
   return __float_as_uint((s > 0.f ? x / s : 0.f) + kRound);
 }
 
@@ -219,10 +221,15 @@ __global__ __launch_bounds__(256) void int8_quant_kernel(Int8Job j0, Int8Job j1,
     const int row = row0 + p * RPP + rl;
     if (row < J.code_rows) {
       const float sp = s[p];
-      const float y = sp >= kMarksteinMinScale ? 1.0f / sp : 0.f;
       unsigned w[8];
+      if (sp >= kMarksteinMinScale) {
+        const float y = 1.0f / sp;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = int8_code_bits(x[p][e], sp, y);
+        for (int e = 0; e < 8; ++e) w[e] = int8_code_bits(x[p][e], sp, y);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = int8_code_bits_div(x[p][e], sp);
+      }
       *reinterpret_cast<uint2*>(J.codes + (static_cast<size_t>(bh) * J.code_rows + row) * D + cg * 8) =
           make_uint2(pack_low_bytes(w[0], w[1], w[2], w[3]), pack_low_bytes(w[4], w[5], w[6], w[7]));
     }
@@ -375,11 +382,18 @@ __global__ __launch_bounds__(256) void v_int8_kernel(const uint16_t* __restrict_
     const int n0 = tb * TT + n16 * 16;
     if (n0 >= ldv) continue;
     const float s = sc[dd];
-    const float y = s >= kMarksteinMinScale ? 1.0f / s : 0.f;
-    unsigned w[16];
+    float x[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      w[j] = int8_code_bits(static_cast<float>(__builtin_bit_cast(_Float16, t[n16 * 16 + j][dd])), s, y);
+    for (int j = 0; j < 16; ++j) x[j] = static_cast<float>(__builtin_bit_cast(_Float16, t[n16 * 16 + j][dd]));
+    unsigned w[16];
+    if (s >= kMarksteinMinScale) {
+      const float y = 1.0f / s;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) w[j] = int8_code_bits(x[j], s, y);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) w[j] = int8_code_bits_div(x[j], s);
+    }
     *reinterpret_cast<uint4*>(codes + (static_cast<size_t>(bh) * D + dd) * ldv + n0) =
         make_uint4(pack_low_bytes(w[0], w[1], w[2], w[3]), pack_low_bytes(w[4], w[5], w[6], w[7]),
                    pack_low_bytes(w[8], w[9], w[10], w[11]), pack_low_bytes(w[12], w[13], w[14], w[15]));

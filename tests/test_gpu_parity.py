@@ -278,3 +278,32 @@ def test_prepare_compute_equals_fwd_and_is_deterministic(sa, mode):
     sa.sage_attn_compute(c, ws, causal=True, mode=mode, q=qd, k=kd)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_layer_selector_on_synthetic_layers(sa):
+    # Two synthetic "layers": Gaussian inputs, where every INT8 variant clears 99.8%, and
+    # heavy-tailed ones (Student-t, nu = 3) where per-block scales fall short. The cosine the
+    # selector measures against the FP16 mode must agree with the oracle's method accuracy.
+    from bit_quantized_attention_mean_amd import selector as S
+    say("layer selector")
+    sel = S.LayerSelector(reps=3)
+    for name, dist, seed in (("gauss", "normal", 51), ("heavy", "student_t", 52)):
+        q, k, v = make_custom(1, 2, 1024, 64, seed=seed, dist=dist, k_offset_std=2.0)
+        qd, kd, vd = _dev(q, k, v)
+        out = sel(name, qd, kd, vd)
+        torch.cuda.synchronize()
+        mode, meas = sel.modes[name], sel.measurements[name]
+        say(f"  {name}: chose {mode}; " + ", ".join(f"m{m.mode} cos {m.cos:.6f} {m.ms:.3f} ms" for m in meas))
+        assert {m.mode for m in meas} == set(S.DEFAULT_CANDIDATES)
+        assert mode == S.choose(meas)
+        ok = [m for m in meas if m.cos >= S.COS_THRESHOLD]
+        assert (mode == sa.SAGE_MODE_FP16) == (not ok)
+        if ok:
+            assert all(next(m for m in meas if m.mode == mode).ms <= m.ms for m in ok)
+        again = sa.sage_attn_fwd(qd, kd, vd, mode=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(out, again)
+        ex = O.exact_attention(q, k, v, causal=False, sm_scale=1 / 8)
+        em = O.int8_attention(q, k, v, causal=False, sm_scale=1 / 8, blk_q=128, blk_k=64)
+        m0 = next(m for m in meas if m.mode == 0)
+        assert abs(m0.cos - O.metrics(em, ex)["cos"]) < 5e-4

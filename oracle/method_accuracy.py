@@ -4,8 +4,9 @@ For each workload, on sampled heads and query rows, compares the
 quantization-emulating oracle with fp64 exact attention (cosine similarity,
 relative L1, RMSE, max abs) for the INT8 per-block path as configured, and the
 ablations the SageAttention page's "Measured effects" table reports the
-direction of: no K smoothing, per-token scales (blocks of 1 token), and INT8
-P and V (per-block and per-token Q, K).
+direction of: K smoothing on and off at per-block, per-token (blocks of 1
+token) and per-tensor granularity, and INT8 P and V (per-block and per-token
+Q, K).
 MXFP4 runs the microscaled-FP4 emulation (and its variant with MX-FP8 P and
 V). Test infrastructure: the numbers
 describe the method (what any faithful kernel computes), not a kernel.
@@ -34,6 +35,19 @@ def sample_rows(N, rng):
     return np.sort(np.concatenate([fixed, extra])).astype(np.int64)
 
 
+def per_tensor(qs, ks, vs, w, rows, scales, smooth):
+    """INT8 attention of one head with per-tensor Q and K scales (taken over the whole
+    workload tensors): the per-block emulation with one block per head holding the
+    tensor scale."""
+    N = qs.shape[2]
+    sq, sk = scales
+    kf = O.smooth_k(ks, O.k_mean(ks)) if smooth else ks.astype(np.float32)
+    quant = dict(q_codes=O.int8_quant_with_scale(qs.astype(np.float32), sq), q_scales=np.full((1, 1, 1), sq),
+                 k_codes=O.int8_quant_with_scale(kf, sk), k_scales=np.full((1, 1, 1), sk), k_mean=None)
+    return O.int8_attention(qs, ks, vs, causal=w.causal, sm_scale=w.sm_scale, blk_q=N, blk_k=N, rows=rows,
+                            quant=quant)
+
+
 def main(names):
     rng = np.random.default_rng(123)
     print("| workload | variant | cos vs fp64 | rel L1 | RMSE | max abs | sample |")
@@ -44,6 +58,13 @@ def main(names):
         q, k, v = make_inputs(name)
         heads = [(0, 0), (w.B - 1, w.H - 1)] if w.B * w.H > 1 else [(0, 0)]
         results = {}
+        if w.mode != "mxfp4":
+            # per-tensor scales of the whole Q and (smoothed or raw) K tensors
+            ks_full = O.smooth_k(k, O.k_mean(k))
+            tensor_scales = {True: (O.int8_tensor_scale(q.astype(np.float32)), O.int8_tensor_scale(ks_full)),
+                             False: (O.int8_tensor_scale(q.astype(np.float32)),
+                                     O.int8_tensor_scale(k.astype(np.float32)))}
+            del ks_full
         for (b, h) in heads:
             qs, ks, vs = (x[b:b + 1, h:h + 1] for x in (q, k, v))
             rows = sample_rows(w.N, rng)
@@ -66,6 +87,11 @@ def main(names):
                                                                        rows=rows, smooth=False),
                     "INT8 per-token": O.int8_attention(qs, ks, vs, causal=w.causal, sm_scale=w.sm_scale,
                                                        blk_q=1, blk_k=1, rows=rows),
+                    "INT8 per-token, no K smoothing": O.int8_attention(qs, ks, vs, causal=w.causal,
+                                                                       sm_scale=w.sm_scale, blk_q=1, blk_k=1,
+                                                                       rows=rows, smooth=False),
+                    "INT8 per-tensor": per_tensor(qs, ks, vs, w, rows, tensor_scales[True], True),
+                    "INT8 per-tensor, no K smoothing": per_tensor(qs, ks, vs, w, rows, tensor_scales[False], False),
                     "INT8 per-block, INT8 P and V": O.int8_pv_attention(qs, ks, vs, causal=w.causal,
                                                                         sm_scale=w.sm_scale, blk_q=bq, blk_k=64,
                                                                         rows=rows),

@@ -173,6 +173,23 @@ def int8_quant_blocks(x32: np.ndarray, blk: int):
     return codes, scales
 
 
+def int8_tensor_scale(x32: np.ndarray) -> np.float32:
+    """One scale for a whole tensor (the per-tensor granularity of the smoothing
+    ablation in [SA-Effects]): s = fp32(max|x| / 127), reading R3 with the block
+    being the whole tensor."""
+    return np.float32(np.float32(np.abs(np.asarray(x32, dtype=np.float32)).max()) / np.float32(127.0))
+
+
+def int8_quant_with_scale(x32: np.ndarray, s: np.float32) -> np.ndarray:
+    """Codes rint_half_even(fp32(x / s)) clamped to [-127, 127] with one given scale
+    (reading R4; s = 0 gives zero codes). Returns int8 codes of x's shape."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    s = np.float32(s)
+    if s == 0:
+        return np.zeros(x32.shape, np.int8)
+    return np.clip(np.rint(x32 / s), -127, 127).astype(np.int8)
+
+
 def quant_qk_int8(q16, k16, *, blk_q: int, blk_k: int, smooth: bool = True):
     """The quantization half of the INT8 path: mu, K_s, Q and K_s codes and scales.
 

@@ -707,3 +707,19 @@ def test_int8_pv_multi_tile_matches_python_loops(causal):
         want = [a / lsum for a in acc]
         assert max(abs(got[0, 0, i, c] - want[c]) for c in range(D)) < 1e-12
     assert moved > 10      # the case really exercises a moving max
+
+
+def test_per_tensor_scale_and_codes():
+    # One scale for the whole tensor: fp32(max|x| / 127) over every head, codes by the
+    # per-block rule; for a one-head tensor it equals the per-block form with a block of N.
+    x = (RNG.standard_normal((2, 3, 40, 8)) * 2.0).astype(np.float32)
+    s = O.int8_tensor_scale(x)
+    assert Fraction(float(s)) == _f32_round(Fraction(float(np.abs(x).max())) / 127)
+    c = O.int8_quant_with_scale(x, s)
+    for idx in [(0, 0, 0, 0), (1, 2, 39, 7), (0, 1, 17, 3)]:
+        assert int(c[idx]) == _round_half_even(_f32_round(Fraction(float(x[idx])) / Fraction(float(s))))
+    assert np.abs(c).max() == 127
+    one = x[:1, :1]
+    cb, sb = O.int8_quant_blocks(one, 40)
+    assert sb[0, 0, 0] == O.int8_tensor_scale(one) and np.array_equal(cb, O.int8_quant_with_scale(one, sb[0, 0, 0]))
+    assert np.all(O.int8_quant_with_scale(x, np.float32(0)) == 0)

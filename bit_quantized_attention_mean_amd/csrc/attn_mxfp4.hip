@@ -32,6 +32,12 @@ __device__ __forceinline__ int lds_row_of_key4(int k) {
   return t * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
 }
 
+// The next float below x (x finite).
+__device__ __forceinline__ float below_ulp4(float x) {
+  if (x == 0.f) return -0x1p-149f;
+  return __uint_as_float(__float_as_uint(x) + (x > 0.f ? 0xffffffffu : 1u));
+}
+
 __device__ __forceinline__ float pair_max4(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -124,30 +130,33 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
   constexpr int VPT4 = (VCHUNKS + 255) / 256;
   unsigned kr[2][4], vr[2][4 * VPT4];
   unsigned ksr[2] = {0, 0}, vsr[2] = {0, 0};
+// Global loads of tile J_ (clamped to the last tile, so the loop issues them
+  // unconditionally) into staging set S_. Every thread loads (threads beyond a
+  // tile's chunk count repeat an in-bounds chunk and do not store it): the code
+  // stays branch-free, so the compiler's counter waits before the LDS stores
+  // wait only for the loads they need, not for the newer prefetch.
 #define SAGE_GLOAD4(J_, S_)                                                                          \
   do {                                                                                               \
-    if (tid < KCHUNKS) {                                                                             \
-      const int row_ = tid / (D / 32), col_ = tid % (D / 32);                                        \
-      const uint4 t_ = *reinterpret_cast<const uint4*>(kb4 + static_cast<size_t>((J_) * kKTile + row_) * (D / 2) + \
+    const int jj_ = min((J_), nkt - 1);                                                              \
+    {                                                                                                \
+      const int i_ = tid % KCHUNKS, row_ = i_ / (D / 32), col_ = i_ % (D / 32);                      \
+      const uint4 t_ = *reinterpret_cast<const uint4*>(kb4 + static_cast<size_t>(jj_ * kKTile + row_) * (D / 2) + \
                                                        col_ * 16);                                   \
       kr[S_][0] = t_.x; kr[S_][1] = t_.y; kr[S_][2] = t_.z; kr[S_][3] = t_.w;                        \
     }                                                                                                \
-    if (tid < kKTile) {                                                                              \
-      const size_t r_ = static_cast<size_t>((J_) * kKTile + tid);                                    \
+    {                                                                                                \
+      const size_t r_ = static_cast<size_t>(jj_ * kKTile + (tid % kKTile));                          \
       ksr[S_] = (NE == 4) ? *reinterpret_cast<const unsigned*>(kbe + r_ * 4)                         \
                       : static_cast<unsigned>(*reinterpret_cast<const uint16_t*>(kbe + r_ * 2));     \
     }                                                                                                \
     _Pragma("unroll") for (int u_ = 0; u_ < VPT4; ++u_) {                                           \
-      const int i_ = tid + 256 * u_;                                                                 \
-      if (i_ < VCHUNKS) {                                                                            \
-        const int row_ = i_ / VCPR, col_ = i_ % VCPR;                                                \
-        const uint4 t_ = *reinterpret_cast<const uint4*>(vb4 + static_cast<size_t>(row_) * vrb +     \
-                                                         (J_) * VTB + col_ * 16);                    \
-        vr[S_][4 * u_] = t_.x; vr[S_][4 * u_ + 1] = t_.y; vr[S_][4 * u_ + 2] = t_.z; vr[S_][4 * u_ + 3] = t_.w; \
-      }                                                                                              \
+      const int i_ = (tid + 256 * u_) % VCHUNKS;                                                     \
+      const int row_ = i_ / VCPR, col_ = i_ % VCPR;                                                  \
+      const uint4 t_ = *reinterpret_cast<const uint4*>(vb4 + static_cast<size_t>(row_) * vrb +       \
+                                                       jj_ * VTB + col_ * 16);                       \
+      vr[S_][4 * u_] = t_.x; vr[S_][4 * u_ + 1] = t_.y; vr[S_][4 * u_ + 2] = t_.z; vr[S_][4 * u_ + 3] = t_.w; \
     }                                                                                                \
-    if (tid < D)                                                                                     \
-      vsr[S_] = *reinterpret_cast<const uint16_t*>(vbe + static_cast<size_t>(tid) * (Npad / 32) + (J_) * 2); \
+    vsr[S_] = *reinterpret_cast<const uint16_t*>(vbe + static_cast<size_t>(tid % D) * (Npad / 32) + jj_ * 2); \
   } while (0)
 #define SAGE_SWRITE4(BUF_, S_)                                                                       \
   do {                                                                                               \
@@ -172,12 +181,14 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
     if (tid < D) *reinterpret_cast<unsigned*>(vs_ + tid * 4) = vsr[S_];                              \
   } while (0)
 
-  v16f o[NT];
+  // o[NT] is the row sum: the quantized P times a block of ones, accumulated
+  // and rescaled with O^T (every one of its rows holds l of the lane's query)
+  v16f o[NT + 1];
 #pragma unroll
-  for (int c = 0; c < NT; ++c)
+  for (int c = 0; c < NT + 1; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[c][i] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY;
 
   // One key tile (J_) from LDS buffer BUF_: scores, softmax, P quantization, P.V.
 #define SAGE_TILE4(J_, BUF_)                                                                         \
@@ -204,11 +215,13 @@ _Pragma("unroll")                                                               
       }                                                                                             \
     }                                                                                               \
                                                                                                     \
+    /* softmax on the raw scores: the max is taken before the sm_scale * log2(e) */                \
+    /* factor (> 0), which one fma per score applies with the max subtraction */                    \
     float p[32];                                                                                    \
 _Pragma("unroll")                                                                                   \
     for (int t = 0; t < 2; ++t)                                                                     \
 _Pragma("unroll")                                                                                   \
-      for (int i = 0; i < 16; ++i) p[t * 16 + i] = s[t][i] * sl2;                                   \
+      for (int i = 0; i < 16; ++i) p[t * 16 + i] = s[t][i];                                         \
     const bool diag = CAUSAL && (j * kKTile + kKTile - 1 > q0 + wave * 32);                         \
     const bool tail = (j * kKTile + kKTile > N);                                                    \
     if (diag || tail) {                                                                             \
@@ -220,21 +233,24 @@ _Pragma("unroll")                                                               
       }                                                                                             \
     }                                                                                               \
                                                                                                     \
-    float mx = p[0];                                                                                \
+    float lmx = p[0];                                                                               \
 _Pragma("unroll")                                                                                   \
-    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, p[e]);                                              \
-    mx = pair_max4(mx);                                                                             \
+    for (int e = 1; e < 32; ++e) lmx = fmaxf(lmx, p[e]);                                            \
+    const float mxr = pair_max4(lmx);                                                               \
+    float mx = mxr * sl2;                                                                           \
+    /* round the new reference down when the product rounded up: the row's */                      \
+    /* largest score then gets P >= 1 (its exact value is 1), so the block */                       \
+    /* exponent of P cannot drop a binade below the exact one */                                    \
+    if (__builtin_fmaf(mxr, sl2, -mx) < 0.f) mx = below_ulp4(mx);                                   \
     const bool need = mx > m + kRefSlack4;                                                          \
     const float mnew = need ? mx : m;                                                               \
     const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;                              \
-    float rs = 0.f, pmax = 0.f;                                                                     \
+    const float nm = -mnew;                                                                         \
 _Pragma("unroll")                                                                                   \
-    for (int e = 0; e < 32; ++e) {                                                                  \
-      p[e] = __builtin_amdgcn_exp2f(p[e] - mnew);                                                   \
-      rs += p[e];                                                                                   \
-      pmax = fmaxf(pmax, p[e]);                                                                     \
-    }                                                                                               \
-    l = l * alpha + rs;  /* the row sum uses the unquantized P */                                   \
+    for (int e = 0; e < 32; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[e], sl2, nm));     \
+    /* the block max of P is the P of the lane's largest score: the same fma and */                 \
+    /* exp2 on the same operands (0 for a fully masked lane) */                                     \
+    const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(lmx, sl2, nm));                        \
     m = mnew;                                                                                       \
                                                                                                     \
     /* MX-quantize this lane's 32 P values (one block of 32 keys): */                              \
@@ -281,7 +297,7 @@ _Pragma("unroll")                                                               
                                                                                                     \
     if (__ballot(need)) {                                                                           \
 _Pragma("unroll")                                                                                   \
-      for (int c = 0; c < NT; ++c)                                                                  \
+      for (int c = 0; c < NT + 1; ++c)                                                              \
 _Pragma("unroll")                                                                                   \
         for (int i = 0; i < 16; ++i) o[c][i] *= alpha;                                              \
     }                                                                                               \
@@ -302,6 +318,16 @@ _Pragma("unroll")                                                               
         o[dt] = mfma_fp4(a, v4i{pq[0], pq[1], pq[2], pq[3]}, vsw, pe8, o[dt]);                      \
       }                                                                                             \
     }                                                                                               \
+    /* row sum of the quantized P: ones (E4M3 0x38 or E2M1 0x2, scale 2^0) times P */              \
+    if (PV8) {                                                                                      \
+      const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,                            \
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};                           \
+      o[NT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pq, o[NT], 0, 0, 0, 127, 0,    \
+                                                              static_cast<int>(pe8));               \
+    } else {                                                                                        \
+      o[NT] = mfma_fp4(v4i{0x22222222, 0x22222222, 0x22222222, 0x22222222},                         \
+                       v4i{pq[0], pq[1], pq[2], pq[3]}, 127u, pe8, o[NT]);                          \
+    }                                                                                               \
   } while (0)
 
   // Tiles are loaded into registers two iterations ahead (two staging sets)
@@ -309,25 +335,25 @@ _Pragma("unroll")                                                               
   // global loads have a whole iteration to arrive before they are stored.
   SAGE_GLOAD4(0, 0);
   SAGE_SWRITE4(0, 0);
-  if (nkt > 1) SAGE_GLOAD4(1, 1);
-  __syncthreads();
+  SAGE_GLOAD4(1, 1);
+  lds_barrier();
   int j2 = 0;
   for (; j2 + 1 < nkt; j2 += 2) {
-    if (j2 + 2 < nkt) SAGE_GLOAD4(j2 + 2, 0);
+    SAGE_GLOAD4(j2 + 2, 0);
     SAGE_TILE4(j2, 0);
     SAGE_SWRITE4(1, 1);
-    __syncthreads();
-    if (j2 + 3 < nkt) SAGE_GLOAD4(j2 + 3, 1);
+    lds_barrier();
+    SAGE_GLOAD4(j2 + 3, 1);
     SAGE_TILE4(j2 + 1, 1);
-    if (j2 + 2 < nkt) SAGE_SWRITE4(0, 0);
-    __syncthreads();
+    SAGE_SWRITE4(0, 0);   /* tile min(j2 + 2, nkt - 1): unused after the last tile */
+    lds_barrier();
   }
   if (j2 < nkt) SAGE_TILE4(j2, 0);
 #undef SAGE_TILE4
 #undef SAGE_GLOAD4
 #undef SAGE_SWRITE4
 
-  const float inv = 1.f / pair_sum4(l);
+  const float inv = 1.f / o[NT][0];
   if (qrow < N) {
     _Float16* orow = out + (static_cast<size_t>(bh) * N + qrow) * D;
 #pragma unroll

@@ -27,6 +27,15 @@ constexpr int kRowPad = 256;
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS reads and
+// writes, then s_barrier. Unlike __syncthreads() it does not wait for
+// outstanding global loads, so tile prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Tokens per partial-sum chunk of the K column sum: at least 256 and large
 // enough that no head has more than 64 chunks.
 inline int ksum_chunk(int N) {

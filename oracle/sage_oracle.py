@@ -48,8 +48,8 @@ Readings where the pages are silent (each also listed in the design doc):
      so P <= 2^8. Any reference point gives the same softmax; this one only
      fixes where P is rounded. P16 = fp16_RNE(P); O accumulates P16 . V and
      the row sum l accumulates the same P16 (so O is an exact weighted mean of
-     V rows up to accumulation rounding). In the MXFP4 path l sums the
-     unquantized P.
+     V rows up to accumulation rounding). In the MXFP4 path l likewise sums
+     the MX-quantized P that multiplies V.
   R7 causal: key j is masked for query i when j > i (N_q = N_k).
   R8 MX blocks: 32 contiguous elements along the contraction dimension (d for
      Q and K_s; tokens, per channel, for V; keys, per query row inside a key
@@ -207,7 +207,7 @@ REF_SLACK = 8.0   # log2 units by which the tile max may exceed the reference ma
 
 
 def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, ref_slack: float = REF_SLACK,
-                      sum_rounded: bool = False):
+                      sum_rounded: bool = False, p_alternatives=None):
     """FlashAttention-2 style online softmax and P.V over key tiles ([SA-Setup]).
 
     S: float64 scores [R, N] (already scaled, -inf where masked).
@@ -216,12 +216,23 @@ def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, re
     MX-quantized P for the FP4 path, identity for an exact run).
     Reading R6: ascending tiles, P against the lazily updated reference max;
     l sums round_p(P) if sum_rounded else P. Returns O [R, d] float64.
+
+    p_alternatives (test tolerance only, with sum_rounded): a callable giving,
+    for a tile's P, other quantized P that an implementation computing P with
+    a slightly different rounding could produce (a code decided by floating
+    point lands on the other side of a rounding boundary). Then the function
+    returns (O, allowance), allowance [R, d] bounding |O' - O| to first order
+    for any mix of those alternatives: a weight that moves by dP changes O by
+    dP * (v_j - O) / l, and |v_j - O| <= |v_j| + max|v| per channel.
     """
     R, N = S.shape
     d = V.shape[1]
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     O = np.zeros((R, d))
+    A = np.zeros((R, d)) if p_alternatives is not None else None
+    dl = np.zeros(R)
+    vbound = np.abs(V) + np.abs(V).max(axis=0, keepdims=True)
     slack = ref_slack * math.log(2.0)
     for t0 in range(0, N, kv_tile):
         St = S[:, t0:t0 + kv_tile]
@@ -234,7 +245,15 @@ def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, re
         Pr = round_p(P)
         l = l * alpha + (Pr if sum_rounded else P).sum(axis=1)
         O = O * alpha[:, None] + Pr @ V[t0:t0 + kv_tile]
+        if A is not None:
+            dP = np.zeros_like(Pr)
+            for alt in p_alternatives(P):
+                dP = np.maximum(dP, np.abs(alt - Pr))
+            A = A * alpha[:, None] + dP @ vbound[t0:t0 + kv_tile]
+            dl = dl * alpha + dP.sum(axis=1)
         m = m_new
+    if A is not None:
+        return O / l[:, None], A / np.maximum(l - dl, 0.5 * l)[:, None]
     return O / l[:, None]
 
 
@@ -513,14 +532,23 @@ def quant_mxfp4(q16, k16, v16, *, smooth: bool = True, v_fp8: bool = False):
 
 def mxfp4_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: int = 64,
                     smooth: bool = True, rows=None, quant=None, quantize_p: bool = True,
-                    ref_slack: float = REF_SLACK, pv_fp8: bool = False):
+                    ref_slack: float = REF_SLACK, pv_fp8: bool = False, flip_delta: float | None = None):
     """Emulated microscaled-FP4 attention ([SA3-Abstract] with the MX format, reading R8).
 
     Q, K_s, V and the softmax P are MXFP4 (with pv_fp8, P and V are MX-FP8
     instead, reading R13); the scores are the exact products of the decoded
     values (what an FP32-accumulating block-scaled matrix unit computes up to
     accumulation rounding); online softmax as in the INT8 path with the
-    MX-quantized P in place of P16. Returns float64 [B, H, len(rows), d].
+    MX-quantized P in place of P16 (l sums the same quantized P, reading R6).
+    Returns float64 [B, H, len(rows), d].
+
+    flip_delta (test tolerance only): the P codes and block exponents are
+    decided by floating point, so an implementation whose P differs by a few
+    ulps can round a P that lies next to a boundary the other way. With
+    flip_delta, P is also quantized after scaling by (1 -+ flip_delta) (a P of
+    exactly 1, the reference score, only upwards) and the function returns
+    (O, allowance) with the first-order bound of online_softmax_pv on what
+    such flips can change.
     """
     B, H, N, d = q16.shape
     if kv_tile % MX_BLOCK:
@@ -537,14 +565,24 @@ def mxfp4_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: in
     else:
         def round_p(P):
             return P
+    alts = None
+    if flip_delta is not None and quantize_p:
+        # a P of exactly 1 is the reference score itself; an implementation that
+        # rounds its reference down keeps that P >= 1, so it only moves up
+        alts = lambda P: [round_p(np.where(P == 1.0, P, P * (1.0 - flip_delta))), round_p(P * (1.0 + flip_delta))]
+    allow = np.zeros_like(out) if alts is not None else None
     for b in range(B):
         for h in range(H):
             S = (qd["q_vals"][b, h, rows] @ qd["k_vals"][b, h].T) * sm_scale
             if causal:
                 S[_causal_mask(rows, keys)] = -np.inf
-            out[b, h] = online_softmax_pv(S, qd["v_vals"][b, h], kv_tile=kv_tile, round_p=round_p,
-                                          ref_slack=ref_slack)
-    return out
+            r = online_softmax_pv(S, qd["v_vals"][b, h], kv_tile=kv_tile, round_p=round_p,
+                                  ref_slack=ref_slack, sum_rounded=True, p_alternatives=alts)
+            if alts is not None:
+                out[b, h], allow[b, h] = r
+            else:
+                out[b, h] = r
+    return (out, allow) if alts is not None else out
 
 
 # ---------------------------------------------------------------------------

@@ -11,13 +11,21 @@ def half_ulp_f16(x: np.ndarray) -> np.ndarray:
     return 0.5 * np.spacing(np.abs(np.asarray(x, dtype=np.float64)).astype(np.float16)).astype(np.float64)
 
 
-def assert_output_parity(got: np.ndarray, ref: np.ndarray, atol: float = OUT_ATOL, what: str = ""):
+def assert_output_parity(got: np.ndarray, ref: np.ndarray, atol: float = OUT_ATOL, what: str = "", extra=None):
+    """|got - ref| <= atol + half an fp16 ulp of ref (+ `extra`, the oracle's allowance for
+    quantization codes that floating point may round either way, where given)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
     err = np.abs(got - ref)
     bound = atol + half_ulp_f16(ref)
+    if extra is not None:
+        used = int(np.sum(err > bound))
+        bound = bound + np.asarray(extra, dtype=np.float64)
+        if used:
+            say(f"  {what}: {used} element(s) within the P-code flip allowance "
+                f"(largest allowance {float(np.max(extra)):.2e})")
     bad = err > bound
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)

@@ -723,3 +723,49 @@ def test_per_tensor_scale_and_codes():
     cb, sb = O.int8_quant_blocks(one, 40)
     assert sb[0, 0, 0] == O.int8_tensor_scale(one) and np.array_equal(cb, O.int8_quant_with_scale(one, sb[0, 0, 0]))
     assert np.all(O.int8_quant_with_scale(x, np.float32(0)) == 0)
+
+
+@pytest.mark.parametrize("pv_fp8", [False, True])
+def test_mxfp4_constant_v_comes_back_exactly(pv_fp8):
+    # Reading R6 for the MXFP4 path: l sums the same MX-quantized P that multiplies V, so a
+    # V that the codec represents exactly (1.5 = E2M1 code 6 at e = -2, or E4M3 at e = -8)
+    # is returned exactly; with l from the unquantized P it would be off by the P
+    # quantization error.
+    q, k, _ = make_custom(1, 1, 200, 64, seed=36)
+    v = np.full((1, 1, 200, 64), 1.5, np.float16)
+    o = O.mxfp4_attention(q, k, v, causal=True, sm_scale=0.125, pv_fp8=pv_fp8)
+    assert np.max(np.abs(o - 1.5)) <= 1e-14
+
+
+def test_flip_allowance_covers_a_p_code_on_a_rounding_boundary():
+    # Row 0 holds a P right at an E2M1 boundary (block max 1 -> e = -2, P = 0.625 -> 2.5,
+    # halfway between codes 2 and 3): the allowance must cover the output with that code
+    # rounded the other way. Row 1 has no P near a boundary (its block max is the
+    # reference score, P = 1, which stays in its binade): its allowance is exactly 0.
+    rng = np.random.default_rng(37)
+    S = np.full((2, 32), -30.0)
+    S[:, 0] = 0.0
+    S[0, 1] = math.log(0.625)
+    S[1, 1] = math.log(0.55)
+    S[:, 2:8] = np.log(rng.uniform(0.05, 0.2, size=(2, 6)))
+    V = rng.standard_normal((32, 4))
+    quant = lambda P: O.mx_quantize(P, axis=1)[2]
+    delta = 2.0 ** -16
+    # as mxfp4_attention builds them: the reference P of exactly 1 only moves up
+    alts = lambda P: [quant(np.where(P == 1.0, P, P * (1 - delta))), quant(P * (1 + delta))]
+    out, allow = O.online_softmax_pv(S, V, kv_tile=32, round_p=quant, sum_rounded=True, p_alternatives=alts,
+                                     ref_slack=0.0)
+    base = O.online_softmax_pv(S, V, kv_tile=32, round_p=quant, sum_rounded=True, ref_slack=0.0)
+    assert np.array_equal(out, base)
+    p1 = quant(np.exp(S))[0, 1]
+    other = 0.75 if p1 == 0.5 else 0.5
+    assert p1 in (0.5, 0.75)
+
+    def forced(P):
+        Q = quant(P)
+        Q[0, 1] = other
+        return Q
+    flipped = O.online_softmax_pv(S, V, kv_tile=32, round_p=forced, sum_rounded=True, ref_slack=0.0)
+    assert np.all(np.abs(flipped[0] - out[0]) <= allow[0] * (1 + 1e-12))
+    assert np.all(allow[0] > 0) and np.all(allow[1] == 0)
+    assert np.max(np.abs(flipped[0] - out[0])) > 0.2 * np.max(allow[0])   # the bound is not vacuous

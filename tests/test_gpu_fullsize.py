@@ -100,3 +100,45 @@ def test_full_size_workload(sa, name):
             ref = O.int8_attention(qs, ks, vs, causal=w.causal, sm_scale=w.sm_scale, blk_q=bq, blk_k=64, rows=rows)
         err = assert_output_parity(got[b, h, rows], ref[0, 0], what=f"{name} head ({b},{h})", extra=extra)
         say(f"  head ({b},{h}): {rows.size} rows, max |gpu - oracle| = {err:.2e}")
+
+
+@pytest.mark.parametrize("name,mode", [("n16k", 6), ("prefill", 7), ("mxfp4", 5)])
+def test_full_size_variant_modes(sa, name, mode):
+    # The INT8 P,V modes and the MX-FP8 P,V mode at full workload sizes, as bench.py --mode
+    # runs them: V codes and scales bit for bit on two heads (INT8 V), attention on sampled
+    # rows of two heads against the oracle.
+    w = WORKLOADS[name]
+    say(f"full-size {name} in mode {mode}: B={w.B} H={w.H} N={w.N} d={w.d}")
+    q, k, v = make_inputs(name)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    if mode in (6, 7):
+        got = sa.sage_quant_v_int8(vd)
+        torch.cuda.synchronize()
+        for (b, h) in heads:
+            codes, scales = O.int8_quant_v_channels(v[b:b + 1, h:h + 1])
+            assert np.array_equal(got["vt_codes"][b, h, :, :w.N].cpu().numpy(), codes[0, 0].T)
+            assert np.array_equal(got["v_scales"][b, h].cpu().numpy().view(np.uint32), scales[0, 0].view(np.uint32))
+        del got
+        say("  INT8 V bit-exact")
+    ws = sa.make_workspace(w.B, w.H, w.N, w.d, mode)
+    out = torch.empty_like(qd)
+    sa.sage_attn_fwd(qd, kd, vd, out, causal=w.causal, sm_scale=w.sm_scale, mode=mode, workspace=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(7)
+    for (b, h) in heads:
+        rows = _rows(w.N, rng, n=128)
+        qs, ks, vs = (x[b:b + 1, h:h + 1] for x in (q, k, v))
+        extra = None
+        if mode == 5:
+            ref, extra = O.mxfp4_attention(qs, ks, vs, causal=w.causal, sm_scale=w.sm_scale, rows=rows, pv_fp8=True,
+                                           flip_delta=FLIP_DELTA)
+            extra = extra[0, 0]
+        else:
+            blk = 1 if mode == 7 else None
+            ref = O.int8_pv_attention(qs, ks, vs, causal=w.causal, sm_scale=w.sm_scale, blk_q=blk or 128,
+                                      blk_k=blk or 64, rows=rows)
+        err = assert_output_parity(got[b, h, rows], ref[0, 0], what=f"{name} mode {mode} head ({b},{h})", extra=extra)
+        say(f"  head ({b},{h}): {rows.size} rows, max |gpu - oracle| = {err:.2e}")

@@ -129,10 +129,10 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
   float* mu = reinterpret_cast<float*>(at(ws, L.kmean));
   if (lo == SAGE_MODE_FP16)  // unquantized baseline: only the V^T layout (smoothing would be a no-op)
     return hip_status(sage::launch_v_transpose(v, at(ws, L.vt), BH, N, L.Npad, d, s), "V transpose kernel");
-  if (smooth)
-    SAGE_TRY(hip_status(sage::launch_kmean(k, reinterpret_cast<long long*>(at(ws, L.ksum)), mu, nullptr, BH, N, d,
-                                           L.chunk, L.nchunk, s), "K mean kernels"));
   if (lo == SAGE_MODE_MXFP4 || lo == SAGE_MODE_MXFP4_FP8PV) {
+    if (smooth)
+      SAGE_TRY(hip_status(sage::launch_kmean(k, reinterpret_cast<long long*>(at(ws, L.ksum)), mu, nullptr, BH, N, d,
+                                             L.chunk, L.nchunk, s), "K mean kernels"));
     sage::MxRowJob jq, jk;
     jq.src = q; jq.fp4 = at(ws, L.q_fp4); jq.e8 = at(ws, L.q_e8); jq.mu = nullptr; jq.rows = L.Npad;
     jk.src = k; jk.fp4 = at(ws, L.k_fp4); jk.e8 = at(ws, L.k_e8); jk.mu = smooth ? mu : nullptr; jk.rows = L.Npad;
@@ -148,19 +148,19 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
   const bool per_token = lo == SAGE_MODE_INT8_PER_TOKEN || lo == SAGE_MODE_INT8_PV_PER_TOKEN;
   const int blk_q = per_token ? 1 : (lo == SAGE_MODE_INT8_Q64_K64 ? 64 : 128);
   const int blk_k = per_token ? 1 : 64;
-  sage::Int8Job jq, jk;
-  jq.src = q; jq.codes = reinterpret_cast<int8_t*>(at(ws, L.q_codes)); jq.scales = reinterpret_cast<float*>(at(ws, L.q_scales));
-  jq.mu = nullptr; jq.blk = blk_q; jq.code_rows = L.Npad; jq.nscale = L.Npad / blk_q; jq.ntile = L.Npad / sage::kQTile;
-  jk.src = k; jk.codes = reinterpret_cast<int8_t*>(at(ws, L.k_codes)); jk.scales = reinterpret_cast<float*>(at(ws, L.k_scales));
-  jk.mu = smooth ? mu : nullptr; jk.blk = blk_k; jk.code_rows = L.Npad; jk.nscale = L.Npad / blk_k; jk.ntile = L.Npad / sage::kQTile;
-  SAGE_TRY(hip_status(sage::launch_int8_quant(jq, jk, BH, N, d, s), "INT8 quantization kernel"));
-  if (sage::mode_pv_int8(lo))
-    return hip_status(sage::launch_v_int8(v, reinterpret_cast<unsigned*>(at(ws, L.vmax)),
-                                          reinterpret_cast<int8_t*>(at(ws, L.vt)),
-                                          reinterpret_cast<float*>(at(ws, L.vscale)), BH, N, L.Npad, d, L.chunk,
-                                          L.nchunk, s), "INT8 V quantization kernels");
-  SAGE_TRY(hip_status(sage::launch_v_transpose(v, at(ws, L.vt), BH, N, L.Npad, d, s), "V transpose kernel"));
-  return SAGE_OK;
+  sage::PrepInt8 P;
+  P.k = k; P.v = v; P.ksum = reinterpret_cast<long long*>(at(ws, L.ksum)); P.kmean = mu;
+  P.chunk = L.chunk; P.nchunk = L.nchunk; P.smooth = smooth; P.Npad = L.Npad;
+  P.jq.src = q; P.jq.codes = reinterpret_cast<int8_t*>(at(ws, L.q_codes)); P.jq.scales = reinterpret_cast<float*>(at(ws, L.q_scales));
+  P.jq.mu = nullptr; P.jq.blk = blk_q; P.jq.code_rows = L.Npad; P.jq.nscale = L.Npad / blk_q; P.jq.ntile = L.Npad / sage::kQTile;
+  P.jk.src = k; P.jk.codes = reinterpret_cast<int8_t*>(at(ws, L.k_codes)); P.jk.scales = reinterpret_cast<float*>(at(ws, L.k_scales));
+  P.jk.mu = smooth ? mu : nullptr; P.jk.blk = blk_k; P.jk.code_rows = L.Npad; P.jk.nscale = L.Npad / blk_k; P.jk.ntile = L.Npad / sage::kQTile;
+  P.vt = at(ws, L.vt);
+  if (sage::mode_pv_int8(lo)) {
+    P.vmax = reinterpret_cast<unsigned*>(at(ws, L.vmax));
+    P.vscale = reinterpret_cast<float*>(at(ws, L.vscale));
+  }
+  return hip_status(sage::launch_prepare_int8(P, BH, N, d, s), "INT8 prepare kernels");
 }
 
 int do_compute(const void* q, const void* k, void* out, int B, int H, int N, int d, int causal, float sm_scale,

@@ -26,14 +26,13 @@ __device__ __forceinline__ long long f16_to_fixed24(unsigned h) {
   return (h & 0x8000u) ? -mag : mag;
 }
 
+// One 256-thread block of the column sums: chunk `bid` (head bid / nchunk).
 template <int D>
-__global__ __launch_bounds__(256) void ksum_partial_kernel(const uint16_t* __restrict__ k,
-                                                           long long* __restrict__ part, int N,
-                                                           int chunk, int nchunk) {
+__device__ __forceinline__ void ksum_partial_block(const uint16_t* __restrict__ k, long long* __restrict__ part,
+                                                   int N, int chunk, int nchunk, int bid, long long (*red)[9]) {
   constexpr int TPR = D / 8;      // threads per token row, 8 channels (16 bytes) each
   constexpr int RPP = 256 / TPR;  // token rows per pass
-  __shared__ long long red[256][9];
-  const int bh = blockIdx.x / nchunk, ci = blockIdx.x % nchunk;
+  const int bh = bid / nchunk, ci = bid % nchunk;
   const int tid = threadIdx.x, cg = tid % TPR;
   const int n0 = ci * chunk, n1 = min(N, n0 + chunk);
   const uint16_t* src = k + static_cast<size_t>(bh) * N * D + cg * 8;
@@ -56,6 +55,14 @@ __global__ __launch_bounds__(256) void ksum_partial_kernel(const uint16_t* __res
     for (int r = 0; r < RPP; ++r) s += red[r * TPR + g][j];
     part[(static_cast<size_t>(bh) * nchunk + ci) * D + tid] = s;
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void ksum_partial_kernel(const uint16_t* __restrict__ k,
+                                                           long long* __restrict__ part, int N,
+                                                           int chunk, int nchunk) {
+  __shared__ long long red[256][9];
+  ksum_partial_block<D>(k, part, N, chunk, nchunk, blockIdx.x, red);
 }
 
 template <int D>
@@ -141,15 +148,13 @@ __device__ __forceinline__ unsigned pack_low_bytes(unsigned w0, unsigned w1, uns
                                __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u), 0x07060100u);
 }
 
+// One 256-thread block of a quantization job: 128-row tile `bid` (head bid / J.ntile).
 template <int D>
-__global__ __launch_bounds__(256) void int8_quant_kernel(Int8Job j0, Int8Job j1, int N) {
+__device__ __forceinline__ void int8_quant_block(const Int8Job& J, int N, int bid, float* rmax, float* bmax) {
   constexpr int TPR = D / 8;         // threads per row
   constexpr int RPP = 256 / TPR;     // rows per pass
   constexpr int NP = kQTile / RPP;   // passes per 128-row tile
-  __shared__ float rmax[kQTile];
-  __shared__ float bmax[kQTile];
-  const Int8Job J = blockIdx.y ? j1 : j0;
-  const int bh = blockIdx.x / J.ntile, tile = blockIdx.x % J.ntile;
+  const int bh = bid / J.ntile, tile = bid % J.ntile;
   const int tid = threadIdx.x, cg = tid % TPR, rl = tid / TPR;
   const int row0 = tile * kQTile;
   const uint16_t* src = static_cast<const uint16_t*>(J.src) + static_cast<size_t>(bh) * N * D + cg * 8;
@@ -249,6 +254,13 @@ __global__ __launch_bounds__(256) void int8_quant_kernel(Int8Job j0, Int8Job j1,
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void int8_quant_kernel(Int8Job j0, Int8Job j1, int N) {
+  __shared__ float rmax[kQTile];
+  __shared__ float bmax[kQTile];
+  int8_quant_block<D>(blockIdx.y ? j1 : j0, N, blockIdx.x, rmax, bmax);
+}
+
 hipError_t launch_int8_quant(const Int8Job& j0, const Int8Job& j1, int BH, int N, int d, hipStream_t s) {
   // Both jobs cover the same rows per head, so they share the tile count.
   dim3 grid(BH * j0.ntile, 2);
@@ -263,13 +275,15 @@ hipError_t launch_int8_quant(const Int8Job& j0, const Int8Job& j1, int BH, int N
 // transposed makes every operand fetch one 16-byte LDS read.
 // ---------------------------------------------------------------------------
 
+constexpr int kVTile = 64;  // tokens per V transpose tile
+
+// One 256-thread block of the V transpose: 64-token tile `bid`.
 template <int D>
-__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v,
-                                                          uint16_t* __restrict__ vt, int N, int Npad) {
-  constexpr int TT = 64;  // tokens per tile
-  __shared__ uint16_t t[TT][D + 8];
+__device__ __forceinline__ void v_transpose_block(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt, int N,
+                                                  int Npad, int bid, uint16_t (*t)[D + 8]) {
+  constexpr int TT = kVTile;
   const int ntile = Npad / TT;
-  const int bh = blockIdx.x / ntile, tb = blockIdx.x % ntile;
+  const int bh = bid / ntile, tb = bid % ntile;
   const int tid = threadIdx.x;
   const uint16_t* src = v + static_cast<size_t>(bh) * N * D;
   constexpr int CPR = D / 8;  // 16-byte chunks per token row
@@ -294,6 +308,13 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __rest
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v,
+                                                          uint16_t* __restrict__ vt, int N, int Npad) {
+  __shared__ uint16_t t[kVTile][D + 8];
+  v_transpose_block<D>(v, vt, N, Npad, blockIdx.x, t);
+}
+
 hipError_t launch_v_transpose(const void* v, void* vt, int BH, int N, int Npad, int d, hipStream_t s) {
   const int grid = BH * (Npad / 64);
   if (d == 128)
@@ -314,13 +335,11 @@ hipError_t launch_v_transpose(const void* v, void* vt, int BH, int N, int Npad, 
 // ---------------------------------------------------------------------------
 
 template <int D>
-__global__ __launch_bounds__(256) void vmax_partial_kernel(const uint16_t* __restrict__ v,
-                                                           unsigned* __restrict__ part, int N,
-                                                           int chunk, int nchunk) {
+__device__ __forceinline__ void vmax_partial_block(const uint16_t* __restrict__ v, unsigned* __restrict__ part,
+                                                   int N, int chunk, int nchunk, int bid, unsigned (*red)[9]) {
   constexpr int TPR = D / 8;      // threads per token row, 8 channels (16 bytes) each
   constexpr int RPP = 256 / TPR;  // token rows per pass
-  __shared__ unsigned red[256][9];
-  const int bh = blockIdx.x / nchunk, ci = blockIdx.x % nchunk;
+  const int bh = bid / nchunk, ci = bid % nchunk;
   const int tid = threadIdx.x, cg = tid % TPR;
   const int n0 = ci * chunk, n1 = min(N, n0 + chunk);
   const uint16_t* src = v + static_cast<size_t>(bh) * N * D + cg * 8;
@@ -346,16 +365,21 @@ __global__ __launch_bounds__(256) void vmax_partial_kernel(const uint16_t* __res
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void v_int8_kernel(const uint16_t* __restrict__ v,
-                                                     const unsigned* __restrict__ part,
-                                                     int8_t* __restrict__ codes, float* __restrict__ scales,
-                                                     int N, int nchunk, int ldv) {
-  constexpr int TT = 64;      // tokens per tile
+__global__ __launch_bounds__(256) void vmax_partial_kernel(const uint16_t* __restrict__ v,
+                                                           unsigned* __restrict__ part, int N,
+                                                           int chunk, int nchunk) {
+  __shared__ unsigned red[256][9];
+  vmax_partial_block<D>(v, part, N, chunk, nchunk, blockIdx.x, red);
+}
+
+template <int D>
+__device__ __forceinline__ void v_int8_block(const uint16_t* __restrict__ v, const unsigned* __restrict__ part,
+                                             int8_t* __restrict__ codes, float* __restrict__ scales, int N,
+                                             int nchunk, int ldv, int bid, uint16_t (*t)[D + 8], float* sc) {
+  constexpr int TT = kVTile;  // tokens per tile
   constexpr int CPR = D / 8;  // 16-byte chunks per token row
-  __shared__ uint16_t t[TT][D + 8];
-  __shared__ float sc[D];
   const int ntile = (ldv + TT - 1) / TT;
-  const int bh = blockIdx.x / ntile, tb = blockIdx.x % ntile;
+  const int bh = bid / ntile, tb = bid % ntile;
   const int tid = threadIdx.x;
   if (tid < D) {
     unsigned m = 0;
@@ -400,6 +424,16 @@ __global__ __launch_bounds__(256) void v_int8_kernel(const uint16_t* __restrict_
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void v_int8_kernel(const uint16_t* __restrict__ v,
+                                                     const unsigned* __restrict__ part,
+                                                     int8_t* __restrict__ codes, float* __restrict__ scales,
+                                                     int N, int nchunk, int ldv) {
+  __shared__ uint16_t t[kVTile][D + 8];
+  __shared__ float sc[D];
+  v_int8_block<D>(v, part, codes, scales, N, nchunk, ldv, blockIdx.x, t, sc);
+}
+
 hipError_t launch_v_int8(const void* v, unsigned* part, int8_t* codes, float* scales, int BH, int N, int ldv,
                          int d, int chunk, int nchunk, hipStream_t s) {
   const auto* vv = static_cast<const uint16_t*>(v);
@@ -410,6 +444,58 @@ hipError_t launch_v_int8(const void* v, unsigned* part, int8_t* codes, float* sc
   } else {
     vmax_partial_kernel<64><<<BH * nchunk, 256, 0, s>>>(vv, part, N, chunk, nchunk);
     v_int8_kernel<64><<<grid, 256, 0, s>>>(vv, part, codes, scales, N, nchunk, ldv);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The prepare phase of the INT8 modes: (1) the K column sums, the Q codes and
+// the fp16 V^T share one grid, as none depends on another; (2) the K mean;
+// (3) the K codes; for INT8 V, (4) its channel maxima and (5) its codes. The
+// INT8 V passes keep launches of their own: in a shared grid their blocks are
+// held to the occupancy of the quantization blocks' registers, which measured
+// slower. Each block runs the same code as the standalone kernels.
+// ---------------------------------------------------------------------------
+
+constexpr int kPrepSmem = 256 * 9 * 8;  // the largest of the blocks' LDS needs
+
+template <int D>
+__global__ __launch_bounds__(256) void prep_int8_phase1_kernel(PrepInt8 P, int N, int n_ksum, int n_q) {
+  static_assert(kVTile * (D + 8) * 2 <= kPrepSmem, "LDS");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kPrepSmem];
+  const auto* k = static_cast<const uint16_t*>(P.k);
+  const auto* v = static_cast<const uint16_t*>(P.v);
+  int bid = blockIdx.x;
+  if (bid < n_ksum) {
+    ksum_partial_block<D>(k, P.ksum, N, P.chunk, P.nchunk, bid, reinterpret_cast<long long (*)[9]>(smem));
+    return;
+  }
+  bid -= n_ksum;
+  if (bid < n_q) {
+    int8_quant_block<D>(P.jq, N, bid, reinterpret_cast<float*>(smem), reinterpret_cast<float*>(smem) + kQTile);
+    return;
+  }
+  bid -= n_q;
+  v_transpose_block<D>(v, static_cast<uint16_t*>(P.vt), N, P.Npad, bid, reinterpret_cast<uint16_t (*)[D + 8]>(smem));
+}
+
+hipError_t launch_prepare_int8(const PrepInt8& P, int BH, int N, int d, hipStream_t s) {
+  const int n_ksum = P.smooth ? BH * P.nchunk : 0;
+  const int n_q = BH * P.jq.ntile;
+  const int n_v1 = P.vmax ? 0 : BH * (P.Npad / kVTile);
+  const dim3 grid_k(BH * P.jk.ntile, 1);
+  if (d == 128) prep_int8_phase1_kernel<128><<<n_ksum + n_q + n_v1, 256, 0, s>>>(P, N, n_ksum, n_q);
+  else prep_int8_phase1_kernel<64><<<n_ksum + n_q + n_v1, 256, 0, s>>>(P, N, n_ksum, n_q);
+  if (P.smooth) {
+    if (d == 128) kmean_kernel<128><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
+    else kmean_kernel<64><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
+  }
+  if (d == 128) int8_quant_kernel<128><<<grid_k, 256, 0, s>>>(P.jk, P.jk, N);
+  else int8_quant_kernel<64><<<grid_k, 256, 0, s>>>(P.jk, P.jk, N);
+  if (P.vmax) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_v_int8(P.v, P.vmax, static_cast<int8_t*>(P.vt), P.vscale, BH, N, P.Npad, d, P.chunk, P.nchunk, s);
   }
   return hipGetLastError();
 }

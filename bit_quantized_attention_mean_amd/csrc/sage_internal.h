@@ -140,6 +140,23 @@ hipError_t launch_v_transpose(const void* v, void* vt, int BH, int N, int Npad, 
 hipError_t launch_v_int8(const void* v, unsigned* part, int8_t* codes, float* scales, int BH, int N, int ldv,
                          int d, int chunk, int nchunk, hipStream_t s);
 
+// The whole prepare phase of the INT8 modes: K column sums, Q codes and the V
+// layout in one launch, the K mean, the K codes, and the INT8 V codes if used.
+struct PrepInt8 {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  long long* ksum = nullptr;   // int64 [BH, nchunk, d]
+  float* kmean = nullptr;      // fp32 [BH, d], written when smooth
+  int chunk = 0, nchunk = 0;
+  bool smooth = true;
+  Int8Job jq, jk;              // jk.mu = kmean when smooth
+  void* vt = nullptr;          // fp16 V^T [BH, d, Npad], or int8 V^T codes when vmax is set
+  unsigned* vmax = nullptr;    // INT8 V: partial channel maxima [BH, nchunk, d]; null: fp16 V^T
+  float* vscale = nullptr;     // INT8 V: scales [BH, d]
+  int Npad = 0;
+};
+hipError_t launch_prepare_int8(const PrepInt8& P, int BH, int N, int d, hipStream_t s);
+
 // MXFP4 quantization along channels: src fp16 [BH, N, d] -> fp4 [BH, rows, d/2],
 // e8 [BH, rows, d/32]; rows in [N, rows) get zero codes and exponent byte 127.
 struct MxRowJob {

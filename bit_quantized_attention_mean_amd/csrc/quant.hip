@@ -148,15 +148,18 @@ __device__ __forceinline__ unsigned pack_low_bytes(unsigned w0, unsigned w1, uns
                                __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u), 0x07060100u);
 }
 
-// One 256-thread block of a quantization job: 128-row tile `bid` (head bid / J.ntile).
-template <int D>
+// One 256-thread block of a quantization job: TR-row tile `bid` (head bid /
+// J.ntile), TR = 128 or 64 (64-row tiles hold half the registers, for jobs
+// with blocks of at most 64 rows).
+template <int D, int TR = kQTile>
 __device__ __forceinline__ void int8_quant_block(const Int8Job& J, int N, int bid, float* rmax, float* bmax) {
+  static_assert(TR == 128 || TR == 64, "tile rows");
   constexpr int TPR = D / 8;         // threads per row
   constexpr int RPP = 256 / TPR;     // rows per pass
-  constexpr int NP = kQTile / RPP;   // passes per 128-row tile
+  constexpr int NP = TR / RPP;       // passes per tile
   const int bh = bid / J.ntile, tile = bid % J.ntile;
   const int tid = threadIdx.x, cg = tid % TPR, rl = tid / TPR;
-  const int row0 = tile * kQTile;
+  const int row0 = tile * TR;
   const uint16_t* src = static_cast<const uint16_t*>(J.src) + static_cast<size_t>(bh) * N * D + cg * 8;
 
   float mu[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -167,27 +170,38 @@ __device__ __forceinline__ void int8_quant_block(const Int8Job& J, int N, int bi
     mu[4] = b.x; mu[5] = b.y; mu[6] = b.z; mu[7] = b.w;
   }
 
-  float x[NP][8];
+  // the tile stays in registers as fp16 (4 registers per 8 values); the fp32
+  // values x - mu are formed once for the maxima and again for the codes
+  uint4 raw[NP];
   float lm[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int row = row0 + p * RPP + rl;
-    if (row < N) {
-      unpack8(*reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * D), x[p]);
+    raw[p] = row < N ? *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * D) : make_uint4(0, 0, 0, 0);
+  }
+  // x = fp32(v) - mu (one RNE subtraction; mu = 0 if off), zero for rows >= N
+  auto values = [&](int p, float* x) {
+    unpack8(raw[p], x);
+    const bool live = row0 + p * RPP + rl < N;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[p][e] = x[p][e] - mu[e];  // fp32 RNE subtraction (mu = 0 if off)
-    } else {
+    for (int e = 0; e < 8; ++e) x[e] = live ? x[e] - mu[e] : 0.f;
+  };
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[p][e] = 0.f;
-    }
+  for (int p = 0; p < NP; ++p) {
+    float x[8];
+    values(p, x);
     float m = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[p][e]));
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
     // max over the TPR consecutive lanes that share this row
 #pragma unroll
     for (int off = 1; off < TPR; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     lm[p] = m;
   }
+  // an empty asm that claims to change the raw registers: the compiler then
+  // forms x - mu again below instead of keeping all 8 * NP fp32 values live
+#pragma unroll
+  for (int p = 0; p < NP; ++p) asm volatile("" : "+v"(raw[p].x), "+v"(raw[p].y), "+v"(raw[p].z), "+v"(raw[p].w));
 
   const int blk = J.blk;
   float s[NP];
@@ -200,9 +214,9 @@ __device__ __forceinline__ void int8_quant_block(const Int8Job& J, int N, int bi
       if (cg == 0) rmax[p * RPP + rl] = lm[p];
     __syncthreads();
     // block maxima by one wave: lane i holds rows i and i + 64, then a
-    // butterfly over the lanes of each block (blk is a power of two)
+    // butterfly over the lanes of each block (blk is a power of two, <= TR)
     if (tid < 64) {
-      float m0 = rmax[tid], m1 = rmax[tid + 64];
+      float m0 = rmax[tid], m1 = TR == 128 ? rmax[tid + 64] : 0.f;
       if (blk >= 128) m0 = m1 = fmaxf(m0, m1);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -213,7 +227,7 @@ __device__ __forceinline__ void int8_quant_block(const Int8Job& J, int N, int bi
       }
       if (tid % blk == 0) {
         bmax[tid / blk] = m0;
-        if (blk < 128) bmax[(tid + 64) / blk] = m1;
+        if (TR == 128 && blk < 128) bmax[(tid + 64) / blk] = m1;
       }
     }
     __syncthreads();
@@ -226,14 +240,16 @@ __device__ __forceinline__ void int8_quant_block(const Int8Job& J, int N, int bi
     const int row = row0 + p * RPP + rl;
     if (row < J.code_rows) {
       const float sp = s[p];
+      float x[8];
+      values(p, x);
       unsigned w[8];
       if (sp >= kMarksteinMinScale) {
         const float y = 1.0f / sp;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = int8_code_bits(x[p][e], sp, y);
+        for (int e = 0; e < 8; ++e) w[e] = int8_code_bits(x[e], sp, y);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = int8_code_bits_div(x[p][e], sp);
+        for (int e = 0; e < 8; ++e) w[e] = int8_code_bits_div(x[e], sp);
       }
       *reinterpret_cast<uint2*>(J.codes + (static_cast<size_t>(bh) * J.code_rows + row) * D + cg * 8) =
           make_uint2(pack_low_bytes(w[0], w[1], w[2], w[3]), pack_low_bytes(w[4], w[5], w[6], w[7]));
@@ -248,17 +264,17 @@ __device__ __forceinline__ void int8_quant_block(const Int8Job& J, int N, int bi
       if (cg == 0 && row < J.nscale) J.scales[static_cast<size_t>(bh) * J.nscale + row] = s[p];
     }
   } else {
-    const int nb = kQTile / blk;
+    const int nb = TR / blk;
     const int bi = tile * nb + tid;
     if (tid < nb && bi < J.nscale) J.scales[static_cast<size_t>(bh) * J.nscale + bi] = bmax[tid] / 127.0f;
   }
 }
 
-template <int D>
+template <int D, int TR = kQTile>
 __global__ __launch_bounds__(256) void int8_quant_kernel(Int8Job j0, Int8Job j1, int N) {
   __shared__ float rmax[kQTile];
   __shared__ float bmax[kQTile];
-  int8_quant_block<D>(blockIdx.y ? j1 : j0, N, blockIdx.x, rmax, bmax);
+  int8_quant_block<D, TR>(blockIdx.y ? j1 : j0, N, blockIdx.x, rmax, bmax);
 }
 
 hipError_t launch_int8_quant(const Int8Job& j0, const Int8Job& j1, int BH, int N, int d, hipStream_t s) {
@@ -483,15 +499,19 @@ hipError_t launch_prepare_int8(const PrepInt8& P, int BH, int N, int d, hipStrea
   const int n_ksum = P.smooth ? BH * P.nchunk : 0;
   const int n_q = BH * P.jq.ntile;
   const int n_v1 = P.vmax ? 0 : BH * (P.Npad / kVTile);
-  const dim3 grid_k(BH * P.jk.ntile, 1);
+  // K codes in 64-row tiles (K blocks are 64 rows or one row): half the
+  // registers of a 128-row tile, so twice the waves in flight
+  Int8Job jk = P.jk;
+  jk.ntile = P.jk.ntile * (kQTile / 64);
+  const dim3 grid_k(BH * jk.ntile, 1);
   if (d == 128) prep_int8_phase1_kernel<128><<<n_ksum + n_q + n_v1, 256, 0, s>>>(P, N, n_ksum, n_q);
   else prep_int8_phase1_kernel<64><<<n_ksum + n_q + n_v1, 256, 0, s>>>(P, N, n_ksum, n_q);
   if (P.smooth) {
     if (d == 128) kmean_kernel<128><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
     else kmean_kernel<64><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
   }
-  if (d == 128) int8_quant_kernel<128><<<grid_k, 256, 0, s>>>(P.jk, P.jk, N);
-  else int8_quant_kernel<64><<<grid_k, 256, 0, s>>>(P.jk, P.jk, N);
+  if (d == 128) int8_quant_kernel<128, 64><<<grid_k, 256, 0, s>>>(jk, jk, N);
+  else int8_quant_kernel<64, 64><<<grid_k, 256, 0, s>>>(jk, jk, N);
   if (P.vmax) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -130,20 +130,13 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
   if (lo == SAGE_MODE_FP16)  // unquantized baseline: only the V^T layout (smoothing would be a no-op)
     return hip_status(sage::launch_v_transpose(v, at(ws, L.vt), BH, N, L.Npad, d, s), "V transpose kernel");
   if (lo == SAGE_MODE_MXFP4 || lo == SAGE_MODE_MXFP4_FP8PV) {
-    if (smooth)
-      SAGE_TRY(hip_status(sage::launch_kmean(k, reinterpret_cast<long long*>(at(ws, L.ksum)), mu, nullptr, BH, N, d,
-                                             L.chunk, L.nchunk, s), "K mean kernels"));
-    sage::MxRowJob jq, jk;
-    jq.src = q; jq.fp4 = at(ws, L.q_fp4); jq.e8 = at(ws, L.q_e8); jq.mu = nullptr; jq.rows = L.Npad;
-    jk.src = k; jk.fp4 = at(ws, L.k_fp4); jk.e8 = at(ws, L.k_e8); jk.mu = smooth ? mu : nullptr; jk.rows = L.Npad;
-    SAGE_TRY(hip_status(sage::launch_mx_rows(jq, jk, BH, N, d, s), "MXFP4 Q/K quantization kernel"));
-    if (lo == SAGE_MODE_MXFP4_FP8PV)
-      SAGE_TRY(hip_status(sage::launch_mx_vt8(v, at(ws, L.vt_fp4), at(ws, L.vt_e8), BH, N, L.Npad, d, s),
-                          "MX-FP8 V quantization kernel"));
-    else
-      SAGE_TRY(hip_status(sage::launch_mx_vt(v, at(ws, L.vt_fp4), at(ws, L.vt_e8), BH, N, L.Npad, d, s),
-                          "MXFP4 V quantization kernel"));
-    return SAGE_OK;
+    sage::PrepMx P;
+    P.BH = BH; P.k = k; P.v = v; P.ksum = reinterpret_cast<long long*>(at(ws, L.ksum)); P.kmean = mu;
+    P.chunk = L.chunk; P.nchunk = L.nchunk; P.smooth = smooth;
+    P.jq.src = q; P.jq.fp4 = at(ws, L.q_fp4); P.jq.e8 = at(ws, L.q_e8); P.jq.mu = nullptr; P.jq.rows = L.Npad;
+    P.jk.src = k; P.jk.fp4 = at(ws, L.k_fp4); P.jk.e8 = at(ws, L.k_e8); P.jk.mu = smooth ? mu : nullptr; P.jk.rows = L.Npad;
+    P.vt = at(ws, L.vt_fp4); P.vte8 = at(ws, L.vt_e8); P.Nv = L.Npad; P.v_fp8 = lo == SAGE_MODE_MXFP4_FP8PV;
+    return hip_status(sage::launch_prepare_mx(P, N, d, s), "MXFP4 prepare kernels");
   }
   const bool per_token = lo == SAGE_MODE_INT8_PER_TOKEN || lo == SAGE_MODE_INT8_PV_PER_TOKEN;
   const int blk_q = per_token ? 1 : (lo == SAGE_MODE_INT8_Q64_K64 ? 64 : 128);

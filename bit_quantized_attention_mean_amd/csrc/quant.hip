@@ -546,6 +546,10 @@ __device__ __forceinline__ unsigned e2m1_code(float x, int e) {
 }
 
 // Quantizes 32 floats: 16 packed bytes (element 2i in the low nibble) + exponent byte.
+// With a normal scale 2^e (e >= -126) the codes come from the hardware
+// conversion v_cvt_scalef32_pk_fp4_f32 (x / 2^e, round to nearest even,
+// saturating at 6, sign of x kept, first operand in the low nibble), two
+// values per instruction; the comparison ladder above covers e = -127.
 __device__ __forceinline__ uint4 mx_block(const float* x, unsigned& e8) {
   float a = 0.f;
 #pragma unroll
@@ -553,16 +557,29 @@ __device__ __forceinline__ uint4 mx_block(const float* x, unsigned& e8) {
   const int e = mx_exponent(a);
   e8 = static_cast<unsigned>(e + 127);
   unsigned w[4] = {0, 0, 0, 0};
+  if (e >= -126) {
+    const float scale = __uint_as_float(e8 << 23);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) w[i / 8] |= e2m1_code(x[i], e) << (4 * (i % 8));
+    for (int k = 0; k < 4; ++k) {
+      unsigned r = 0;
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[8 * k + 0], x[8 * k + 1], scale, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[8 * k + 2], x[8 * k + 3], scale, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[8 * k + 4], x[8 * k + 5], scale, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[8 * k + 6], x[8 * k + 7], scale, 3);
+      w[k] = r;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i / 8] |= e2m1_code(x[i], e) << (4 * (i % 8));
+  }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// 256 consecutive 32-element row blocks of a job (one per thread), starting at block 256 * bid.
 template <int D>
-__global__ __launch_bounds__(256) void mx_rows_kernel(MxRowJob j0, MxRowJob j1, int BH, int N) {
+__device__ __forceinline__ void mx_rows_block(const MxRowJob& J, int BH, int N, int bid) {
   constexpr int NB = D / 32;  // blocks per row
-  const MxRowJob J = blockIdx.y ? j1 : j0;
-  const long long gb = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const long long gb = static_cast<long long>(bid) * 256 + threadIdx.x;
   const long long per_head = static_cast<long long>(J.rows) * NB;
   if (gb >= per_head * BH) return;
   const int bh = static_cast<int>(gb / per_head);
@@ -590,49 +607,20 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(MxRowJob j0, MxRowJob j1, 
   J.e8[r * NB + db] = static_cast<uint8_t>(e8);
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void mx_rows_kernel(MxRowJob j0, MxRowJob j1, int BH, int N) {
+  mx_rows_block<D>(blockIdx.y ? j1 : j0, BH, N, blockIdx.x);
+}
+
+inline unsigned mx_rows_blocks(const MxRowJob& j, int BH, int d) {
+  return static_cast<unsigned>((static_cast<long long>(BH) * j.rows * (d / 32) + 255) / 256);
+}
+
 hipError_t launch_mx_rows(const MxRowJob& j0, const MxRowJob& j1, int BH, int N, int d, hipStream_t s) {
-  const long long nblk = static_cast<long long>(BH) * j0.rows * (d / 32);
-  dim3 grid(static_cast<unsigned>((nblk + 255) / 256), 2);
+  dim3 grid(mx_rows_blocks(j0, BH, d), 2);
   if (d == 128) mx_rows_kernel<128><<<grid, 256, 0, s>>>(j0, j1, BH, N);
   else mx_rows_kernel<64><<<grid, 256, 0, s>>>(j0, j1, BH, N);
   return hipGetLastError();
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void mx_vt_kernel(const uint16_t* __restrict__ v, uint8_t* __restrict__ fp4,
-                                                    uint8_t* __restrict__ e8, int N, int Nv) {
-  constexpr int TT = 256 * 32 / D;  // tokens per tile: every thread owns one (channel, 32-token block)
-  constexpr int CPR = D / 8;
-  __shared__ uint16_t t[TT][D + 2];
-  const int ntile = (Nv + TT - 1) / TT;
-  const int bh = blockIdx.x / ntile, tb = blockIdx.x % ntile;
-  const int tid = threadIdx.x;
-  const uint16_t* src = v + static_cast<size_t>(bh) * N * D;
-#pragma unroll
-  for (int u = 0; u < TT * CPR / 256; ++u) {
-    const int i = tid + 256 * u, r = i / CPR, c8 = i % CPR;
-    const int n = tb * TT + r;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (n < N) val = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(n) * D + c8 * 8);
-    const unsigned w[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      t[r][c8 * 8 + 2 * j] = static_cast<uint16_t>(w[j] & 0xffffu);
-      t[r][c8 * 8 + 2 * j + 1] = static_cast<uint16_t>(w[j] >> 16);
-    }
-  }
-  __syncthreads();
-  const int c = tid % D, b = tid / D;
-  const int n0 = tb * TT + b * 32;
-  if (n0 >= Nv) return;
-  float x[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = static_cast<float>(__builtin_bit_cast(_Float16, t[b * 32 + i][c]));
-  unsigned eb;
-  const uint4 packed = mx_block(x, eb);
-  const size_t rowc = static_cast<size_t>(bh) * D + c;
-  *reinterpret_cast<uint4*>(fp4 + rowc * (Nv / 2) + n0 / 2) = packed;
-  e8[rowc * (Nv / 32) + n0 / 32] = static_cast<uint8_t>(eb);
 }
 
 // ---------------------------------------------------------------------------
@@ -677,14 +665,18 @@ __device__ __forceinline__ void mx_block8(const float* x, uint4& lo, uint4& hi, 
   hi = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void mx_vt8_kernel(const uint16_t* __restrict__ v, uint8_t* __restrict__ fp8,
-                                                     uint8_t* __restrict__ e8, int N, int Nv) {
-  constexpr int TT = 256 * 32 / D;  // tokens per tile: every thread owns one (channel, 32-token block)
+// V^T in MX blocks of 32 tokens per channel: one tile of TT tokens, every
+// thread owns one (channel, 32-token block). Neighbouring threads own the
+// blocks of one channel, so their code stores are contiguous. FP8: E4M3
+// codes (one byte each), else packed E2M1.
+template <int D, bool FP8>
+__device__ __forceinline__ void mx_vt_block(const uint16_t* __restrict__ v, uint8_t* __restrict__ codes,
+                                            uint8_t* __restrict__ e8, int N, int Nv, int bid, uint16_t (*t)[D + 2]) {
+  constexpr int TT = 256 * 32 / D;  // tokens per tile
+  constexpr int NBT = TT / 32;      // 32-token blocks per tile
   constexpr int CPR = D / 8;
-  __shared__ uint16_t t[TT][D + 2];
   const int ntile = (Nv + TT - 1) / TT;
-  const int bh = blockIdx.x / ntile, tb = blockIdx.x % ntile;
+  const int bh = bid / ntile, tb = bid % ntile;
   const int tid = threadIdx.x;
   const uint16_t* src = v + static_cast<size_t>(bh) * N * D;
 #pragma unroll
@@ -701,34 +693,92 @@ __global__ __launch_bounds__(256) void mx_vt8_kernel(const uint16_t* __restrict_
     }
   }
   __syncthreads();
-  const int c = tid % D, b = tid / D;
+  const int c = tid / NBT, b = tid % NBT;
   const int n0 = tb * TT + b * 32;
   if (n0 >= Nv) return;
   float x[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) x[i] = static_cast<float>(__builtin_bit_cast(_Float16, t[b * 32 + i][c]));
   unsigned eb;
-  uint4 lo, hi;
-  mx_block8(x, lo, hi, eb);
   const size_t rowc = static_cast<size_t>(bh) * D + c;
-  *reinterpret_cast<uint4*>(fp8 + rowc * Nv + n0) = lo;
-  *reinterpret_cast<uint4*>(fp8 + rowc * Nv + n0 + 16) = hi;
+  if (FP8) {
+    uint4 lo, hi;
+    mx_block8(x, lo, hi, eb);
+    *reinterpret_cast<uint4*>(codes + rowc * Nv + n0) = lo;
+    *reinterpret_cast<uint4*>(codes + rowc * Nv + n0 + 16) = hi;
+  } else {
+    *reinterpret_cast<uint4*>(codes + rowc * (Nv / 2) + n0 / 2) = mx_block(x, eb);
+  }
   e8[rowc * (Nv / 32) + n0 / 32] = static_cast<uint8_t>(eb);
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void mx_vt_kernel(const uint16_t* __restrict__ v, uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ e8, int N, int Nv) {
+  __shared__ uint16_t t[256 * 32 / D][D + 2];
+  mx_vt_block<D, FP8>(v, codes, e8, N, Nv, blockIdx.x, t);
 }
 
 hipError_t launch_mx_vt8(const void* v, uint8_t* fp8, uint8_t* e8, int BH, int N, int Nv, int d, hipStream_t s) {
   const int TT = 256 * 32 / d;
   const int grid = BH * ((Nv + TT - 1) / TT);
-  if (d == 128) mx_vt8_kernel<128><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp8, e8, N, Nv);
-  else mx_vt8_kernel<64><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp8, e8, N, Nv);
+  if (d == 128) mx_vt_kernel<128, true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp8, e8, N, Nv);
+  else mx_vt_kernel<64, true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp8, e8, N, Nv);
   return hipGetLastError();
 }
 
 hipError_t launch_mx_vt(const void* v, uint8_t* fp4, uint8_t* e8, int BH, int N, int Nv, int d, hipStream_t s) {
   const int TT = 256 * 32 / d;
   const int grid = BH * ((Nv + TT - 1) / TT);
-  if (d == 128) mx_vt_kernel<128><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp4, e8, N, Nv);
-  else mx_vt_kernel<64><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp4, e8, N, Nv);
+  if (d == 128) mx_vt_kernel<128, false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp4, e8, N, Nv);
+  else mx_vt_kernel<64, false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), fp4, e8, N, Nv);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The prepare phase of the MXFP4 modes, like the INT8 one: (1) the K column
+// sums, the Q codes and the V^T codes share one grid; (2) the K mean; (3) the
+// K codes.
+// ---------------------------------------------------------------------------
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void prep_mx_phase1_kernel(PrepMx P, int N, int n_ksum, int n_q) {
+  static_assert(256 * 32 / D * (D + 2) * 2 <= kPrepSmem, "LDS");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kPrepSmem];
+  int bid = blockIdx.x;
+  if (bid < n_ksum) {
+    ksum_partial_block<D>(static_cast<const uint16_t*>(P.k), P.ksum, N, P.chunk, P.nchunk, bid,
+                          reinterpret_cast<long long (*)[9]>(smem));
+    return;
+  }
+  bid -= n_ksum;
+  if (bid < n_q) {
+    mx_rows_block<D>(P.jq, P.BH, N, bid);
+    return;
+  }
+  bid -= n_q;
+  mx_vt_block<D, FP8>(static_cast<const uint16_t*>(P.v), P.vt, P.vte8, N, P.Nv, bid,
+                      reinterpret_cast<uint16_t (*)[D + 2]>(smem));
+}
+
+hipError_t launch_prepare_mx(const PrepMx& P, int N, int d, hipStream_t s) {
+  const int BH = P.BH;
+  const int n_ksum = P.smooth ? BH * P.nchunk : 0;
+  const int n_q = static_cast<int>(mx_rows_blocks(P.jq, BH, d));
+  const int TT = 256 * 32 / d;
+  const int n_v = BH * ((P.Nv + TT - 1) / TT);
+  const int grid = n_ksum + n_q + n_v;
+#define SAGE_PHASE1(D_, F_) prep_mx_phase1_kernel<D_, F_><<<grid, 256, 0, s>>>(P, N, n_ksum, n_q)
+  if (d == 128) { if (P.v_fp8) SAGE_PHASE1(128, true); else SAGE_PHASE1(128, false); }
+  else { if (P.v_fp8) SAGE_PHASE1(64, true); else SAGE_PHASE1(64, false); }
+#undef SAGE_PHASE1
+  if (P.smooth) {
+    if (d == 128) kmean_kernel<128><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
+    else kmean_kernel<64><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
+  }
+  const dim3 grid_k(mx_rows_blocks(P.jk, BH, d), 1);
+  if (d == 128) mx_rows_kernel<128><<<grid_k, 256, 0, s>>>(P.jk, P.jk, BH, N);
+  else mx_rows_kernel<64><<<grid_k, 256, 0, s>>>(P.jk, P.jk, BH, N);
   return hipGetLastError();
 }
 

@@ -168,6 +168,24 @@ struct MxRowJob {
 };
 hipError_t launch_mx_rows(const MxRowJob& j0, const MxRowJob& j1, int BH, int N, int d, hipStream_t s);
 
+// The whole prepare phase of the MXFP4 modes: K column sums, Q codes and V^T
+// codes (E2M1, or E4M3 when v_fp8) in one launch, the K mean, then the K codes.
+struct PrepMx {
+  int BH = 0;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  long long* ksum = nullptr;
+  float* kmean = nullptr;
+  int chunk = 0, nchunk = 0;
+  bool smooth = true;
+  MxRowJob jq, jk;          // jk.mu = kmean when smooth
+  uint8_t* vt = nullptr;    // V^T codes [BH, d, Nv/2] (E2M1) or [BH, d, Nv] (E4M3)
+  uint8_t* vte8 = nullptr;  // [BH, d, Nv/32]
+  int Nv = 0;
+  bool v_fp8 = false;
+};
+hipError_t launch_prepare_mx(const PrepMx& P, int N, int d, hipStream_t s);
+
 // MXFP4 quantization of V along tokens: -> fp4 [BH, d, Nv/2], e8 [BH, d, Nv/32]
 // (Nv a multiple of 32, tokens >= N are zeros).
 hipError_t launch_mx_vt(const void* v, uint8_t* fp4, uint8_t* e8, int BH, int N, int Nv, int d, hipStream_t s);

@@ -24,7 +24,7 @@ __all__ = [
     "SAGE_MODE_FP16", "SAGE_MODE_MXFP4_FP8PV", "SAGE_MODE_INT8_PV", "SAGE_MODE_INT8_PV_PER_TOKEN",
     "SAGE_FLAG_NO_SMOOTH", "SAGE_FLAG_FP8_V", "SageError", "LIB_PATH", "lib",
     "sage_attn_fwd", "sage_attn_prepare", "sage_attn_compute", "sage_attn_workspace_size",
-    "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_quant_v_int8", "sage_status_string", "sage_last_error",
+    "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_quant_v_int8", "sage_attn_dump_scores", "sage_status_string", "sage_last_error",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -53,6 +53,7 @@ _SIGS = {
     "sage_quant_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sage_quant_mxfp4": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sage_quant_v_int8": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "sage_attn_dump_scores": (_i, [_vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _i, _i, _vp, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -257,3 +258,19 @@ def sage_quant_v_int8(v, *, stream=None):
                                _stream(stream))
     _check(rc, "sage_quant_v_int8")
     return res
+
+
+def sage_attn_dump_scores(out, workspace, *, bh, q_tile, k_tile, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64,
+                          stream=None):
+    """Test hook: runs the INT8 attention kernel (non-causal) on a prepared workspace and returns the
+    int32 scores its matrix op produced for key tile k_tile and query tile q_tile of head bh ([256, 64])."""
+    torch = _torch()
+    B, H, N, d = _shape4(out)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    s_out = torch.zeros((256, 64), dtype=torch.int32, device=out.device)
+    rc = lib.sage_attn_dump_scores(_dev_ptr(out, "out", torch.float16), B, H, N, d, float(sm_scale), int(mode),
+                                   _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                   int(bh), int(q_tile), int(k_tile), _dev_ptr(s_out, "s_out"), _stream(stream))
+    _check(rc, "sage_attn_dump_scores")
+    return s_out

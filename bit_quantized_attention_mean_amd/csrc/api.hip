@@ -252,6 +252,37 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
   return do_compute(q, k, out, B, H, N, d, causal, sm_scale, mode, workspace, s);
 }
 
+int sage_attn_dump_scores(void* out, int B, int H, int N, int d, float sm_scale, int mode, const void* workspace,
+                          size_t workspace_bytes, int bh, int q_tile, int k_tile, int32_t* s_out, void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_ptr(out, "out", 16));
+  SAGE_TRY(check_ptr(s_out, "s_out", 16));
+  SAGE_TRY(check_scale(sm_scale));
+  SAGE_TRY(validate_attn(B, H, N, d, mode, workspace, workspace_bytes));
+  const int lo = mode & SAGE_MODE_MASK;
+  if (lo != SAGE_MODE_INT8_Q128_K64 && lo != SAGE_MODE_INT8_Q64_K64 && lo != SAGE_MODE_INT8_PER_TOKEN)
+    return fail(SAGE_ERR_UNSUPPORTED, "the score dump covers the INT8 modes 0, 1 and 3 (got %d)", lo);
+  const long long BH = static_cast<long long>(B) * H;
+  if (bh < 0 || bh >= BH) return fail(SAGE_ERR_INVALID_ARG, "bh = %d is outside [0, %lld)", bh, BH);
+  const int nqt = (N + sage::kWGQ - 1) / sage::kWGQ, nkt = (N + sage::kKTile - 1) / sage::kKTile;
+  if (q_tile < 0 || q_tile >= nqt) return fail(SAGE_ERR_INVALID_ARG, "q_tile = %d is outside [0, %d)", q_tile, nqt);
+  if (k_tile < 0 || k_tile >= nkt) return fail(SAGE_ERR_INVALID_ARG, "k_tile = %d is outside [0, %d)", k_tile, nkt);
+  SAGE_TRY(check_device());
+  const sage::Layout L = sage::make_layout(BH, N, d, lo, true);
+  sage::AttnArgs a;
+  a.BH = static_cast<int>(BH); a.N = N; a.Npad = L.Npad; a.d = d; a.causal = false;
+  a.sl2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  a.mode = lo; a.out = out;
+  (void)hipGetLastError();
+  return hip_status(sage::launch_attn_int8_dump(a, at(workspace, L.q_codes), at(workspace, L.k_codes),
+                                                at(workspace, L.vt),
+                                                reinterpret_cast<const float*>(at(workspace, L.q_scales)),
+                                                reinterpret_cast<const float*>(at(workspace, L.k_scales)),
+                                                reinterpret_cast<int*>(s_out), bh, q_tile, k_tile,
+                                                static_cast<hipStream_t>(stream)),
+                    "INT8 attention kernel (score dump)");
+}
+
 int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, int blk_q, int blk_k, int flags,
                   int8_t* q_codes, float* q_scales, int8_t* k_codes, float* k_scales, float* k_mean,
                   void* workspace, size_t workspace_bytes, void* stream) {

@@ -140,14 +140,19 @@ __device__ __forceinline__ void map_workgroup(int bid, int BH, int nqt, bool cau
 // the FP16 matrix op (the FlashAttention-style baseline of the same design).
 constexpr int kScoresInt8Block = 0, kScoresInt8Token = 1, kScoresF16 = 2;
 
-template <int D, bool CAUSAL, int SM, bool PV8>
+// DUMP: a test instance that also copies the integer scores of key tile dkt,
+// as the score matrix op produced them, for the 256 queries of query tile dqt
+// of head dbh into dump (int32 [256, 64], query-major).
+template <int D, bool CAUSAL, int SM, bool PV8, bool DUMP = false>
 __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     const void* __restrict__ qsrc, const void* __restrict__ ksrc, const void* __restrict__ vt,
     const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vsc,
-    _Float16* __restrict__ out, int N, int Npad, int qblk, float sl2, int BH) {
+    _Float16* __restrict__ out, int N, int Npad, int qblk, float sl2, int BH, int* __restrict__ dump = nullptr,
+    int dbh = 0, int dqt = 0, int dkt = 0) {
   constexpr bool PERTOK = SM == kScoresInt8Token;
   constexpr bool F16 = SM == kScoresF16;
   static_assert(!(PV8 && F16), "INT8 P.V goes with INT8 scores");
+  static_assert(!(DUMP && F16), "the score dump is for the integer scores");
   constexpr float SLACK = PV8 ? 0.f : kRefSlack;
   constexpr float PLOG = PV8 ? kLog2_127 : 0.f;  // P (fp16 form) or 127 P (INT8 form)
   constexpr int EB = F16 ? 2 : 1;        // bytes per Q / K element
@@ -634,11 +639,21 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   // last tile) and jp_ (V) are staged meanwhile into the free buffers KBN_ and
   // VBC_. The first (jp_ = 0) and last (jp_ = nkt) periods are peeled, so the
   // steady-state loop has no conditional work and no register copies.
+  // Score register (t, i) of lane group g holds key g*32 + t*16 + i of the tile
+  // (the permuted K rows), for query wrow0 + l32.
+#define SAGE_DUMP_S(J_)                                                                          \
+  do {                                                                                           \
+    if (DUMP && (J_) == dkt && bh == dbh && qt == dqt) {                                         \
+      _Pragma("unroll") for (int t = 0; t < 2; ++t)                                              \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i)                                           \
+          dump[(wave * 32 + l32) * kKTile + g * 32 + t * 16 + i] = s[t][i];                      \
+    }                                                                                            \
+  } while (0)
 #define SAGE_PHASE_MATRIX(HAS_PV_, HAS_K_, KB_, VBP_)                                                     \
   __builtin_amdgcn_s_setprio(1);                                                                 \
   if (HAS_PV_) { SAGE_PV(VBP_); }                                                                \
   __builtin_amdgcn_sched_barrier(0);                                                             \
-  if (HAS_K_) { SAGE_SCORES(KB_); }                                                              \
+  if (HAS_K_) { SAGE_SCORES(KB_); SAGE_DUMP_S(jp_); }                                            \
   __builtin_amdgcn_s_setprio(0);
 #define SAGE_PERIOD(J_, KB_, KBN_, VBC_, VBP_, FIRST_, LAST_)                                    \
   do {                                                                                           \
@@ -684,6 +699,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     SAGE_PERIOD(nkt, odd ? KB1 : KB0, odd ? KB0 : KB1, odd ? VB1 : VB0, odd ? VB0 : VB1, false, true);
   }
 #undef SAGE_PHASE_MATRIX
+#undef SAGE_DUMP_S
 #undef SAGE_PERIOD
 #undef SAGE_SOFTMAX
 #undef SAGE_SOFTMAX_ILP
@@ -752,6 +768,26 @@ hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, con
   }
 #undef SAGE_LAUNCH_SM
 #undef SAGE_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_int8_dump(const AttnArgs& a, const void* q, const void* k, const void* vt,
+                                 const float* qs, const float* ks, int* dump, int dbh, int dqt, int dkt,
+                                 hipStream_t s) {
+  const int nqt = a.Npad / kWGQ;
+  const dim3 grid(a.BH * nqt), block(512);
+  const bool tok = a.mode == 3;
+  const int qblk = tok ? 1 : (a.mode == 1 ? 64 : 128);
+  auto* o = static_cast<_Float16*>(a.out);
+#define SAGE_LAUNCH_DUMP(D_, S_)                                                                          \
+  attn_int8_kernel<D_, false, S_, false, true><<<grid, block, 0, s>>>(q, k, vt, qs, ks, nullptr, o, a.N, a.Npad, \
+                                                                       qblk, a.sl2, a.BH, dump, dbh, dqt, dkt)
+  if (a.d == 128) {
+    if (tok) SAGE_LAUNCH_DUMP(128, kScoresInt8Token); else SAGE_LAUNCH_DUMP(128, kScoresInt8Block);
+  } else {
+    if (tok) SAGE_LAUNCH_DUMP(64, kScoresInt8Token); else SAGE_LAUNCH_DUMP(64, kScoresInt8Block);
+  }
+#undef SAGE_LAUNCH_DUMP
   return hipGetLastError();
 }
 

@@ -206,6 +206,12 @@ struct AttnArgs {
 // scales vs [BH, d] (unused otherwise).
 hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, const void* vt,
                             const float* qs, const float* ks, const float* vs, hipStream_t s);
+// The INT8 attention kernel (non-causal, modes 0, 1, 3) with a copy of the
+// integer scores of key tile dkt for query tile dqt of head dbh into dump
+// (int32 [256, 64], query-major).
+hipError_t launch_attn_int8_dump(const AttnArgs& a, const void* q, const void* k, const void* vt,
+                                 const float* qs, const float* ks, int* dump, int dbh, int dqt, int dkt,
+                                 hipStream_t s);
 // v4 holds E2M1 V^T codes, or E4M3 ones for SAGE_MODE_MXFP4_FP8PV (a.mode 5,
 // where P is quantized to MX-FP8 as well).
 hipError_t launch_attn_mxfp4(const AttnArgs& a, const uint8_t* q4, const uint8_t* qe,

@@ -130,6 +130,22 @@ int sage_attn_compute(const void* q, const void* k, void* out, int B, int H, int
                       int causal, float sm_scale, int mode, const void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * Test hook for the integer scores of the INT8 modes (SageAttention page,
+ * "Approach": QK^T of the INT8 codes with integer accumulation). Runs the
+ * attention kernel of `mode` (0, 1 or 3; non-causal) on a workspace prepared by
+ * sage_attn_prepare for the same B, H, N, d and mode, writing `out` as
+ * sage_attn_compute does, and copies the int32 scores q_codes . k_codes^T that
+ * the kernel's INT8 matrix op produced for key tile `k_tile` (keys 64 k_tile ..
+ * +63) and query tile `q_tile` (queries 256 q_tile .. +255) of head `bh` into
+ * s_out, int32 [256, 64] device, query-major. Rows and keys at or past N hold
+ * the scores of the zero-padded codes (0).
+ *   bh in [0, B*H), q_tile in [0, ceil(N/256)), k_tile in [0, ceil(N/64)).
+ */
+int sage_attn_dump_scores(void* out, int B, int H, int N, int d, float sm_scale, int mode,
+                          const void* workspace, size_t workspace_bytes, int bh, int q_tile, int k_tile,
+                          int32_t* s_out, void* stream);
+
 /* Bytes of device workspace sage_quant_qk, sage_quant_mxfp4 and
  * sage_quant_v_int8 need. */
 size_t sage_quant_workspace_size(int B, int H, int N, int d);

@@ -105,6 +105,14 @@ def test_prepare_compute_and_quant_validation():
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 0, A16, A16, A16, A16, None, A16, 8, None) == WS
     assert lib.sage_quant_mxfp4(A16, A16, A16, 1, 2, 256, 64, 0, A16, A16, A16, A16, A16 + 4, A16, None, A16, qw,
                                 None) == INVALID
+    # the integer-score dump: INT8 modes 0, 1, 3 only, tile indices in range
+    assert lib.sage_attn_dump_scores(A16, 1, 2, 1000, 64, 0.1, 0, A16, ws0 * 4, 0, 0, 0, None, None) == INVALID
+    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 2, A16, 1 << 30, 0, 0, 0, A16, None) == UNSUP
+    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 4, A16, 1 << 30, 0, 0, 0, A16, None) == UNSUP
+    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 2, 0, 0, A16, None) == INVALID
+    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 0, 1, 0, A16, None) == INVALID
+    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 0, 0, 4, A16, None) == INVALID
+    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.0, 0, A16, ws0, 0, 0, 0, A16, None) == INVALID
     assert lib.sage_quant_v_int8(None, 1, 2, 256, 64, A16, A16, A16, qw, None) == INVALID
     assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16 + 8, A16, A16, qw, None) == INVALID
     assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16, A16 + 2, A16, qw, None) == INVALID
@@ -128,3 +136,5 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 0, A16, A16, A16, A16, None, A16, qw, None) == NODEV
     assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16, A16, A16, qw, None) == NODEV
     assert _fwd(mode=6) == NODEV and _fwd(mode=7) == NODEV
+    ws0 = sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
+    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 1, 0, 3, A16, None) == NODEV

@@ -200,6 +200,44 @@ def test_mxfp4_attention_matches_oracle(sa, case):
         f"oracle {O.metrics(ref, ex)['cos']:.6f}")
 
 
+SINT_CASES = [
+    # B, H, N, d, mode, [(bh, q_tile, k_tile), ...]
+    (1, 2, 1000, 128, 0, [(0, 0, 0), (1, 3, 15), (1, 1, 7)]),   # q tile 3 and k tile 15 hold the ragged tail
+    (2, 1, 333, 64, 1, [(1, 1, 5), (0, 0, 2)]),
+    (1, 2, 300, 128, 3, [(1, 1, 4), (0, 0, 0)]),
+]
+
+
+@pytest.mark.parametrize("case", SINT_CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"-m{c[4]}")
+def test_int8_scores_are_the_exact_integer_products(sa, case):
+    # The scores the kernel's INT8 matrix op produces, dumped from inside the attention
+    # kernel, equal q_codes . k_codes^T computed in int64 from the oracle's codes, bit for bit.
+    B, H, N, d, mode, tiles = case
+    say("int8 scores", case)
+    q, k, v = make_custom(B, H, N, d, seed=23 * N + d)
+    bq, bk = _int8_blocks(mode)
+    ref = O.quant_qk_int8(q, k, blk_q=bq, blk_k=bk)
+    qd, kd, vd = _dev(q, k, v)
+    ws = sa.make_workspace(B, H, N, d, mode)
+    sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode)
+    out = torch.empty_like(qd)
+    for (bh, qt, kt) in tiles:
+        got = sa.sage_attn_dump_scores(out, ws, bh=bh, q_tile=qt, k_tile=kt, mode=mode)
+        torch.cuda.synchronize()
+        b, h = divmod(bh, H)
+        qc = np.zeros((256, d), np.int64)
+        kc = np.zeros((64, d), np.int64)
+        rows = np.arange(256 * qt, min(256 * qt + 256, N))
+        keys = np.arange(64 * kt, min(64 * kt + 64, N))
+        qc[:rows.size] = ref["q_codes"][b, h, rows]
+        kc[:keys.size] = ref["k_codes"][b, h, keys]
+        want = qc @ kc.T
+        assert np.array_equal(got.cpu().numpy().astype(np.int64), want), (bh, qt, kt)
+    # the dump instance also computes the attention itself
+    ex = O.int8_attention(q, k, v, causal=False, sm_scale=1.0 / np.sqrt(d), blk_q=bq, blk_k=bk)
+    assert_output_parity(out.cpu().numpy(), ex, what=f"int8 scores {case}")
+
+
 VQ_CASES = [(1, 2, 256, 64, "normal"), (2, 3, 1000, 128, "normal"), (1, 2, 777, 64, "student_t"),
             (1, 1, 1, 128, "normal"), (1, 2, 70, 128, "zero_channel")]
 

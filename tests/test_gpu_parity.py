@@ -43,6 +43,8 @@ QUANT_CASES = [
     (1, 2, 65, 128, 16, 32, 0, "normal"),
     (1, 2, 300, 128, 1, 1, 0, "normal"),
     (1, 2, 300, 64, 128, 64, 0x100, "normal"),
+    (1, 2, 64, 128, 64, 64, 0, "normal"),
+    (1, 3, 127, 64, 128, 64, 0, "student_t"),
 ]
 
 
@@ -321,6 +323,18 @@ def test_prepare_compute_equals_fwd_and_is_deterministic(sa, mode):
     sa.sage_attn_compute(c, ws, causal=True, mode=mode, q=qd, k=kd)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
+    # another stream, and the phases launched with an unrelated call in between
+    st = torch.cuda.Stream()
+    other = _dev(*make_custom(1, 1, 300, 128, seed=12))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        ws2 = sa.make_workspace(1, 2, 700, 128, mode)
+        d2 = torch.empty_like(qd)
+        sa.sage_attn_prepare(qd, kd, vd, ws2, mode=mode)
+        sa.sage_attn_fwd(*other, causal=False, mode=mode)
+        sa.sage_attn_compute(d2, ws2, causal=True, mode=mode, q=qd, k=kd)
+    st.synchronize()
+    assert torch.equal(a, d2)
 
 
 def test_layer_selector_on_synthetic_layers(sa):

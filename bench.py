@@ -235,7 +235,10 @@ def main():
                 "traffic": load_traffic(f"{src[:-4]}_{w.name}", src) if (mode_name == w.mode and not flags) else None,
                 "kernel": kernel, "kernel_ms": round(ms_attn, 4)}
     if mode in (0, 1, 3):
-        roofline["mixed_int8_fp16_peak"] = round(2 / (1 / PEAK["int8"] + 1 / PEAK["fp16"]), 1)
+        # half the work (Q K^T) at the INT8 rate, half (P V) at the FP16 rate
+        mixed = 2 / (1 / PEAK["int8"] + 1 / PEAK["fp16"])
+        roofline["mixed_int8_fp16_peak"] = round(mixed, 1)
+        roofline["frac_of_mixed"] = round(tops_attn / mixed, 4)
     # context: PyTorch's own fused FP16 attention (scaled_dot_product_attention,
     # the flash backend of this ROCm build) on the same resident inputs
     sdpa = None

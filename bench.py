@@ -22,6 +22,11 @@ Also on the JSON line:
   cpu_baseline  the CPU oracle (oracle.int8_attention / mxfp4_attention in
                 float64) timed on a bounded sample of the same workload
                 (whole heads) on one host thread.
+  median_ms_per_step  median of per-step times (separate pass, an event
+                between steps).
+  shader_clock_mhz  the shader clock measured by a probe wave (cycle counter
+                against the device wall clock) on a second stream while steps
+                run, and on an idle GPU (throttling shows as under_load < idle).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 """
 import argparse
@@ -78,6 +83,30 @@ def timed(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def median_step_ms(fn, steps, torch):
+    """Median of per-step durations (an event between consecutive steps; separate pass)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return d[len(d) // 2] if len(d) % 2 else 0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(name: str, mode_name: str, budget_s: float = 12.0):
     """The oracle on whole heads of the workload until ~budget_s of CPU time (1 thread)."""
     from threadpoolctl import threadpool_limits
@@ -107,6 +136,7 @@ def cpu_baseline(name: str, mode_name: str, budget_s: float = 12.0):
             ops += 4.0 * w.N * w.N * w.d / (2 if w.causal else 1)
             heads += 1
     return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cores_available": len(os.sched_getaffinity(0)),
             "sample": f"{heads} whole head(s) of the {name} workload (N={w.N}, d={w.d}): "
                       f"quantization + tiled fp64 emulation, {t_total:.1f} s on 1 thread"}
 
@@ -202,6 +232,14 @@ def main():
     ms_attn, _ = timed(comp, args.steps, args.warmup, torch)
     log(f"[bench] {w.name}: step {ms_step:.4f} ms (wall {wall_step:.4f}), attention kernel {ms_attn:.4f} ms, "
         f"quantization phase {ms_prep:.4f} ms")
+    med_step = median_step_ms(step, args.steps, torch)
+    # shader clock: one probe wave on a second stream while steps run (the clock
+    # under this load), and alone on an otherwise idle GPU
+    probe_cycles = 12_000_000
+    reps = max(5, int(probe_cycles / 2.4e6 / ms_step) + 1)
+    clk_load = sa.measure_clock_mhz(probe_cycles, during=lambda: [step() for _ in range(reps)])
+    clk_idle = sa.measure_clock_mhz(probe_cycles)
+    log(f"[bench] median step {med_step:.4f} ms; shader clock {clk_load:.0f} MHz under load, {clk_idle:.0f} MHz idle")
 
     ops = w.attention_ops()
     tops_step = ops / (ms_step * 1e-3) / 1e12
@@ -266,6 +304,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "median_ms_per_step": round(med_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -280,6 +319,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "torch_sdpa_fp16": sdpa,
+        "shader_clock_mhz": {"under_load": round(clk_load), "idle": round(clk_idle)},
     }
     print(json.dumps(line), flush=True)
 

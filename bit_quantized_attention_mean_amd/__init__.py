@@ -12,6 +12,7 @@ Functions carry the C names:
   sage_quant_qk(q, k, blk_q, blk_k, flags)  -> dict of codes/scales/mean
   sage_quant_mxfp4(q, k, v, flags)         -> dict of packed codes/exponents
   sage_quant_v_int8(v)                     -> dict of V^T codes and channel scales
+  sage_clock_probe / measure_clock_mhz     (shader clock, for throughput reports)
 """
 from __future__ import annotations
 
@@ -25,6 +26,7 @@ __all__ = [
     "SAGE_FLAG_NO_SMOOTH", "SAGE_FLAG_FP8_V", "SageError", "LIB_PATH", "lib",
     "sage_attn_fwd", "sage_attn_prepare", "sage_attn_compute", "sage_attn_workspace_size",
     "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_quant_v_int8", "sage_attn_dump_scores", "sage_status_string", "sage_last_error",
+    "sage_clock_probe", "sage_wall_clock_khz", "measure_clock_mhz",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -54,6 +56,8 @@ _SIGS = {
     "sage_quant_mxfp4": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sage_quant_v_int8": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "sage_attn_dump_scores": (_i, [_vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _i, _i, _vp, _vp]),
+    "sage_clock_probe": (_i, [ctypes.c_longlong, _vp, _vp]),
+    "sage_wall_clock_khz": (_i, [ctypes.POINTER(_i)]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -274,3 +278,44 @@ def sage_attn_dump_scores(out, workspace, *, bh, q_tile, k_tile, sm_scale=None, 
                                    int(bh), int(q_tile), int(k_tile), _dev_ptr(s_out, "s_out"), _stream(stream))
     _check(rc, "sage_attn_dump_scores")
     return s_out
+
+
+
+def sage_wall_clock_khz() -> int:
+    khz = ctypes.c_int(0)
+    _check(lib.sage_wall_clock_khz(ctypes.byref(khz)), "sage_wall_clock_khz")
+    return int(khz.value)
+
+
+def sage_clock_probe(cycles: int, out, stream=None):
+    """Enqueues the clock probe; `out` is an int64 CUDA tensor of at least 2 elements."""
+    torch = _torch()
+    if out.numel() < 2:
+        raise ValueError("out needs 2 int64 elements")
+    _check(lib.sage_clock_probe(int(cycles), _dev_ptr(out, "out", torch.int64), _stream(stream)), "sage_clock_probe")
+    return out
+
+
+def measure_clock_mhz(cycles: int = 12_000_000, stream=None, during=None) -> float:
+    """Shader clock in MHz over `cycles` clocks of one probe wave.
+
+    With `during` (a callable that enqueues work on the current stream) the
+    probe runs on `stream` (a second stream) while that work runs, and the
+    result is the clock under that load; the call synchronizes the device.
+    """
+    torch = _torch()
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    if during is not None:
+        if stream is None:
+            stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        during()          # the load is enqueued first, so it occupies the GPU when the probe starts
+        sage_clock_probe(cycles, out, stream)
+        during()
+    else:
+        sage_clock_probe(cycles, out, stream)
+    torch.cuda.synchronize()
+    c, w = (int(x) for x in out.cpu())
+    if c <= 0 or w <= 0:
+        raise RuntimeError(f"clock probe returned {c} cycles over {w} ticks")
+    return c / w * sage_wall_clock_khz() / 1000.0

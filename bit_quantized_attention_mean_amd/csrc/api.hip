@@ -380,4 +380,22 @@ int sage_quant_v_int8(const void* v, int B, int H, int N, int d, int8_t* vt_code
                     "INT8 V quantization kernels");
 }
 
+int sage_clock_probe(long long cycles, long long* out, void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_ptr(out, "out", 8));
+  if (cycles < 1 || cycles > (1LL << 32)) return fail(SAGE_ERR_INVALID_ARG, "cycles = %lld is outside [1, 2^32]", cycles);
+  SAGE_TRY(check_device());
+  (void)hipGetLastError();
+  return hip_status(sage::launch_clock_probe(cycles, out, static_cast<hipStream_t>(stream)), "clock probe kernel");
+}
+
+int sage_wall_clock_khz(int* khz) {
+  g_err[0] = 0;
+  SAGE_TRY(check_ptr(khz, "khz", 4));
+  SAGE_TRY(check_device());
+  int dev = 0;
+  SAGE_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  return hip_status(hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev), "hipDeviceGetAttribute");
+}
+
 }  // extern "C"

@@ -218,4 +218,8 @@ hipError_t launch_attn_mxfp4(const AttnArgs& a, const uint8_t* q4, const uint8_t
                              const uint8_t* k4, const uint8_t* ke, const uint8_t* v4,
                              const uint8_t* ve, hipStream_t s);
 
+// One wave spins for `cycles` shader clocks and writes to out[0..1] the
+// cycles counted and the device wall-clock ticks over the same interval.
+hipError_t launch_clock_probe(long long cycles, long long* out, hipStream_t s);
+
 }  // namespace sage

@@ -210,6 +210,21 @@ int sage_quant_mxfp4(const void* q, const void* k, const void* v, int B, int H, 
 int sage_quant_v_int8(const void* v, int B, int H, int N, int d, int8_t* vt_codes, float* v_scales,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Shader-clock probe, for throughput reports (not part of the attention path).
+ * One wave spins until the device's shader-clock counter has advanced by
+ * `cycles` (1 <= cycles <= 2^32) and writes to `out` (device, int64 [2],
+ * 8-byte aligned) the cycles it counted and the ticks of the device's
+ * constant-rate wall clock over the same interval:
+ *   shader clock (kHz) = out[0] / out[1] * sage_wall_clock_khz().
+ * Enqueued on a second stream while a workload runs, it gives the clock under
+ * that load (lower than nominal when the chip throttles). It occupies one
+ * wave slot of one compute unit for its duration.
+ */
+int sage_clock_probe(long long cycles, long long* out, void* stream);
+/* The current device's wall-clock rate in kHz, written to *khz (host). */
+int sage_wall_clock_khz(int* khz);
+
 #ifdef __cplusplus
 }
 #endif

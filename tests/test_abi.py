@@ -120,6 +120,14 @@ def test_prepare_compute_and_quant_validation():
     assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16, A16, A16, 8, None) == WS
 
 
+def test_clock_probe_validation():
+    assert lib.sage_clock_probe(1000, None, None) == INVALID
+    assert lib.sage_clock_probe(1000, A16 + 4, None) == INVALID
+    assert lib.sage_clock_probe(0, A16, None) == INVALID
+    assert lib.sage_clock_probe((1 << 32) + 1, A16, None) == INVALID
+    assert lib.sage_wall_clock_khz(None) == INVALID
+
+
 def _gpu_visible():
     try:
         import torch
@@ -138,3 +146,4 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _fwd(mode=6) == NODEV and _fwd(mode=7) == NODEV
     ws0 = sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
     assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 1, 0, 3, A16, None) == NODEV
+    assert lib.sage_clock_probe(1000, A16, None) == NODEV

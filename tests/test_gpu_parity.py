@@ -337,6 +337,18 @@ def test_prepare_compute_equals_fwd_and_is_deterministic(sa, mode):
     assert torch.equal(a, d2)
 
 
+def test_clock_probe_reads_a_plausible_shader_clock(sa):
+    say("clock probe")
+    idle = sa.measure_clock_mhz(2_400_000)
+    qd, kd, vd = _dev(*make_custom(1, 32, 2048, 128, seed=5))
+    out = torch.empty_like(qd)
+    ws = sa.make_workspace(1, 32, 2048, 128, 0)
+    run = lambda: [sa.sage_attn_fwd(qd, kd, vd, out, mode=0, workspace=ws) for _ in range(20)]
+    loaded = sa.measure_clock_mhz(2_400_000, during=run)
+    say(f"  shader clock idle {idle:.0f} MHz, under load {loaded:.0f} MHz, wall clock {sa.sage_wall_clock_khz()} kHz")
+    assert 300 < idle < 3500 and 300 < loaded < 3500
+
+
 def test_layer_selector_on_synthetic_layers(sa):
     # Two synthetic "layers": Gaussian inputs, where every INT8 variant clears 99.8%, and
     # heavy-tailed ones (Student-t, nu = 3) where per-block scales fall short. The cosine the

@@ -64,12 +64,19 @@ __device__ __forceinline__ void map_workgroup4(int bid, int BH, int nqt, bool ca
   }
 }
 
-// 32x32x64 FP4 x FP4 block-scaled MFMA; the scale byte is byte 0 of sa / sb.
+// 32x32x64 FP4 x FP4 block-scaled MFMA; the scale exponents are byte SEL of sa
+// and of sb (the matrix op's op_sel picks the byte: checked on the GPU).
+template <int SEL>
 __device__ __forceinline__ v16f mfma_fp4(const v4i a, const v4i b, unsigned sa, unsigned sb, v16f c) {
   const v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
   const v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, static_cast<int>(sa), 0,
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, SEL, static_cast<int>(sa), SEL,
                                                           static_cast<int>(sb));
+}
+
+// Raw buffer resource over `bytes` bytes at p (gfx9 descriptor word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
 }
 
 }  // namespace
@@ -91,9 +98,9 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
   constexpr int VTB = PV8 ? 64 : 32;  // bytes of one V^T row per key tile (64 keys)
   constexpr int VROW = VTB + 16;      // LDS bytes per V^T row
   constexpr int KT_BYTES = kKTile * KROW;
-  constexpr int KS_BYTES = kKTile * 4;
+  constexpr int KS_BYTES = kKTile * 8;  // per K row: its exponent word, and the word >> 8
   constexpr int VT_BYTES = D * VROW;
-  constexpr int VS_BYTES = D * 4;
+  constexpr int VS_BYTES = D * 8;       // per V^T row: likewise
   constexpr int BUF = KT_BYTES + KS_BYTES + VT_BYTES + VS_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
 
@@ -121,6 +128,12 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
   const int vrb = PV8 ? Npad : Npad / 2;  // bytes per V^T row in HBM
   const uint8_t* vb4 = v4 + static_cast<size_t>(bh) * D * vrb;
   const uint8_t* vbe = ve + static_cast<size_t>(bh) * D * (Npad / 32);
+  // the tile loads are buffer loads: a per-lane offset fixed for the whole loop
+  // and the tile's offset in a scalar register
+  const auto rk4 = buffer_rsrc(kb4, static_cast<unsigned>(Npad) * (D / 2));
+  const auto rke = buffer_rsrc(kbe, static_cast<unsigned>(Npad) * NE);
+  const auto rv4 = buffer_rsrc(vb4, static_cast<unsigned>(D) * vrb);
+  const auto rve = buffer_rsrc(vbe, static_cast<unsigned>(D) * (Npad / 32));
 
   // staging registers, two sets (tiles are loaded two iterations ahead): one
   // 16-byte K chunk, one K exponent word, one 16-byte V^T chunk, one V^T exponent pair
@@ -130,6 +143,20 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
   constexpr int VPT4 = (VCHUNKS + 255) / 256;
   unsigned kr[2][4], vr[2][4 * VPT4];
   unsigned ksr[2] = {0, 0}, vsr[2] = {0, 0};
+  // per-lane byte offsets of this thread's chunks within a tile (every thread
+  // loads; threads beyond a tile's chunk count repeat an in-bounds chunk)
+  int k_off, ke_off, ve_off, v_off[VPT4];
+  {
+    const int i = tid % KCHUNKS;
+    k_off = (i / (D / 32)) * (D / 2) + (i % (D / 32)) * 16;
+    ke_off = (tid % kKTile) * NE;
+    ve_off = (tid % D) * (Npad / 32);
+#pragma unroll
+    for (int u = 0; u < VPT4; ++u) {
+      const int c = (tid + 256 * u) % VCHUNKS;
+      v_off[u] = (c / VCPR) * vrb + (c % VCPR) * 16;
+    }
+  }
 // Global loads of tile J_ (clamped to the last tile, so the loop issues them
   // unconditionally) into staging set S_. Every thread loads (threads beyond a
   // tile's chunk count repeat an in-bounds chunk and do not store it): the code
@@ -139,24 +166,17 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
   do {                                                                                               \
     const int jj_ = min((J_), nkt - 1);                                                              \
     {                                                                                                \
-      const int i_ = tid % KCHUNKS, row_ = i_ / (D / 32), col_ = i_ % (D / 32);                      \
-      const uint4 t_ = *reinterpret_cast<const uint4*>(kb4 + static_cast<size_t>(jj_ * kKTile + row_) * (D / 2) + \
-                                                       col_ * 16);                                   \
-      kr[S_][0] = t_.x; kr[S_][1] = t_.y; kr[S_][2] = t_.z; kr[S_][3] = t_.w;                        \
+      const auto t_ = __builtin_amdgcn_raw_buffer_load_b128(rk4, k_off, jj_ * (kKTile * D / 2), 0);  \
+      kr[S_][0] = t_[0]; kr[S_][1] = t_[1]; kr[S_][2] = t_[2]; kr[S_][3] = t_[3];                    \
     }                                                                                                \
-    {                                                                                                \
-      const size_t r_ = static_cast<size_t>(jj_ * kKTile + (tid % kKTile));                          \
-      ksr[S_] = (NE == 4) ? *reinterpret_cast<const unsigned*>(kbe + r_ * 4)                         \
-                      : static_cast<unsigned>(*reinterpret_cast<const uint16_t*>(kbe + r_ * 2));     \
-    }                                                                                                \
+    ksr[S_] = (NE == 4) ? __builtin_amdgcn_raw_buffer_load_b32(rke, ke_off, jj_ * (kKTile * NE), 0)   \
+                        : static_cast<unsigned>(__builtin_amdgcn_raw_buffer_load_b16(rke, ke_off,   \
+                                                                                  jj_ * (kKTile * NE), 0)); \
     _Pragma("unroll") for (int u_ = 0; u_ < VPT4; ++u_) {                                           \
-      const int i_ = (tid + 256 * u_) % VCHUNKS;                                                     \
-      const int row_ = i_ / VCPR, col_ = i_ % VCPR;                                                  \
-      const uint4 t_ = *reinterpret_cast<const uint4*>(vb4 + static_cast<size_t>(row_) * vrb +       \
-                                                       jj_ * VTB + col_ * 16);                       \
-      vr[S_][4 * u_] = t_.x; vr[S_][4 * u_ + 1] = t_.y; vr[S_][4 * u_ + 2] = t_.z; vr[S_][4 * u_ + 3] = t_.w; \
+      const auto t_ = __builtin_amdgcn_raw_buffer_load_b128(rv4, v_off[u_], jj_ * VTB, 0);           \
+      vr[S_][4 * u_] = t_[0]; vr[S_][4 * u_ + 1] = t_[1]; vr[S_][4 * u_ + 2] = t_[2]; vr[S_][4 * u_ + 3] = t_[3]; \
     }                                                                                                \
-    vsr[S_] = *reinterpret_cast<const uint16_t*>(vbe + static_cast<size_t>(tid % D) * (Npad / 32) + jj_ * 2); \
+    vsr[S_] = __builtin_amdgcn_raw_buffer_load_b16(rve, ve_off, jj_ * 2, 0);                          \
   } while (0)
 #define SAGE_SWRITE4(BUF_, S_)                                                                       \
   do {                                                                                               \
@@ -169,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
       *reinterpret_cast<uint4*>(kt_ + lds_row_of_key4(row_) * KROW + col_ * 16) =                    \
           make_uint4(kr[S_][0], kr[S_][1], kr[S_][2], kr[S_][3]);                                    \
     }                                                                                                \
-    if (tid < kKTile) *reinterpret_cast<unsigned*>(ks_ + lds_row_of_key4(tid) * 4) = ksr[S_];        \
+    if (tid < kKTile) *reinterpret_cast<uint2*>(ks_ + lds_row_of_key4(tid) * 8) = make_uint2(ksr[S_], ksr[S_] >> 8); \
     _Pragma("unroll") for (int u_ = 0; u_ < VPT4; ++u_) {                                           \
       const int i_ = tid + 256 * u_;                                                                 \
       if (i_ < VCHUNKS) {                                                                            \
@@ -178,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
             make_uint4(vr[S_][4 * u_], vr[S_][4 * u_ + 1], vr[S_][4 * u_ + 2], vr[S_][4 * u_ + 3]);  \
       }                                                                                              \
     }                                                                                                \
-    if (tid < D) *reinterpret_cast<unsigned*>(vs_ + tid * 4) = vsr[S_];                              \
+    if (tid < D) *reinterpret_cast<uint2*>(vs_ + tid * 8) = make_uint2(vsr[S_], vsr[S_] >> 8);      \
   } while (0)
 
   // o[NT] is the row sum: the quantized P times a block of ones, accumulated
@@ -207,11 +227,12 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                   \
       for (int i = 0; i < 16; ++i) s[t][i] = 0.f;                                                   \
       const int krow = t * 32 + l32;                                                                \
-      const unsigned ksw = *reinterpret_cast<const unsigned*>(ksl + krow * 4) >> (8 * g);           \
+      const unsigned ksw = *reinterpret_cast<const unsigned*>(ksl + krow * 8 + g * 4);              \
 _Pragma("unroll")                                                                                   \
       for (int c = 0; c < NC; ++c) {                                                                \
         const v4i a = *reinterpret_cast<const v4i*>(kt + krow * KROW + c * 32 + g * 16);            \
-        s[t] = mfma_fp4(a, qf[c], ksw >> (16 * c), qsw >> (16 * c), s[t]);                          \
+        /* block c*2+g of the K row and of the Q row: byte 2c of ksw and qsw */                     \
+        s[t] = (c == 0) ? mfma_fp4<0>(a, qf[c], ksw, qsw, s[t]) : mfma_fp4<2>(a, qf[c], ksw, qsw, s[t]); \
       }                                                                                             \
     }                                                                                               \
                                                                                                     \
@@ -304,7 +325,7 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                   \
     for (int dt = 0; dt < NT; ++dt) {                                                               \
       const int vrow = dt * 32 + l32;                                                               \
-      const unsigned vsw = *reinterpret_cast<const unsigned*>(vsl + vrow * 4) >> (8 * g);           \
+      const unsigned vsw = *reinterpret_cast<const unsigned*>(vsl + vrow * 8 + g * 4);              \
       if (PV8) {                                                                                    \
         /* keys g*16 .. +15 and 32 + g*16 .. +15 of the tile (see the P swap) */                    \
         const v4i a0 = *reinterpret_cast<const v4i*>(vl + vrow * VROW + g * 16);                    \
@@ -315,7 +336,7 @@ _Pragma("unroll")                                                               
                                                                 static_cast<int>(pe8));             \
       } else {                                                                                      \
         const v4i a = *reinterpret_cast<const v4i*>(vl + vrow * VROW + g * 16);                     \
-        o[dt] = mfma_fp4(a, v4i{pq[0], pq[1], pq[2], pq[3]}, vsw, pe8, o[dt]);                      \
+        o[dt] = mfma_fp4<0>(a, v4i{pq[0], pq[1], pq[2], pq[3]}, vsw, pe8, o[dt]);                   \
       }                                                                                             \
     }                                                                                               \
     /* row sum of the quantized P: ones (E4M3 0x38 or E2M1 0x2, scale 2^0) times P */              \
@@ -325,7 +346,7 @@ _Pragma("unroll")                                                               
       o[NT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pq, o[NT], 0, 0, 0, 127, 0,    \
                                                               static_cast<int>(pe8));               \
     } else {                                                                                        \
-      o[NT] = mfma_fp4(v4i{0x22222222, 0x22222222, 0x22222222, 0x22222222},                         \
+      o[NT] = mfma_fp4<0>(v4i{0x22222222, 0x22222222, 0x22222222, 0x22222222},                         \
                        v4i{pq[0], pq[1], pq[2], pq[3]}, 127u, pe8, o[NT]);                          \
     }                                                                                               \
   } while (0)

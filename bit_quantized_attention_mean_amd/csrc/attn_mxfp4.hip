@@ -74,11 +74,6 @@ __device__ __forceinline__ v16f mfma_fp4(const v4i a, const v4i b, unsigned sa, 
                                                           static_cast<int>(sb));
 }
 
-// Raw buffer resource over `bytes` bytes at p (gfx9 descriptor word 3).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
-}
-
 }  // namespace
 
 // PV8: P and V in MX-FP8 (E4M3) instead of MXFP4 (the accuracy variant; Q and

@@ -665,20 +665,20 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   __builtin_amdgcn_sched_barrier(0);                                                             \
   if (HAS_K_) { SAGE_SCORES(KB_); SAGE_DUMP_S(jp_); }                                            \
   __builtin_amdgcn_s_setprio(0);
-#define SAGE_PERIOD(J_, KB_, KBN_, VBC_, VBP_, FIRST_, LAST_)                                    \
+#define SAGE_PERIOD(J_, KB_, KBN_, VBC_, VBP_, FIRST_, LAST_, G_)                                \
   do {                                                                                           \
     const int jp_ = (J_);                                                                        \
     if (!(LAST_)) {                                                                              \
       SAGE_LOAD_K(min(jp_ + 1, nkt - 1))                                                         \
       SAGE_LOAD_V(jp_)                                                                           \
     }                                                                                            \
-    if (grp == 0) {                                                                              \
+    if ((G_) == 0) {                                                                             \
       SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), KB_, VBP_)                                          \
     } else if (!(FIRST_)) {                                                                      \
       SAGE_SOFTMAX(jp_ - 1);                                                                     \
     }                                                                                            \
     __syncthreads();                                                                             \
-    if (grp == 1) {                                                                              \
+    if ((G_) == 1) {                                                                             \
       SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), KB_, VBP_)                                          \
     } else if (!(LAST_)) {                                                                       \
       SAGE_SOFTMAX(jp_);                                                                         \
@@ -697,17 +697,27 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   // wait on the tile prefetch before each period's score MFMAs.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  SAGE_PERIOD(0, KB0, KB1, VB0, VB1, true, false);
-  int jt = 1;
-  for (; jt + 1 < nkt; jt += 2) {
-    SAGE_PERIOD(jt, KB1, KB0, VB1, VB0, false, false);
-    SAGE_PERIOD(jt + 1, KB0, KB1, VB0, VB1, false, false);
-  }
-  if (jt < nkt) SAGE_PERIOD(jt, KB1, KB0, VB1, VB0, false, false);
-  {
-    const int odd = nkt & 1;
-    SAGE_PERIOD(nkt, odd ? KB1 : KB0, odd ? KB0 : KB1, odd ? VB1 : VB0, odd ? VB0 : VB1, false, true);
-  }
+  // The period sequence, compiled once per group for non-causal launches (the
+  // group's phase order is then fixed in the code: no register copies where the
+  // two orders would otherwise merge; 3-9% faster). Causal launches keep one
+  // sequence with the order chosen at run time (the specialized form measured
+  // 1% slower there). Both groups pass the same barriers in the same order.
+#define SAGE_PERIODS(G_)                                                                         \
+  do {                                                                                           \
+    SAGE_PERIOD(0, KB0, KB1, VB0, VB1, true, false, G_);                                         \
+    int jt = 1;                                                                                  \
+    for (; jt + 1 < nkt; jt += 2) {                                                              \
+      SAGE_PERIOD(jt, KB1, KB0, VB1, VB0, false, false, G_);                                     \
+      SAGE_PERIOD(jt + 1, KB0, KB1, VB0, VB1, false, false, G_);                                 \
+    }                                                                                            \
+    if (jt < nkt) SAGE_PERIOD(jt, KB1, KB0, VB1, VB0, false, false, G_);                         \
+    const int odd = nkt & 1;                                                                     \
+    SAGE_PERIOD(nkt, odd ? KB1 : KB0, odd ? KB0 : KB1, odd ? VB1 : VB0, odd ? VB0 : VB1, false, true, G_); \
+  } while (0)
+  if (CAUSAL) SAGE_PERIODS(grp);
+  else if (grp == 0) SAGE_PERIODS(0);
+  else SAGE_PERIODS(1);
+#undef SAGE_PERIODS
 #undef SAGE_PHASE_MATRIX
 #undef SAGE_DUMP_S
 #undef SAGE_PERIOD

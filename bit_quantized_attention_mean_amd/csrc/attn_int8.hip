@@ -60,6 +60,7 @@ constexpr float kRefSlack = 8.0f;
 constexpr float kLog2_127 = 6.98868468677216585f;
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 constexpr v2h kOnes2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 
 // LDS row (0..63) holding key k of a 64-key tile. Row t*32 + r feeds row r of
@@ -622,7 +623,12 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
       l = l * alpha_ + rsum_;                                                                    \
     } else {                                                                                     \
       _Pragma("unroll") for (int c = 0; c < 4; ++c)                                              \
-        _Pragma("unroll") for (int e = 0; e < 8; ++e) pf[c][e] = static_cast<_Float16>(p[c * 8 + e]); \
+        _Pragma("unroll") for (int e = 0; e < 8; e += 2) {                                       \
+          /* a pair per v_cvt_pk_f16_f32 (round to nearest even) */                             \
+          const v2h h_ = __builtin_convertvector((v2f){p[c * 8 + e], p[c * 8 + e + 1]}, v2h);  \
+          pf[c][e] = h_[0];                                                                      \
+          pf[c][e + 1] = h_[1];                                                                  \
+        }                                                                                        \
       /* row sum of the fp16 P that multiplies V: two products per v_dot2_f32_f16 */            \
       float rs0_ = 0.f, rs1_ = 0.f;                                                              \
       _Pragma("unroll") for (int c = 0; c < 4; ++c)                                              \

@@ -25,8 +25,12 @@ Also on the JSON line:
   median_ms_per_step  median of per-step times (separate pass, an event
                 between steps).
   shader_clock_mhz  the shader clock measured by a probe wave (cycle counter
-                against the device wall clock) on a second stream while steps
-                run, and on an idle GPU (throttling shows as under_load < idle).
+                against the device wall clock) on a second stream during the
+                last warm-up steps, and on an idle GPU (throttling shows as
+                under_load < idle). The warm-up (default 50 steps) also covers
+                the clock transient that follows an idle GPU: the first ~25
+                launches of the attention kernel after idling run up to 35%
+                slower.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 """
 import argparse
@@ -81,6 +85,33 @@ def timed(fn, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     return e0.elapsed_time(e1) / steps, wall
+
+
+def warmup_with_clock_probe(fn, warmup, sa, torch):
+    """Runs `warmup` steps; a clock-probe wave on a second stream starts after
+    3/5 of them (past the clock transient that follows an idle GPU) and spans at
+    most ~60% of the rest. Returns the shader clock in MHz over that window."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    est_ms = e0.elapsed_time(e1)
+    k0 = max(1, (3 * warmup) // 5)
+    rest_ms = max(1, warmup - k0) * est_ms
+    cycles = int(min(12e6, max(2.4e5, rest_ms * 0.6 * 2.4e6)))
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    for i in range(max(warmup, 1)):
+        fn()
+        if i == k0 - 1:
+            ev.record()
+            side.wait_event(ev)
+            sa.sage_clock_probe(cycles, out, side)
+    torch.cuda.synchronize()
+    c, w = (int(x) for x in out.cpu())
+    return c / w * sa.sage_wall_clock_khz() / 1000.0
 
 
 def median_step_ms(fn, steps, torch):
@@ -164,7 +195,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sdpa", action="store_true", help="skip timing torch's FP16 SDPA for context")
@@ -224,7 +255,8 @@ def main():
     # whole step
     step = lambda: sa.sage_attn_fwd(qd, kd, vd, out, causal=w.causal, sm_scale=w.sm_scale, mode=mode | flags,
                                     workspace=ws)
-    ms_step, wall_step = timed(step, args.steps, args.warmup, torch)
+    clk_load = warmup_with_clock_probe(step, args.warmup, sa, torch)
+    ms_step, wall_step = timed(step, args.steps, 0, torch)
     # the two phases separately
     prep = lambda: sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode | flags)
     ms_prep, _ = timed(prep, args.steps, args.warmup, torch)
@@ -233,12 +265,8 @@ def main():
     log(f"[bench] {w.name}: step {ms_step:.4f} ms (wall {wall_step:.4f}), attention kernel {ms_attn:.4f} ms, "
         f"quantization phase {ms_prep:.4f} ms")
     med_step = median_step_ms(step, args.steps, torch)
-    # shader clock: one probe wave on a second stream while steps run (the clock
-    # under this load), and alone on an otherwise idle GPU
-    probe_cycles = 12_000_000
-    reps = max(5, int(probe_cycles / 2.4e6 / ms_step) + 1)
-    clk_load = sa.measure_clock_mhz(probe_cycles, during=lambda: [step() for _ in range(reps)])
-    clk_idle = sa.measure_clock_mhz(probe_cycles)
+    # shader clock of the idle GPU, for comparison with the one under load
+    clk_idle = sa.measure_clock_mhz(12_000_000)
     log(f"[bench] median step {med_step:.4f} ms; shader clock {clk_load:.0f} MHz under load, {clk_idle:.0f} MHz idle")
 
     ops = w.attention_ops()

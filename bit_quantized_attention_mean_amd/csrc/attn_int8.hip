@@ -415,7 +415,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     rsum_ = static_cast<float>(r0_ + r1_);                                                       \
   } while (0)
 
-#define SAGE_SOFTMAX_ILP(J_)                                                                         \
+#define SAGE_SOFTMAX_ILP(J_, KS_)                                                                    \
   do {                                                                                           \
     const int j_ = (J_);                                                                         \
     const bool masked_ = (CAUSAL && (j_ * kKTile + kKTile - 1 > wrow0)) || (j_ * kKTile + kKTile > N); \
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     } else {                                                                                     \
       /* one scale per (query block, key tile): the max of the integer scores, */               \
       /* scaled once, is the max of the dequantized scores (the scale is >= 0) */               \
-      const float sc_ = sq * ksh[j_] * sl2;                                                      \
+      const float sc_ = sq * (KS_) * sl2;                                                        \
       if (masked_) {                                                                             \
         _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
           const int key = kb_ + e;                                                               \
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     alpha = alpha_;                                                                              \
   } while (0)
 
-#define SAGE_SOFTMAX_SEQ(J_)                                                                         \
+#define SAGE_SOFTMAX_SEQ(J_, KS_)                                                                    \
   do {                                                                                           \
     const int j_ = (J_);                                                                         \
     const bool masked_ = (CAUSAL && (j_ * kKTile + kKTile - 1 > wrow0)) || (j_ * kKTile + kKTile > N); \
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     } else {                                                                                     \
       /* one scale per (query block, key tile): the max of the integer scores, */               \
       /* scaled once, is the max of the dequantized scores (the scale is >= 0) */               \
-      const float sc_ = sq * ksh[j_] * sl2;                                                      \
+      const float sc_ = sq * (KS_) * sl2;                                                        \
       if (masked_) {                                                                             \
         _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
           const int key = kb_ + e;                                                               \
@@ -642,9 +642,9 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     alpha = alpha_;                                                                              \
   } while (0)
 
-#define SAGE_SOFTMAX(J_)                                                                         \
+#define SAGE_SOFTMAX(J_, KS_)                                                                    \
   do {                                                                                           \
-    if (CAUSAL) { SAGE_SOFTMAX_ILP(J_); } else { SAGE_SOFTMAX_SEQ(J_); }                         \
+    if (CAUSAL) { SAGE_SOFTMAX_ILP(J_, KS_); } else { SAGE_SOFTMAX_SEQ(J_, KS_); }               \
   } while (0)
 
   // One period of the ping-pong. Key tile jp_ is in K buffer KB_, tile jp_-1
@@ -674,6 +674,9 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
 #define SAGE_PERIOD(J_, KB_, KBN_, VBC_, VBP_, FIRST_, LAST_, G_)                                \
   do {                                                                                           \
     const int jp_ = (J_);                                                                        \
+    /* per-block K scale of tile jp_, loaded a phase before group 0's softmax */                \
+    /* uses it; group 1's softmax of tile jp_ - 1 uses the one of the last period */           \
+    const float ksn_ = (SM == kScoresInt8Block) ? ksh[min(jp_, nkt - 1)] : 0.f;                 \
     if (!(LAST_)) {                                                                              \
       SAGE_LOAD_K(min(jp_ + 1, nkt - 1))                                                         \
       SAGE_LOAD_V(jp_)                                                                           \
@@ -681,19 +684,20 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     if ((G_) == 0) {                                                                             \
       SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), KB_, VBP_)                                          \
     } else if (!(FIRST_)) {                                                                      \
-      SAGE_SOFTMAX(jp_ - 1);                                                                     \
+      SAGE_SOFTMAX(jp_ - 1, ksp);                                                                \
     }                                                                                            \
     __syncthreads();                                                                             \
     if ((G_) == 1) {                                                                             \
       SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), KB_, VBP_)                                          \
     } else if (!(LAST_)) {                                                                       \
-      SAGE_SOFTMAX(jp_);                                                                         \
+      SAGE_SOFTMAX(jp_, ksn_);                                                                   \
     }                                                                                            \
     if (!(LAST_)) {                                                                              \
       SAGE_STORE_K(KBN_)                                                                         \
       SAGE_STORE_V(VBC_)                                                                         \
     }                                                                                            \
     __syncthreads();                                                                             \
+    ksp = ksn_;                                                                                  \
   } while (0)
 
   SAGE_LOAD_K(0)
@@ -720,6 +724,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     const int odd = nkt & 1;                                                                     \
     SAGE_PERIOD(nkt, odd ? KB1 : KB0, odd ? KB0 : KB1, odd ? VB1 : VB0, odd ? VB0 : VB1, false, true, G_); \
   } while (0)
+  float ksp = 0.f;
   if (CAUSAL) SAGE_PERIODS(grp);
   else if (grp == 0) SAGE_PERIODS(0);
   else SAGE_PERIODS(1);

@@ -372,11 +372,9 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   // Softmax of key tile J_ on the scores in s: dequantize to base-2 logits,
   // mask, move the reference max if needed (rescaling l now and O in the next
   // P.V), P = exp2(S - m), row sum, P -> fp16 in pf (keys g*32 + c*8 .. +7 in
-  // pf[c]). Two forms of the same arithmetic: SAGE_SOFTMAX_ILP works in place
-  // on the 32 score registers (fp32 bits replace the integers) with a tree row
-  // max, which measured faster where many tiles need masking (causal);
-  // SAGE_SOFTMAX_SEQ, a plain per-score sequence, measured faster on unmasked
-  // tiles, so non-causal launches use it.
+  // pf[c]), as a plain per-score sequence (an in-place form with tree row
+  // maxima measured slower once each wave group's period sequence is compiled
+  // on its own).
   // INT8 form: the exponent offset nm_ = log2(127) - m is lowered by whole
   // ulps until the tile's largest exponent Y_ (the same expression the
   // values use) is at most log2(127), so every weight round(127 P) stays <= 127
@@ -413,114 +411,6 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
       r1_ = __builtin_amdgcn_sdot4(pq[u_][3], 0x01010101, r1_, false);                           \
     }                                                                                            \
     rsum_ = static_cast<float>(r0_ + r1_);                                                       \
-  } while (0)
-
-#define SAGE_SOFTMAX_ILP(J_, KS_)                                                                    \
-  do {                                                                                           \
-    const int j_ = (J_);                                                                         \
-    const bool masked_ = (CAUSAL && (j_ * kKTile + kKTile - 1 > wrow0)) || (j_ * kKTile + kKTile > N); \
-    const int kb_ = j_ * kKTile + g * 32;                                                        \
-    float mt_, mnew_;                                                                            \
-    bool need_;                                                                                  \
-    if (PERTOK) {                                                                                \
-      /* per-token dequantization to fp32 logits, in place */                                    \
-      const float scq_ = sq * sl2;                                                               \
-      const float4* k4_ = reinterpret_cast<const float4*>(ksh + kb_);                            \
-      _Pragma("unroll") for (int u = 0; u < 8; ++u) {                                            \
-        const float4 kk_ = k4_[u];                                                               \
-        const float kv_[4] = {kk_.x, kk_.y, kk_.z, kk_.w};                                       \
-        _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                          \
-          const int e = 4 * u + r;                                                               \
-          s[e >> 4][e & 15] = __float_as_int(static_cast<float>(s[e >> 4][e & 15]) * scq_ * kv_[r]); \
-        }                                                                                        \
-      }                                                                                          \
-      if (masked_) {                                                                             \
-        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
-          const int key = kb_ + e;                                                               \
-          if ((CAUSAL && key > qrow) || key >= N) s[e >> 4][e & 15] = __float_as_int(-INFINITY); \
-        }                                                                                        \
-      }                                                                                          \
-      mt_ = pair_max(max32_f(s[0], s[1]));                                                       \
-      need_ = mt_ > m + SLACK;                                                               \
-      mnew_ = need_ ? mt_ : m;                                                                   \
-      /* exp2(-inf - finite) = 0 for masked keys */                                              \
-      float nm_ = PLOG - mnew_;                                                                  \
-      SAGE_CAP_P8(mt_ + nm_);                                                                    \
-      _Pragma("unroll") for (int e = 0; e < 32; ++e)                                             \
-        s[e >> 4][e & 15] = __float_as_int(__builtin_amdgcn_exp2f(__int_as_float(s[e >> 4][e & 15]) + nm_)); \
-    } else if (F16) {                                                                            \
-      /* fp32 scores (bits in s): the max is taken before the sm_scale * log2(e) */             \
-      /* factor, which is > 0, and the factor is applied in the fma */                          \
-      const float sc_ = sl2;                                                                     \
-      if (masked_) {                                                                             \
-        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
-          const int key = kb_ + e;                                                               \
-          if ((CAUSAL && key > qrow) || key >= N) s[e >> 4][e & 15] = __float_as_int(-INFINITY); \
-        }                                                                                        \
-      }                                                                                          \
-      const float mx_ = pair_max(max32_f(s[0], s[1]));                                           \
-      mt_ = (mx_ == -INFINITY) ? -INFINITY : mx_ * sc_;                                          \
-      need_ = mt_ > m + SLACK;                                                               \
-      mnew_ = need_ ? mt_ : m;                                                                   \
-      float nm_ = PLOG - mnew_;                                                                  \
-      SAGE_CAP_P8(__builtin_fmaf(mx_, sc_, nm_));                                                \
-      if (masked_) {                                                                             \
-        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
-          const float x_ = __int_as_float(s[e >> 4][e & 15]);                                    \
-          s[e >> 4][e & 15] = __float_as_int(                                                    \
-              (x_ == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x_, sc_, nm_)));   \
-        }                                                                                        \
-      } else {                                                                                   \
-        _Pragma("unroll") for (int e = 0; e < 32; ++e)                                           \
-          s[e >> 4][e & 15] = __float_as_int(                                                    \
-              __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[e >> 4][e & 15]), sc_, nm_))); \
-      }                                                                                          \
-    } else {                                                                                     \
-      /* one scale per (query block, key tile): the max of the integer scores, */               \
-      /* scaled once, is the max of the dequantized scores (the scale is >= 0) */               \
-      const float sc_ = sq * (KS_) * sl2;                                                        \
-      if (masked_) {                                                                             \
-        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
-          const int key = kb_ + e;                                                               \
-          if ((CAUSAL && key > qrow) || key >= N) s[e >> 4][e & 15] = INT_MIN;                   \
-        }                                                                                        \
-      }                                                                                          \
-      const int mi_ = pair_max_i(max32_i(s[0], s[1]));                                           \
-      mt_ = (mi_ == INT_MIN) ? -INFINITY : static_cast<float>(mi_) * sc_;                        \
-      need_ = mt_ > m + SLACK;                                                               \
-      mnew_ = need_ ? mt_ : m;                                                                   \
-      float nm_ = PLOG - mnew_;                                                                  \
-      SAGE_CAP_P8(__builtin_fmaf(static_cast<float>(mi_), sc_, nm_));                            \
-      if (masked_) {                                                                             \
-        _Pragma("unroll") for (int e = 0; e < 32; ++e) {                                         \
-          const int si_ = s[e >> 4][e & 15];                                                     \
-          const float x_ = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(si_), sc_, nm_)); \
-          s[e >> 4][e & 15] = __float_as_int(si_ == INT_MIN ? 0.f : x_);                         \
-        }                                                                                        \
-      } else {                                                                                   \
-        _Pragma("unroll") for (int e = 0; e < 32; ++e)                                           \
-          s[e >> 4][e & 15] = __float_as_int(                                                    \
-              __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[e >> 4][e & 15]), sc_, nm_))); \
-      }                                                                                          \
-    }                                                                                            \
-    const float alpha_ = need_ ? __builtin_amdgcn_exp2f(m - mnew_) : 1.f;                       \
-    if (PV8) {                                                                                   \
-      SAGE_PACK_P8(__int_as_float(s[(E_) >> 4][(E_) & 15]));                                     \
-      l = l * alpha_ + rsum_;                                                                    \
-    } else {                                                                                     \
-      _Pragma("unroll") for (int c = 0; c < 4; ++c)                                              \
-        _Pragma("unroll") for (int e = 0; e < 8; ++e)                                            \
-          pf[c][e] = static_cast<_Float16>(__int_as_float(s[(c * 8 + e) >> 4][(c * 8 + e) & 15])); \
-      /* row sum of the fp16 P that multiplies V: two products per v_dot2_f32_f16, */           \
-      /* four independent partial sums */                                                        \
-      float rs_[4] = {0.f, 0.f, 0.f, 0.f};                                                       \
-      _Pragma("unroll") for (int c = 0; c < 4; ++c)                                              \
-        _Pragma("unroll") for (int e = 0; e < 8; e += 2)                                         \
-          rs_[e >> 1] = __builtin_amdgcn_fdot2(v2h{pf[c][e], pf[c][e + 1]}, kOnes2, rs_[e >> 1], false); \
-      l = l * alpha_ + ((rs_[0] + rs_[1]) + (rs_[2] + rs_[3]));                                  \
-    }                                                                                            \
-    m = mnew_;                                                                                   \
-    alpha = alpha_;                                                                              \
   } while (0)
 
 #define SAGE_SOFTMAX_SEQ(J_, KS_)                                                                    \
@@ -644,7 +534,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
 
 #define SAGE_SOFTMAX(J_, KS_)                                                                    \
   do {                                                                                           \
-    if (CAUSAL) { SAGE_SOFTMAX_ILP(J_, KS_); } else { SAGE_SOFTMAX_SEQ(J_, KS_); }               \
+    SAGE_SOFTMAX_SEQ(J_, KS_);                                                                   \
   } while (0)
 
   // One period of the ping-pong. Key tile jp_ is in K buffer KB_, tile jp_-1
@@ -707,11 +597,10 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   // wait on the tile prefetch before each period's score MFMAs.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // The period sequence, compiled once per group for non-causal launches (the
-  // group's phase order is then fixed in the code: no register copies where the
-  // two orders would otherwise merge; 3-9% faster). Causal launches keep one
-  // sequence with the order chosen at run time (the specialized form measured
-  // 1% slower there). Both groups pass the same barriers in the same order.
+  // The period sequence, compiled once per wave group (the group's phase order
+  // is then fixed in the code: no register copies where the two orders would
+  // otherwise merge; 3-16% faster). Both groups pass the same barriers in the
+  // same order.
 #define SAGE_PERIODS(G_)                                                                         \
   do {                                                                                           \
     SAGE_PERIOD(0, KB0, KB1, VB0, VB1, true, false, G_);                                         \
@@ -725,15 +614,13 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     SAGE_PERIOD(nkt, odd ? KB1 : KB0, odd ? KB0 : KB1, odd ? VB1 : VB0, odd ? VB0 : VB1, false, true, G_); \
   } while (0)
   float ksp = 0.f;
-  if (CAUSAL) SAGE_PERIODS(grp);
-  else if (grp == 0) SAGE_PERIODS(0);
+  if (grp == 0) SAGE_PERIODS(0);
   else SAGE_PERIODS(1);
 #undef SAGE_PERIODS
 #undef SAGE_PHASE_MATRIX
 #undef SAGE_DUMP_S
 #undef SAGE_PERIOD
 #undef SAGE_SOFTMAX
-#undef SAGE_SOFTMAX_ILP
 #undef SAGE_SOFTMAX_SEQ
 #undef SAGE_PACK_P8
 #undef SAGE_CAP_P8

@@ -38,9 +38,13 @@ __device__ __forceinline__ float below_ulp4(float x) {
   return __uint_as_float(__float_as_uint(x) + (x > 0.f ? 0xffffffffu : 1u));
 }
 
+// Maxima of scores use the NaN-propagating maximum: the same result as fmaxf
+// on finite and infinite values, without the quieting of possible signaling
+// NaNs that fmaxf costs on matrix-op results.
+__device__ __forceinline__ float max4(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float pair_max4(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max4(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum4(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -251,7 +255,7 @@ _Pragma("unroll")                                                               
                                                                                                     \
     float lmx = p[0];                                                                               \
 _Pragma("unroll")                                                                                   \
-    for (int e = 1; e < 32; ++e) lmx = fmaxf(lmx, p[e]);                                            \
+    for (int e = 1; e < 32; ++e) lmx = max4(lmx, p[e]);                                             \
     const float mxr = pair_max4(lmx);                                                               \
     float mx = mxr * sl2;                                                                           \
     /* round the new reference down when the product rounded up: the row's */                      \

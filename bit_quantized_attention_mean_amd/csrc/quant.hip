@@ -114,6 +114,21 @@ __device__ __forceinline__ void unpack8(const uint4 raw, float* x) {
   }
 }
 
+// fp32(v) - mu for the 8 fp16 values in raw, one mixed-precision fma each:
+// v is widened inside the fma and multiplied by `one` (an fp16 1.0 the
+// compiler cannot see as a constant, so it keeps the fma form), which is exact,
+// so the result is the single rounding of fp32(v) - mu.
+__device__ __forceinline__ void unpack8_sub(const uint4 raw, const float* mu, _Float16 one, float* x) {
+  const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j] & 0xffffu));
+    const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j] >> 16));
+    x[2 * j] = __builtin_fmaf(static_cast<float>(lo), static_cast<float>(one), -mu[2 * j]);
+    x[2 * j + 1] = __builtin_fmaf(static_cast<float>(hi), static_cast<float>(one), -mu[2 * j + 1]);
+  }
+}
+
 // Codes. fp32(x / s) is formed without a division per element: with
 // y = fp32(1 / s) (one IEEE division per scale) and q0 = fp32(x * y), the
 // remainder x - q0 * s is exact in one fma and q0 + r * y rounded once is the
@@ -180,11 +195,17 @@ __device__ __forceinline__ void int8_quant_block(const Int8Job& J, int N, int bi
     raw[p] = row < N ? *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * D) : make_uint4(0, 0, 0, 0);
   }
   // x = fp32(v) - mu (one RNE subtraction; mu = 0 if off), zero for rows >= N
+  // (only the last tile of a head can hold such rows)
+  _Float16 one = 1;
+  asm volatile("" : "+v"(one));
+  const bool full = row0 + TR <= N;
   auto values = [&](int p, float* x) {
-    unpack8(raw[p], x);
-    const bool live = row0 + p * RPP + rl < N;
+    unpack8_sub(raw[p], mu, one, x);
+    if (!full) {
+      const bool live = row0 + p * RPP + rl < N;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = live ? x[e] - mu[e] : 0.f;
+      for (int e = 0; e < 8; ++e) x[e] = live ? x[e] : 0.f;
+    }
   };
 #pragma unroll
   for (int p = 0; p < NP; ++p) {

@@ -610,12 +610,15 @@ __device__ __forceinline__ void mx_rows_block(const MxRowJob& J, int BH, int N, 
   if (row < N) {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(J.src) +
                                                     (static_cast<size_t>(bh) * N + row) * D + db * 32);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) unpack8(p[u], x + 8 * u);
     if (J.mu) {
       const float* m = J.mu + static_cast<size_t>(bh) * D + db * 32;
+      _Float16 one = 1;
+      asm volatile("" : "+v"(one));
 #pragma unroll
-      for (int i = 0; i < 32; ++i) x[i] = x[i] - m[i];
+      for (int u = 0; u < 4; ++u) unpack8_sub(p[u], m + 8 * u, one, x + 8 * u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) unpack8(p[u], x + 8 * u);
     }
   } else {
 #pragma unroll

@@ -102,6 +102,9 @@ ATTN_CASES = [
     (1, 1, 1, 64, True, 0, "normal"),
     (1, 2, 300, 128, False, 3, "normal"),      # per-token scales
     (1, 2, 300, 64, True, 3, "normal"),
+    # odd tile counts (11 and 13 key tiles): the period loop's single-tile tail
+    (1, 2, 700, 128, False, 0, "normal"),
+    (1, 2, 777, 128, True, 0, "normal"),
 ]
 
 
@@ -134,6 +137,7 @@ F16_CASES = [
     (1, 2, 1000, 128, True, "normal"),
     (2, 1, 777, 64, True, "student_t"),
     (1, 1, 1, 128, False, "normal"),
+    (1, 1, 777, 128, True, "normal"),
 ]
 
 
@@ -157,6 +161,7 @@ MXATTN_CASES = [
     (1, 2, 1000, 128, False),
     (1, 2, 1000, 128, True),
     (1, 2, 333, 64, True),
+    (1, 2, 700, 128, False),
 ]
 
 
@@ -272,6 +277,7 @@ PV8_CASES = [
     (1, 2, 300, 128, False, 7, "normal"),
     (1, 1, 1, 128, False, 6, "normal"),
     (1, 1, 1, 64, True, 7, "normal"),
+    (1, 2, 777, 128, True, 6, "normal"),
 ]
 
 

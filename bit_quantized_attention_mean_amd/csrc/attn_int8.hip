@@ -141,11 +141,24 @@ __device__ __forceinline__ void map_workgroup(int bid, int BH, int nqt, bool cau
 // the FP16 matrix op (the FlashAttention-style baseline of the same design).
 constexpr int kScoresInt8Block = 0, kScoresInt8Token = 1, kScoresF16 = 2;
 
+// Schedule of a kernel instance. The two-group ping-pong (8 waves, 256 query
+// rows per workgroup) overlaps one group's matrix ops with the other's
+// softmax. Where the VALU work dwarfs the matrix work (d = 64 with per-token
+// scores or INT8 P.V) the matrix pipe would idle in it, so those instances run
+// 4 waves (128 rows) that do their matrix ops and softmax in turn, three
+// workgroups per CU, the waves of different workgroups filling each other's
+// gaps (measured +19% per token, +24% INT8 P.V; the plain INT8 modes at d = 64
+// measured 0.8% slower that way and keep the ping-pong).
+constexpr bool attn_pingpong(int D, int SM, bool PV8, bool DUMP) {
+  return D == 128 || DUMP || SM == kScoresF16 || (SM == kScoresInt8Block && !PV8);
+}
+
 // DUMP: a test instance that also copies the integer scores of key tile dkt,
 // as the score matrix op produced them, for the 256 queries of query tile dqt
 // of head dbh into dump (int32 [256, 64], query-major).
 template <int D, bool CAUSAL, int SM, bool PV8, bool DUMP = false>
-__global__ __launch_bounds__(512, 1) void attn_int8_kernel(
+__global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
+                             attn_pingpong(D, SM, PV8, DUMP) ? 1 : 3) void attn_int8_kernel(
     const void* __restrict__ qsrc, const void* __restrict__ ksrc, const void* __restrict__ vt,
     const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vsc,
     _Float16* __restrict__ out, int N, int Npad, int qblk, float sl2, int BH, int* __restrict__ dump = nullptr,
@@ -167,19 +180,22 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   constexpr int KB0 = 0, KB1 = KT_BYTES, VB0 = 2 * KT_BYTES, VB1 = 2 * KT_BYTES + VT_BYTES;
   constexpr int KCHN = kKTile * D * EB / 16;  // 16-byte chunks of a K tile
   constexpr int RPV = PV8 ? 2 : 4;       // 16-byte V^T reads (= matrix ops) per 32-channel tile
-  constexpr int KPT = (KCHN + 511) / 512;
+  constexpr bool PP = attn_pingpong(D, SM, PV8, DUMP);
+  constexpr int NTH = PP ? 512 : 256;          // threads per workgroup
+  constexpr int WGQ = PP ? kWGQ : kWGQ / 2;    // query rows per workgroup
+  constexpr int KPT = (KCHN + NTH - 1) / NTH;
   constexpr int VCPR = kKTile * VEB / 16;  // 16-byte chunks per V^T row
   constexpr int VCHN = D * VCPR;           // 16-byte chunks of a V^T tile
-  constexpr int VPT = (VCHN + 511) / 512;
+  constexpr int VPT = (VCHN + NTH - 1) / NTH;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KT_BYTES + 2 * VT_BYTES];
 
-  const int nqt = Npad / kWGQ;
+  const int nqt = Npad / WGQ;
   int bh, qt;
   map_workgroup(blockIdx.x, BH, nqt, CAUSAL, bh, qt);
-  const int q0 = qt * kWGQ;
+  const int q0 = qt * WGQ;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;                     // 0 or 1: which half of the ping-pong
+  const int grp = PP ? wave >> 2 : 0;            // 0 or 1: which half of the ping-pong
   const int wrow0 = q0 + grp * 128 + (wave & 3) * 32;   // first query row of this wave
   const int qrow = wrow0 + l32;
 
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   }
 
   int nkt = (N + kKTile - 1) / kKTile;
-  if (CAUSAL) nkt = min(nkt, (q0 + kWGQ) / kKTile);
+  if (CAUSAL) nkt = min(nkt, (q0 + WGQ) / kKTile);
 
   // K: INT8 codes zero-padded to Npad rows, or fp16 K as given ([N, d] per head).
   const unsigned char* kbase = static_cast<const unsigned char*>(ksrc) +
@@ -229,11 +245,11 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   // Loading: every thread moves at most KPT 16-byte K chunks and VPT V^T chunks
   // per tile, global -> registers at the start of a period, registers -> LDS
   // at its end. K rows go to their permuted LDS rows.
-  const bool kload_last = (tid + 512 * (KPT - 1)) < KCHN;
+  const bool kload_last = (tid + NTH * (KPT - 1)) < KCHN;
   int kg[KPT], kl[KPT], krw[KPT];
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    const int i = tid + 512 * u, row = i / (D * EB / 16), col = i % (D * EB / 16);
+    const int i = tid + NTH * u, row = i / (D * EB / 16), col = i % (D * EB / 16);
     kg[u] = row * D * EB + col * 16;
     kl[u] = lds_row_of_key(row) * KROW + col * 16;
     krw[u] = row;
@@ -241,11 +257,11 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
   int vg[VPT], vls[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
-    const int i = tid + 512 * u, row = i / VCPR, col = i % VCPR;
+    const int i = tid + NTH * u, row = i / VCPR, col = i % VCPR;
     vg[u] = row * Npad * VEB + col * 16;
     vls[u] = row * VROW + col * 16;
   }
-  const bool vload_last = (tid + 512 * (VPT - 1)) < VCHN;
+  const bool vload_last = (tid + NTH * (VPT - 1)) < VCHN;
   unsigned kr[4 * KPT], vr[4 * VPT];
   const int ka = l32 * KROW + g * 16;   // score A operand: K row l32 of each 32-key half
   const int va = l32 * VROW + g * 32 * VEB;   // P.V A operand: V^T row l32 of each 32-channel tile
@@ -576,7 +592,7 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
     } else if (!(FIRST_)) {                                                                      \
       SAGE_SOFTMAX(jp_ - 1, ksp);                                                                \
     }                                                                                            \
-    __syncthreads();                                                                             \
+    if (PP) __syncthreads();  /* the ping-pong's phase switch */                                 \
     if ((G_) == 1) {                                                                             \
       SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), KB_, VBP_)                                          \
     } else if (!(LAST_)) {                                                                       \
@@ -658,16 +674,19 @@ __global__ __launch_bounds__(512, 1) void attn_int8_kernel(
 
 hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, const void* vt,
                             const float* qs, const float* ks, const float* vs, hipStream_t s) {
-  const int nqt = a.Npad / kWGQ;
-  const dim3 grid(a.BH * nqt), block(512);
   // modes: 0 Q128/K64, 1 Q64/K64, 3 per token, 4 FP16, 6 Q128/K64 + INT8 P.V, 7 per token + INT8 P.V
   const bool tok = a.mode == 3 || a.mode == 7;
   const int qblk = tok ? 1 : (a.mode == 1 ? 64 : 128);
   const int sm = tok ? kScoresInt8Token : (a.mode == 4 ? kScoresF16 : kScoresInt8Block);
   const bool pv8 = mode_pv_int8(a.mode);
   auto* o = static_cast<_Float16*>(a.out);
-#define SAGE_LAUNCH(D_, C_, S_, P_) \
-  attn_int8_kernel<D_, C_, S_, P_><<<grid, block, 0, s>>>(q, k, vt, qs, ks, vs, o, a.N, a.Npad, qblk, a.sl2, a.BH)
+#define SAGE_LAUNCH(D_, C_, S_, P_)                                                                  \
+  do {                                                                                               \
+    constexpr bool pp_ = attn_pingpong(D_, S_, P_, false);                                           \
+    const dim3 grid_(a.BH * (a.Npad / (pp_ ? kWGQ : kWGQ / 2))), block_(pp_ ? 512 : 256);            \
+    attn_int8_kernel<D_, C_, S_, P_><<<grid_, block_, 0, s>>>(q, k, vt, qs, ks, vs, o, a.N, a.Npad,  \
+                                                              qblk, a.sl2, a.BH);                    \
+  } while (0)
 #define SAGE_LAUNCH_SM(D_, C_)                                                    \
   do {                                                                            \
     if (sm == kScoresF16) SAGE_LAUNCH(D_, C_, kScoresF16, false);                 \

@@ -207,7 +207,7 @@ REF_SLACK = 8.0   # log2 units by which the tile max may exceed the reference ma
 
 
 def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, ref_slack: float = REF_SLACK,
-                      sum_rounded: bool = False, p_alternatives=None):
+                      sum_rounded: bool = False, p_alternatives=None, rescale_quantum=None):
     """FlashAttention-2 style online softmax and P.V over key tiles ([SA-Setup]).
 
     S: float64 scores [R, N] (already scaled, -inf where masked).
@@ -224,14 +224,23 @@ def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, re
     returns (O, allowance), allowance [R, d] bounding |O' - O| to first order
     for any mix of those alternatives: a weight that moves by dP changes O by
     dP * (v_j - O) / l, and |v_j - O| <= |v_j| + max|v| per channel.
+
+    rescale_quantum (test tolerance only): per channel, the step [d] to which an
+    implementation rounds the accumulated sum l * O every time the reference
+    max moves (an integer accumulator rescaled through fp32 and rounded back).
+    Each such move after the first tile can then shift l * O by half a step
+    plus the fp32 rounding of the rescale, which is added to the allowance
+    (returned as with p_alternatives).
     """
     R, N = S.shape
     d = V.shape[1]
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     O = np.zeros((R, d))
-    A = np.zeros((R, d)) if p_alternatives is not None else None
+    want = p_alternatives is not None or rescale_quantum is not None
+    A = np.zeros((R, d)) if want else None
     dl = np.zeros(R)
+    moves = np.zeros(R)
     vbound = np.abs(V) + np.abs(V).max(axis=0, keepdims=True)
     slack = ref_slack * math.log(2.0)
     for t0 in range(0, N, kv_tile):
@@ -243,9 +252,10 @@ def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, re
             alpha = np.where(np.isneginf(m_new), 0.0, np.exp(m - m_new))
             P = np.where(np.isneginf(St), 0.0, np.exp(St - m_new[:, None]))
         Pr = round_p(P)
+        moves += (m_new > m) & np.isfinite(m)
         l = l * alpha + (Pr if sum_rounded else P).sum(axis=1)
         O = O * alpha[:, None] + Pr @ V[t0:t0 + kv_tile]
-        if A is not None:
+        if p_alternatives is not None:
             dP = np.zeros_like(Pr)
             for alt in p_alternatives(P):
                 dP = np.maximum(dP, np.abs(alt - Pr))
@@ -253,7 +263,12 @@ def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, re
             dl = dl * alpha + dP.sum(axis=1)
         m = m_new
     if A is not None:
-        return O / l[:, None], A / np.maximum(l - dl, 0.5 * l)[:, None]
+        out = O / l[:, None]
+        A = A / np.maximum(l - dl, 0.5 * l)[:, None]
+        if rescale_quantum is not None:
+            q = np.asarray(rescale_quantum, dtype=np.float64)[None, :]
+            A = A + moves[:, None] * (0.5 * q / l[:, None] + 2.0 ** -22 * np.abs(out))
+        return out, A
     return O / l[:, None]
 
 
@@ -315,7 +330,8 @@ def int8_quant_v_channels(v16):
 
 
 def int8_pv_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, blk_k: int,
-                      kv_tile: int = 64, smooth: bool = True, rows=None, quant=None):
+                      kv_tile: int = 64, smooth: bool = True, rows=None, quant=None,
+                      flip_delta: float | None = None):
     """The INT8 P,V variant ([SA-Effects]: "Quantize P,V to INT8 rather than
     retaining FP16"; [SA-Approach]: the faster kernel chosen per layer where
     cosine similarity stays above 99.8%), float64 out.
@@ -325,6 +341,16 @@ def int8_pv_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: in
     max (R6 with slack 0), P quantized to rint(127 P) / 127 (R14); l sums the
     quantized P; O accumulates quantized P times dequantized V.
     Returns float64 [B, H, len(rows), d].
+
+    flip_delta (test tolerance only): the P codes are decided by floating
+    point, so an implementation whose P differs by a few ulps can round a
+    127 P that lies next to a half-integer the other way. With flip_delta, P
+    is also quantized after scaling by (1 -+ flip_delta) (never above 1, the
+    largest P: its code is 127 either way) and the function returns
+    (O, allowance) with the first-order bound of online_softmax_pv on what
+    such flips can change. The allowance also covers an integer accumulator of
+    sum(code_P * code_V) (one unit = s_v / 127 of l * O in channel c) that is
+    rounded back to an integer when the running max moves (rescale_quantum).
     """
     B, H, N, d = q16.shape
     rows = np.arange(N) if rows is None else np.asarray(rows)
@@ -332,7 +358,11 @@ def int8_pv_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: in
     qd = quant if quant is not None else quant_qk_int8(q16, k16, blk_q=blk_q, blk_k=blk_k, smooth=smooth)
     vc, vs = int8_quant_v_channels(v16)
     round127 = lambda P: np.rint(127.0 * P) / 127.0
+    alts = None
+    if flip_delta is not None:
+        alts = lambda P: [round127(P * (1.0 - flip_delta)), round127(np.minimum(P * (1.0 + flip_delta), 1.0))]
     out = np.empty((B, H, rows.size, d))
+    allow = np.zeros_like(out) if alts is not None else None
     for b in range(B):
         for h in range(H):
             cq = qd["q_codes"][b, h, rows].astype(np.float64)
@@ -343,9 +373,14 @@ def int8_pv_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: in
             if causal:
                 S[_causal_mask(rows, keys)] = -np.inf
             Vh = vc[b, h].astype(np.float64) * vs[b, h].astype(np.float64)[None, :]
-            out[b, h] = online_softmax_pv(S, Vh, kv_tile=kv_tile, round_p=round127, ref_slack=0.0,
-                                          sum_rounded=True)
-    return out
+            quantum = vs[b, h].astype(np.float64) / 127.0 if alts is not None else None
+            r = online_softmax_pv(S, Vh, kv_tile=kv_tile, round_p=round127, ref_slack=0.0,
+                                  sum_rounded=True, p_alternatives=alts, rescale_quantum=quantum)
+            if alts is not None:
+                out[b, h], allow[b, h] = r
+            else:
+                out[b, h] = r
+    return (out, allow) if alts is not None else out
 
 
 def fp16_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: int = 64, rows=None,

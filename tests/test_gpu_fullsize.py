@@ -102,7 +102,7 @@ def test_full_size_workload(sa, name):
         say(f"  head ({b},{h}): {rows.size} rows, max |gpu - oracle| = {err:.2e}")
 
 
-@pytest.mark.parametrize("name,mode", [("n16k", 6), ("prefill", 7), ("mxfp4", 5)])
+@pytest.mark.parametrize("name,mode", [("n16k", 6), ("prefill", 7), ("mxfp4", 5), ("video_dit", 6), ("video_dit", 7)])
 def test_full_size_variant_modes(sa, name, mode):
     # The INT8 P,V modes and the MX-FP8 P,V mode at full workload sizes, as bench.py --mode
     # runs them: V codes and scales bit for bit on two heads (INT8 V), attention on sampled
@@ -138,7 +138,8 @@ def test_full_size_variant_modes(sa, name, mode):
             extra = extra[0, 0]
         else:
             blk = 1 if mode == 7 else None
-            ref = O.int8_pv_attention(qs, ks, vs, causal=w.causal, sm_scale=w.sm_scale, blk_q=blk or 128,
-                                      blk_k=blk or 64, rows=rows)
+            ref, extra = O.int8_pv_attention(qs, ks, vs, causal=w.causal, sm_scale=w.sm_scale, blk_q=blk or 128,
+                                             blk_k=blk or 64, rows=rows, flip_delta=FLIP_DELTA)
+            extra = extra[0, 0]
         err = assert_output_parity(got[b, h, rows], ref[0, 0], what=f"{name} mode {mode} head ({b},{h})", extra=extra)
         say(f"  head ({b},{h}): {rows.size} rows, max |gpu - oracle| = {err:.2e}")

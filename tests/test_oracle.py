@@ -737,6 +737,101 @@ def test_mxfp4_constant_v_comes_back_exactly(pv_fp8):
     assert np.max(np.abs(o - 1.5)) <= 1e-14
 
 
+def test_int8_p_flip_allowance_covers_a_code_on_a_half_integer():
+    # INT8 P (R14): code = rint(127 P). Row 0 holds P = 1/2, i.e. 127 P = 63.5 on the
+    # tie between codes 63 and 64; row 1 only holds P with 127 P a quarter away from
+    # any half-integer. The allowance built as int8_pv_attention builds it must cover
+    # row 0 with that code rounded the other way and be exactly 0 on row 1.
+    rng = np.random.default_rng(41)
+    S = np.full((2, 64), -40.0)
+    S[:, 0] = 0.0                                   # P = 1: code 127 either way
+    S[0, 1] = math.log(0.5)
+    S[1, 1] = math.log(67.25 / 127)
+    ks = rng.integers(1, 120, size=(2, 10))
+    S[:, 2:12] = np.log((ks + 0.25) / 127)
+    V = rng.standard_normal((64, 4))
+    round127 = lambda P: np.rint(127.0 * P) / 127.0
+    delta = 2.0 ** -16
+    alts = lambda P: [round127(P * (1 - delta)), round127(np.minimum(P * (1 + delta), 1.0))]
+    out, allow = O.online_softmax_pv(S, V, kv_tile=64, round_p=round127, sum_rounded=True, ref_slack=0.0,
+                                     p_alternatives=alts)
+    base = O.online_softmax_pv(S, V, kv_tile=64, round_p=round127, sum_rounded=True, ref_slack=0.0)
+    assert np.array_equal(out, base)
+    c1 = round127(np.exp(S))[0, 1] * 127
+    assert c1 in (63.0, 64.0)
+
+    def forced(P):
+        Q = round127(P)
+        Q[0, 1] = (127.0 - c1) / 127.0   # 63 <-> 64
+        return Q
+    flipped = O.online_softmax_pv(S, V, kv_tile=64, round_p=forced, sum_rounded=True, ref_slack=0.0)
+    assert np.all(np.abs(flipped[0] - out[0]) <= allow[0] * (1 + 1e-12))
+    assert np.all(allow[0] > 0) and np.all(allow[1] == 0)
+    assert np.max(np.abs(flipped[0] - out[0])) > 0.2 * np.max(allow[0])   # the bound is not vacuous
+
+
+def test_int8_pv_attention_with_flip_delta_keeps_its_output():
+    q, k, v = (_rand16(1, 2, 150, 64, scale=2.0) for _ in range(3))
+    plain = O.int8_pv_attention(q, k, v, causal=True, sm_scale=0.3, blk_q=64, blk_k=64)
+    out, allow = O.int8_pv_attention(q, k, v, causal=True, sm_scale=0.3, blk_q=64, blk_k=64, flip_delta=2.0 ** -16)
+    assert np.array_equal(out, plain)
+    assert np.all(allow >= 0) and np.all(np.isfinite(allow))
+    # a wider window catches more codes, never fewer
+    _, wide = O.int8_pv_attention(q, k, v, causal=True, sm_scale=0.3, blk_q=64, blk_k=64, flip_delta=0.02)
+    assert np.all(wide >= allow) and np.count_nonzero(wide.max(axis=-1)) > 0
+
+
+def _int_accumulator_pv(S, vcodes, vscale, tile):
+    """An INT8 P.V implementation with an integer accumulator of code_P * code_V that is
+    rescaled and rounded back to an integer whenever the running max moves (written
+    here independently of the oracle's online_softmax_pv)."""
+    R, N = S.shape
+    out = np.zeros((R, vcodes.shape[1]))
+    for r in range(R):
+        m, acc, lsum = -np.inf, np.zeros(vcodes.shape[1]), 0.0
+        for t0 in range(0, N, tile):
+            st = S[r, t0:t0 + tile]
+            mn = max(m, st.max())
+            if np.isfinite(m) and mn > m:
+                a = math.exp(m - mn)
+                acc = np.rint(acc * a)
+                lsum = lsum * a
+            codes = np.rint(127.0 * np.exp(st - mn))
+            acc = acc + codes @ vcodes[t0:t0 + tile]
+            lsum += codes.sum()
+            m = mn
+        out[r] = acc * vscale / lsum
+    return out
+
+
+def test_int8_pv_rescale_allowance_covers_an_integer_accumulator():
+    # Row 0: the max moves by 3 log2 units on every tile and channel 0 of V has one
+    # nonzero code (key 0), so the integer sum 127 * 1 is scaled by 1/8 per tile and
+    # rounded until it vanishes (the exact result is tiny but not 0). Row 1: one move
+    # by 1 log2 unit turns the sum 127 into 63.5, rounded by half a unit, the most
+    # one move can do. Row 2: random scores. The allowance of int8_pv_attention's
+    # tolerance path must cover all three and be reached on row 1.
+    rng = np.random.default_rng(43)
+    tile, N = 16, 96
+    S = np.full((3, N), -60.0)
+    S[0] = np.repeat(np.arange(N // tile) * 3 * math.log(2.0), tile) + rng.uniform(-0.3, 0.0, N)
+    S[1, 0] = 0.0
+    S[1, tile] = math.log(2.0)
+    S[2] = rng.standard_normal(N) * 2
+    vcodes = rng.integers(-127, 128, size=(N, 3)).astype(np.float64)
+    vcodes[:, 0] = 0
+    vcodes[0, 0] = 1
+    vscale = np.array([0.4, 0.01, 0.02])
+    V = vcodes * vscale[None, :]
+    round127 = lambda P: np.rint(127.0 * P) / 127.0
+    exact, allow = O.online_softmax_pv(S, V, kv_tile=tile, round_p=round127, sum_rounded=True, ref_slack=0.0,
+                                       rescale_quantum=vscale / 127.0)
+    impl = _int_accumulator_pv(S, vcodes, vscale, tile)
+    assert impl[0, 0] == 0.0 and exact[0, 0] != 0.0
+    assert np.all(np.abs(impl - exact) <= allow * (1 + 1e-12))
+    assert np.abs(impl[1, 0] - exact[1, 0]) > 0.99 * allow[1, 0]   # the bound is reached
+
+
 def test_flip_allowance_covers_a_p_code_on_a_rounding_boundary():
     # Row 0 holds a P right at an E2M1 boundary (block max 1 -> e = -2, P = 0.625 -> 2.5,
     # halfway between codes 2 and 3): the allowance must cover the output with that code

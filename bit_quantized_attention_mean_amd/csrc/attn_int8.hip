@@ -143,14 +143,15 @@ constexpr int kScoresInt8Block = 0, kScoresInt8Token = 1, kScoresF16 = 2;
 
 // Schedule of a kernel instance. The two-group ping-pong (8 waves, 256 query
 // rows per workgroup) overlaps one group's matrix ops with the other's
-// softmax. Where the VALU work dwarfs the matrix work (d = 64 with per-token
-// scores or INT8 P.V) the matrix pipe would idle in it, so those instances run
+// softmax. Where the VALU work outweighs the matrix work more (per-token
+// scores, INT8 P.V) the matrix pipe would idle in it, so those instances run
 // 4 waves (128 rows) that do their matrix ops and softmax in turn, three
-// workgroups per CU, the waves of different workgroups filling each other's
-// gaps (measured +19% per token, +24% INT8 P.V; the plain INT8 modes at d = 64
-// measured 0.8% slower that way and keep the ping-pong).
+// workgroups per CU at d = 64 and two at d = 128, the waves of different
+// workgroups filling each other's gaps (measured +17 to +25% at d = 64, +1 to
+// +9% at d = 128; the plain INT8 modes at d = 64 measured 0.8% slower that way
+// and keep the ping-pong).
 constexpr bool attn_pingpong(int D, int SM, bool PV8, bool DUMP) {
-  return D == 128 || DUMP || SM == kScoresF16 || (SM == kScoresInt8Block && !PV8);
+  return DUMP || SM == kScoresF16 || (SM == kScoresInt8Block && !PV8);
 }
 
 // DUMP: a test instance that also copies the integer scores of key tile dkt,
@@ -158,7 +159,7 @@ constexpr bool attn_pingpong(int D, int SM, bool PV8, bool DUMP) {
 // of head dbh into dump (int32 [256, 64], query-major).
 template <int D, bool CAUSAL, int SM, bool PV8, bool DUMP = false>
 __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
-                             attn_pingpong(D, SM, PV8, DUMP) ? 1 : 3) void attn_int8_kernel(
+                             attn_pingpong(D, SM, PV8, DUMP) ? 1 : (D == 64 ? 3 : 2)) void attn_int8_kernel(
     const void* __restrict__ qsrc, const void* __restrict__ ksrc, const void* __restrict__ vt,
     const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vsc,
     _Float16* __restrict__ out, int N, int Npad, int qblk, float sl2, int BH, int* __restrict__ dump = nullptr,

@@ -85,8 +85,11 @@ __device__ __forceinline__ v16f mfma_fp4(const v4i a, const v4i b, unsigned sa, 
 // lane (format code 0 = E4M3), laid out (measured on the GPU) as keys g*16 ..
 // g*16+15 and 32 + g*16 .. 32+g*16+15 for lane group g, with the block scale
 // of keys 32b .. 32b+31 taken from lane group b.
+// Two workgroups per CU; three for the MX-FP8 P.V instance at d = 64, which
+// fits in 168 registers (+9% at the video_dit shape; the FP4 one spills there
+// and measured 13% slower).
 template <int D, bool CAUSAL, bool PV8>
-__global__ __launch_bounds__(256, 2) void attn_mxfp4_kernel(
+__global__ __launch_bounds__(256, (D == 64 && PV8) ? 3 : 2) void attn_mxfp4_kernel(
     const uint8_t* __restrict__ q4, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k4,
     const uint8_t* __restrict__ ke, const uint8_t* __restrict__ v4, const uint8_t* __restrict__ ve,
     _Float16* __restrict__ out, int N, int Npad, float sl2, int BH) {

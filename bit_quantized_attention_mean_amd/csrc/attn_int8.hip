@@ -13,7 +13,10 @@
 //     its matrix ops for a key tile (P.V of the previous tile, then the scores
 //     of this one), the other runs its softmax on the VALU; a workgroup
 //     barrier separates the phases. 64-key tiles of K and V^T are staged in
-//     LDS (double-buffered) and shared by all 8 waves.
+//     LDS (double-buffered) and shared by all 8 waves. Instances whose VALU
+//     work outweighs their matrix work more (per-token scores, INT8 P.V) use
+//     4-wave workgroups of 128 rows instead, several per CU, each wave doing
+//     its matrix ops and softmax in turn (attn_pingpong below).
 //   * scores are computed transposed, S^T = K Q^T, on v_mfma_i32_32x32x32_i8:
 //     in the 32x32 accumulator layout every lane owns one query column
 //     (lane % 32) and 16 key rows, so the row max and row sum of the softmax

@@ -114,6 +114,12 @@ __device__ __forceinline__ void unpack8(const uint4 raw, float* x) {
   }
 }
 
+// x from the lane the DPP control CTRL names (all rows and banks enabled).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 // fp32(v) - mu for the 8 fp16 values in raw, one mixed-precision fma each:
 // v is widened inside the fma and multiplied by `one` (an fp16 1.0 the
 // compiler cannot see as a constant, so it keeps the fma form), which is exact,
@@ -214,9 +220,13 @@ __device__ __forceinline__ void int8_quant_block(const Int8Job& J, int N, int bi
     float m = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
-    // max over the TPR consecutive lanes that share this row
-#pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    // max over the TPR consecutive lanes that share this row, by DPP lane
+    // swaps: pairs, then quad halves, then the two quads of each 8 lanes
+    // (half-row mirror), then the two halves of each 16 (row mirror)
+    m = fmaxf(m, dpp_f32<0xB1>(m));
+    m = fmaxf(m, dpp_f32<0x4E>(m));
+    m = fmaxf(m, dpp_f32<0x141>(m));
+    if (TPR == 16) m = fmaxf(m, dpp_f32<0x140>(m));
     lm[p] = m;
   }
   // an empty asm that claims to change the raw registers: the compiler then

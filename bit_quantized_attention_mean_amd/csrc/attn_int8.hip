@@ -59,6 +59,14 @@ namespace {
 // The INT8 P.V variant needs P <= 1 for its fixed 1/127 scale and follows the
 // running max exactly (slack 0).
 constexpr float kRefSlack = 8.0f;
+// The integer nearest x (|x| < 2^31), ties upwards: one v_cvt_rpi_i32_f32
+// (floor(x + 1/2)); the compiler's own rounding takes four instructions.
+__device__ __forceinline__ int round_half_up(float x) {
+  int r;
+  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 // log2(127): exp2(x + log2(127)) = 127 * exp2(x), the integer P weight's scale.
 constexpr float kLog2_127 = 6.98868468677216585f;
 
@@ -358,7 +366,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
       if (PV8) {                                                                                 \
         _Pragma("unroll") for (int c = 0; c < NC; ++c)                                           \
           _Pragma("unroll") for (int i = 0; i < 16; ++i)                                         \
-            o[c][i] = __int_as_float(__float2int_rn(static_cast<float>(__float_as_int(o[c][i])) * alpha)); \
+            o[c][i] = __int_as_float(round_half_up(static_cast<float>(__float_as_int(o[c][i])) * alpha)); \
       } else {                                                                                   \
         _Pragma("unroll") for (int c = 0; c < NC; ++c)                                           \
           _Pragma("unroll") for (int i = 0; i < 16; ++i) o[c][i] *= alpha;                       \

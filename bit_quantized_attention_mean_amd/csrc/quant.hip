@@ -429,8 +429,19 @@ __device__ __forceinline__ void v_int8_block(const uint16_t* __restrict__ v, con
   const int bh = bid / ntile, tb = bid % ntile;
   const int tid = threadIdx.x;
   if (tid < D) {
+    // the channel's partial maxima, eight independent loads at a time (a
+    // chain of one load per chunk made long heads latency-bound)
+    const unsigned* pp = part + static_cast<size_t>(bh) * nchunk * D + tid;
     unsigned m = 0;
-    for (int i = 0; i < nchunk; ++i) m = max(m, part[(static_cast<size_t>(bh) * nchunk + i) * D + tid]);
+    int i = 0;
+    for (; i + 8 <= nchunk; i += 8) {
+      unsigned r[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = pp[(i + j) * D];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = max(m, r[j]);
+    }
+    for (; i < nchunk; ++i) m = max(m, pp[i * D]);
     const float a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(m)));
     const float s = a / 127.0f;
     sc[tid] = s;

@@ -260,7 +260,7 @@ def main():
     # the two phases separately
     prep = lambda: sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode | flags)
     ms_prep, _ = timed(prep, args.steps, args.warmup, torch)
-    comp = lambda: sa.sage_attn_compute(out, ws, causal=w.causal, sm_scale=w.sm_scale, mode=mode | flags, q=qd, k=kd)
+    comp = lambda: sa.sage_attn_compute(out, ws, causal=w.causal, sm_scale=w.sm_scale, mode=mode | flags, q=qd, k=kd, v=vd)
     ms_attn, _ = timed(comp, args.steps, args.warmup, torch)
     log(f"[bench] {w.name}: step {ms_step:.4f} ms (wall {wall_step:.4f}), attention kernel {ms_attn:.4f} ms, "
         f"quantization phase {ms_prep:.4f} ms")

@@ -51,11 +51,11 @@ _SIGS = {
     "sage_quant_workspace_size": (_sz, [_i, _i, _i, _i]),
     "sage_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "sage_attn_prepare": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
-    "sage_attn_compute": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "sage_attn_compute": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "sage_quant_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sage_quant_mxfp4": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sage_quant_v_int8": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
-    "sage_attn_dump_scores": (_i, [_vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _i, _i, _vp, _vp]),
+    "sage_attn_dump_scores": (_i, [_vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _i, _i, _vp, _vp]),
     "sage_clock_probe": (_i, [ctypes.c_longlong, _vp, _vp]),
     "sage_wall_clock_khz": (_i, [ctypes.POINTER(_i)]),
 }
@@ -179,18 +179,20 @@ def sage_attn_prepare(q, k, v, workspace, *, mode=SAGE_MODE_INT8_Q128_K64, strea
 
 
 def sage_attn_compute(out, workspace, *, causal=False, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64, q=None, k=None,
-                      stream=None):
-    """Attention from a prepared workspace. q, k (the tensors given to prepare) are needed by SAGE_MODE_FP16 only."""
+                      v=None, stream=None):
+    """Attention from a prepared workspace. q, k (the tensors given to prepare) are needed by SAGE_MODE_FP16
+    only; v (the V given to prepare) by every mode with an fp16 P.V (all but the MXFP4 and INT8 P.V modes)."""
     torch = _torch()
     B, H, N, d = _shape4(out)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
-    for t, name in ((q, "q"), (k, "k")):
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
         if t is not None and tuple(t.shape) != (B, H, N, d):
             raise ValueError(f"{name} and out must have the same shape")
     qp = None if q is None else _dev_ptr(q, "q", torch.float16)
     kp = None if k is None else _dev_ptr(k, "k", torch.float16)
-    rc = lib.sage_attn_compute(qp, kp, _dev_ptr(out, "out", torch.float16), B, H, N, d, int(bool(causal)),
+    vp = None if v is None else _dev_ptr(v, "v", torch.float16)
+    rc = lib.sage_attn_compute(qp, kp, vp, _dev_ptr(out, "out", torch.float16), B, H, N, d, int(bool(causal)),
                                float(sm_scale), int(mode), _dev_ptr(workspace, "workspace"),
                                workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "sage_attn_compute")
@@ -264,16 +266,18 @@ def sage_quant_v_int8(v, *, stream=None):
     return res
 
 
-def sage_attn_dump_scores(out, workspace, *, bh, q_tile, k_tile, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64,
+def sage_attn_dump_scores(out, workspace, *, v, bh, q_tile, k_tile, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64,
                           stream=None):
-    """Test hook: runs the INT8 attention kernel (non-causal) on a prepared workspace and returns the
+    """Test hook: runs the INT8 attention kernel (non-causal) on a prepared workspace and V and returns the
     int32 scores its matrix op produced for key tile k_tile and query tile q_tile of head bh ([256, 64])."""
     torch = _torch()
     B, H, N, d = _shape4(out)
+    if tuple(v.shape) != (B, H, N, d):
+        raise ValueError("v and out must have the same shape")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     s_out = torch.zeros((256, 64), dtype=torch.int32, device=out.device)
-    rc = lib.sage_attn_dump_scores(_dev_ptr(out, "out", torch.float16), B, H, N, d, float(sm_scale), int(mode),
+    rc = lib.sage_attn_dump_scores(_dev_ptr(v, "v", torch.float16), _dev_ptr(out, "out", torch.float16), B, H, N, d, float(sm_scale), int(mode),
                                    _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                    int(bh), int(q_tile), int(k_tile), _dev_ptr(s_out, "s_out"), _stream(stream))
     _check(rc, "sage_attn_dump_scores")

@@ -114,6 +114,12 @@ int validate_attn(int B, int H, int N, int d, int mode, const void* ws, size_t w
   return SAGE_OK;
 }
 
+// Modes whose attention kernel reads the caller's fp16 V (all but the MXFP4
+// and INT8 P.V modes, which read V codes from the workspace).
+bool reads_fp16_v(int mode_lo) {
+  return !(mode_lo == SAGE_MODE_MXFP4 || mode_lo == SAGE_MODE_MXFP4_FP8PV || sage::mode_pv_int8(mode_lo));
+}
+
 int check_scale(float sm_scale) {
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   return SAGE_OK;
@@ -127,8 +133,8 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
   const sage::Layout L = sage::make_layout(BH, N, d, lo, true);
   (void)hipGetLastError();
   float* mu = reinterpret_cast<float*>(at(ws, L.kmean));
-  if (lo == SAGE_MODE_FP16)  // unquantized baseline: only the V^T layout (smoothing would be a no-op)
-    return hip_status(sage::launch_v_transpose(v, at(ws, L.vt), BH, N, L.Npad, d, s), "V transpose kernel");
+  if (lo == SAGE_MODE_FP16)  // unquantized baseline: the attention kernel reads Q, K and V as given
+    return SAGE_OK;
   if (lo == SAGE_MODE_MXFP4 || lo == SAGE_MODE_MXFP4_FP8PV) {
     sage::PrepMx P;
     P.BH = BH; P.k = k; P.v = v; P.ksum = reinterpret_cast<long long*>(at(ws, L.ksum)); P.kmean = mu;
@@ -148,15 +154,15 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
   P.jq.mu = nullptr; P.jq.blk = blk_q; P.jq.code_rows = L.Npad; P.jq.nscale = L.Npad / blk_q; P.jq.ntile = L.Npad / sage::kQTile;
   P.jk.src = k; P.jk.codes = reinterpret_cast<int8_t*>(at(ws, L.k_codes)); P.jk.scales = reinterpret_cast<float*>(at(ws, L.k_scales));
   P.jk.mu = smooth ? mu : nullptr; P.jk.blk = blk_k; P.jk.code_rows = L.Npad; P.jk.nscale = L.Npad / blk_k; P.jk.ntile = L.Npad / sage::kQTile;
-  P.vt = at(ws, L.vt);
   if (sage::mode_pv_int8(lo)) {
+    P.vt = at(ws, L.vt);
     P.vmax = reinterpret_cast<unsigned*>(at(ws, L.vmax));
     P.vscale = reinterpret_cast<float*>(at(ws, L.vscale));
   }
   return hip_status(sage::launch_prepare_int8(P, BH, N, d, s), "INT8 prepare kernels");
 }
 
-int do_compute(const void* q, const void* k, void* out, int B, int H, int N, int d, int causal, float sm_scale,
+int do_compute(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d, int causal, float sm_scale,
                int mode, const void* ws, hipStream_t s) {
   const int BH = B * H;
   const int lo = mode & SAGE_MODE_MASK;
@@ -170,9 +176,10 @@ int do_compute(const void* q, const void* k, void* out, int B, int H, int N, int
     return hip_status(sage::launch_attn_mxfp4(a, at(ws, L.q_fp4), at(ws, L.q_e8), at(ws, L.k_fp4), at(ws, L.k_e8),
                                               at(ws, L.vt_fp4), at(ws, L.vt_e8), s), "MXFP4 attention kernel");
   if (lo == SAGE_MODE_FP16)
-    return hip_status(sage::launch_attn_int8(a, q, k, at(ws, L.vt), nullptr, nullptr, nullptr, s),
+    return hip_status(sage::launch_attn_int8(a, q, k, v, nullptr, nullptr, nullptr, s),
                       "FP16 attention kernel");
-  return hip_status(sage::launch_attn_int8(a, at(ws, L.q_codes), at(ws, L.k_codes), at(ws, L.vt),
+  return hip_status(sage::launch_attn_int8(a, at(ws, L.q_codes), at(ws, L.k_codes),
+                                           sage::mode_pv_int8(lo) ? at(ws, L.vt) : v,
                                            reinterpret_cast<const float*>(at(ws, L.q_scales)),
                                            reinterpret_cast<const float*>(at(ws, L.k_scales)),
                                            sage::mode_pv_int8(lo) ? reinterpret_cast<const float*>(at(ws, L.vscale))
@@ -220,19 +227,22 @@ int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H,
   return do_prepare(q, k, v, B, H, N, d, mode, workspace, static_cast<hipStream_t>(stream));
 }
 
-int sage_attn_compute(const void* q, const void* k, void* out, int B, int H, int N, int d, int causal,
-                      float sm_scale, int mode, const void* workspace, size_t workspace_bytes, void* stream) {
+int sage_attn_compute(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                      int causal, float sm_scale, int mode, const void* workspace, size_t workspace_bytes,
+                      void* stream) {
   g_err[0] = 0;
-  if ((mode & SAGE_MODE_MASK) == SAGE_MODE_FP16) {
+  const int lo = mode & SAGE_MODE_MASK;
+  if (lo == SAGE_MODE_FP16) {
     SAGE_TRY(check_ptr(q, "q", 16));
     SAGE_TRY(check_ptr(k, "k", 16));
   }
+  if (reads_fp16_v(lo)) SAGE_TRY(check_ptr(v, "v", 16));
   SAGE_TRY(check_ptr(out, "out", 16));
   if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
   SAGE_TRY(check_scale(sm_scale));
   SAGE_TRY(validate_attn(B, H, N, d, mode, workspace, workspace_bytes));
   SAGE_TRY(check_device());
-  return do_compute(q, k, out, B, H, N, d, causal, sm_scale, mode, workspace, static_cast<hipStream_t>(stream));
+  return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, mode, workspace, static_cast<hipStream_t>(stream));
 }
 
 int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
@@ -249,12 +259,14 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
   SAGE_TRY(check_device());
   const hipStream_t s = static_cast<hipStream_t>(stream);
   SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, workspace, s));
-  return do_compute(q, k, out, B, H, N, d, causal, sm_scale, mode, workspace, s);
+  return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, mode, workspace, s);
 }
 
-int sage_attn_dump_scores(void* out, int B, int H, int N, int d, float sm_scale, int mode, const void* workspace,
-                          size_t workspace_bytes, int bh, int q_tile, int k_tile, int32_t* s_out, void* stream) {
+int sage_attn_dump_scores(const void* v, void* out, int B, int H, int N, int d, float sm_scale, int mode,
+                          const void* workspace, size_t workspace_bytes, int bh, int q_tile, int k_tile,
+                          int32_t* s_out, void* stream) {
   g_err[0] = 0;
+  SAGE_TRY(check_ptr(v, "v", 16));
   SAGE_TRY(check_ptr(out, "out", 16));
   SAGE_TRY(check_ptr(s_out, "s_out", 16));
   SAGE_TRY(check_scale(sm_scale));
@@ -275,7 +287,7 @@ int sage_attn_dump_scores(void* out, int B, int H, int N, int d, float sm_scale,
   a.mode = lo; a.out = out;
   (void)hipGetLastError();
   return hip_status(sage::launch_attn_int8_dump(a, at(workspace, L.q_codes), at(workspace, L.k_codes),
-                                                at(workspace, L.vt),
+                                                v,
                                                 reinterpret_cast<const float*>(at(workspace, L.q_scales)),
                                                 reinterpret_cast<const float*>(at(workspace, L.k_scales)),
                                                 reinterpret_cast<int*>(s_out), bh, q_tile, k_tile,

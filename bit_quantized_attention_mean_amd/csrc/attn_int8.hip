@@ -12,7 +12,7 @@
 //     SIMD. The groups alternate phases ("ping-pong"): while one group runs
 //     its matrix ops for a key tile (P.V of the previous tile, then the scores
 //     of this one), the other runs its softmax on the VALU; a workgroup
-//     barrier separates the phases. 64-key tiles of K and V^T are staged in
+//     barrier separates the phases. 64-key tiles of K and V are staged in
 //     LDS (double-buffered) and shared by all 8 waves. Instances whose VALU
 //     work outweighs their matrix work more (per-token scores, INT8 P.V) use
 //     4-wave workgroups of 128 rows instead, several per CU, each wave doing
@@ -26,6 +26,11 @@
 //     tile, in order. Those values, rounded to fp16, are already the B operand
 //     of O^T = V^T P^T on v_mfma_f32_32x32x16_f16: no shuffle and no LDS round
 //     trip for P.
+//   * fp16 V is read as the caller gave it ([N, d] per head, 64 key rows of
+//     d channels per tile, rows past N read as zeros by the buffer's range
+//     check): the V^T operand comes from gfx950's transposing LDS read
+//     (ds_read_b64_tr_b16, 4 keys x 16 channels per 16 lanes), so no
+//     transposed copy of V is written to HBM and read back.
 //   * O^T accumulates in fp32 (CDNA4's FP16 matrix op accumulates in FP32; the
 //     page reports no accuracy difference between FP16 and FP32 accumulators).
 //   * softmax in base 2: the row max is taken on the integer scores, then one
@@ -65,6 +70,17 @@ __device__ __forceinline__ int round_half_up(float x) {
   int r;
   asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
   return r;
+}
+
+// Two of gfx950's transposing LDS reads (ds_read_b64_tr_b16), at p and at
+// p + stride, as one 8-value fp16 operand.
+__device__ __forceinline__ v8h lds_read_tr_v8h(const unsigned char* p, int stride) {
+  typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  typedef __attribute__((address_space(3))) h4 lds_h4;
+  typedef unsigned u2 __attribute__((ext_vector_type(2)));
+  const u2 a = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)(p)));
+  const u2 b = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4*)(p + stride)));
+  return __builtin_bit_cast(v8h, v4u{a[0], a[1], b[0], b[1]});
 }
 
 // log2(127): exp2(x + log2(127)) = 127 * exp2(x), the integer P weight's scale.
@@ -171,7 +187,7 @@ constexpr bool attn_pingpong(int D, int SM, bool PV8, bool DUMP) {
 template <int D, bool CAUSAL, int SM, bool PV8, bool DUMP = false>
 __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
                              attn_pingpong(D, SM, PV8, DUMP) ? 1 : (D == 64 ? 3 : 2)) void attn_int8_kernel(
-    const void* __restrict__ qsrc, const void* __restrict__ ksrc, const void* __restrict__ vt,
+    const void* __restrict__ qsrc, const void* __restrict__ ksrc, const void* __restrict__ vsrc,
     const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vsc,
     _Float16* __restrict__ out, int N, int Npad, int qblk, float sl2, int BH, int* __restrict__ dump = nullptr,
     int dbh = 0, int dqt = 0, int dkt = 0) {
@@ -185,19 +201,23 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   constexpr int NC = D / 32;             // 32-channel tiles of O^T
   constexpr int NQF = F16 ? D / 16 : D / 32;  // score matrix ops per 32 keys (16 bytes of Q each)
   constexpr int KROW = D * EB + 16;      // LDS bytes per K row (16 bytes of padding)
-  constexpr int VEB = PV8 ? 1 : 2;       // bytes per V element
-  constexpr int VROW = kKTile * VEB + 16;  // LDS bytes per V^T row
+  // V in LDS: fp16 V as given, 64 key rows of d channels (+64 bytes, so that
+  // the 4 rows x 64 bytes of one transposing read fall in distinct banks), or
+  // the INT8 V^T codes, d channel rows of 64 keys (+16 bytes).
+  constexpr bool VRM = !PV8;
+  constexpr int VROW = VRM ? D * 2 + 64 : kKTile + 16;  // LDS bytes per V row
   constexpr int KT_BYTES = kKTile * KROW;
-  constexpr int VT_BYTES = D * VROW;
+  constexpr int VT_BYTES = (VRM ? kKTile : D) * VROW;
   constexpr int KB0 = 0, KB1 = KT_BYTES, VB0 = 2 * KT_BYTES, VB1 = 2 * KT_BYTES + VT_BYTES;
   constexpr int KCHN = kKTile * D * EB / 16;  // 16-byte chunks of a K tile
-  constexpr int RPV = PV8 ? 2 : 4;       // 16-byte V^T reads (= matrix ops) per 32-channel tile
+  constexpr int RPV = PV8 ? 2 : 4;       // P.V matrix ops per 32-channel tile
+  constexpr int VRD = VRM ? 2 : 1;       // LDS reads per P.V A operand
   constexpr bool PP = attn_pingpong(D, SM, PV8, DUMP);
   constexpr int NTH = PP ? 512 : 256;          // threads per workgroup
   constexpr int WGQ = PP ? kWGQ : kWGQ / 2;    // query rows per workgroup
   constexpr int KPT = (KCHN + NTH - 1) / NTH;
-  constexpr int VCPR = kKTile * VEB / 16;  // 16-byte chunks per V^T row
-  constexpr int VCHN = D * VCPR;           // 16-byte chunks of a V^T tile
+  constexpr int VCPR = VRM ? D * 2 / 16 : kKTile / 16;  // 16-byte chunks per V row in global memory
+  constexpr int VCHN = (VRM ? kKTile : D) * VCPR;      // 16-byte chunks of a V tile
   constexpr int VPT = (VCHN + NTH - 1) / NTH;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KT_BYTES + 2 * VT_BYTES];
 
@@ -247,12 +267,13 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   // K: INT8 codes zero-padded to Npad rows, or fp16 K as given ([N, d] per head).
   const unsigned char* kbase = static_cast<const unsigned char*>(ksrc) +
                                static_cast<size_t>(bh) * (F16 ? N : Npad) * D * EB;
-  const unsigned char* vbase = static_cast<const unsigned char*>(vt) + static_cast<size_t>(bh) * D * Npad * VEB;
+  // V: fp16 as given ([N, d] per head), or INT8 V^T codes zero-padded to Npad keys.
+  const unsigned char* vbase = static_cast<const unsigned char*>(vsrc) + static_cast<size_t>(bh) * (VRM ? N * 2 : Npad) * D;
   // d = 128: the tile loads are buffer loads (per-lane offset fixed for the
   // loop, the tile's offset in a scalar register; +1% at d = 128, -1.4% at
   // d = 64, where plain global loads are kept)
   const auto rk = buffer_rsrc(kbase, static_cast<unsigned>(F16 ? N : Npad) * (D * EB));
-  const auto rv = buffer_rsrc(vbase, static_cast<unsigned>(D) * Npad * VEB);
+  const auto rv = buffer_rsrc(vbase, static_cast<unsigned>(D) * (VRM ? N * 2 : Npad));
 
   // Loading: every thread moves at most KPT 16-byte K chunks and VPT V^T chunks
   // per tile, global -> registers at the start of a period, registers -> LDS
@@ -270,13 +291,21 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int i = tid + NTH * u, row = i / VCPR, col = i % VCPR;
-    vg[u] = row * Npad * VEB + col * 16;
+    vg[u] = row * (VRM ? D * 2 : Npad) + col * 16;
     vls[u] = row * VROW + col * 16;
   }
   const bool vload_last = (tid + NTH * (VPT - 1)) < VCHN;
   unsigned kr[4 * KPT], vr[4 * VPT];
   const int ka = l32 * KROW + g * 16;   // score A operand: K row l32 of each 32-key half
-  const int va = l32 * VROW + g * 32 * VEB;   // P.V A operand: V^T row l32 of each 32-channel tile
+  // P.V A operand (channel l32 of a 32-channel tile, keys g*32 + 8c .. +7):
+  // INT8 V^T row l32; or, from row-major fp16 V, two transposing reads of 4
+  // keys each. In such a read, lane i of each 16-lane group receives element
+  // i % 4 of the 8 bytes addressed by lane 4j + i / 4 as its element j; so the
+  // lane at position r of its group addresses key row r / 4 and channels
+  // 16 h + 4 (r % 4) .. +3 (h: which half of the 32 channels), and every lane
+  // receives channel 16 h + (its position) for 4 consecutive keys.
+  const int va = VRM ? (g * 32 + ((lane & 15) >> 2)) * VROW + ((lane >> 4) & 1) * 32 + (lane & 3) * 8
+                     : l32 * VROW + g * 32;
 
   v16f o[NC];
 #pragma unroll
@@ -305,8 +334,15 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
 #define SAGE_LOAD_V(J_)                                                                          \
   _Pragma("unroll") for (int u = 0; u < VPT; ++u) {                                              \
     if (u < VPT - 1 || vload_last) {                                                             \
-      const v4u t_ = (D == 128) ? __builtin_amdgcn_raw_buffer_load_b128(rv, vg[u], (J_) * (kKTile * VEB), 0) \
-                                : *reinterpret_cast<const v4u*>(vbase + (J_) * kKTile * VEB + vg[u]); \
+      v4u t_ = {0u, 0u, 0u, 0u};                                                                 \
+      /* INT8 V^T codes are padded; fp16 V rows >= N lie past the buffer's range, */            \
+      /* which reads them as zeros (their P is 0) without a branch */                           \
+      if (VRM) {                                                                                 \
+        t_ = __builtin_amdgcn_raw_buffer_load_b128(rv, vg[u] + (J_) * (kKTile * D * 2), 0, 0);   \
+      } else {                                                                                   \
+        t_ = (D == 128) ? __builtin_amdgcn_raw_buffer_load_b128(rv, vg[u], (J_) * kKTile, 0)     \
+                        : *reinterpret_cast<const v4u*>(vbase + (J_) * kKTile + vg[u]);          \
+      }                                                                                          \
       vr[4 * u] = t_[0]; vr[4 * u + 1] = t_[1]; vr[4 * u + 2] = t_[2]; vr[4 * u + 3] = t_[3];   \
     }                                                                                            \
   }
@@ -360,6 +396,9 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   // INT8 form O^T holds int32 sums (in the same registers): the rescale goes
   // through fp32 and rounds back to the nearest integer, and each 32-channel
   // tile takes two INT8 matrix ops (32 keys each) instead of four.
+#define SAGE_VA(VB_, DT_, C_)                                                                    \
+  (VRM ? lds_read_tr_v8h(smem + (VB_) + va + (C_) * 8 * VROW + (DT_) * 64, 4 * VROW)             \
+       : *reinterpret_cast<const v8h*>(smem + (VB_) + va + (DT_) * 32 * VROW + (C_) * 16))
 #define SAGE_PV(VB_)                                                                             \
   do {                                                                                           \
     if (__ballot(alpha != 1.f)) {                                                                \
@@ -374,12 +413,10 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
     }                                                                                            \
     v8h va_[2][RPV];                                                                             \
     _Pragma("unroll") for (int c = 0; c < RPV; ++c)                                              \
-      va_[0][c] = *reinterpret_cast<const v8h*>(smem + (VB_) + va + c * 16);                     \
+      va_[0][c] = SAGE_VA(VB_, 0, c);                                                            \
     _Pragma("unroll") for (int dt = 0; dt < NC; ++dt) {                                          \
       if (dt + 1 < NC) {                                                                         \
-        _Pragma("unroll") for (int c = 0; c < RPV; ++c)                                          \
-          va_[(dt + 1) & 1][c] =                                                                 \
-              *reinterpret_cast<const v8h*>(smem + (VB_) + va + (dt + 1) * 32 * VROW + c * 16);  \
+        _Pragma("unroll") for (int c = 0; c < RPV; ++c) va_[(dt + 1) & 1][c] = SAGE_VA(VB_, dt + 1, c); \
       }                                                                                          \
       _Pragma("unroll") for (int c = 0; c < RPV; ++c) {                                          \
         if (PV8)                                                                                 \
@@ -389,10 +426,10 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va_[dt & 1][c], pf[c], o[dt], 0, 0, 0); \
       }                                                                                          \
     }                                                                                            \
-    __builtin_amdgcn_sched_group_barrier(0x100, RPV, 2);                                         \
+    __builtin_amdgcn_sched_group_barrier(0x100, RPV * VRD, 2);                                   \
     _Pragma("unroll") for (int u = 0; u < RPV * NC - RPV; ++u) {                                 \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                         \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, VRD, 2);                                       \
     }                                                                                            \
     __builtin_amdgcn_sched_group_barrier(0x008, RPV, 2);                                         \
   } while (0)
@@ -653,6 +690,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
 #undef SAGE_PACK_P8
 #undef SAGE_CAP_P8
 #undef SAGE_PV
+#undef SAGE_VA
 #undef SAGE_SCORES
 #undef SAGE_STORE_V
 #undef SAGE_STORE_K

@@ -316,60 +316,7 @@ hipError_t launch_int8_quant(const Int8Job& j0, const Int8Job& j1, int BH, int N
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// V transpose for the INT8 path: V^T [BH, d, Npad] fp16, tokens >= N zeroed.
-// The P.V matrix op consumes V with keys along the contraction; storing it
-// transposed makes every operand fetch one 16-byte LDS read.
-// ---------------------------------------------------------------------------
-
-constexpr int kVTile = 64;  // tokens per V transpose tile
-
-// One 256-thread block of the V transpose: 64-token tile `bid`.
-template <int D>
-__device__ __forceinline__ void v_transpose_block(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt, int N,
-                                                  int Npad, int bid, uint16_t (*t)[D + 8]) {
-  constexpr int TT = kVTile;
-  const int ntile = Npad / TT;
-  const int bh = bid / ntile, tb = bid % ntile;
-  const int tid = threadIdx.x;
-  const uint16_t* src = v + static_cast<size_t>(bh) * N * D;
-  constexpr int CPR = D / 8;  // 16-byte chunks per token row
-#pragma unroll
-  for (int u = 0; u < TT * CPR / 256; ++u) {
-    const int i = tid + 256 * u, r = i / CPR, c8 = i % CPR;
-    const int n = tb * TT + r;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (n < N) val = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(n) * D + c8 * 8);
-    *reinterpret_cast<uint4*>(&t[r][c8 * 8]) = val;
-  }
-  __syncthreads();
-  uint16_t* dst = vt + static_cast<size_t>(bh) * D * Npad + tb * TT;
-#pragma unroll
-  for (int u = 0; u < D * (TT / 8) / 256; ++u) {
-    const int i = tid + 256 * u, dd = i / (TT / 8), n8 = i % (TT / 8);
-    unsigned w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = static_cast<unsigned>(t[n8 * 8 + 2 * j][dd]) | (static_cast<unsigned>(t[n8 * 8 + 2 * j + 1][dd]) << 16);
-    *reinterpret_cast<uint4*>(dst + static_cast<size_t>(dd) * Npad + n8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v,
-                                                          uint16_t* __restrict__ vt, int N, int Npad) {
-  __shared__ uint16_t t[kVTile][D + 8];
-  v_transpose_block<D>(v, vt, N, Npad, blockIdx.x, t);
-}
-
-hipError_t launch_v_transpose(const void* v, void* vt, int BH, int N, int Npad, int d, hipStream_t s) {
-  const int grid = BH * (Npad / 64);
-  if (d == 128)
-    v_transpose_kernel<128><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), N, Npad);
-  else
-    v_transpose_kernel<64><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(v), static_cast<uint16_t*>(vt), N, Npad);
-  return hipGetLastError();
-}
+constexpr int kVTile = 64;  // tokens per INT8 V tile
 
 // ---------------------------------------------------------------------------
 // INT8 V for the INT8 P.V variant: one scale per (head, channel) over all
@@ -507,8 +454,8 @@ hipError_t launch_v_int8(const void* v, unsigned* part, int8_t* codes, float* sc
 }
 
 // ---------------------------------------------------------------------------
-// The prepare phase of the INT8 modes: (1) the K column sums, the Q codes and
-// the fp16 V^T share one grid, as none depends on another; (2) the K mean;
+// The prepare phase of the INT8 modes: (1) the K column sums and the Q codes
+// share one grid, as neither depends on the other; (2) the K mean;
 // (3) the K codes; for INT8 V, (4) its channel maxima and (5) its codes. The
 // INT8 V passes keep launches of their own: in a shared grid their blocks are
 // held to the occupancy of the quantization blocks' registers, which measured
@@ -519,35 +466,28 @@ constexpr int kPrepSmem = 256 * 9 * 8;  // the largest of the blocks' LDS needs
 
 template <int D>
 __global__ __launch_bounds__(256) void prep_int8_phase1_kernel(PrepInt8 P, int N, int n_ksum, int n_q) {
-  static_assert(kVTile * (D + 8) * 2 <= kPrepSmem, "LDS");
   __shared__ __attribute__((aligned(16))) unsigned char smem[kPrepSmem];
   const auto* k = static_cast<const uint16_t*>(P.k);
-  const auto* v = static_cast<const uint16_t*>(P.v);
   int bid = blockIdx.x;
   if (bid < n_ksum) {
     ksum_partial_block<D>(k, P.ksum, N, P.chunk, P.nchunk, bid, reinterpret_cast<long long (*)[9]>(smem));
     return;
   }
   bid -= n_ksum;
-  if (bid < n_q) {
+  if (bid < n_q)
     int8_quant_block<D>(P.jq, N, bid, reinterpret_cast<float*>(smem), reinterpret_cast<float*>(smem) + kQTile);
-    return;
-  }
-  bid -= n_q;
-  v_transpose_block<D>(v, static_cast<uint16_t*>(P.vt), N, P.Npad, bid, reinterpret_cast<uint16_t (*)[D + 8]>(smem));
 }
 
 hipError_t launch_prepare_int8(const PrepInt8& P, int BH, int N, int d, hipStream_t s) {
   const int n_ksum = P.smooth ? BH * P.nchunk : 0;
   const int n_q = BH * P.jq.ntile;
-  const int n_v1 = P.vmax ? 0 : BH * (P.Npad / kVTile);
   // K codes in 64-row tiles (K blocks are 64 rows or one row): half the
   // registers of a 128-row tile, so twice the waves in flight
   Int8Job jk = P.jk;
   jk.ntile = P.jk.ntile * (kQTile / 64);
   const dim3 grid_k(BH * jk.ntile, 1);
-  if (d == 128) prep_int8_phase1_kernel<128><<<n_ksum + n_q + n_v1, 256, 0, s>>>(P, N, n_ksum, n_q);
-  else prep_int8_phase1_kernel<64><<<n_ksum + n_q + n_v1, 256, 0, s>>>(P, N, n_ksum, n_q);
+  if (d == 128) prep_int8_phase1_kernel<128><<<n_ksum + n_q, 256, 0, s>>>(P, N, n_ksum, n_q);
+  else prep_int8_phase1_kernel<64><<<n_ksum + n_q, 256, 0, s>>>(P, N, n_ksum, n_q);
   if (P.smooth) {
     if (d == 128) kmean_kernel<128><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
     else kmean_kernel<64><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);

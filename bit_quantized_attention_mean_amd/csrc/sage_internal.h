@@ -61,7 +61,7 @@ struct Layout {
   // INT8 modes
   size_t q_codes = 0, k_codes = 0;    // int8 [BH, Npad, d]
   size_t q_scales = 0, k_scales = 0;  // fp32 [BH, Npad] (enough for any block size)
-  size_t vt = 0;                      // V^T [BH, d, Npad], zero-padded: fp16, or int8 codes (INT8 P.V)
+  size_t vt = 0;                      // int8 V^T codes [BH, d, Npad], zero-padded (INT8 P.V only)
   size_t vscale = 0;                  // fp32 [BH, d] per-channel V scales (INT8 P.V)
   size_t vmax = 0;                    // uint32 [BH, nchunk, d] partial channel maxima of |V|
   // MXFP4 mode
@@ -96,16 +96,14 @@ inline Layout make_layout(long long BH, int N, int d, int mode_lo, bool attentio
       L.k_e8 = take(rows * d / 32);
       L.vt_fp4 = take(mode_lo == 5 ? rows * d : rows * d / 2);  // V^T codes: E2M1 (packed) or E4M3
       L.vt_e8 = take(rows * d / 32);
-    } else if (mode_lo == 4) {  // SAGE_MODE_FP16: V^T only
-      L.vt = take(rows * d * 2);
-    } else {
+    } else if (mode_lo != 4) {  // (SAGE_MODE_FP16 reads Q, K and V as given)
       const bool pv8 = mode_pv_int8(mode_lo);
       L.q_codes = take(rows * d);
       L.k_codes = take(rows * d);
       L.q_scales = take(rows * 4);
       L.k_scales = take(rows * 4);
-      L.vt = take(rows * d * (pv8 ? 1 : 2));
       if (pv8) {
+        L.vt = take(rows * d);
         L.vscale = take(size_t(BH) * d * 4);
         L.vmax = take(size_t(BH) * L.nchunk * d * 4);
       }
@@ -139,17 +137,15 @@ struct Int8Job {
 };
 hipError_t launch_int8_quant(const Int8Job& j0, const Int8Job& j1, int BH, int N, int d, hipStream_t s);
 
-// fp16 V [BH, N, d] -> V^T [BH, d, Npad] with zero-padded tokens.
-hipError_t launch_v_transpose(const void* v, void* vt, int BH, int N, int Npad, int d, hipStream_t s);
-
 // Per-channel INT8 V: channel maxima over chunks of `chunk` tokens into part
 // [BH, nchunk, d], then scales [BH, d] and codes V^T [BH, d, ldv] (ldv a
 // multiple of 16, tokens >= N zero).
 hipError_t launch_v_int8(const void* v, unsigned* part, int8_t* codes, float* scales, int BH, int N, int ldv,
                          int d, int chunk, int nchunk, hipStream_t s);
 
-// The whole prepare phase of the INT8 modes: K column sums, Q codes and the V
-// layout in one launch, the K mean, the K codes, and the INT8 V codes if used.
+// The whole prepare phase of the INT8 modes: K column sums and Q codes in one
+// launch, the K mean, the K codes, and the INT8 V codes if used (fp16 V is
+// read by the attention kernel as given).
 struct PrepInt8 {
   const void* k = nullptr;
   const void* v = nullptr;
@@ -158,8 +154,8 @@ struct PrepInt8 {
   int chunk = 0, nchunk = 0;
   bool smooth = true;
   Int8Job jq, jk;              // jk.mu = kmean when smooth
-  void* vt = nullptr;          // fp16 V^T [BH, d, Npad], or int8 V^T codes when vmax is set
-  unsigned* vmax = nullptr;    // INT8 V: partial channel maxima [BH, nchunk, d]; null: fp16 V^T
+  void* vt = nullptr;          // INT8 V: V^T codes [BH, d, Npad]
+  unsigned* vmax = nullptr;    // INT8 V: partial channel maxima [BH, nchunk, d]; null: no V work
   float* vscale = nullptr;     // INT8 V: scales [BH, d]
   int Npad = 0;
 };
@@ -210,14 +206,14 @@ struct AttnArgs {
 };
 // q, k: INT8 codes (padded to Npad rows) with scales qs, ks; or, for
 // SAGE_MODE_FP16, the caller's fp16 Q and K [BH, N, d] (qs, ks unused).
-// vt: fp16 V^T, or for the INT8 P.V modes int8 V^T codes with per-channel
-// scales vs [BH, d] (unused otherwise).
-hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, const void* vt,
+// v: the caller's fp16 V [BH, N, d], or for the INT8 P.V modes int8 V^T codes
+// [BH, d, Npad] with per-channel scales vs [BH, d] (unused otherwise).
+hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, const void* v,
                             const float* qs, const float* ks, const float* vs, hipStream_t s);
 // The INT8 attention kernel (non-causal, modes 0, 1, 3) with a copy of the
 // integer scores of key tile dkt for query tile dqt of head dbh into dump
 // (int32 [256, 64], query-major).
-hipError_t launch_attn_int8_dump(const AttnArgs& a, const void* q, const void* k, const void* vt,
+hipError_t launch_attn_int8_dump(const AttnArgs& a, const void* q, const void* k, const void* v,
                                  const float* qs, const float* ks, int* dump, int dbh, int dqt, int dkt,
                                  hipStream_t s);
 // v4 holds E2M1 V^T codes, or E4M3 ones for SAGE_MODE_MXFP4_FP8PV (a.mode 5,

@@ -111,8 +111,10 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
 
 /*
  * First phase of sage_attn_fwd: the K channel mean and the quantization of
- * Q, K (and V's layout, or its MXFP4 codes) into `workspace`. The steps are
- * those of sage_quant_qk / sage_quant_mxfp4; the workspace layout is private.
+ * Q, K (and of V, in the modes that quantize it: MXFP4, MX-FP8 or INT8 codes)
+ * into `workspace`. The steps are those of sage_quant_qk / sage_quant_mxfp4 /
+ * sage_quant_v_int8; the workspace layout is private. SAGE_MODE_FP16 has
+ * nothing to prepare (the call only validates its arguments).
  */
 int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d,
                       int mode, void* workspace, size_t workspace_bytes, void* stream);
@@ -125,9 +127,13 @@ int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H,
  *   q, k  the fp16 tensors given to sage_attn_prepare. Only SAGE_MODE_FP16
  *         reads them here (the quantized modes read their codes from the
  *         workspace and accept NULL).
+ *   v     the fp16 V given to sage_attn_prepare, read here by every mode whose
+ *         P.V runs in fp16 (all but SAGE_MODE_MXFP4, SAGE_MODE_MXFP4_FP8PV and
+ *         the INT8 P.V modes, which read V codes from the workspace and
+ *         accept NULL). Its contents must not change between the two calls.
  */
-int sage_attn_compute(const void* q, const void* k, void* out, int B, int H, int N, int d,
-                      int causal, float sm_scale, int mode, const void* workspace,
+int sage_attn_compute(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
+                      int d, int causal, float sm_scale, int mode, const void* workspace,
                       size_t workspace_bytes, void* stream);
 
 /*
@@ -135,14 +141,15 @@ int sage_attn_compute(const void* q, const void* k, void* out, int B, int H, int
  * "Approach": QK^T of the INT8 codes with integer accumulation). Runs the
  * attention kernel of `mode` (0, 1 or 3; non-causal) on a workspace prepared by
  * sage_attn_prepare for the same B, H, N, d and mode, writing `out` as
- * sage_attn_compute does, and copies the int32 scores q_codes . k_codes^T that
+ * sage_attn_compute does (reading fp16 `v`, the V given to sage_attn_prepare),
+ * and copies the int32 scores q_codes . k_codes^T that
  * the kernel's INT8 matrix op produced for key tile `k_tile` (keys 64 k_tile ..
  * +63) and query tile `q_tile` (queries 256 q_tile .. +255) of head `bh` into
  * s_out, int32 [256, 64] device, query-major. Rows and keys at or past N hold
  * the scores of the zero-padded codes (0).
  *   bh in [0, B*H), q_tile in [0, ceil(N/256)), k_tile in [0, ceil(N/64)).
  */
-int sage_attn_dump_scores(void* out, int B, int H, int N, int d, float sm_scale, int mode,
+int sage_attn_dump_scores(const void* v, void* out, int B, int H, int N, int d, float sm_scale, int mode,
                           const void* workspace, size_t workspace_bytes, int bh, int q_tile, int k_tile,
                           int32_t* s_out, void* stream);
 

@@ -46,12 +46,12 @@ def test_workspace_sizes():
     small = sa.sage_attn_workspace_size(1, 2, 256, 128, 0)
     big = sa.sage_attn_workspace_size(1, 2, 4096, 128, 0)
     assert big > small
-    # INT8: codes (2 B/elem) + V^T (2 B/elem) dominate; MXFP4: ~1.6 B/elem
+    # INT8 with fp16 P.V: Q, K codes (2 B/elem) dominate (V is read as given); MXFP4: ~1.6 B/elem
     n = 4 * 32 * 4096 * 128
-    assert 4 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 0) < 4.2 * n
+    assert 2 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 0) < 2.2 * n
     assert 1.5 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 2) < 1.8 * n
-    # FP16 baseline: only V^T (2 B/elem); MXFP4 with MX-FP8 V: ~2.1 B/elem
-    assert 2 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 4) < 2.1 * n
+    # FP16 baseline: only the K mean (Q, K, V are read as given); MXFP4 with MX-FP8 V: ~2.1 B/elem
+    assert 0 < sa.sage_attn_workspace_size(4, 32, 4096, 128, 4) < 0.05 * n
     assert 2 * n <= sa.sage_attn_workspace_size(4, 32, 4096, 128, 5) < 2.3 * n
     # INT8 P.V: Q, K codes (2 B/elem) + INT8 V^T (1 B/elem)
     for mode in (6, 7):
@@ -86,18 +86,22 @@ def test_prepare_compute_and_quant_validation():
     ws = sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
     assert lib.sage_attn_prepare(None, A16, A16, 1, 2, 256, 64, 0, A16, ws, None) == INVALID
     assert lib.sage_attn_prepare(A16, A16, A16, 1, 2, 256, 64, 0, A16, 10, None) == WS
-    assert lib.sage_attn_compute(None, None, A16, 1, 2, 256, 64, 0, 0.0, 0, A16, ws, None) == INVALID
-    assert lib.sage_attn_compute(None, None, A16, 1, 2, 256, 48, 0, 0.1, 0, A16, ws, None) == UNSUP
+    assert lib.sage_attn_compute(None, None, A16, A16, 1, 2, 256, 64, 0, 0.0, 0, A16, ws, None) == INVALID
+    assert lib.sage_attn_compute(None, None, A16, A16, 1, 2, 256, 48, 0, 0.1, 0, A16, ws, None) == UNSUP
+    # the fp16 P.V modes read v in the attention phase: null or misaligned is refused
+    assert lib.sage_attn_compute(None, None, None, A16, 1, 2, 256, 64, 0, 0.1, 0, A16, ws, None) == INVALID
+    assert lib.sage_attn_compute(None, None, A16 + 2, A16, 1, 2, 256, 64, 0, 0.1, 0, A16, ws, None) == INVALID
     # the unquantized baseline reads q and k in the attention phase
     ws4 = sa.sage_attn_workspace_size(1, 2, 256, 64, 4)
-    assert lib.sage_attn_compute(None, A16, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
-    assert lib.sage_attn_compute(A16, A16 + 2, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
-    assert lib.sage_attn_compute(A16, A16, A16, 1, 2, 256, 64, 0, 0.1, 8, A16, ws4, None) == UNSUP
-    # the INT8 P.V workspace also holds INT8 V^T and its channel scales
+    assert lib.sage_attn_compute(None, A16, A16, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
+    assert lib.sage_attn_compute(A16, A16 + 2, A16, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
+    assert lib.sage_attn_compute(A16, A16, None, A16, 1, 2, 256, 64, 0, 0.1, 4, A16, ws4, None) == INVALID
+    assert lib.sage_attn_compute(A16, A16, A16, A16, 1, 2, 256, 64, 0, 0.1, 8, A16, ws4, None) == UNSUP
+    # the INT8 P.V workspace also holds INT8 V^T and its channel scales (and v may be null)
     ws0 = sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
     ws6 = sa.sage_attn_workspace_size(1, 2, 256, 64, 6)
     assert ws6 != ws0
-    assert lib.sage_attn_compute(None, None, A16, 1, 2, 256, 64, 0, 0.1, 6, A16, ws6 - 1, None) == WS
+    assert lib.sage_attn_compute(None, None, None, A16, 1, 2, 256, 64, 0, 0.1, 6, A16, ws6 - 1, None) == WS
     qw = sa.sage_quant_workspace_size(1, 2, 256, 64)
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 48, 64, 0, A16, A16, A16, A16, None, A16, qw, None) == UNSUP
     assert lib.sage_quant_qk(A16, A16, 1, 2, 256, 64, 64, 64, 4, A16, A16, A16, A16, None, A16, qw, None) == UNSUP
@@ -106,13 +110,13 @@ def test_prepare_compute_and_quant_validation():
     assert lib.sage_quant_mxfp4(A16, A16, A16, 1, 2, 256, 64, 0, A16, A16, A16, A16, A16 + 4, A16, None, A16, qw,
                                 None) == INVALID
     # the integer-score dump: INT8 modes 0, 1, 3 only, tile indices in range
-    assert lib.sage_attn_dump_scores(A16, 1, 2, 1000, 64, 0.1, 0, A16, ws0 * 4, 0, 0, 0, None, None) == INVALID
-    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 2, A16, 1 << 30, 0, 0, 0, A16, None) == UNSUP
-    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 4, A16, 1 << 30, 0, 0, 0, A16, None) == UNSUP
-    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 2, 0, 0, A16, None) == INVALID
-    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 0, 1, 0, A16, None) == INVALID
-    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 0, 0, 4, A16, None) == INVALID
-    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.0, 0, A16, ws0, 0, 0, 0, A16, None) == INVALID
+    assert lib.sage_attn_dump_scores(A16, A16, 1, 2, 1000, 64, 0.1, 0, A16, ws0 * 4, 0, 0, 0, None, None) == INVALID
+    assert lib.sage_attn_dump_scores(A16, A16, 1, 2, 256, 64, 0.1, 2, A16, 1 << 30, 0, 0, 0, A16, None) == UNSUP
+    assert lib.sage_attn_dump_scores(A16, A16, 1, 2, 256, 64, 0.1, 4, A16, 1 << 30, 0, 0, 0, A16, None) == UNSUP
+    assert lib.sage_attn_dump_scores(A16, A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 2, 0, 0, A16, None) == INVALID
+    assert lib.sage_attn_dump_scores(A16, A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 0, 1, 0, A16, None) == INVALID
+    assert lib.sage_attn_dump_scores(A16, A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 0, 0, 4, A16, None) == INVALID
+    assert lib.sage_attn_dump_scores(A16, A16, 1, 2, 256, 64, 0.0, 0, A16, ws0, 0, 0, 0, A16, None) == INVALID
     assert lib.sage_quant_v_int8(None, 1, 2, 256, 64, A16, A16, A16, qw, None) == INVALID
     assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16 + 8, A16, A16, qw, None) == INVALID
     assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16, A16 + 2, A16, qw, None) == INVALID
@@ -145,5 +149,5 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert lib.sage_quant_v_int8(A16, 1, 2, 256, 64, A16, A16, A16, qw, None) == NODEV
     assert _fwd(mode=6) == NODEV and _fwd(mode=7) == NODEV
     ws0 = sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
-    assert lib.sage_attn_dump_scores(A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 1, 0, 3, A16, None) == NODEV
+    assert lib.sage_attn_dump_scores(A16, A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 1, 0, 3, A16, None) == NODEV
     assert lib.sage_clock_probe(1000, A16, None) == NODEV

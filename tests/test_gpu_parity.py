@@ -230,7 +230,7 @@ def test_int8_scores_are_the_exact_integer_products(sa, case):
     sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode)
     out = torch.empty_like(qd)
     for (bh, qt, kt) in tiles:
-        got = sa.sage_attn_dump_scores(out, ws, bh=bh, q_tile=qt, k_tile=kt, mode=mode)
+        got = sa.sage_attn_dump_scores(out, ws, v=vd, bh=bh, q_tile=qt, k_tile=kt, mode=mode)
         torch.cuda.synchronize()
         b, h = divmod(bh, H)
         qc = np.zeros((256, d), np.int64)
@@ -328,7 +328,7 @@ def test_prepare_compute_equals_fwd_and_is_deterministic(sa, mode):
     ws = sa.make_workspace(1, 2, 700, 128, mode)
     c = torch.empty_like(qd)
     sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode)
-    sa.sage_attn_compute(c, ws, causal=True, mode=mode, q=qd, k=kd)
+    sa.sage_attn_compute(c, ws, causal=True, mode=mode, q=qd, k=kd, v=vd)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
     # another stream, and the phases launched with an unrelated call in between
@@ -340,7 +340,7 @@ def test_prepare_compute_equals_fwd_and_is_deterministic(sa, mode):
         d2 = torch.empty_like(qd)
         sa.sage_attn_prepare(qd, kd, vd, ws2, mode=mode)
         sa.sage_attn_fwd(*other, causal=False, mode=mode)
-        sa.sage_attn_compute(d2, ws2, causal=True, mode=mode, q=qd, k=kd)
+        sa.sage_attn_compute(d2, ws2, causal=True, mode=mode, q=qd, k=kd, v=vd)
     st.synchronize()
     assert torch.equal(a, d2)
 

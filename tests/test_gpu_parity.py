@@ -384,3 +384,20 @@ def test_layer_selector_on_synthetic_layers(sa):
         em = O.int8_attention(q, k, v, causal=False, sm_scale=1 / 8, blk_q=128, blk_k=64)
         m0 = next(m for m in meas if m.mode == 0)
         assert abs(m0.cos - O.metrics(em, ex)["cos"]) < 5e-4
+
+
+@pytest.mark.parametrize("mode,d", [(0, 128), (4, 128), (3, 64), (0, 64)])
+def test_ragged_tail_reads_no_row_of_the_next_head(sa, mode, d):
+    # fp16 V is read as given, [N, d] per head: the last key tile of head 0
+    # (keys 640..703 with N = 700) must read zeros past N, not the first rows
+    # of head 1. Head 1's V is all NaN here; head 0 must equal a run on head 0
+    # alone, bit for bit.
+    say("ragged tail head isolation", mode, d)
+    q, k, v = make_custom(1, 2, 700, d, seed=37)
+    vn = v.copy()
+    vn[0, 1] = np.nan
+    out = sa.sage_attn_fwd(*_dev(q, k, vn), mode=mode)
+    alone = sa.sage_attn_fwd(*_dev(q[:, :1].copy(), k[:, :1].copy(), v[:, :1].copy()), mode=mode)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[:, :1]).all()
+    assert torch.equal(out[:, :1], alone)

@@ -151,3 +151,17 @@ def test_valid_arguments_without_a_device_report_no_device():
     ws0 = sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
     assert lib.sage_attn_dump_scores(A16, A16, 1, 2, 256, 64, 0.1, 0, A16, ws0, 1, 0, 3, A16, None) == NODEV
     assert lib.sage_clock_probe(1000, A16, None) == NODEV
+
+
+def test_binding_checks_v_before_any_device_call():
+    # the attention phase and the score dump take the caller's fp16 V: a shape
+    # that differs from out, or a host tensor, is refused in the binding
+    torch = pytest.importorskip("torch")
+    out = torch.empty(1, 2, 256, 64, dtype=torch.float16)
+    ws = torch.empty(16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        sa.sage_attn_compute(out, ws, v=torch.empty(1, 2, 128, 64, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        sa.sage_attn_dump_scores(out, ws, v=torch.empty(1, 1, 256, 64, dtype=torch.float16), bh=0, q_tile=0, k_tile=0)
+    with pytest.raises(TypeError):
+        sa.sage_attn_compute(out, ws, v=torch.empty(1, 2, 256, 64, dtype=torch.float16))

@@ -41,15 +41,14 @@ Readings where the pages are silent (each also listed in the design doc):
   R4 INT8 code: rint_half_even(fp32(x / s)), clamp [-127, 127]; a = 0 gives
      s = 0 and all codes 0.
   R5 sm_scale is applied at dequantization, not folded into Q.
-  R6 online softmax over key tiles of `kv_tile` keys in ascending order. P is
-     formed against a per-row reference max m that follows the running max
-     lazily: m moves to the tile's row max only when that exceeds m by more
-     than `ref_slack` (in log2 units; 8 by default, 0 = the plain running max),
-     so P <= 2^8. Any reference point gives the same softmax; this one only
-     fixes where P is rounded. P16 = fp16_RNE(P); O accumulates P16 . V and
-     the row sum l accumulates the same P16 (so O is an exact weighted mean of
-     V rows up to accumulation rounding). In the MXFP4 path l likewise sums
-     the MX-quantized P that multiplies V.
+  R6 online softmax over key tiles of `kv_tile` keys in ascending order
+     (FlashAttention-2 style, [SA-Setup]): m_t = max(m_{t-1}, tile row max), the
+     plain running max; P = exp(S - m_t) is formed against it; what was
+     accumulated under m_{t-1} is scaled by exp(m_{t-1} - m_t). P16 =
+     fp16_RNE(P); O accumulates P16 . V and the row sum l accumulates the same
+     P16, so O is an exact weighted mean of V rows up to accumulation rounding
+     (a constant V comes back exactly). In the MXFP4 path l likewise sums the
+     MX-quantized P that multiplies V.
   R7 causal: key j is masked for query i when j > i (N_q = N_k).
   R8 MX blocks: 32 contiguous elements along the contraction dimension (d for
      Q and K_s; tokens, per channel, for V; keys, per query row inside a key
@@ -57,11 +56,11 @@ Readings where the pages are silent (each also listed in the design doc):
      a = 0 gives e = 0 and all codes 0. Element code = nearest E2M1 value to
      x * 2^-e, ties to the even code index, saturating at +-6; the sign bit is
      the sign bit of x. Packing: element 2k in the low nibble of byte k.
-  R14 INT8 P and V (the "Quantize P,V to INT8" ablation of [SA-Effects];
-     the page gives no granularity): V gets one scale per (head, channel) over
+  R14 INT8 P and V (the INT8 P,V ablation of [SA-Effects]; the page gives no
+     granularity): V gets one scale per (head, channel) over
      all tokens, with the R3/R4 rules (a = max|V|, s = fp32(a / 127), code =
-     rint_half_even(fp32(V / s))); P is formed against the plain running max
-     (slack 0), so 0 <= P <= 1, and quantized with the fixed scale 1/127:
+     rint_half_even(fp32(V / s))); P is formed against the running max (R6),
+     so 0 <= P <= 1, and quantized with the fixed scale 1/127:
      code = rint_half_even(127 P). l sums the quantized P, O accumulates the
      quantized P times the dequantized V.
   R13 MX-FP8 variant for P and V (not on the pages; the accuracy variant of
@@ -203,19 +202,16 @@ def quant_qk_int8(q16, k16, *, blk_q: int, blk_k: int, smooth: bool = True):
     return dict(q_codes=qc, q_scales=qs, k_codes=kc, k_scales=kscl, k_mean=mu)
 
 
-REF_SLACK = 8.0   # log2 units by which the tile max may exceed the reference max (reading R6)
-
-
-def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, ref_slack: float = REF_SLACK,
-                      sum_rounded: bool = False, p_alternatives=None, rescale_quantum=None):
+def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p,
+                      sum_rounded: bool = False, p_alternatives=None):
     """FlashAttention-2 style online softmax and P.V over key tiles ([SA-Setup]).
 
     S: float64 scores [R, N] (already scaled, -inf where masked).
     V: float64 values [N, d] (already in the precision P.V consumes).
     round_p(P_tile) -> the P that multiplies V (fp16 RNE for the INT8 path, the
     MX-quantized P for the FP4 path, identity for an exact run).
-    Reading R6: ascending tiles, P against the lazily updated reference max;
-    l sums round_p(P) if sum_rounded else P. Returns O [R, d] float64.
+    Reading R6: ascending tiles, P against the running max; l sums round_p(P)
+    if sum_rounded else P. Returns O [R, d] float64.
 
     p_alternatives (test tolerance only, with sum_rounded): a callable giving,
     for a tile's P, other quantized P that an implementation computing P with
@@ -224,35 +220,23 @@ def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, re
     returns (O, allowance), allowance [R, d] bounding |O' - O| to first order
     for any mix of those alternatives: a weight that moves by dP changes O by
     dP * (v_j - O) / l, and |v_j - O| <= |v_j| + max|v| per channel.
-
-    rescale_quantum (test tolerance only): per channel, the step [d] to which an
-    implementation rounds the accumulated sum l * O every time the reference
-    max moves (an integer accumulator rescaled through fp32 and rounded back).
-    Each such move after the first tile can then shift l * O by half a step
-    plus the fp32 rounding of the rescale, which is added to the allowance
-    (returned as with p_alternatives).
     """
     R, N = S.shape
     d = V.shape[1]
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     O = np.zeros((R, d))
-    want = p_alternatives is not None or rescale_quantum is not None
-    A = np.zeros((R, d)) if want else None
+    A = np.zeros((R, d)) if p_alternatives is not None else None
     dl = np.zeros(R)
-    moves = np.zeros(R)
     vbound = np.abs(V) + np.abs(V).max(axis=0, keepdims=True)
-    slack = ref_slack * math.log(2.0)
     for t0 in range(0, N, kv_tile):
         St = S[:, t0:t0 + kv_tile]
         with np.errstate(invalid="ignore"):
-            tmax = St.max(axis=1)
-            m_new = np.where(tmax > m + slack, tmax, m)
+            m_new = np.maximum(m, St.max(axis=1))
             # factor for what was accumulated under the old max (0 before any valid key)
             alpha = np.where(np.isneginf(m_new), 0.0, np.exp(m - m_new))
             P = np.where(np.isneginf(St), 0.0, np.exp(St - m_new[:, None]))
         Pr = round_p(P)
-        moves += (m_new > m) & np.isfinite(m)
         l = l * alpha + (Pr if sum_rounded else P).sum(axis=1)
         O = O * alpha[:, None] + Pr @ V[t0:t0 + kv_tile]
         if p_alternatives is not None:
@@ -263,18 +247,13 @@ def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p, re
             dl = dl * alpha + dP.sum(axis=1)
         m = m_new
     if A is not None:
-        out = O / l[:, None]
-        A = A / np.maximum(l - dl, 0.5 * l)[:, None]
-        if rescale_quantum is not None:
-            q = np.asarray(rescale_quantum, dtype=np.float64)[None, :]
-            A = A + moves[:, None] * (0.5 * q / l[:, None] + 2.0 ** -22 * np.abs(out))
-        return out, A
+        return O / l[:, None], A / np.maximum(l - dl, 0.5 * l)[:, None]
     return O / l[:, None]
 
 
 def int8_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, blk_k: int,
                    kv_tile: int = 64, smooth: bool = True, rows=None, quantize: bool = True,
-                   quant=None, ref_slack: float = REF_SLACK):
+                   quant=None):
     """Emulated INT8 SageAttention forward ([SA-Approach], [SA-Summary]), float64 out.
 
     Steps: mu and K_s (R1, R2); per-block INT8 codes of Q and K_s (R3, R4);
@@ -309,7 +288,7 @@ def int8_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, 
             if causal:
                 S[_causal_mask(rows, keys)] = -np.inf
             out[b, h] = online_softmax_pv(S, as_f64(v16[b, h]), kv_tile=kv_tile, round_p=round16,
-                                          ref_slack=ref_slack, sum_rounded=True)
+                                          sum_rounded=True)
     return out
 
 
@@ -332,13 +311,13 @@ def int8_quant_v_channels(v16):
 def int8_pv_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, blk_k: int,
                       kv_tile: int = 64, smooth: bool = True, rows=None, quant=None,
                       flip_delta: float | None = None):
-    """The INT8 P,V variant ([SA-Effects]: "Quantize P,V to INT8 rather than
-    retaining FP16"; [SA-Approach]: the faster kernel chosen per layer where
+    """The INT8 P,V variant ([SA-Effects]: the ablation with P and V in INT8
+    instead of FP16; [SA-Approach]: the faster kernel chosen per layer where
     cosine similarity stays above 99.8%), float64 out.
 
     Q and K_s as in int8_attention (R1-R5; blk_q = blk_k = 1 is the per-token
-    form). V: per-channel INT8 (R14). Online softmax against the plain running
-    max (R6 with slack 0), P quantized to rint(127 P) / 127 (R14); l sums the
+    form). V: per-channel INT8 (R14). Online softmax against the running max
+    (R6), P quantized to rint(127 P) / 127 (R14); l sums the
     quantized P; O accumulates quantized P times dequantized V.
     Returns float64 [B, H, len(rows), d].
 
@@ -348,9 +327,7 @@ def int8_pv_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: in
     is also quantized after scaling by (1 -+ flip_delta) (never above 1, the
     largest P: its code is 127 either way) and the function returns
     (O, allowance) with the first-order bound of online_softmax_pv on what
-    such flips can change. The allowance also covers an integer accumulator of
-    sum(code_P * code_V) (one unit = s_v / 127 of l * O in channel c) that is
-    rounded back to an integer when the running max moves (rescale_quantum).
+    such flips can change.
     """
     B, H, N, d = q16.shape
     rows = np.arange(N) if rows is None else np.asarray(rows)
@@ -373,9 +350,8 @@ def int8_pv_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: in
             if causal:
                 S[_causal_mask(rows, keys)] = -np.inf
             Vh = vc[b, h].astype(np.float64) * vs[b, h].astype(np.float64)[None, :]
-            quantum = vs[b, h].astype(np.float64) / 127.0 if alts is not None else None
-            r = online_softmax_pv(S, Vh, kv_tile=kv_tile, round_p=round127, ref_slack=0.0,
-                                  sum_rounded=True, p_alternatives=alts, rescale_quantum=quantum)
+            r = online_softmax_pv(S, Vh, kv_tile=kv_tile, round_p=round127, sum_rounded=True,
+                                  p_alternatives=alts)
             if alts is not None:
                 out[b, h], allow[b, h] = r
             else:
@@ -383,8 +359,7 @@ def int8_pv_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: in
     return (out, allow) if alts is not None else out
 
 
-def fp16_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: int = 64, rows=None,
-                   ref_slack: float = REF_SLACK):
+def fp16_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: int = 64, rows=None):
     """Unquantized FlashAttention-style forward, the baseline the method is
     measured against ([SA-Setup]: the kernels build on FlashAttention-2's
     tiled online softmax; [SA-Summary]: the speedup is quoted over it).
@@ -405,7 +380,7 @@ def fp16_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: int
             if causal:
                 S[_causal_mask(rows, keys)] = -np.inf
             out[b, h] = online_softmax_pv(S, as_f64(v16[b, h]), kv_tile=kv_tile, round_p=round16,
-                                          ref_slack=ref_slack, sum_rounded=True)
+                                          sum_rounded=True)
     return out
 
 
@@ -567,7 +542,7 @@ def quant_mxfp4(q16, k16, v16, *, smooth: bool = True, v_fp8: bool = False):
 
 def mxfp4_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: int = 64,
                     smooth: bool = True, rows=None, quant=None, quantize_p: bool = True,
-                    ref_slack: float = REF_SLACK, pv_fp8: bool = False, flip_delta: float | None = None):
+                    pv_fp8: bool = False, flip_delta: float | None = None):
     """Emulated microscaled-FP4 attention ([SA3-Abstract] with the MX format, reading R8).
 
     Q, K_s, V and the softmax P are MXFP4 (with pv_fp8, P and V are MX-FP8
@@ -602,7 +577,7 @@ def mxfp4_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: in
             return P
     alts = None
     if flip_delta is not None and quantize_p:
-        # a P of exactly 1 is the reference score itself; an implementation that
+        # a P of exactly 1 is the row's running max itself; an implementation that
         # rounds its reference down keeps that P >= 1, so it only moves up
         alts = lambda P: [round_p(np.where(P == 1.0, P, P * (1.0 - flip_delta))), round_p(P * (1.0 + flip_delta))]
     allow = np.zeros_like(out) if alts is not None else None
@@ -612,7 +587,7 @@ def mxfp4_attention(q16, k16, v16, *, causal: bool, sm_scale: float, kv_tile: in
             if causal:
                 S[_causal_mask(rows, keys)] = -np.inf
             r = online_softmax_pv(S, qd["v_vals"][b, h], kv_tile=kv_tile, round_p=round_p,
-                                  ref_slack=ref_slack, sum_rounded=True, p_alternatives=alts)
+                                  sum_rounded=True, p_alternatives=alts)
             if alts is not None:
                 out[b, h], allow[b, h] = r
             else:

@@ -519,23 +519,24 @@ def test_oracle_regression_fixture():
     assert mg.build() == stored
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_reference_max_slack_only_moves_rounding(causal):
-    # Softmax is invariant to the reference point: without P rounding, any slack gives the
-    # same output; with fp16 P, the slack only changes where P is rounded.
-    q, k, v = make_custom(1, 2, 300, 32, seed=21)
-    a = O.int8_attention(q, k, v, causal=causal, sm_scale=0.3, blk_q=64, blk_k=64, quantize=False, ref_slack=0.0)
-    b = O.int8_attention(q, k, v, causal=causal, sm_scale=0.3, blk_q=64, blk_k=64, quantize=False, ref_slack=8.0)
-    assert np.max(np.abs(a - b)) < 1e-12
-    c = O.int8_attention(q, k, v, causal=causal, sm_scale=0.3, blk_q=64, blk_k=64, ref_slack=0.0)
-    e = O.int8_attention(q, k, v, causal=causal, sm_scale=0.3, blk_q=64, blk_k=64, ref_slack=8.0)
-    assert 0 < np.max(np.abs(c - e)) < 2 ** -10 * np.abs(v.astype(float)).max()
-    # with slack 8 the reference max lags the running max by at most 8 (log2 units): P <= 2^8
-    S = np.array([[0.0, 1.0, 2.0, 3.0], [0.0, 0.0, 0.0, 10.0]]) * np.log(2.0)
-    V = np.eye(4)
+def test_online_softmax_forms_p_against_the_running_max():
+    # Reading R6: P of each tile is exp(S - m_t) with m_t the running max. Row 0 climbs
+    # (the max moves on every tile), row 1 has its max in the first tile, row 2 starts
+    # masked. The largest P handed to the rounding in a tile is exp(tile max - m_t): 1
+    # where the tile holds the running max, below 1 where it does not.
+    S = np.array([[0.0, 1.0, 2.0, 3.0, 2.5, 4.0],
+                  [5.0, 1.0, 2.0, 3.0, 2.5, 4.0],
+                  [-np.inf, -np.inf, 1.0, 0.5, -2.0, 0.0]])
+    V = np.arange(12, dtype=np.float64).reshape(6, 2)
     seen = []
-    O.online_softmax_pv(S, V, kv_tile=1, round_p=lambda P: (seen.append(P.max()), P)[1], ref_slack=8.0)
-    assert abs(max(seen) - 8.0) < 1e-12   # row 0: the reference stays at 0 while the max climbs to 3
+    got = O.online_softmax_pv(S, V, kv_tile=2, round_p=lambda P: (seen.append(P.copy()), P)[1])
+    want_max = [[1.0, 1.0, 1.0], [1.0, math.exp(3.0 - 5.0), math.exp(4.0 - 5.0)], [0.0, 1.0, math.exp(0.0 - 1.0)]]
+    for t, P in enumerate(seen):
+        for r in range(3):
+            assert abs(P[r].max() - want_max[r][t]) < 1e-15
+    assert abs(seen[1][0, 0] - math.exp(2.0 - 3.0)) < 1e-15          # tile 1 of row 0: against m = 3
+    ex = np.exp(S - S.max(axis=1, keepdims=True))
+    assert np.max(np.abs(got - (ex @ V) / ex.sum(axis=1, keepdims=True))) < 1e-13
 
 
 # ---------------------------------------------------------------------------
@@ -635,12 +636,12 @@ def test_int8_pv_running_max_moves_the_weights():
     # tile 0 weight round(127) = 127, tile 1 weight 127 and tile 0 becomes 127 e^-3.
     S = np.array([[0.0, 3.0]])
     V = np.array([[1.0], [0.0]])
-    got = O.online_softmax_pv(S, V, kv_tile=1, round_p=lambda P: np.rint(127.0 * P) / 127.0, ref_slack=0.0,
+    got = O.online_softmax_pv(S, V, kv_tile=1, round_p=lambda P: np.rint(127.0 * P) / 127.0,
                               sum_rounded=True)
     w0 = 127 * math.exp(-3.0)
     assert abs(got[0, 0] - w0 / (w0 + 127)) < 1e-15
     # single-tile form of the same row: weights against the final max, round(127 e^-3) = 6
-    one = O.online_softmax_pv(S, V, kv_tile=2, round_p=lambda P: np.rint(127.0 * P) / 127.0, ref_slack=0.0,
+    one = O.online_softmax_pv(S, V, kv_tile=2, round_p=lambda P: np.rint(127.0 * P) / 127.0,
                               sum_rounded=True)
     assert abs(one[0, 0] - 6 / 133) < 1e-15
 
@@ -657,7 +658,7 @@ def test_int8_pv_constant_v_and_weights_in_range():
     S = np.array([[0.0, -0.001, -5.0, -0.5, 2.0, 1.9999]])
     O.online_softmax_pv(S, np.ones((6, 1)), kv_tile=2,
                         round_p=lambda P: (seen.append(np.rint(127.0 * P)), np.rint(127.0 * P) / 127.0)[1],
-                        ref_slack=0.0, sum_rounded=True)
+                        sum_rounded=True)
     w = np.concatenate(seen, axis=1)
     assert w.min() >= 0 and w.max() == 127 and np.all(w == np.rint(w))
 
@@ -753,9 +754,9 @@ def test_int8_p_flip_allowance_covers_a_code_on_a_half_integer():
     round127 = lambda P: np.rint(127.0 * P) / 127.0
     delta = 2.0 ** -16
     alts = lambda P: [round127(P * (1 - delta)), round127(np.minimum(P * (1 + delta), 1.0))]
-    out, allow = O.online_softmax_pv(S, V, kv_tile=64, round_p=round127, sum_rounded=True, ref_slack=0.0,
+    out, allow = O.online_softmax_pv(S, V, kv_tile=64, round_p=round127, sum_rounded=True,
                                      p_alternatives=alts)
-    base = O.online_softmax_pv(S, V, kv_tile=64, round_p=round127, sum_rounded=True, ref_slack=0.0)
+    base = O.online_softmax_pv(S, V, kv_tile=64, round_p=round127, sum_rounded=True)
     assert np.array_equal(out, base)
     c1 = round127(np.exp(S))[0, 1] * 127
     assert c1 in (63.0, 64.0)
@@ -764,7 +765,7 @@ def test_int8_p_flip_allowance_covers_a_code_on_a_half_integer():
         Q = round127(P)
         Q[0, 1] = (127.0 - c1) / 127.0   # 63 <-> 64
         return Q
-    flipped = O.online_softmax_pv(S, V, kv_tile=64, round_p=forced, sum_rounded=True, ref_slack=0.0)
+    flipped = O.online_softmax_pv(S, V, kv_tile=64, round_p=forced, sum_rounded=True)
     assert np.all(np.abs(flipped[0] - out[0]) <= allow[0] * (1 + 1e-12))
     assert np.all(allow[0] > 0) and np.all(allow[1] == 0)
     assert np.max(np.abs(flipped[0] - out[0])) > 0.2 * np.max(allow[0])   # the bound is not vacuous
@@ -779,57 +780,6 @@ def test_int8_pv_attention_with_flip_delta_keeps_its_output():
     # a wider window catches more codes, never fewer
     _, wide = O.int8_pv_attention(q, k, v, causal=True, sm_scale=0.3, blk_q=64, blk_k=64, flip_delta=0.02)
     assert np.all(wide >= allow) and np.count_nonzero(wide.max(axis=-1)) > 0
-
-
-def _int_accumulator_pv(S, vcodes, vscale, tile):
-    """An INT8 P.V implementation with an integer accumulator of code_P * code_V that is
-    rescaled and rounded back to an integer whenever the running max moves (written
-    here independently of the oracle's online_softmax_pv)."""
-    R, N = S.shape
-    out = np.zeros((R, vcodes.shape[1]))
-    for r in range(R):
-        m, acc, lsum = -np.inf, np.zeros(vcodes.shape[1]), 0.0
-        for t0 in range(0, N, tile):
-            st = S[r, t0:t0 + tile]
-            mn = max(m, st.max())
-            if np.isfinite(m) and mn > m:
-                a = math.exp(m - mn)
-                acc = np.rint(acc * a)
-                lsum = lsum * a
-            codes = np.rint(127.0 * np.exp(st - mn))
-            acc = acc + codes @ vcodes[t0:t0 + tile]
-            lsum += codes.sum()
-            m = mn
-        out[r] = acc * vscale / lsum
-    return out
-
-
-def test_int8_pv_rescale_allowance_covers_an_integer_accumulator():
-    # Row 0: the max moves by 3 log2 units on every tile and channel 0 of V has one
-    # nonzero code (key 0), so the integer sum 127 * 1 is scaled by 1/8 per tile and
-    # rounded until it vanishes (the exact result is tiny but not 0). Row 1: one move
-    # by 1 log2 unit turns the sum 127 into 63.5, rounded by half a unit, the most
-    # one move can do. Row 2: random scores. The allowance of int8_pv_attention's
-    # tolerance path must cover all three and be reached on row 1.
-    rng = np.random.default_rng(43)
-    tile, N = 16, 96
-    S = np.full((3, N), -60.0)
-    S[0] = np.repeat(np.arange(N // tile) * 3 * math.log(2.0), tile) + rng.uniform(-0.3, 0.0, N)
-    S[1, 0] = 0.0
-    S[1, tile] = math.log(2.0)
-    S[2] = rng.standard_normal(N) * 2
-    vcodes = rng.integers(-127, 128, size=(N, 3)).astype(np.float64)
-    vcodes[:, 0] = 0
-    vcodes[0, 0] = 1
-    vscale = np.array([0.4, 0.01, 0.02])
-    V = vcodes * vscale[None, :]
-    round127 = lambda P: np.rint(127.0 * P) / 127.0
-    exact, allow = O.online_softmax_pv(S, V, kv_tile=tile, round_p=round127, sum_rounded=True, ref_slack=0.0,
-                                       rescale_quantum=vscale / 127.0)
-    impl = _int_accumulator_pv(S, vcodes, vscale, tile)
-    assert impl[0, 0] == 0.0 and exact[0, 0] != 0.0
-    assert np.all(np.abs(impl - exact) <= allow * (1 + 1e-12))
-    assert np.abs(impl[1, 0] - exact[1, 0]) > 0.99 * allow[1, 0]   # the bound is reached
 
 
 def test_flip_allowance_covers_a_p_code_on_a_rounding_boundary():
@@ -848,9 +798,8 @@ def test_flip_allowance_covers_a_p_code_on_a_rounding_boundary():
     delta = 2.0 ** -16
     # as mxfp4_attention builds them: the reference P of exactly 1 only moves up
     alts = lambda P: [quant(np.where(P == 1.0, P, P * (1 - delta))), quant(P * (1 + delta))]
-    out, allow = O.online_softmax_pv(S, V, kv_tile=32, round_p=quant, sum_rounded=True, p_alternatives=alts,
-                                     ref_slack=0.0)
-    base = O.online_softmax_pv(S, V, kv_tile=32, round_p=quant, sum_rounded=True, ref_slack=0.0)
+    out, allow = O.online_softmax_pv(S, V, kv_tile=32, round_p=quant, sum_rounded=True, p_alternatives=alts)
+    base = O.online_softmax_pv(S, V, kv_tile=32, round_p=quant, sum_rounded=True)
     assert np.array_equal(out, base)
     p1 = quant(np.exp(S))[0, 1]
     other = 0.75 if p1 == 0.5 else 0.5
@@ -860,7 +809,77 @@ def test_flip_allowance_covers_a_p_code_on_a_rounding_boundary():
         Q = quant(P)
         Q[0, 1] = other
         return Q
-    flipped = O.online_softmax_pv(S, V, kv_tile=32, round_p=forced, sum_rounded=True, ref_slack=0.0)
+    flipped = O.online_softmax_pv(S, V, kv_tile=32, round_p=forced, sum_rounded=True)
     assert np.all(np.abs(flipped[0] - out[0]) <= allow[0] * (1 + 1e-12))
     assert np.all(allow[0] > 0) and np.all(allow[1] == 0)
     assert np.max(np.abs(flipped[0] - out[0])) > 0.2 * np.max(allow[0])   # the bound is not vacuous
+
+
+def _mx_block_py(xs, fp8):
+    """One MX block of nonnegative values in plain Python (reading R8 / R13): shared
+    exponent e = floor(log2 max) - 2 (E2M1) or - 8 (E4M3) from frexp; each value goes
+    to the nearest grid magnitude of x * 2^-e, a tie to the even code; the grid's top
+    value is where larger ones saturate."""
+    import bisect
+    if fp8:
+        grid = [(c & 7) * 2.0 ** -9 if c >> 3 == 0 else (8 + (c & 7)) * 2.0 ** ((c >> 3) - 10) for c in range(0x7F)]
+    else:
+        grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    a = max(xs)
+    if a == 0.0:
+        return [0.0] * len(xs)
+    e = max(min(math.frexp(a)[1] - 1 - (8 if fp8 else 2), 127), -127)
+    out = []
+    for x in xs:
+        y = x * 2.0 ** -e
+        i = bisect.bisect_left(grid, y)
+        if i == len(grid):
+            c = len(grid) - 1
+        elif i == 0 or grid[i] == y:
+            c = i
+        else:
+            dl, dh = y - grid[i - 1], grid[i] - y
+            c = i - 1 if (dl < dh or (dl == dh and (i - 1) % 2 == 0)) else i
+        out.append(grid[c] * 2.0 ** e)
+    return out
+
+
+@pytest.mark.parametrize("causal,fp8", [(False, False), (True, False), (False, True), (True, True)])
+def test_mxfp4_p_quantization_matches_python_loops(causal, fp8):
+    # The MXFP4 path's P quantization (R6, R8, R13) written as plain loops: for each query
+    # row, 64-key tiles in order (the last one ragged: 150 = 2 * 64 + 22), the running max,
+    # P = exp(S - m) with masked and missing keys at 0, one MX block per 32 keys of the tile,
+    # l and O summing the quantized P. Scores come from the separately pinned MX codecs of
+    # Q, K_s and V; everything after them is independent of the oracle's own code.
+    q, k, v = make_custom(1, 1, 150, 64, seed=38, k_offset_std=1.0)
+    sm = 0.3
+    got = O.mxfp4_attention(q, k, v, causal=causal, sm_scale=sm, pv_fp8=fp8)
+    d = O.quant_mxfp4(q, k, v, v_fp8=fp8)
+    qv, kv, vv = d["q_vals"][0, 0], d["k_vals"][0, 0], d["v_vals"][0, 0]
+    N, D = 150, 64
+    moved = 0
+    for i in range(N):
+        m, lsum, acc = -math.inf, 0.0, [0.0] * D
+        for t0 in range(0, N, 64):
+            S = []
+            for j in range(t0, t0 + 64):
+                if j >= N or (causal and j > i):
+                    S.append(-math.inf)
+                else:
+                    S.append(math.fsum(float(qv[i, c]) * float(kv[j, c]) for c in range(D)) * sm)
+            mt = max(m, max(S))
+            if mt > m:
+                f = math.exp(m - mt) if m > -math.inf else 0.0
+                lsum, acc = lsum * f, [x * f for x in acc]
+                moved += m > -math.inf
+                m = mt
+            P = [math.exp(s - m) if s > -math.inf else 0.0 for s in S]
+            Pq = _mx_block_py(P[:32], fp8) + _mx_block_py(P[32:], fp8)
+            for jj, w in enumerate(Pq):
+                if w:
+                    lsum += w
+                    for c in range(D):
+                        acc[c] += w * float(vv[t0 + jj, c])
+        want = [x / lsum for x in acc]
+        assert max(abs(got[0, 0, i, c] - want[c]) for c in range(D)) < 1e-12, i
+    assert moved > 20      # the running max really moves between tiles

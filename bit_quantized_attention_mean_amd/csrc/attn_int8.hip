@@ -46,9 +46,13 @@
 //     the integer round(127 P) in one v_cvt_pk_u8_f32 per value, and O^T
 //     accumulates exactly in int32 on v_mfma_i32_32x32x32_i8 (half the matrix
 //     ops of the FP16 form). There is no INT8 matrix op with a float
-//     accumulator, so when a row max moves the int32 accumulator is rescaled
-//     by alpha through fp32 and rounded back; the row sum adds the integer
-//     weights on v_dot4_i32_i8, and the epilogue applies the channel scales.
+//     accumulator, and an int32 sum cannot be rescaled by alpha without
+//     rounding; so the int32 sum only ever holds weights formed against one
+//     reference max, and when a row max moves it is flushed into an fp32 O^T
+//     kept against a fixed per-row reference m0 (O_f += float(sum) *
+//     2^(m_old - m0)), the next P.V starting a fresh int32 sum. The row sum
+//     adds the integer weights on v_dot4_i32_i8, and the epilogue combines
+//     the two accumulators and applies the channel scales.
 #include "sage_internal.h"
 
 #include <limits.h>
@@ -58,19 +62,16 @@ namespace sage {
 
 namespace {
 
-// The softmax reference max of a row moves only when a tile's row max exceeds
-// it by more than this (log2 units), so P <= 2^8 and the O rescale is skipped
-// on most tiles; the result is the same softmax, rounded at a different point.
-// The INT8 P.V variant needs P <= 1 for its fixed 1/127 scale and follows the
-// running max exactly (slack 0).
+// The fp16-P kernels move a row's softmax reference max only when a tile's row
+// max exceeds it by more than this (log2 units), so P <= 2^8 and the O rescale
+// is skipped on most tiles: the same softmax, with P rounded to fp16 at a point
+// a power of at most 2^8 away from the running max's (a relative difference of
+// at most half an fp16 ulp per weight). The INT8 P.V variant forms P against
+// the running max exactly (slack 0): its weights round(127 P) are the method's.
 constexpr float kRefSlack = 8.0f;
-// The integer nearest x (|x| < 2^31), ties upwards: one v_cvt_rpi_i32_f32
-// (floor(x + 1/2)); the compiler's own rounding takes four instructions.
-__device__ __forceinline__ int round_half_up(float x) {
-  int r;
-  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
-  return r;
-}
+// INT8 P.V: the fp32 accumulator's reference m0 is moved up to the current
+// one when the factor 2^(m - m0) would exceed 2^kRebase (fp32 range guard).
+constexpr float kRebase = 32.0f;
 
 // Two of gfx950's transposing LDS reads (ds_read_b64_tr_b16), at p and at
 // p + stride, as one 8-value fp16 operand.
@@ -313,6 +314,14 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[c][i] = 0.f;
   float m = -INFINITY, l = 0.f, alpha = 1.f;
+  // INT8 P.V: fp32 O^T against reference m0 (of), and the reference under
+  // which the int32 sum in o was accumulated (mpv)
+  v16f of[PV8 ? NC : 1];
+#pragma unroll
+  for (int c = 0; c < (PV8 ? NC : 1); ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) of[c][i] = 0.f;
+  float m0 = 0.f, mpv = -INFINITY;
   v16i s[2];
   v8h pf[4];   // fp16 P, keys g*32 + c*8 .. +7 in pf[c]
   v4i pq[2];   // INT8 form: round(127 P), keys g*32 + u*16 .. +15 in pq[u]
@@ -393,24 +402,15 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   // O^T = alpha * O^T + V^T P^T from the V buffer VB_ (FP16 MFMA, FP32
   // accumulation). The rescale by the last softmax's alpha is done here, in the
   // matrix phase, so the softmax phase never touches the O registers. In the
-  // INT8 form O^T holds int32 sums (in the same registers): the rescale goes
-  // through fp32 and rounds back to the nearest integer, and each 32-channel
-  // tile takes two INT8 matrix ops (32 keys each) instead of four.
+  // INT8 form O^T holds int32 sums (in the same registers), each 32-channel
+  // tile takes two INT8 matrix ops (32 keys each) instead of four, and a moved
+  // max flushes the int32 sums into the fp32 accumulator (of) instead of
+  // rescaling them: the first matrix op of each tile then starts from zero.
 #define SAGE_VA(VB_, DT_, C_)                                                                    \
   (VRM ? lds_read_tr_v8h(smem + (VB_) + va + (C_) * 8 * VROW + (DT_) * 64, 4 * VROW)             \
        : *reinterpret_cast<const v8h*>(smem + (VB_) + va + (DT_) * 32 * VROW + (C_) * 16))
-#define SAGE_PV(VB_)                                                                             \
+#define SAGE_PV_MMA(VB_, Z_)                                                                     \
   do {                                                                                           \
-    if (__ballot(alpha != 1.f)) {                                                                \
-      if (PV8) {                                                                                 \
-        _Pragma("unroll") for (int c = 0; c < NC; ++c)                                           \
-          _Pragma("unroll") for (int i = 0; i < 16; ++i)                                         \
-            o[c][i] = __int_as_float(round_half_up(static_cast<float>(__float_as_int(o[c][i])) * alpha)); \
-      } else {                                                                                   \
-        _Pragma("unroll") for (int c = 0; c < NC; ++c)                                           \
-          _Pragma("unroll") for (int i = 0; i < 16; ++i) o[c][i] *= alpha;                       \
-      }                                                                                          \
-    }                                                                                            \
     v8h va_[2][RPV];                                                                             \
     _Pragma("unroll") for (int c = 0; c < RPV; ++c)                                              \
       va_[0][c] = SAGE_VA(VB_, 0, c);                                                            \
@@ -419,11 +419,14 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
         _Pragma("unroll") for (int c = 0; c < RPV; ++c) va_[(dt + 1) & 1][c] = SAGE_VA(VB_, dt + 1, c); \
       }                                                                                          \
       _Pragma("unroll") for (int c = 0; c < RPV; ++c) {                                          \
-        if (PV8)                                                                                 \
+        if (PV8) {                                                                               \
+          const v16i z_ = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};                      \
           o[dt] = __builtin_bit_cast(v16f, __builtin_amdgcn_mfma_i32_32x32x32_i8(                \
-                      __builtin_bit_cast(v4i, va_[dt & 1][c]), pq[c], __builtin_bit_cast(v16i, o[dt]), 0, 0, 0)); \
-        else                                                                                     \
+                      __builtin_bit_cast(v4i, va_[dt & 1][c]), pq[c],                            \
+                      ((Z_) && c == 0) ? z_ : __builtin_bit_cast(v16i, o[dt]), 0, 0, 0));        \
+        } else {                                                                                 \
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va_[dt & 1][c], pf[c], o[dt], 0, 0, 0); \
+        }                                                                                        \
       }                                                                                          \
     }                                                                                            \
     __builtin_amdgcn_sched_group_barrier(0x100, RPV * VRD, 2);                                   \
@@ -432,6 +435,34 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
       __builtin_amdgcn_sched_group_barrier(0x100, VRD, 2);                                       \
     }                                                                                            \
     __builtin_amdgcn_sched_group_barrier(0x008, RPV, 2);                                         \
+  } while (0)
+#define SAGE_PV(VB_)                                                                             \
+  do {                                                                                           \
+    if (PV8) {                                                                                   \
+      if (__ballot(alpha != 1.f)) {                                                              \
+        /* flush: of += float(int32 sum) * 2^(mpv - m0), moving m0 up to mpv */                 \
+        /* first if that factor would leave the fp32 range guard */                             \
+        if (__ballot(mpv - m0 > kRebase)) {                                                      \
+          const float r_ = (mpv - m0 > kRebase) ? __builtin_amdgcn_exp2f(m0 - mpv) : 1.f;        \
+          m0 = (mpv - m0 > kRebase) ? mpv : m0;                                                  \
+          _Pragma("unroll") for (int c = 0; c < NC; ++c)                                         \
+            _Pragma("unroll") for (int i = 0; i < 16; ++i) of[c][i] *= r_;                       \
+        }                                                                                        \
+        const float f_ = __builtin_amdgcn_exp2f(mpv - m0);                                       \
+        _Pragma("unroll") for (int c = 0; c < NC; ++c)                                           \
+          _Pragma("unroll") for (int i = 0; i < 16; ++i)                                         \
+            of[PV8 ? c : 0][i] = __builtin_fmaf(static_cast<float>(__float_as_int(o[c][i])), f_, of[PV8 ? c : 0][i]); \
+        _Pragma("unroll") for (int c = 0; c < NC; ++c)                                           \
+          _Pragma("unroll") for (int i = 0; i < 16; ++i) o[c][i] = 0.f;                          \
+      }                                                                                          \
+      SAGE_PV_MMA(VB_, false);                                                                   \
+    } else {                                                                                     \
+      if (__ballot(alpha != 1.f)) {                                                              \
+        _Pragma("unroll") for (int c = 0; c < NC; ++c)                                           \
+          _Pragma("unroll") for (int i = 0; i < 16; ++i) o[c][i] *= alpha;                       \
+      }                                                                                          \
+      SAGE_PV_MMA(VB_, false);                                                                   \
+    }                                                                                            \
   } while (0)
 
   // Softmax of key tile J_ on the scores in s: dequantize to base-2 logits,
@@ -593,6 +624,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
         }                                                                                        \
       l = l * alpha_ + (rs0_ + rs1_);                                                            \
     }                                                                                            \
+    mpv = m;                                                                                     \
     m = mnew_;                                                                                   \
     alpha = alpha_;                                                                              \
   } while (0)
@@ -669,6 +701,8 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
 #define SAGE_PERIODS(G_)                                                                         \
   do {                                                                                           \
     SAGE_PERIOD(0, KB0, KB1, VB0, VB1, true, false, G_);                                         \
+    /* INT8 P.V: the fp32 accumulator's reference is the first tile's max */                    \
+    m0 = m;                                                                                      \
     int jt = 1;                                                                                  \
     for (; jt + 1 < nkt; jt += 2) {                                                              \
       SAGE_PERIOD(jt, KB1, KB0, VB1, VB0, false, false, G_);                                     \
@@ -690,6 +724,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
 #undef SAGE_PACK_P8
 #undef SAGE_CAP_P8
 #undef SAGE_PV
+#undef SAGE_PV_MMA
 #undef SAGE_VA
 #undef SAGE_SCORES
 #undef SAGE_STORE_V
@@ -699,6 +734,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
 
   // epilogue: O = O^T / l, rows >= N are padding and are not stored
   const float inv = 1.f / pair_sum(l);
+  const float f0 = PV8 ? __builtin_amdgcn_exp2f(m0 - m) : 1.f;  // of's reference against the final max
   if (qrow < N) {
     _Float16* orow = out + (static_cast<size_t>(bh) * N + qrow) * D;
 #pragma unroll
@@ -707,12 +743,16 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
       for (int r = 0; r < 4; ++r) {
         v4h h;
         if (PV8) {
-          // int32 sums of weight * code; channel c's value is code * scale[c]
+          // sums of weight * code against the final max: the fp32 part (against
+          // m0) and the int32 part; channel c's value is code * scale[c]
           const float4 vs4 = *reinterpret_cast<const float4*>(vsc + static_cast<size_t>(bh) * D + dt * 32 + r * 8 + g * 4);
           const float vsv[4] = {vs4.x, vs4.y, vs4.z, vs4.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            h[i] = static_cast<_Float16>(static_cast<float>(__float_as_int(o[dt][r * 4 + i])) * (vsv[i] * inv));
+          for (int i = 0; i < 4; ++i) {
+            const float sum = __builtin_fmaf(of[PV8 ? dt : 0][r * 4 + i], f0,
+                                             static_cast<float>(__float_as_int(o[dt][r * 4 + i])));
+            h[i] = static_cast<_Float16>(sum * (vsv[i] * inv));
+          }
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(o[dt][r * 4 + i] * inv);

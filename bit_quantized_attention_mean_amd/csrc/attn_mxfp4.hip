@@ -24,9 +24,6 @@ namespace {
 
 typedef short v2s __attribute__((ext_vector_type(2)));
 
-// Reference-max slack of the online softmax (log2 units), as in the INT8 kernel.
-constexpr float kRefSlack4 = 8.0f;
-
 __device__ __forceinline__ int lds_row_of_key4(int k) {
   const int g = k >> 5, t = (k >> 4) & 1, i = k & 15;
   return t * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
@@ -265,7 +262,8 @@ _Pragma("unroll")                                                               
     /* largest score then gets P >= 1 (its exact value is 1), so the block */                       \
     /* exponent of P cannot drop a binade below the exact one */                                    \
     if (__builtin_fmaf(mxr, sl2, -mx) < 0.f) mx = below_ulp4(mx);                                   \
-    const bool need = mx > m + kRefSlack4;                                                          \
+    /* P is formed against the running max, so its MX codes are the method's */                    \
+    const bool need = mx > m;                                                                       \
     const float mnew = need ? mx : m;                                                               \
     const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;                              \
     const float nm = -mnew;                                                                         \

@@ -5,6 +5,11 @@ import numpy as np
 
 OUT_ATOL = 2e-3   # max-abs bar against the quantization-emulating oracle (unit-variance inputs)
 
+# One record per output comparison of this session: (what, elements compared, max
+# error, elements excused by the flip allowance, largest excess over the bar).
+# tests/conftest.py prints them at the end of the run, whatever pytest captured.
+RECORDS = []
+
 
 def half_ulp_f16(x: np.ndarray) -> np.ndarray:
     """Half the fp16 spacing at |x|: the kernel stores fp16, so this much is format resolution."""
@@ -36,6 +41,8 @@ def assert_output_parity(got: np.ndarray, ref: np.ndarray, atol: float = OUT_ATO
             f"(largest excess over the bar {used:.2e}; allowance capped at {atol:.0e})")
         bound = bound + extra
     bad = err > bound
+    RECORDS.append((what, err.size, float(err.max()) if err.size else 0.0,
+                    n_exc if extra is not None else 0, used if extra is not None else 0.0))
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} elements over tolerance; worst at {i}: got {got[i]!r} "

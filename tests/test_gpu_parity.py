@@ -401,3 +401,80 @@ def test_ragged_tail_reads_no_row_of_the_next_head(sa, mode, d):
     torch.cuda.synchronize()
     assert torch.isfinite(out[:, :1]).all()
     assert torch.equal(out[:, :1], alone)
+
+
+# Configurations and edge cases of the method run through sage_attn_fwd: K smoothing
+# off (the pages' smoothing ablation), per-token scales at d = 64 on heavy-tailed data
+# (the per-layer selector's choice there), Q blocks of 64 at d = 128, and the cases
+# where a quantization block is all zeros (scale 0, codes 0: a score of exactly 0).
+EDGE_CASES = [
+    # name, B, H, N, d, causal, mode, dist, edit
+    ("nosmooth-int8", 1, 2, 1000, 128, False, 0 | 0x100, "normal", None),
+    ("nosmooth-int8-causal", 1, 2, 777, 64, True, 0 | 0x100, "normal", None),
+    ("nosmooth-mxfp4", 1, 2, 1000, 128, False, 2 | 0x100, "normal", None),
+    ("nosmooth-mxfp4-causal", 1, 2, 333, 64, True, 2 | 0x100, "normal", None),
+    ("nosmooth-int8pv", 1, 2, 700, 128, False, 6 | 0x100, "normal", None),
+    ("pertoken-d64-t", 2, 2, 777, 64, False, 3, "student_t", None),
+    ("q64-d128", 1, 2, 1000, 128, False, 1, "normal", None),
+    ("q64-d128-causal", 1, 2, 700, 128, True, 1, "normal", None),
+    ("const-k-int8", 1, 2, 300, 64, False, 0, "normal", "const_k"),
+    ("const-k-int8-causal", 1, 2, 300, 128, True, 0, "normal", "const_k"),
+    ("const-k-mxfp4", 1, 2, 300, 128, False, 2, "normal", "const_k"),
+    ("const-k-int8pv", 1, 2, 300, 64, False, 6, "normal", "const_k"),
+    ("zero-q-int8", 1, 2, 300, 128, False, 0, "normal", "zero_q"),
+    ("zero-q-mxfp4", 1, 2, 300, 64, True, 2, "normal", "zero_q"),
+    ("zero-q-pertoken", 1, 2, 300, 64, False, 3, "normal", "zero_q"),
+    ("zero-blocks-int8", 1, 2, 700, 128, False, 0 | 0x100, "normal", "zero_blocks"),
+    ("zero-blocks-int8-causal", 1, 2, 700, 64, True, 1 | 0x100, "normal", "zero_blocks"),
+    ("zero-blocks-mxfp4", 1, 2, 700, 128, False, 2 | 0x100, "normal", "zero_blocks"),
+    ("zero-blocks-int8pv", 1, 2, 700, 128, True, 7 | 0x100, "normal", "zero_blocks"),
+]
+
+
+def _edit_inputs(q, k, v, edit):
+    if edit == "const_k":        # every token's K equal: smoothing makes K_s exactly 0
+        k[:] = k[:, :, :1, :]
+    elif edit == "zero_q":       # every score 0: uniform attention over the visible keys
+        q[:] = 0
+    elif edit == "zero_blocks":  # Q rows 128..255 and K rows 64..127 all zero (no smoothing)
+        q[:, :, 128:256] = 0
+        k[:, :, 64:128] = 0
+    return q, k, v
+
+
+def _oracle_for_mode(q, k, v, *, causal, sm, mode):
+    lo, smooth = mode & 0xFF, not (mode & 0x100)
+    if lo in (0, 1, 3):
+        bq, bk = _int8_blocks(lo)
+        return O.int8_attention(q, k, v, causal=causal, sm_scale=sm, blk_q=bq, blk_k=bk, smooth=smooth), None
+    if lo in (6, 7):
+        b = 1 if lo == 7 else None
+        return O.int8_pv_attention(q, k, v, causal=causal, sm_scale=sm, blk_q=b or 128, blk_k=b or 64,
+                                   smooth=smooth, flip_delta=FLIP_DELTA)
+    if lo in (2, 5):
+        return O.mxfp4_attention(q, k, v, causal=causal, sm_scale=sm, smooth=smooth, pv_fp8=lo == 5,
+                                 flip_delta=FLIP_DELTA)
+    raise ValueError(mode)
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=lambda c: c[0])
+def test_configuration_and_zero_block_edge_cases(sa, case):
+    name, B, H, N, d, causal, mode, dist, edit = case
+    say("edge case", case)
+    q, k, v = make_custom(B, H, N, d, seed=29 * N + d + (mode & 0xFF), dist=dist)
+    q, k, v = _edit_inputs(q, k, v, edit)
+    sm = 1.0 / np.sqrt(d)
+    ref, extra = _oracle_for_mode(q, k, v, causal=causal, sm=sm, mode=mode)
+    qd, kd, vd = _dev(q, k, v)
+    out = sa.sage_attn_fwd(qd, kd, vd, causal=causal, sm_scale=sm, mode=mode)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = assert_output_parity(got, ref, what=name, extra=extra)
+    if edit in ("const_k", "zero_q") and not causal:
+        # uniform weights: every output row is the plain mean of V (up to V's own codec)
+        vmean = v.astype(np.float64).mean(axis=2, keepdims=True)
+        tol = 2e-3 if (mode & 0xFF) in (0, 1, 3) else 0.3 * np.abs(v).max()
+        assert np.max(np.abs(got - vmean)) <= tol
+    ex = O.exact_attention(q, k, v, causal=causal, sm_scale=sm)
+    say(f"  max err vs oracle {err:.2e}; cos vs fp64 gpu {O.metrics(got, ex)['cos']:.6f} "
+        f"oracle {O.metrics(ref, ex)['cos']:.6f}")

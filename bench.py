@@ -5,10 +5,11 @@ V quantization, fused attention kernel) over one synthetic workload whose
 inputs are already resident in HBM. `value` is attention TOPS: 4*B*H*N^2*d
 per step (halved when causal) divided by the step time.
 
-Default workload: LLM prefill, B=4, H=32, N=4096, d=128, non-causal, INT8
-Q/K with Q scale blocks of 128 tokens and K blocks of 64, FP16 P.V.
---workload picks another: n16k (B=1, H=32, N=16384, d=128, the kernel
-throughput target shape), long_causal, video_dit, mxfp4, tiny.
+Default workload: n16k, B=1, H=32, N=16384, d=128, non-causal, INT8 Q/K
+with Q scale blocks of 128 tokens and K blocks of 64, FP16 P.V (the shape the
+kernel throughput target is set at). --workload picks another: prefill
+(B=4, H=32, N=4096, d=128, outlier K channels), long_causal, video_dit,
+mxfp4, tiny.
 
 Also on the JSON line:
   roofline      the fused attention kernel alone (sage_attn_compute), timed
@@ -20,8 +21,11 @@ Also on the JSON line:
                 same inputs (context for the quantized path's speedup; not
                 vs_baseline).
   cpu_baseline  the CPU oracle (oracle.int8_attention / mxfp4_attention in
-                float64) timed on a bounded sample of the same workload
-                (whole heads) on one host thread.
+                float64, as it stands) on the same workload, spread over every
+                host core available to the process (one worker process per
+                core, one BLAS thread each, blocks of query rows of whole
+                heads as work units), for a bounded wall time; run before the
+                GPU is touched. `cores` is the number of workers.
   median_ms_per_step  median of per-step times (separate pass, an event
                 between steps).
   shader_clock_mhz  the shader clock measured by a probe wave (cycle counter
@@ -39,6 +43,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -138,38 +144,74 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(name: str, mode_name: str, budget_s: float = 12.0):
-    """The oracle on whole heads of the workload until ~budget_s of CPU time (1 thread)."""
+_CPU = {}   # inputs shared with the forked oracle workers (copy-on-write)
+
+
+def _cpu_unit(unit):
+    """One work unit of the CPU baseline: the oracle on query rows r0:r1 of head (b, h)."""
+    import oracle as O
+    from synthetic import WORKLOADS
+
+    b, h, r0, r1 = unit
+    w, mode_name = WORKLOADS[_CPU["name"]], _CPU["mode"]
+    q, k, v = (x[b:b + 1, h:h + 1] for x in _CPU["qkv"])
+    rows = np.arange(r0, r1)
+    t0 = time.perf_counter()
+    if mode_name in ("mxfp4", "mxfp4_fp8pv"):
+        O.mxfp4_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, rows=rows, pv_fp8=mode_name == "mxfp4_fp8pv")
+    elif mode_name == "fp16":
+        O.fp16_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, rows=rows)
+    elif mode_name in ("int8_pv", "int8_pv_per_token"):
+        bl = 1 if mode_name == "int8_pv_per_token" else None
+        O.int8_pv_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, blk_q=bl or 128, blk_k=bl or 64, rows=rows)
+    else:
+        bq, bk = {"int8_q128_k64": (128, 64), "int8_q64_k64": (64, 64), "int8_per_token": (1, 1)}[mode_name]
+        O.int8_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, blk_q=bq, blk_k=bk, rows=rows)
+    # ops by the metric's convention: 4 d per visible (query, key) pair
+    pairs = (np.minimum(rows + 1, w.N).sum() if w.causal else rows.size * w.N)
+    return 4.0 * w.d * float(pairs), time.perf_counter() - t0
+
+
+def cpu_baseline(name: str, mode_name: str, budget_s: float = 20.0):
+    """The oracle on the workload, one forked worker per available host core.
+
+    Work units are blocks of query rows of one head (rows are independent given
+    the head's keys; each unit quantizes its head and runs the tiled fp64
+    emulation on its rows). Units are handed out in a seeded shuffled order
+    until `budget_s` of wall time has passed; the value is the metric's ops of
+    the finished units over the wall time. Must run before the process touches
+    the GPU (the workers are plain forks)."""
+    import multiprocessing as mp
     from threadpoolctl import threadpool_limits
 
-    import oracle as O
     from synthetic import WORKLOADS, make_inputs
 
     w = WORKLOADS[name]
-    ops = 0.0
-    t_total = 0.0
-    heads = 0
+    cores = len(os.sched_getaffinity(0))
+    _CPU.update(name=name, mode=mode_name, qkv=make_inputs(name))
+    rb = min(w.N, 512)
+    units = [(b, h, r0, min(r0 + rb, w.N)) for b in range(w.B) for h in range(w.H) for r0 in range(0, w.N, rb)]
+    np.random.default_rng(0).shuffle(units)
+    ops, busy, done = 0.0, 0.0, 0
     with threadpool_limits(limits=1):
-        while t_total < budget_s and heads < w.B * w.H:
-            q, k, v = make_inputs(name, B=1, H=1, seed=1000 + heads)   # one head, same recipe
-            t0 = time.perf_counter()
-            if mode_name in ("mxfp4", "mxfp4_fp8pv"):
-                O.mxfp4_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, pv_fp8=mode_name == "mxfp4_fp8pv")
-            elif mode_name == "fp16":
-                O.fp16_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale)
-            elif mode_name in ("int8_pv", "int8_pv_per_token"):
-                b = 1 if mode_name == "int8_pv_per_token" else None
-                O.int8_pv_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, blk_q=b or 128, blk_k=b or 64)
-            else:
-                bq, bk = {"int8_q128_k64": (128, 64), "int8_q64_k64": (64, 64), "int8_per_token": (1, 1)}[mode_name]
-                O.int8_attention(q, k, v, causal=w.causal, sm_scale=w.sm_scale, blk_q=bq, blk_k=bk)
-            t_total += time.perf_counter() - t0
-            ops += 4.0 * w.N * w.N * w.d / (2 if w.causal else 1)
-            heads += 1
-    return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "cpu_model": cpu_model(), "host_cores_available": len(os.sched_getaffinity(0)),
-            "sample": f"{heads} whole head(s) of the {name} workload (N={w.N}, d={w.d}): "
-                      f"quantization + tiled fp64 emulation, {t_total:.1f} s on 1 thread"}
+        ctx = mp.get_context("fork")
+        t0 = time.perf_counter()
+        with ctx.Pool(cores) as pool:
+            for o, t in pool.imap_unordered(_cpu_unit, units, chunksize=1):
+                ops += o
+                busy += t
+                done += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            wall = time.perf_counter() - t0
+            pool.terminate()
+    _CPU.clear()
+    return {"value": ops / wall / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cores_available": cores,
+            "sample": f"{done} of {len(units)} work units (blocks of {rb} query rows of one head) of the {name} "
+                      f"workload (B={w.B}, H={w.H}, N={w.N}, d={w.d}, mode {mode_name}): per-head quantization + "
+                      f"tiled fp64 emulation, {wall:.1f} s wall on {cores} worker processes "
+                      f"({busy:.1f} s of worker time), ops of the finished units / wall time"}
 
 
 def select_layers(names, torch, sa):
@@ -196,7 +238,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--workload", default="n16k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sdpa", action="store_true", help="skip timing torch's FP16 SDPA for context")
     ap.add_argument("--mode", default=None,
@@ -230,8 +272,19 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}), flush=True)
         return
 
-    import bit_quantized_attention_mean_amd as sa
     from synthetic import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    mode_name = args.mode or w.mode
+    # the CPU oracle baseline first: its workers are forks of this process, which
+    # has neither touched the GPU nor loaded the HIP library yet
+    cpu = None
+    if not args.no_cpu and args.select is None:
+        log(f"[bench] timing the CPU oracle on {len(os.sched_getaffinity(0))} host cores ...")
+        cpu = cpu_baseline(w.name, mode_name)
+        log(f"[bench] cpu oracle: {cpu['value']:.3e} TOPS ({cpu['sample']})")
+
+    import bit_quantized_attention_mean_amd as sa
 
     if args.select is not None:
         select_layers(args.select or ["tiny", "prefill", "long_causal", "video_dit", "n16k"], torch, sa)
@@ -239,8 +292,6 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    w = WORKLOADS[args.workload]
-    mode_name = args.mode or w.mode
     mode = {"int8_q128_k64": 0, "int8_q64_k64": 1, "mxfp4": 2, "int8_per_token": 3, "fp16": 4,
             "mxfp4_fp8pv": 5, "int8_pv": 6, "int8_pv_per_token": 7}[mode_name]
     flags = sa.SAGE_FLAG_NO_SMOOTH if args.no_smooth else 0
@@ -273,29 +324,38 @@ def main():
     tops_step = ops / (ms_step * 1e-3) / 1e12
     tops_attn = ops / (ms_attn * 1e-3) / 1e12
     n_el = w.B * w.H * w.N * w.d
+    smooth = not args.no_smooth
+    # Algorithmic bytes of the prepare phase: each tensor it quantizes is read once
+    # (2 B per element) and its codes written once, plus the scales; K's second read
+    # (the channel-mean pass) and V's (the INT8 V channel maxima) are not counted,
+    # they are reported separately as `quant_phase_rereads_bytes`.
+    n_rows = w.B * w.H * w.N
     if mode in (2, 5):
-        # read K (mean), Q, K, V (2 B each); write packed codes (0.5 B) + exponents (1/32 B)
-        # for Q and K, and for V 0.5 B (E2M1) or 1 B (E4M3) + exponents
-        quant_bytes = n_el * 8 + 2 * n_el * (0.5 + 1 / 32) + n_el * ((1.0 if mode == 5 else 0.5) + 1 / 32)
+        # Q, K, V: 2 B read; E2M1 codes 0.5 B (V in mode 5: E4M3, 1 B) + one E8M0 byte per 32 elements
+        quant_bytes = 3 * n_el * 2 + 2 * n_el * (0.5 + 1 / 32) + n_el * ((1.0 if mode == 5 else 0.5) + 1 / 32)
+        rereads = n_el * 2 if smooth else 0
         # mode 5: half the work (Q K^T) on FP4, half (P V) on FP8
         peak = PEAK["mxfp4"] if mode == 2 else round(2 / (1 / PEAK["mxfp4"] + 1 / PEAK["fp8"]), 1)
         kernel = f"attn_mxfp4_kernel<{w.d},{str(w.causal).lower()},{str(mode == 5).lower()}>"
         src = "attn_mxfp4.hip"
     elif mode == 4:
         # unquantized baseline: nothing to prepare (the kernel reads Q, K, V as given)
-        quant_bytes = 0
+        quant_bytes, rereads = 0, 0
         peak, src = PEAK["fp16"], "attn_int8.hip"
         kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},2,false>"
-    elif mode in (6, 7):
-        # read K (mean), Q, K, V (channel maxima), V (codes) (2 B each); write Q/K/V^T codes (1 B each)
-        quant_bytes = n_el * 10 + n_el * 3
-        peak, src = PEAK["int8"], "attn_int8.hip"
-        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},{1 if mode == 7 else 0},true>"
     else:
-        # read K (mean), Q, K (2 B each); write Q/K codes (1 B each); V is read as given by the kernel
-        quant_bytes = n_el * 6 + n_el * 2
+        qblk = 1 if mode in (3, 7) else (64 if mode == 1 else 128)
+        kblk = 1 if mode in (3, 7) else 64
+        # Q and K: 2 B read + 1 B code per element, 4 B per scale
+        quant_bytes = n_el * 6 + 4 * (n_rows // qblk + n_rows // kblk)
+        rereads = n_el * 2 if smooth else 0
+        if mode in (6, 7):
+            # V: 2 B read + 1 B code per element, one 4 B scale per channel; the
+            # channel-maxima pass reads V a second time
+            quant_bytes += n_el * 3 + 4 * w.B * w.H * w.d
+            rereads += n_el * 2
         peak, src = PEAK["int8"], "attn_int8.hip"
-        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},{1 if mode == 3 else 0},false>"
+        kernel = f"attn_int8_kernel<{w.d},{str(w.causal).lower()},{1 if mode in (3, 7) else 0},{str(mode in (6, 7)).lower()}>"
     roofline = {"bound": "mfma", "achieved": round(tops_attn, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tops_attn / peak, 4),
                 "traffic": load_traffic(f"{src[:-4]}_{w.name}", src) if (mode_name == w.mode and not flags) else None,
@@ -318,11 +378,6 @@ def main():
     del qd, kd, vd, ws, out
     torch.cuda.empty_cache()
 
-    cpu = None
-    if not args.no_cpu:
-        log("[bench] timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(w.name, mode_name)
-        log(f"[bench] cpu oracle: {cpu['value']:.3e} TOPS")
 
     line = {
         "metric": "attention TOPS (4*B*H*N^2*d per step / step time, halved if causal)",
@@ -344,6 +399,8 @@ def main():
         "attn_kernel_tops": round(tops_attn, 2),
         "quant_phase_ms": round(ms_prep, 4),
         "quant_phase_gbs": round(quant_bytes / (ms_prep * 1e-3) / 1e9, 1) if quant_bytes else None,
+        "quant_phase_bytes": int(quant_bytes),
+        "quant_phase_rereads_bytes": int(rereads),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "torch_sdpa_fp16": sdpa,

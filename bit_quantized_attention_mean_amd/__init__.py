@@ -7,6 +7,7 @@ built, importing this package raises ImportError; there is no fallback path.
 
 Functions carry the C names:
   sage_attn_fwd(q, k, v, ...)          -> out
+  sage_attn_fwd_noalloc(q, k, v, out, ...)  (no workspace: the library's per-device scratch)
   sage_attn_prepare / sage_attn_compute  (the two phases of sage_attn_fwd)
   sage_attn_workspace_size(B, H, N, d, mode)
   sage_quant_qk(q, k, blk_q, blk_k, flags)  -> dict of codes/scales/mean
@@ -24,7 +25,7 @@ __all__ = [
     "SAGE_MODE_INT8_Q128_K64", "SAGE_MODE_INT8_Q64_K64", "SAGE_MODE_MXFP4", "SAGE_MODE_INT8_PER_TOKEN",
     "SAGE_MODE_FP16", "SAGE_MODE_MXFP4_FP8PV", "SAGE_MODE_INT8_PV", "SAGE_MODE_INT8_PV_PER_TOKEN",
     "SAGE_FLAG_NO_SMOOTH", "SAGE_FLAG_FP8_V", "SageError", "LIB_PATH", "lib",
-    "sage_attn_fwd", "sage_attn_prepare", "sage_attn_compute", "sage_attn_workspace_size",
+    "sage_attn_fwd", "sage_attn_fwd_noalloc", "SAGE_NOALLOC_SCRATCH_BYTES", "sage_attn_prepare", "sage_attn_compute", "sage_attn_workspace_size",
     "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_quant_v_int8", "sage_attn_dump_scores", "sage_status_string", "sage_last_error",
     "sage_clock_probe", "sage_wall_clock_khz", "measure_clock_mhz",
     "EXPORTED_SYMBOLS",
@@ -40,6 +41,7 @@ SAGE_MODE_INT8_PV = 6
 SAGE_MODE_INT8_PV_PER_TOKEN = 7
 SAGE_FLAG_NO_SMOOTH = 0x100
 SAGE_FLAG_FP8_V = 0x200
+SAGE_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_attn.so")
 
@@ -50,6 +52,7 @@ _SIGS = {
     "sage_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "sage_quant_workspace_size": (_sz, [_i, _i, _i, _i]),
     "sage_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "sage_attn_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "sage_attn_prepare": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "sage_attn_compute": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "sage_quant_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -165,6 +168,23 @@ def sage_attn_fwd(q, k, v, out=None, *, causal=False, sm_scale=None, mode=SAGE_M
                            _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                            _stream(stream))
     _check(rc, "sage_attn_fwd")
+    return out
+
+
+def sage_attn_fwd_noalloc(q, k, v, out, *, causal=False, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64, stream=None):
+    """sage_attn_fwd with the library's own per-device scratch as workspace (the C entry
+    point allocates nothing; `out` must be given). Calls on one device share that scratch."""
+    torch = _torch()
+    B, H, N, d = _shape4(q)
+    for t, name in ((k, "k"), (v, "v"), (out, "out")):
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"q and {name} must have the same shape")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    rc = lib.sage_attn_fwd_noalloc(_dev_ptr(q, "q", torch.float16), _dev_ptr(k, "k", torch.float16),
+                                   _dev_ptr(v, "v", torch.float16), _dev_ptr(out, "out", torch.float16),
+                                   B, H, N, d, int(bool(causal)), float(sm_scale), int(mode), _stream(stream))
+    _check(rc, "sage_attn_fwd_noalloc")
     return out
 
 

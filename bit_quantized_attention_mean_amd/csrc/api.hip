@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "sage_attn.h"
 #include "sage_internal.h"
@@ -187,6 +188,37 @@ int do_compute(const void* q, const void* k, const void* v, void* out, int B, in
                     "INT8 attention kernel");
 }
 
+// Scratch of sage_attn_fwd_noalloc: the workspace of that entry point, a global
+// of this code object, so each device the library runs on holds its own copy
+// (allocated with the code object, kept until the process ends). Host code
+// never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, taken once per device on the first call there.
+static __device__ __align__(256) unsigned char scratch[SAGE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+int scratch_address(void** addr) {
+  int dev = -1;
+  SAGE_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SAGE_ERR_UNSUPPORTED, "device %d: the scratch table covers devices 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !a) {
+      (void)hipGetLastError();
+      return fail(SAGE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    }
+    g_scratch_addr[dev] = a;
+  }
+  *addr = g_scratch_addr[dev];
+  return SAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -260,6 +292,33 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
   const hipStream_t s = static_cast<hipStream_t>(stream);
   SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, workspace, s));
   return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, mode, workspace, s);
+}
+
+int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                          int causal, float sm_scale, int mode, void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_ptr(q, "q", 16));
+  SAGE_TRY(check_ptr(k, "k", 16));
+  SAGE_TRY(check_ptr(v, "v", 16));
+  SAGE_TRY(check_ptr(out, "out", 16));
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  SAGE_TRY(check_scale(sm_scale));
+  SAGE_TRY(check_dims(B, H, N, d));
+  SAGE_TRY(check_mode(mode, true));
+  if (sage::mode_pv_int8(mode & SAGE_MODE_MASK) && N > kMaxNPv8)
+    return fail(SAGE_ERR_UNSUPPORTED, "N = %d exceeds %d, the limit of the INT8 P.V modes", N, kMaxNPv8);
+  const size_t need = sage::make_layout(static_cast<long long>(B) * H, N, d, mode & SAGE_MODE_MASK, true).total;
+  if (need > SAGE_NOALLOC_SCRATCH_BYTES)
+    return fail(SAGE_ERR_WORKSPACE,
+                "this problem needs %zu bytes of workspace; sage_attn_fwd_noalloc holds %zu "
+                "(use sage_attn_fwd with a caller-provided workspace)",
+                need, static_cast<size_t>(SAGE_NOALLOC_SCRATCH_BYTES));
+  SAGE_TRY(check_device());
+  void* ws = nullptr;
+  SAGE_TRY(scratch_address(&ws));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, ws, s));
+  return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, mode, ws, s);
 }
 
 int sage_attn_dump_scores(const void* v, void* out, int B, int H, int N, int d, float sm_scale, int mode,

@@ -109,6 +109,30 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
                   int d, int causal, float sm_scale, int mode, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* Bytes of device scratch sage_attn_fwd_noalloc holds on each device. */
+#define SAGE_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/*
+ * sage_attn_fwd for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation. Same arguments (without the workspace), kernels and results as
+ * sage_attn_fwd; the workspace is a scratch array of SAGE_NOALLOC_SCRATCH_BYTES
+ * (256 MiB) that the library holds on every device it runs on, from the
+ * loading of its code object until the process ends. The call allocates and
+ * frees nothing; its first call on a device looks up that device's scratch
+ * address once.
+ *   Limit: a problem whose workspace (sage_attn_workspace_size) exceeds
+ *   SAGE_NOALLOC_SCRATCH_BYTES returns SAGE_ERR_WORKSPACE and enqueues nothing.
+ *   Sharing: every call on one device uses that device's one scratch array.
+ *   Calls whose work can overlap on a device (unordered streams, several host
+ *   threads) race on it and may produce wrong outputs; order them on one
+ *   stream. The scratch keeps the last call's quantized operands; each call's
+ *   prepare phase writes every byte its attention kernel reads, so nothing has
+ *   to be cleared between calls.
+ */
+int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
+                          int d, int causal, float sm_scale, int mode, void* stream);
+
 /*
  * First phase of sage_attn_fwd: the K channel mean and the quantization of
  * Q, K (and of V, in the modes that quantize it: MXFP4, MX-FP8 or INT8 codes)

@@ -165,3 +165,22 @@ def test_binding_checks_v_before_any_device_call():
         sa.sage_attn_dump_scores(out, ws, v=torch.empty(1, 1, 256, 64, dtype=torch.float16), bh=0, q_tile=0, k_tile=0)
     with pytest.raises(TypeError):
         sa.sage_attn_compute(out, ws, v=torch.empty(1, 2, 256, 64, dtype=torch.float16))
+
+
+def test_noalloc_entry_point_validation():
+    # sage_attn_fwd_noalloc: the same argument checks as sage_attn_fwd, and a problem whose
+    # workspace exceeds the library's per-device scratch is refused before any HIP call
+    f = lambda q=A16, out=A16, B=1, H=2, N=256, d=64, causal=0, scale=0.125, mode=0: \
+        lib.sage_attn_fwd_noalloc(q, A16, A16, out, B, H, N, d, causal, scale, mode, None)
+    assert f(q=None) == INVALID and f(out=A16 + 2) == INVALID
+    assert f(d=96) == UNSUP and f(mode=9) == UNSUP and f(mode=6, N=(1 << 17) + 1) == UNSUP
+    assert f(scale=0.0) == INVALID and f(causal=3) == INVALID
+    big = sa.sage_attn_workspace_size(1, 64, 32768, 128, 0)
+    assert big > sa.SAGE_NOALLOC_SCRATCH_BYTES
+    assert f(B=1, H=64, N=32768, d=128) == WS
+    assert "sage_attn_fwd_noalloc holds" in sa.sage_last_error()
+    # the largest workloads it serves: prefill-sized INT8 and MXFP4 problems fit
+    assert sa.sage_attn_workspace_size(4, 32, 4096, 128, 0) <= sa.SAGE_NOALLOC_SCRATCH_BYTES
+    assert sa.sage_attn_workspace_size(4, 32, 8192, 128, 2) <= sa.SAGE_NOALLOC_SCRATCH_BYTES
+    if not _gpu_visible():
+        assert f() == NODEV

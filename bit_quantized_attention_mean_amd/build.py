@@ -45,6 +45,22 @@ def _run(cmd):
     return out
 
 
+def check_kernel_stubs(objs) -> None:
+    """Every kernel a launcher references must be defined in its object. The host
+    pass of hipcc can drop a kernel template instantiation without a diagnostic
+    (its host stub then stays undefined and the library would lack the kernel),
+    so an undefined __device_stub__ symbol fails the build."""
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    for o in objs:
+        r = subprocess.run([nm, o], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"{nm} {o} failed:\n{r.stdout}")
+        missing = [l.split()[-1] for l in r.stdout.splitlines()
+                   if "__device_stub__" in l and l.split()[-2:-1] == ["U"]]
+        if missing:
+            raise RuntimeError(f"{os.path.basename(o)}: kernel(s) dropped by the host pass: {missing[:4]}")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
@@ -57,6 +73,7 @@ def build(verbose: bool = False) -> str:
         for o in outs:
             if o:
                 print(o)
+    check_kernel_stubs(objs)
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
     os.replace(tmp, LIB)

@@ -84,6 +84,35 @@ __device__ __forceinline__ v8h lds_read_tr_v8h(const unsigned char* p, int strid
   return __builtin_bit_cast(v8h, v4u{a[0], a[1], b[0], b[1]});
 }
 
+// Waits until at most n (0..7, wave-uniform) of this wave's vector memory
+// operations are outstanding (s_waitcnt with only the vmcnt field set).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0xF71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0xF73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0xF75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
+    default: __builtin_amdgcn_s_waitcnt(0xF77); break;
+  }
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// lds + 16 l (buffer_load_dwordx4 with an LDS destination; the LDS address
+// is wave-uniform). Kept out of the kernel template: the host-side pass of a
+// template instantiation that names this builtin silently drops the kernel.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Key tile row held in LDS row r: the inverse of lds_row_of_key below.
+__device__ __forceinline__ int key_of_lds_row(int r) {
+  const int t = r >> 5, rem = r & 31;
+  return ((rem >> 2) & 1) * 32 + t * 16 + ((rem >> 3) << 2) + (rem & 3);
+}
+
 // log2(127): exp2(x + log2(127)) = 127 * exp2(x), the integer P weight's scale.
 constexpr float kLog2_127 = 6.98868468677216585f;
 
@@ -201,26 +230,55 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   constexpr int EB = F16 ? 2 : 1;        // bytes per Q / K element
   constexpr int NC = D / 32;             // 32-channel tiles of O^T
   constexpr int NQF = F16 ? D / 16 : D / 32;  // score matrix ops per 32 keys (16 bytes of Q each)
-  constexpr int KROW = D * EB + 16;      // LDS bytes per K row (16 bytes of padding)
-  // V in LDS: fp16 V as given, 64 key rows of d channels (+64 bytes, so that
-  // the 4 rows x 64 bytes of one transposing read fall in distinct banks), or
+  constexpr bool PP = attn_pingpong(D, SM, PV8, DUMP);
+  // The INT8 ping-pong instances load tiles straight into LDS (buffer loads
+  // with an LDS destination, 1 KiB per wave instruction) into three stages,
+  // two tiles ahead, with unpadded rows whose 16-byte chunks are permuted
+  // within the row (XOR swizzle) so the matrix ops' LDS reads stay free of
+  // bank conflicts; the others stage tiles through registers into two
+  // buffers of padded rows.
+  constexpr bool DMA = PP && !F16;
+  // K in LDS: 64 key rows of d codes (fp16: 2d bytes), +16 bytes of padding
+  // per row without DMA.
+  constexpr int KROW = DMA ? D * EB : D * EB + 16;   // LDS bytes per K row
+  // V in LDS: fp16 V as given, 64 key rows of d channels (without DMA +64
+  // bytes, so that the 4 rows x 64 bytes of one transposing read fall in
+  // distinct banks; with DMA the 64-byte segments are swizzled instead), or
   // the INT8 V^T codes, d channel rows of 64 keys (+16 bytes).
   constexpr bool VRM = !PV8;
-  constexpr int VROW = VRM ? D * 2 + 64 : kKTile + 16;  // LDS bytes per V row
+  constexpr int VROW = VRM ? (DMA ? D * 2 : D * 2 + 64) : kKTile + 16;  // LDS bytes per V row
+  // swizzles of the DMA layouts: K row r keeps data chunk q at chunk
+  // q ^ kswz(r); V row r keeps data segment s (64 bytes = 32 channels) at
+  // segment s ^ vswz(r). kswz(r) = (r >> KSH) & (KCPR - 1) makes any 16
+  // consecutive rows put a given chunk in distinct banks; vswz(r) = (r >> VSH)
+  // & (VSEG - 1) does the same for the 4 rows of a transposing read.
+  constexpr int KCPR = D * EB / 16;                  // 16-byte chunks per K row
+  constexpr int KSH = KCPR == 8 ? 1 : (KCPR == 4 ? 2 : 0);
+  constexpr int VSEG = D * 2 / 64;                   // 64-byte segments per V row
+  constexpr int VSH = VSEG == 4 ? 0 : 1;
   constexpr int KT_BYTES = kKTile * KROW;
   constexpr int VT_BYTES = (VRM ? kKTile : D) * VROW;
   constexpr int KB0 = 0, KB1 = KT_BYTES, VB0 = 2 * KT_BYTES, VB1 = 2 * KT_BYTES + VT_BYTES;
   constexpr int KCHN = kKTile * D * EB / 16;  // 16-byte chunks of a K tile
   constexpr int RPV = PV8 ? 2 : 4;       // P.V matrix ops per 32-channel tile
   constexpr int VRD = VRM ? 2 : 1;       // LDS reads per P.V A operand
-  constexpr bool PP = attn_pingpong(D, SM, PV8, DUMP);
   constexpr int NTH = PP ? 512 : 256;          // threads per workgroup
   constexpr int WGQ = PP ? kWGQ : kWGQ / 2;    // query rows per workgroup
   constexpr int KPT = (KCHN + NTH - 1) / NTH;
   constexpr int VCPR = VRM ? D * 2 / 16 : kKTile / 16;  // 16-byte chunks per V row in global memory
   constexpr int VCHN = (VRM ? kKTile : D) * VCPR;      // 16-byte chunks of a V tile
   constexpr int VPT = (VCHN + NTH - 1) / NTH;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * KT_BYTES + 2 * VT_BYTES];
+  // register-staged tiles: two K and two V buffers in one array; LDS-loaded
+  // tiles: three stages of each, separate arrays (the compiler then tells
+  // the stages apart and does not wait for a stage's loads before reading
+  // another one)
+  __shared__ __attribute__((aligned(16))) unsigned char smem[DMA ? 16 : 2 * KT_BYTES + 2 * VT_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char smk0[DMA ? KT_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char smk1[DMA ? KT_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char smk2[DMA ? KT_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char smv0[DMA ? VT_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char smv1[DMA ? VT_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char smv2[DMA ? VT_BYTES : 16];
 
   const int nqt = Npad / WGQ;
   int bh, qt;
@@ -298,6 +356,11 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   const bool vload_last = (tid + NTH * (VPT - 1)) < VCHN;
   unsigned kr[4 * KPT], vr[4 * VPT];
   const int ka = l32 * KROW + g * 16;   // score A operand: K row l32 of each 32-key half
+  // with DMA: the A operand of score matrix op c (data chunk 2c + g of row
+  // l32; the swizzle of row t * 32 + l32 is that of row l32)
+  int kc[NQF];
+#pragma unroll
+  for (int c = 0; c < NQF; ++c) kc[c] = l32 * KROW + (((2 * c + g) ^ ((l32 >> KSH) & (KCPR - 1))) * 16);
   // P.V A operand (channel l32 of a 32-channel tile, keys g*32 + 8c .. +7):
   // INT8 V^T row l32; or, from row-major fp16 V, two transposing reads of 4
   // keys each. In such a read, lane i of each 16-lane group receives element
@@ -307,6 +370,14 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   // receives channel 16 h + (its position) for 4 consecutive keys.
   const int va = VRM ? (g * 32 + ((lane & 15) >> 2)) * VROW + ((lane >> 4) & 1) * 32 + (lane & 3) * 8
                      : l32 * VROW + g * 32;
+  // with DMA: the same read for 32-channel tile dt, in its swizzled segment
+  // (the rows this lane addresses, g*32 + 8c + (lane & 15)/4 (+4), share the
+  // swizzle of row (lane & 15)/4)
+  int vdt[NC];
+#pragma unroll
+  for (int dt = 0; dt < NC; ++dt)
+    vdt[dt] = (g * 32 + ((lane & 15) >> 2)) * VROW + ((dt ^ ((((lane & 15) >> 2) >> VSH) & (VSEG - 1))) * 64) +
+              ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
 
   v16f o[NC];
 #pragma unroll
@@ -378,7 +449,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
     v4i ka_[2 * NQF];                                                                            \
     _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
       _Pragma("unroll") for (int c = 0; c < NQF; ++c)                                            \
-        ka_[t * NQF + c] = *reinterpret_cast<const v4i*>(smem + (KB_) + ka + t * 32 * KROW + c * 32); \
+        ka_[t * NQF + c] = *reinterpret_cast<const v4i*>((KB_) + (DMA ? kc[c] : ka + c * 32) + t * 32 * KROW); \
     _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                              \
       _Pragma("unroll") for (int i = 0; i < 16; ++i) s[t][i] = 0;                                \
       _Pragma("unroll") for (int c = 0; c < NQF; ++c) {                                          \
@@ -407,8 +478,8 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   // max flushes the int32 sums into the fp32 accumulator (of) instead of
   // rescaling them: the first matrix op of each tile then starts from zero.
 #define SAGE_VA(VB_, DT_, C_)                                                                    \
-  (VRM ? lds_read_tr_v8h(smem + (VB_) + va + (C_) * 8 * VROW + (DT_) * 64, 4 * VROW)             \
-       : *reinterpret_cast<const v8h*>(smem + (VB_) + va + (DT_) * 32 * VROW + (C_) * 16))
+  (VRM ? lds_read_tr_v8h((VB_) + (DMA ? vdt[DT_] : va + (DT_) * 64) + (C_) * 8 * VROW, 4 * VROW)    \
+       : *reinterpret_cast<const v8h*>((VB_) + va + (DT_) * 32 * VROW + (C_) * 16))
 #define SAGE_PV_MMA(VB_, Z_)                                                                     \
   do {                                                                                           \
     v8h va_[2][RPV];                                                                             \
@@ -669,13 +740,13 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
       SAGE_LOAD_V(jp_)                                                                           \
     }                                                                                            \
     if ((G_) == 0) {                                                                             \
-      SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), KB_, VBP_)                                          \
+      SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), smem + (KB_), smem + (VBP_))                        \
     } else if (!(FIRST_)) {                                                                      \
       SAGE_SOFTMAX(jp_ - 1, ksp);                                                                \
     }                                                                                            \
     if (PP) __syncthreads();  /* the ping-pong's phase switch */                                 \
     if ((G_) == 1) {                                                                             \
-      SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), KB_, VBP_)                                          \
+      SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), smem + (KB_), smem + (VBP_))                        \
     } else if (!(LAST_)) {                                                                       \
       SAGE_SOFTMAX(jp_, ksn_);                                                                   \
     }                                                                                            \
@@ -687,17 +758,19 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
     ksp = ksn_;                                                                                  \
   } while (0)
 
-  SAGE_LOAD_K(0)
-  SAGE_STORE_K(KB0)
-  // Drain every outstanding load here (Q fragments included): otherwise the
-  // counter-based waits inside the loop cannot tell the Q loads are done and
-  // wait on the tile prefetch before each period's score MFMAs.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // The period sequence, compiled once per wave group (the group's phase order
-  // is then fixed in the code: no register copies where the two orders would
-  // otherwise merge; 3-16% faster). Both groups pass the same barriers in the
-  // same order.
+  float ksp = 0.f;
+  if (!DMA) {
+    SAGE_LOAD_K(0)
+    SAGE_STORE_K(KB0)
+    // Drain every outstanding load here (Q fragments included): otherwise the
+    // counter-based waits inside the loop cannot tell the Q loads are done and
+    // wait on the tile prefetch before each period's score MFMAs.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // The period sequence, compiled once per wave group (the group's phase order
+    // is then fixed in the code: no register copies where the two orders would
+    // otherwise merge; 3-16% faster). Both groups pass the same barriers in the
+    // same order.
 #define SAGE_PERIODS(G_)                                                                         \
   do {                                                                                           \
     SAGE_PERIOD(0, KB0, KB1, VB0, VB1, true, false, G_);                                         \
@@ -712,9 +785,126 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
     const int odd = nkt & 1;                                                                     \
     SAGE_PERIOD(nkt, odd ? KB1 : KB0, odd ? KB0 : KB1, odd ? VB1 : VB0, odd ? VB0 : VB1, false, true, G_); \
   } while (0)
-  float ksp = 0.f;
-  if (grp == 0) SAGE_PERIODS(0);
-  else SAGE_PERIODS(1);
+    if (grp == 0) SAGE_PERIODS(0);
+    else SAGE_PERIODS(1);
+  } else {
+    // Three LDS stages per operand: key tile t in K stage t % 3, value tile t
+    // in V stage t % 3. Period jp_ reads K(jp_) and V(jp_ - 1) and issues the
+    // loads of K(jp_ + 2) and V(jp_ + 1) (clamped to the last tile; a
+    // clamped copy lands in a stage nobody reads again), which then have two
+    // periods to arrive: at the end of a period each wave waits only for the
+    // loads it issued before that period. Each wave instruction fills 1 KiB of
+    // a stage (lane l: bytes 16 l .. +15); every lane's source is the 16 bytes
+    // the padded, permuted tile layout puts there (pad bytes: a repeat of the
+    // row's first chunk). Rows past N read as zeros by the buffer's range check.
+    constexpr int NW = NTH / 64;
+    constexpr int KI = KT_BYTES / 1024, VI = VT_BYTES / 1024;   // wave instructions per tile
+    static_assert(!DMA || (KT_BYTES % 1024 == 0 && VT_BYTES % 1024 == 0), "tiles fill whole wave instructions");
+    constexpr int KIW = (KI + NW - 1) / NW, VIW = (VI + NW - 1) / NW;
+    constexpr int KDATA = D * EB, VDATA = D * 2;   // data bytes per K / V row
+    static_assert(!DMA || (KROW == KDATA && VROW == VDATA), "unpadded rows");
+    int kdo[KIW], vdo[VIW];
+    int nvm = 0;   // this wave's tile load instructions per period
+#pragma unroll
+    for (int u = 0; u < KIW; ++u) {
+      const int b = (wave + NW * u) * 1024 + lane * 16, row = b / KROW, q = (b % KROW) / 16;
+      kdo[u] = key_of_lds_row(row) * KDATA + ((q ^ ((row >> KSH) & (KCPR - 1))) * 16);
+      nvm += (wave + NW * u < KI) ? 1 : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < VIW; ++u) {
+      const int b = (wave + NW * u) * 1024 + lane * 16, row = b / VROW, q = (b % VROW) / 16;
+      vdo[u] = row * VDATA + ((((q >> 2) ^ ((row >> VSH) & (VSEG - 1))) * 4 + (q & 3)) * 16);
+      nvm += (wave + NW * u < VI) ? 1 : 0;
+    }
+    // every wave issues the same number of loads when the tiles split evenly:
+    // the waits are then single instructions
+    if (KI % NW == 0 && VI % NW == 0) nvm = KI / NW + VI / NW;
+#define SAGE_SK(I_) ((I_) == 0 ? smk0 : ((I_) == 1 ? smk1 : smk2))
+#define SAGE_SV(I_) ((I_) == 0 ? smv0 : ((I_) == 1 ? smv1 : smv2))
+#define SAGE_DMA_K(J_, ST_)                                                                      \
+    _Pragma("unroll") for (int u = 0; u < KIW; ++u) {                                            \
+      if (wave + NW * u < KI)                                                                    \
+        lds_dma16(rk, SAGE_SK(ST_) + (wave + NW * u) * 1024, kdo[u], (J_) * (kKTile * KDATA));   \
+    }
+#define SAGE_DMA_V(J_, ST_)                                                                      \
+    _Pragma("unroll") for (int u = 0; u < VIW; ++u) {                                            \
+      if (wave + NW * u < VI)                                                                    \
+        lds_dma16(rv, SAGE_SV(ST_) + (wave + NW * u) * 1024, vdo[u], (J_) * (kKTile * VDATA));   \
+    }
+  // end of a period: this wave's loads issued before it have landed (the ones
+  // issued in it may still be in flight), then the barrier; the acquire fence
+  // keeps the next period's LDS reads behind it (a release fence would wait
+  // for every load in flight)
+#define SAGE_END_BARRIER(N_)                                                                     \
+  do {                                                                                           \
+    wait_vmcnt(N_);                                                                              \
+    __builtin_amdgcn_s_barrier();                                                                \
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");                              \
+  } while (0)
+  // Period jp_ with K stage SK_ = jp_ % 3 (a compile-time constant): reads
+  // K(jp_) from stage SK_ and V(jp_ - 1) from stage (SK_ + 2) % 3; loads
+  // K(jp_ + 2) into stage (SK_ + 2) % 3 (K(jp_ - 1)'s, read in the last
+  // period) and V(jp_ + 1) into stage (SK_ + 1) % 3 (V(jp_ - 2)'s).
+#define SAGE_PERIOD_DMA(J_, SK_, FIRST_, LAST_, G_)                                              \
+  do {                                                                                           \
+    const int jp_ = (J_);                                                                        \
+    const float ksn_ = (SM == kScoresInt8Block) ? ksh[min(jp_, nkt - 1)] : 0.f;                 \
+    if (!(LAST_)) {                                                                              \
+      SAGE_DMA_K(min(jp_ + 2, nkt - 1), ((SK_) + 2) % 3)                                         \
+      SAGE_DMA_V(min(jp_ + 1, nkt - 1), ((SK_) + 1) % 3)                                         \
+    }                                                                                            \
+    if ((G_) == 0) {                                                                             \
+      SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), SAGE_SK(SK_), SAGE_SV(((SK_) + 2) % 3))             \
+    } else if (!(FIRST_)) {                                                                      \
+      SAGE_SOFTMAX(jp_ - 1, ksp);                                                                \
+    }                                                                                            \
+    /* the ping-pong's phase switch: it orders no LDS data (the loads in */                     \
+    /* flight write stages nobody reads in this period) */                                      \
+    __builtin_amdgcn_s_barrier();                                                                \
+    if ((G_) == 1) {                                                                             \
+      SAGE_PHASE_MATRIX(!(FIRST_), !(LAST_), SAGE_SK(SK_), SAGE_SV(((SK_) + 2) % 3))             \
+    } else if (!(LAST_)) {                                                                       \
+      SAGE_SOFTMAX(jp_, ksn_);                                                                   \
+    }                                                                                            \
+    /* K(jp_ + 1) and V(jp_), issued a period earlier, must have landed */                      \
+    if (!(LAST_)) SAGE_END_BARRIER(nvm);                                                         \
+    ksp = ksn_;                                                                                  \
+  } while (0)
+    // prologue: K(0) -> stage 0, K(1) -> stage 1, V(0) -> stage 0; the Q
+    // fragments and K(0) must have landed before period 0
+    SAGE_DMA_K(0, 0)
+    SAGE_DMA_K(min(1, nkt - 1), 1)
+    SAGE_DMA_V(0, 0)
+    SAGE_END_BARRIER(nvm);   // nvm = this wave's K(1) + V(0) instructions
+#define SAGE_PERIODS_DMA(G_)                                                                     \
+  do {                                                                                           \
+    SAGE_PERIOD_DMA(0, 0, true, false, G_);                                                      \
+    int jt = 1;                                                                                  \
+    for (; jt + 2 < nkt; jt += 3) {                                                              \
+      SAGE_PERIOD_DMA(jt, 1, false, false, G_);                                                  \
+      SAGE_PERIOD_DMA(jt + 1, 2, false, false, G_);                                              \
+      SAGE_PERIOD_DMA(jt + 2, 0, false, false, G_);                                              \
+    }                                                                                            \
+    if (jt < nkt) SAGE_PERIOD_DMA(jt, 1, false, false, G_);                                      \
+    if (jt + 1 < nkt) SAGE_PERIOD_DMA(jt + 1, 2, false, false, G_);                              \
+    const int sl = nkt % 3;                                                                      \
+    if (sl == 0) SAGE_PERIOD_DMA(nkt, 0, false, true, G_);                                       \
+    else if (sl == 1) SAGE_PERIOD_DMA(nkt, 1, false, true, G_);                                  \
+    else SAGE_PERIOD_DMA(nkt, 2, false, true, G_);                                               \
+    /* no load may still be writing this workgroup's LDS when it ends */                        \
+    wait_vmcnt(0);                                                                               \
+  } while (0)
+    if (grp == 0) SAGE_PERIODS_DMA(0);
+    else SAGE_PERIODS_DMA(1);
+#undef SAGE_PERIODS_DMA
+#undef SAGE_PERIOD_DMA
+#undef SAGE_END_BARRIER
+#undef SAGE_DMA_V
+#undef SAGE_DMA_K
+#undef SAGE_SV
+#undef SAGE_SK
+  }
 #undef SAGE_PERIODS
 #undef SAGE_PHASE_MATRIX
 #undef SAGE_DUMP_S

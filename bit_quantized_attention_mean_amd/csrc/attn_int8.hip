@@ -797,8 +797,15 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
     // a stage (lane l: bytes 16 l .. +15); every lane's source is the 16 bytes
     // the padded, permuted tile layout puts there (pad bytes: a repeat of the
     // row's first chunk). Rows past N read as zeros by the buffer's range check.
-    constexpr int NW = NTH / 64;
     constexpr int KI = KT_BYTES / 1024, VI = VT_BYTES / 1024;   // wave instructions per tile
+    // the loads are spread over all waves when that gives each the same
+    // count, else over the first wave group only (a compile-time set in the
+    // period sequence, which is compiled per group): every issuing wave then
+    // waits for a constant count
+    constexpr int NW = ((KI + VI) % (NTH / 64) == 0 && KI % (NTH / 64) == 0) ? NTH / 64 : NTH / 128;
+    static_assert(!DMA || (KI % NW == 0 && VI % NW == 0), "tile loads split evenly over the issuing waves");
+    constexpr int NVMC = KI / NW + VI / NW;   // loads per issuing wave and period
+    const bool issuer = wave < NW;
     static_assert(!DMA || (KT_BYTES % 1024 == 0 && VT_BYTES % 1024 == 0), "tiles fill whole wave instructions");
     constexpr int KIW = (KI + NW - 1) / NW, VIW = (VI + NW - 1) / NW;
     constexpr int KDATA = D * EB, VDATA = D * 2;   // data bytes per K / V row
@@ -817,9 +824,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
       vdo[u] = row * VDATA + ((((q >> 2) ^ ((row >> VSH) & (VSEG - 1))) * 4 + (q & 3)) * 16);
       nvm += (wave + NW * u < VI) ? 1 : 0;
     }
-    // every wave issues the same number of loads when the tiles split evenly:
-    // the waits are then single instructions
-    if (KI % NW == 0 && VI % NW == 0) nvm = KI / NW + VI / NW;
+    nvm = issuer ? NVMC : 0;
 #define SAGE_SK(I_) ((I_) == 0 ? smk0 : ((I_) == 1 ? smk1 : smk2))
 #define SAGE_SV(I_) ((I_) == 0 ? smv0 : ((I_) == 1 ? smv1 : smv2))
 #define SAGE_DMA_K(J_, ST_)                                                                      \
@@ -850,7 +855,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   do {                                                                                           \
     const int jp_ = (J_);                                                                        \
     const float ksn_ = (SM == kScoresInt8Block) ? ksh[min(jp_, nkt - 1)] : 0.f;                 \
-    if (!(LAST_)) {                                                                              \
+    if (!(LAST_) && ((G_) == 0 || NW == NTH / 64)) {                                             \
       SAGE_DMA_K(min(jp_ + 2, nkt - 1), ((SK_) + 2) % 3)                                         \
       SAGE_DMA_V(min(jp_ + 1, nkt - 1), ((SK_) + 1) % 3)                                         \
     }                                                                                            \
@@ -868,14 +873,16 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
       SAGE_SOFTMAX(jp_, ksn_);                                                                   \
     }                                                                                            \
     /* K(jp_ + 1) and V(jp_), issued a period earlier, must have landed */                      \
-    if (!(LAST_)) SAGE_END_BARRIER(nvm);                                                         \
+    if (!(LAST_)) SAGE_END_BARRIER(((G_) == 0 || NW == NTH / 64) ? NVMC : 0);                   \
     ksp = ksn_;                                                                                  \
   } while (0)
     // prologue: K(0) -> stage 0, K(1) -> stage 1, V(0) -> stage 0; the Q
     // fragments and K(0) must have landed before period 0
-    SAGE_DMA_K(0, 0)
-    SAGE_DMA_K(min(1, nkt - 1), 1)
-    SAGE_DMA_V(0, 0)
+    if (issuer) {
+      SAGE_DMA_K(0, 0)
+      SAGE_DMA_K(min(1, nkt - 1), 1)
+      SAGE_DMA_V(0, 0)
+    }
     SAGE_END_BARRIER(nvm);   // nvm = this wave's K(1) + V(0) instructions
 #define SAGE_PERIODS_DMA(G_)                                                                     \
   do {                                                                                           \

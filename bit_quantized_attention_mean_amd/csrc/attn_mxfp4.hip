@@ -208,6 +208,22 @@ __global__ __launch_bounds__(256, (D == 64 && PV8) ? 3 : 2) void attn_mxfp4_kern
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[c][i] = 0.f;
   float m = -INFINITY;
+  // the block of ones of the row-sum matrix op (E2M1 1.0 = 0x2, E4M3 1.0 =
+  // 0x38 in every element), kept in registers (asm values are not
+  // rematerialized for every tile), except where the 8 registers of the E4M3
+  // block would not fit (MX-FP8 P.V at d = 64, three workgroups per CU)
+  constexpr bool KEEP8 = PV8 && D == 128;
+  v4i ones4;
+  v8i ones8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (KEEP8) asm volatile("v_mov_b32 %0, 0x38383838" : "=v"(ones8[i]));
+    else ones8[i] = 0x38383838;
+    if (i < 4) {
+      if (PV8) ones4[i] = 0;
+      else asm volatile("v_mov_b32 %0, 0x22222222" : "=v"(ones4[i]));
+    }
+  }
 
   // One key tile (J_) from LDS buffer BUF_: scores, softmax, P quantization, P.V.
 #define SAGE_TILE4(J_, BUF_)                                                                         \
@@ -290,7 +306,8 @@ _Pragma("unroll")                                                               
     if (PV8) {                                                                                      \
       const float plim = 448.f * pscale;                                                            \
       _Pragma("unroll") for (int w = 0; w < 8; ++w) {                                               \
-        v2s r = {0, 0};                                                                             \
+        /* both halves are written below: no zeroing */                                           \
+        v2s r = __builtin_nondeterministic_value(r);                                                \
         r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(p[4 * w], plim), fminf(p[4 * w + 1], plim), pscale, false); \
         r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(p[4 * w + 2], plim), fminf(p[4 * w + 3], plim), pscale, true); \
         pq[w] = __builtin_bit_cast(int, r);                                                         \
@@ -306,7 +323,7 @@ _Pragma("unroll")                                                               
       }                                                                                             \
     } else {                                                                                        \
       _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                               \
-        unsigned r = 0;                                                                             \
+        unsigned r = __builtin_nondeterministic_value(r);  /* all four bytes are written below */  \
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 0], p[8 * w + 1], pscale, 0);     \
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 2], p[8 * w + 3], pscale, 1);     \
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, p[8 * w + 4], p[8 * w + 5], pscale, 2);     \
@@ -318,9 +335,11 @@ _Pragma("unroll")                                                               
                                                                                                     \
     if (__ballot(need)) {                                                                           \
 _Pragma("unroll")                                                                                   \
-      for (int c = 0; c < NT + 1; ++c)                                                              \
+      for (int c = 0; c < NT; ++c)                                                                  \
 _Pragma("unroll")                                                                                   \
         for (int i = 0; i < 16; ++i) o[c][i] *= alpha;                                              \
+      /* every row of the row-sum product holds l; only register 0 is read */                       \
+      o[NT][0] *= alpha;                                                                            \
     }                                                                                               \
 _Pragma("unroll")                                                                                   \
     for (int dt = 0; dt < NT; ++dt) {                                                               \
@@ -341,13 +360,10 @@ _Pragma("unroll")                                                               
     }                                                                                               \
     /* row sum of the quantized P: ones (E4M3 0x38 or E2M1 0x2, scale 2^0) times P */              \
     if (PV8) {                                                                                      \
-      const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,                            \
-                        0x38383838, 0x38383838, 0x38383838, 0x38383838};                           \
-      o[NT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pq, o[NT], 0, 0, 0, 127, 0,    \
+      o[NT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pq, o[NT], 0, 0, 0, 127, 0,   \
                                                               static_cast<int>(pe8));               \
     } else {                                                                                        \
-      o[NT] = mfma_fp4<0>(v4i{0x22222222, 0x22222222, 0x22222222, 0x22222222},                         \
-                       v4i{pq[0], pq[1], pq[2], pq[3]}, 127u, pe8, o[NT]);                          \
+      o[NT] = mfma_fp4<0>(ones4, v4i{pq[0], pq[1], pq[2], pq[3]}, 127u, pe8, o[NT]);              \
     }                                                                                               \
   } while (0)
 

@@ -40,6 +40,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -60,9 +61,15 @@ def log(*a):
 
 
 def kernel_source_hash(name: str) -> str:
+    """sha256[:16] of a kernel source's code: comments dropped and whitespace runs
+    collapsed, so an edit to comments alone keeps counters taken on that code."""
     path = os.path.join(ROOT, "bit_quantized_attention_mean_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    code = " ".join(text.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def load_traffic(tag: str, source: str):

@@ -39,8 +39,8 @@
 //     (see kRefSlack); the row sum adds the fp16 P pairwise on v_dot2_f32_f16.
 //   * causal: key tiles wholly above the workgroup's last query are skipped;
 //     masking runs only on tiles that cross the diagonal or the ragged tail.
-//   * INT8 P.V variant (the page's "Quantize P,V to INT8" ablation, "Measured
-//     effects"; the faster kernel its "Approach" picks per layer where
+//   * INT8 P.V variant (the SageAttention page's "Measured effects" ablation
+//     with P and V in INT8; the faster kernel its "Approach" picks per layer where
 //     accuracy allows): V^T arrives as INT8 codes with one scale per channel,
 //     P is formed against the exact running max (so P <= 1) and converted to
 //     the integer round(127 P) in one v_cvt_pk_u8_f32 per value, and O^T

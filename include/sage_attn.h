@@ -12,9 +12,9 @@
  * FP4 idea of "SageAttention3: Microscaling FP4 Attention for Inference and
  * An Exploration of 8-Bit Training" (abstract), using E2M1 elements with one
  * E8M0 scale per 32 elements (the MX format its reference list names).
- * INT8 P.V variants (modes 6, 7): the page's "Measured effects" ablation that
- * quantizes P and V to INT8 as well ("Quantize P,V to INT8 rather than
- * retaining FP16"), the faster kernel its "Approach" selects per layer where
+ * INT8 P.V variants (modes 6, 7): the page's "Measured effects" ablation in
+ * which the second product also runs in INT8 (P and V quantized, no FP16
+ * operand left), the faster kernel its "Approach" selects per layer where
  * cosine similarity stays above 99.8%: V with one scale per (head, channel)
  * over all tokens, P = exp(S - running row max) in [0, 1] as the integer
  * weight round(127 P), P.V accumulated exactly in int32, the row sum from the
@@ -30,8 +30,10 @@
  *     work is enqueued on it; the library never synchronizes, allocates or
  *     frees device memory. Results are valid once the stream reaches them.
  *   - The caller owns every buffer. The library keeps no state besides a
- *     per-device architecture check and a thread-local error message, so calls
- *     are re-entrant; calls that share a workspace must be stream-ordered.
+ *     per-device architecture check, a thread-local error message and, for
+ *     sage_attn_fwd_noalloc only, one static device scratch array per GPU, so
+ *     calls are re-entrant; calls that share a workspace (or, for the
+ *     allocation-free entry point, a GPU) must be stream-ordered.
  *   - Supported head dims d: 64 and 128. 1 <= N <= 4194304. B, H >= 1.
  *   - Every argument check happens before the first HIP call, so every error
  *     except SAGE_ERR_HIP and SAGE_ERR_NO_DEVICE is reported on a host with no

@@ -203,7 +203,7 @@ def quant_qk_int8(q16, k16, *, blk_q: int, blk_k: int, smooth: bool = True):
 
 
 def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p,
-                      sum_rounded: bool = False, p_alternatives=None):
+                      sum_rounded: bool = False, p_alternatives=None, lse_out=None):
     """FlashAttention-2 style online softmax and P.V over key tiles ([SA-Setup]).
 
     S: float64 scores [R, N] (already scaled, -inf where masked).
@@ -220,6 +220,10 @@ def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p,
     returns (O, allowance), allowance [R, d] bounding |O' - O| to first order
     for any mix of those alternatives: a weight that moves by dP changes O by
     dP * (v_j - O) / l, and |v_j - O| <= |v_j| + max|v| per channel.
+
+    lse_out (optional float64 [R] array): receives the row log-sum-exp m + ln(l)
+    of the final running max and row sum (reading Rb5), what a backward pass
+    recomputes P from.
     """
     R, N = S.shape
     d = V.shape[1]
@@ -246,6 +250,8 @@ def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p,
             A = A * alpha[:, None] + dP @ vbound[t0:t0 + kv_tile]
             dl = dl * alpha + dP.sum(axis=1)
         m = m_new
+    if lse_out is not None:
+        lse_out[...] = m + np.log(l)
     if A is not None:
         return O / l[:, None], A / np.maximum(l - dl, 0.5 * l)[:, None]
     return O / l[:, None]
@@ -253,7 +259,7 @@ def online_softmax_pv(S: np.ndarray, V: np.ndarray, *, kv_tile: int, round_p,
 
 def int8_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, blk_k: int,
                    kv_tile: int = 64, smooth: bool = True, rows=None, quantize: bool = True,
-                   quant=None):
+                   quant=None, lse=None):
     """Emulated INT8 SageAttention forward ([SA-Approach], [SA-Summary]), float64 out.
 
     Steps: mu and K_s (R1, R2); per-block INT8 codes of Q and K_s (R3, R4);
@@ -261,7 +267,8 @@ def int8_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, 
     causal mask (R7); online softmax with fp16 P and fp16 V, l from the fp16 P (R6).
     quantize=False replaces every code by the unquantized value (scale 1) and
     P16 by P: the same tiled arithmetic then reduces to exact attention.
-    `quant` may pass a precomputed quant_qk_int8 result.
+    `quant` may pass a precomputed quant_qk_int8 result. `lse` (optional float64
+    [B, H, len(rows)]) receives each row's log-sum-exp (online_softmax_pv).
     Returns float64 [B, H, len(rows), d].
     """
     B, H, N, d = q16.shape
@@ -288,7 +295,7 @@ def int8_attention(q16, k16, v16, *, causal: bool, sm_scale: float, blk_q: int, 
             if causal:
                 S[_causal_mask(rows, keys)] = -np.inf
             out[b, h] = online_softmax_pv(S, as_f64(v16[b, h]), kv_tile=kv_tile, round_p=round16,
-                                          sum_rounded=True)
+                                          sum_rounded=True, lse_out=None if lse is None else lse[b, h])
     return out
 
 

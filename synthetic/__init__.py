@@ -21,6 +21,11 @@ workload description names, from numpy's PCG64 generator:
      K channel (draw plus offset) is multiplied by the outlier factor.
   4. Offsets and outliers are applied in float32, then every tensor is cast to
      float16 with round-to-nearest-even.
+
+For the backward pass, the gradient of the loss with respect to the attention
+output (dO) stands in for what the layers above would send back: a standard
+normal float32 draw of shape [B, H, N, d] from its own PCG64 stream (seed
+derived from the workload's), cast to float16 the same way.
 """
 from __future__ import annotations
 
@@ -29,7 +34,7 @@ import math
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_custom"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_custom", "make_grad"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -109,3 +114,11 @@ def make_inputs(name: str, *, N: int | None = None, B: int | None = None, H: int
     return make_custom(B or w.B, H or w.H, N or w.N, w.d, seed=w.seed if seed is None else seed,
                        dist=w.dist, k_offset_std=w.k_offset_std, outlier_frac=w.outlier_frac,
                        outlier_scale=w.outlier_scale, nu=w.nu)
+
+
+def make_grad(B: int, H: int, N: int, d: int, *, seed: int, scale: float = 1.0):
+    """Draw the output gradient dO (fp16 [B, H, N, d], C-contiguous): standard
+    normal times `scale`, from PCG64(seed + 1000) so it never repeats a Q/K/V stream."""
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    g = rng.standard_normal((B, H, N, d), dtype=np.float32) * np.float32(scale)
+    return g.astype(np.float16)

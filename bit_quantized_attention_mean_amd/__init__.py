@@ -10,6 +10,9 @@ Functions carry the C names:
   sage_attn_fwd_noalloc(q, k, v, out, ...)  (no workspace: the library's per-device scratch)
   sage_attn_prepare / sage_attn_compute  (the two phases of sage_attn_fwd)
   sage_attn_workspace_size(B, H, N, d, mode)
+  sage_attn_fwd_lse(q, k, v, ...)      -> (out, lse)   (the forward a training step saves)
+  sage_attn_bwd(q, k, v, out, dout, lse, ...) -> (dq, dk, dv)   (INT8 backward pass)
+  sage_attn_bwd_workspace_size(B, H, N, d, mode)
   sage_quant_qk(q, k, blk_q, blk_k, flags)  -> dict of codes/scales/mean
   sage_quant_mxfp4(q, k, v, flags)         -> dict of packed codes/exponents
   sage_quant_v_int8(v)                     -> dict of V^T codes and channel scales
@@ -28,6 +31,7 @@ __all__ = [
     "sage_attn_fwd", "sage_attn_fwd_noalloc", "SAGE_NOALLOC_SCRATCH_BYTES", "sage_attn_prepare", "sage_attn_compute", "sage_attn_workspace_size",
     "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_quant_v_int8", "sage_attn_dump_scores", "sage_status_string", "sage_last_error",
     "sage_clock_probe", "sage_wall_clock_khz", "measure_clock_mhz",
+    "sage_attn_fwd_lse", "sage_attn_bwd", "sage_attn_bwd_workspace_size", "make_bwd_workspace",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -60,6 +64,9 @@ _SIGS = {
     "sage_quant_v_int8": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "sage_attn_dump_scores": (_i, [_vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _i, _i, _vp, _vp]),
     "sage_clock_probe": (_i, [ctypes.c_longlong, _vp, _vp]),
+    "sage_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "sage_attn_fwd_lse": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "sage_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "sage_wall_clock_khz": (_i, [ctypes.POINTER(_i)]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
@@ -169,6 +176,71 @@ def sage_attn_fwd(q, k, v, out=None, *, causal=False, sm_scale=None, mode=SAGE_M
                            _stream(stream))
     _check(rc, "sage_attn_fwd")
     return out
+
+
+def sage_attn_bwd_workspace_size(B: int, H: int, N: int, d: int, mode: int = 0) -> int:
+    return int(lib.sage_attn_bwd_workspace_size(B, H, N, d, mode))
+
+
+def make_bwd_workspace(B, H, N, d, mode=0, device=None):
+    """A device workspace tensor (uint8) for sage_attn_bwd (it also serves sage_attn_fwd_lse)."""
+    torch = _torch()
+    n = sage_attn_bwd_workspace_size(B, H, N, d, mode)
+    if n == 0:
+        raise ValueError("invalid problem size or mode for the backward pass")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def sage_attn_fwd_lse(q, k, v, out=None, lse=None, *, causal=False, sm_scale=None,
+                      mode=SAGE_MODE_INT8_Q128_K64, workspace=None, stream=None):
+    """(out fp16 [B,H,N,d], lse fp32 [B,H,N]): the forward pass and its row log-sum-exp."""
+    torch = _torch()
+    B, H, N, d = _shape4(q)
+    if tuple(k.shape) != (B, H, N, d) or tuple(v.shape) != (B, H, N, d):
+        raise ValueError("q, k, v must have the same shape")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = make_workspace(B, H, N, d, mode, q.device)
+    rc = lib.sage_attn_fwd_lse(_dev_ptr(q, "q", torch.float16), _dev_ptr(k, "k", torch.float16),
+                               _dev_ptr(v, "v", torch.float16), _dev_ptr(out, "out", torch.float16),
+                               _dev_ptr(lse, "lse", torch.float32), B, H, N, d, int(bool(causal)),
+                               float(sm_scale), int(mode), _dev_ptr(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "sage_attn_fwd_lse")
+    return out, lse
+
+
+def sage_attn_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, *, causal=False, sm_scale=None,
+                  mode=SAGE_MODE_INT8_Q128_K64, workspace=None, stream=None):
+    """(dq, dk, dv) fp32 [B,H,N,d]: gradients of sum(out * dout) by the INT8 backward pass."""
+    torch = _torch()
+    B, H, N, d = _shape4(q)
+    for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{name} must have the shape of q")
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be [B, H, N]")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dv is None else dv
+    if workspace is None:
+        workspace = make_bwd_workspace(B, H, N, d, mode, q.device)
+    rc = lib.sage_attn_bwd(_dev_ptr(q, "q", torch.float16), _dev_ptr(k, "k", torch.float16),
+                           _dev_ptr(v, "v", torch.float16), _dev_ptr(out, "out", torch.float16),
+                           _dev_ptr(dout, "dout", torch.float16), _dev_ptr(lse, "lse", torch.float32),
+                           _dev_ptr(dq, "dq", torch.float32), _dev_ptr(dk, "dk", torch.float32),
+                           _dev_ptr(dv, "dv", torch.float32), B, H, N, d, int(bool(causal)), float(sm_scale),
+                           int(mode), _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                           _stream(stream))
+    _check(rc, "sage_attn_bwd")
+    return dq, dk, dv
 
 
 def sage_attn_fwd_noalloc(q, k, v, out, *, causal=False, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64, stream=None):

@@ -164,14 +164,14 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
 }
 
 int do_compute(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d, int causal, float sm_scale,
-               int mode, const void* ws, hipStream_t s) {
+               int mode, const void* ws, hipStream_t s, float* lse = nullptr) {
   const int BH = B * H;
   const int lo = mode & SAGE_MODE_MASK;
   const sage::Layout L = sage::make_layout(BH, N, d, lo, true);
   sage::AttnArgs a;
   a.BH = BH; a.N = N; a.Npad = L.Npad; a.d = d; a.causal = causal != 0;
   a.sl2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);  // sm_scale * log2(e)
-  a.mode = lo; a.out = out;
+  a.mode = lo; a.out = out; a.lse = lse;
   (void)hipGetLastError();
   if (lo == SAGE_MODE_MXFP4 || lo == SAGE_MODE_MXFP4_FP8PV)
     return hip_status(sage::launch_attn_mxfp4(a, at(ws, L.q_fp4), at(ws, L.q_e8), at(ws, L.k_fp4), at(ws, L.k_e8),
@@ -186,6 +186,16 @@ int do_compute(const void* q, const void* k, const void* v, void* out, int B, in
                                            sage::mode_pv_int8(lo) ? reinterpret_cast<const float*>(at(ws, L.vscale))
                                                                   : nullptr, s),
                     "INT8 attention kernel");
+}
+
+// The training forward and the backward pass run the per-block INT8 modes.
+int check_train_mode(int mode) {
+  SAGE_TRY(check_mode(mode, true));
+  const int lo = mode & SAGE_MODE_MASK;
+  if (lo != SAGE_MODE_INT8_Q128_K64 && lo != SAGE_MODE_INT8_Q64_K64)
+    return fail(SAGE_ERR_UNSUPPORTED, "mode %d: the training forward and the backward pass support the per-block "
+                "INT8 modes %d and %d", lo, SAGE_MODE_INT8_Q128_K64, SAGE_MODE_INT8_Q64_K64);
+  return SAGE_OK;
 }
 
 // Scratch of sage_attn_fwd_noalloc: the workspace of that entry point, a global
@@ -319,6 +329,86 @@ int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out
   const hipStream_t s = static_cast<hipStream_t>(stream);
   SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, ws, s));
   return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, mode, ws, s);
+}
+
+size_t sage_attn_bwd_workspace_size(int B, int H, int N, int d, int mode) {
+  if (check_dims(B, H, N, d) != SAGE_OK || check_train_mode(mode) != SAGE_OK) return 0;
+  return sage::make_bwd_layout(static_cast<long long>(B) * H, N, d, mode & SAGE_MODE_MASK).total;
+}
+
+int sage_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N, int d,
+                      int causal, float sm_scale, int mode, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_ptr(q, "q", 16));
+  SAGE_TRY(check_ptr(k, "k", 16));
+  SAGE_TRY(check_ptr(v, "v", 16));
+  SAGE_TRY(check_ptr(out, "out", 16));
+  SAGE_TRY(check_ptr(lse, "lse", 4));
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  SAGE_TRY(check_scale(sm_scale));
+  SAGE_TRY(check_train_mode(mode));
+  SAGE_TRY(validate_attn(B, H, N, d, mode, workspace, workspace_bytes));
+  SAGE_TRY(check_device());
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, workspace, s));
+  return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, mode, workspace, s, lse);
+}
+
+int sage_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                  float* dq, float* dk, float* dv, int B, int H, int N, int d, int causal, float sm_scale, int mode,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  SAGE_TRY(check_ptr(q, "q", 16));
+  SAGE_TRY(check_ptr(k, "k", 16));
+  SAGE_TRY(check_ptr(v, "v", 16));
+  SAGE_TRY(check_ptr(out, "out", 16));
+  SAGE_TRY(check_ptr(dout, "dout", 16));
+  SAGE_TRY(check_ptr(lse, "lse", 4));
+  SAGE_TRY(check_ptr(dq, "dq", 16));
+  SAGE_TRY(check_ptr(dk, "dk", 16));
+  SAGE_TRY(check_ptr(dv, "dv", 16));
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  SAGE_TRY(check_scale(sm_scale));
+  SAGE_TRY(check_dims(B, H, N, d));
+  SAGE_TRY(check_train_mode(mode));
+  SAGE_TRY(check_ptr(workspace, "workspace", 256));
+  const int BH = B * H;
+  const int lo = mode & SAGE_MODE_MASK;
+  const sage::BwdLayout L = sage::make_bwd_layout(BH, N, d, lo);
+  if (workspace_bytes < L.total)
+    return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+  SAGE_TRY(check_device());
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the forward's codes of Q and K_s (same kernels, same layout), then V per
+  // token and dO per 64 rows
+  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, workspace, s));
+  const int Npad = L.f.Npad;
+  sage::Int8Job jv, jg;
+  jv.src = v; jv.codes = reinterpret_cast<int8_t*>(at(workspace, L.vc)); jv.scales = reinterpret_cast<float*>(at(workspace, L.vs));
+  jv.blk = 1; jv.code_rows = Npad; jv.nscale = Npad; jv.ntile = Npad / sage::kQTile;
+  jg.src = dout; jg.codes = reinterpret_cast<int8_t*>(at(workspace, L.gc)); jg.scales = reinterpret_cast<float*>(at(workspace, L.gs));
+  jg.blk = 64; jg.code_rows = Npad; jg.nscale = Npad / 64; jg.ntile = Npad / sage::kQTile;
+  SAGE_TRY(hip_status(sage::launch_int8_quant(jv, jg, BH, N, d, s), "backward quantization kernel"));
+  sage::BwdLaunch b;
+  b.BH = BH; b.N = N; b.Npad = Npad; b.d = d; b.causal = causal != 0;
+  b.qblk = lo == SAGE_MODE_INT8_Q64_K64 ? 64 : 128;
+  b.sm = sm_scale;
+  b.sl2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  b.o = static_cast<const _Float16*>(out); b.dout = static_cast<const _Float16*>(dout); b.lse = lse;
+  b.qc = reinterpret_cast<const int8_t*>(at(workspace, L.f.q_codes));
+  b.kc = reinterpret_cast<const int8_t*>(at(workspace, L.f.k_codes));
+  b.vc = reinterpret_cast<const int8_t*>(at(workspace, L.vc));
+  b.gc = reinterpret_cast<const int8_t*>(at(workspace, L.gc));
+  b.qt = reinterpret_cast<int8_t*>(at(workspace, L.qt));
+  b.kt = reinterpret_cast<int8_t*>(at(workspace, L.kt));
+  b.gt = reinterpret_cast<int8_t*>(at(workspace, L.gt));
+  b.qs = reinterpret_cast<const float*>(at(workspace, L.f.q_scales));
+  b.ks = reinterpret_cast<const float*>(at(workspace, L.f.k_scales));
+  b.vs = reinterpret_cast<const float*>(at(workspace, L.vs));
+  b.gs = reinterpret_cast<const float*>(at(workspace, L.gs));
+  b.ld = reinterpret_cast<float2*>(at(workspace, L.ld));
+  b.dq = dq; b.dk = dk; b.dv = dv;
+  return hip_status(sage::launch_attn_bwd(b, s), "backward kernels");
 }
 
 int sage_attn_dump_scores(const void* v, void* out, int B, int H, int N, int d, float sm_scale, int mode,

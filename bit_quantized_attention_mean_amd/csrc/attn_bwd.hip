@@ -1,0 +1,470 @@
+// INT8 attention backward pass for gfx950 (CDNA4).
+//
+// The 8-bit backward of "SageAttention3: Microscaling FP4 Attention for
+// Inference and An Exploration of 8-Bit Training" (abstract; the trainable
+// attention is INT8 on the scifaro.com page of related papers), laid out as
+// FlashAttention-2's backward, which the SageAttention page's "Experimental
+// setup" names as the base: the scores are recomputed from the forward's Q and
+// K codes, P = exp(S - L) from the forward's row log-sum-exp L, and
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO o O),  dS = P o (dP - D),
+//   dQ = sm_scale dS K_s,  dK = sm_scale dS^T Q,
+// every product on v_mfma_i32_32x32x32_i8 with int32 accumulation:
+//   * S: the forward's codes (Q per 128- or 64-token block, K_s per 64 keys);
+//   * dP: dO per 64-token block, V per token (one scale per key);
+//   * dV, dK, dQ: P and dS quantized per aligned 32 x 32 tile of the N x N
+//     matrices (a = max|x| over the tile, s = a / 127, code = rint(x / s)), so
+//     each product sums one tile exactly in int32 and the tile's partial is
+//     scaled and added in fp32.
+//
+// Work decomposition
+//   * bwd_dkdv_kernel: a workgroup owns 128 keys of one head (4 waves x 32)
+//     and walks the query tiles (64 queries, two 32-query sub-blocks). Per
+//     sub-block a wave computes S and dP for its 32 keys x 32 queries (K and V
+//     codes of its keys are the B operands, kept in registers; Q and dO rows
+//     come from LDS), P and dS in registers, their tile codes, then
+//     dV^T += dO^T P and dK^T += Q^T dS with the transposed Q and dO codes
+//     from LDS as A operands.
+//   * bwd_dq_kernel: a workgroup owns 128 queries (4 waves x 32) and walks the
+//     key tiles; per 32-key sub-block a wave computes S^T and dP^T (Q and dO
+//     codes of its queries in registers, K and V rows from LDS), dS and its
+//     tile codes, and dQ^T += K^T dS^T.
+//   * Both kernels form P and dS with the same fp32 expressions, so the two
+//     quantize every dS tile identically.
+//   * The first product's A rows are read in a permuted order (row r of the
+//     32-row operand holds index perm32(r)) so that the accumulator register i
+//     of lane group g holds index g*16 + i: the 16 codes of a lane are then,
+//     byte for byte, the B operand of the second product, whose A operand
+//     reads 16 consecutive indices at offset g*16.
+#include "sage_internal.h"
+
+#include <math.h>
+
+namespace sage {
+
+namespace {
+
+constexpr int kBT = 64;    // loop tile: queries (dK/dV) or keys (dQ)
+constexpr int kBW = 128;   // rows of the fixed dimension per workgroup (4 waves x 32)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Index held by row r of a 32-row A operand: the accumulator layout puts row
+// (i/4)*8 + g*4 + i%4 in register i of lane group g, and this makes that
+// index g*16 + i.
+__device__ __forceinline__ int perm32(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// INT8 codes of a 32 x 32 tile held as one accumulator (16 values per lane):
+// a = max|x| over the tile, s = fp32(a / 127), code = rint(x * fp32(1 / s)),
+// codes of register i in byte i of the returned operand. Returns s.
+__device__ __forceinline__ float tile_codes(const float (&x)[16], v4i& codes) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(x[i]));
+  const float a = wave_max(m);
+  const float s = a / 127.0f;
+  const float r = s > 0.f ? 1.0f / s : 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    unsigned word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float c = __builtin_rintf(x[w * 4 + b] * r);
+      c = fminf(fmaxf(c, -127.f), 127.f);
+      word |= (static_cast<unsigned>(static_cast<int>(c)) & 0xffu) << (8 * b);
+    }
+    codes[w] = static_cast<int>(word);
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Row terms: (L2, D) per query row, L2 = L * log2(e) from the forward's
+// natural-log L, D = sum_c dO_c O_c (products of fp16 values are exact in fp32,
+// summed in fp64, rounded once). Rows >= N: L2 = +inf (P = 0), D = 0.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const _Float16* __restrict__ o, const _Float16* __restrict__ dout,
+                                                       const float* __restrict__ lse, float2* __restrict__ ld,
+                                                       int N, int Npad, int BH) {
+  const long long r = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (r >= static_cast<long long>(BH) * Npad) return;
+  const int bh = static_cast<int>(r / Npad), n = static_cast<int>(r % Npad);
+  float2 out = make_float2(INFINITY, 0.f);
+  if (n < N) {
+    const size_t row = static_cast<size_t>(bh) * N + n;
+    const v8h* op = reinterpret_cast<const v8h*>(o + row * D);
+    const v8h* gp = reinterpret_cast<const v8h*>(dout + row * D);
+    double acc = 0.0;
+#pragma unroll 4
+    for (int c = 0; c < D / 8; ++c) {
+      const v8h a = op[c], b = gp[c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += static_cast<double>(static_cast<float>(a[e]) * static_cast<float>(b[e]));
+    }
+    out = make_float2(lse[row] * kLog2e, static_cast<float>(acc));
+  }
+  ld[r] = out;
+}
+
+// ---------------------------------------------------------------------------
+// Transposed copies of INT8 codes: src [BH, Npad, D] -> dst [BH, D, Npad],
+// 64 tokens per workgroup through LDS; blockIdx.y picks one of three jobs.
+// ---------------------------------------------------------------------------
+struct TJob {
+  const int8_t* src;
+  int8_t* dst;
+};
+template <int D>
+__global__ __launch_bounds__(256) void transpose_codes_kernel(TJob j0, TJob j1, TJob j2, int Npad) {
+  const TJob J = blockIdx.y == 0 ? j0 : (blockIdx.y == 1 ? j1 : j2);
+  constexpr int ROW = D + 4;
+  __shared__ unsigned char t[64 * ROW];
+  const int ntile = Npad / 64;
+  const int bh = blockIdx.x / ntile, n0 = (blockIdx.x % ntile) * 64;
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(J.src) + (static_cast<size_t>(bh) * Npad + n0) * D;
+  for (int i = threadIdx.x; i < 64 * D / 4; i += 256) {
+    const int row = i / (D / 4), col = i % (D / 4);
+    *reinterpret_cast<unsigned*>(t + row * ROW + col * 4) = *reinterpret_cast<const unsigned*>(src + row * D + col * 4);
+  }
+  __syncthreads();
+  unsigned char* dst = reinterpret_cast<unsigned char*>(J.dst) + static_cast<size_t>(bh) * D * Npad + n0;
+  for (int i = threadIdx.x; i < D * 16; i += 256) {
+    const int ch = i / 16, q = i % 16;  // 4 tokens 4q .. 4q+3 of channel ch
+    unsigned w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) w |= static_cast<unsigned>(t[(q * 4 + b) * ROW + ch]) << (8 * b);
+    *reinterpret_cast<unsigned*>(dst + static_cast<size_t>(ch) * Npad + q * 4) = w;
+  }
+}
+
+// Arguments shared by the two gradient kernels. Codes are zero-padded to
+// Npad rows; transposed codes are [BH, D, Npad].
+struct BwdArgs {
+  const int8_t* qc; const int8_t* qt; const float* qs; int qblk;  // Q codes, Q^T codes, scales [BH, Npad/qblk]
+  const int8_t* kc; const int8_t* kt; const float* ks;            // K_s codes, K_s^T codes, scales [BH, Npad/64]
+  const int8_t* vc; const float* vs;                              // V codes, scales [BH, Npad] (per token)
+  const int8_t* gc; const int8_t* gt; const float* gs;            // dO codes, dO^T codes, scales [BH, Npad/64]
+  const float2* ld;                                               // (L2, D) per row [BH, Npad]
+  float* dq; float* dk; float* dv;                                // fp32 [BH, N, D]
+  int N, Npad, BH;
+  float sl2, sm;                                                  // sm_scale * log2(e), sm_scale
+};
+
+// Workgroup id -> (head, 128-row block), heads spread contiguously over the
+// 8 XCDs (dispatch is round-robin over XCDs by id % 8) so a head's tiles stay
+// in one XCD's L2.
+__device__ __forceinline__ void map_wg(int id, int BH, int nblk, int& bh, int& blk) {
+  const int total = BH * nblk;
+  const int per = (total + 7) / 8;
+  const int x = id % 8, k = id / 8;
+  int lin = x * per + k;
+  if (total % 8 != 0 || lin >= total) lin = id;  // uneven split: plain order
+  bh = lin / nblk;
+  blk = lin % nblk;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NCH = D / 32;        // 32-channel chunks
+  constexpr int QROW = D + 16;       // LDS bytes per Q / dO row
+  constexpr int TROW = kBT + 16;     // LDS bytes per channel row of Q^T / dO^T
+  __shared__ __attribute__((aligned(16))) unsigned char sq[kBT * QROW];
+  __shared__ __attribute__((aligned(16))) unsigned char sg[kBT * QROW];
+  __shared__ __attribute__((aligned(16))) unsigned char sqt[D * TROW];
+  __shared__ __attribute__((aligned(16))) unsigned char sgt[D * TROW];
+  __shared__ float2 sld[kBT];
+
+  const int Npad = a.Npad, N = a.N;
+  const int nkb = Npad / kBW;
+  int bh, kblk;
+  map_wg(blockIdx.x, a.BH, nkb, bh, kblk);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k0w = kblk * kBW + wave * 32;   // first key of this wave
+  const int key = k0w + l32;
+
+  // B operands of S and dP: this lane's key, 16 channels per matrix op
+  v4i kb[NCH], vb[NCH];
+  {
+    const int8_t* kp = a.kc + (static_cast<size_t>(bh) * Npad + key) * D + g * 16;
+    const int8_t* vp = a.vc + (static_cast<size_t>(bh) * Npad + key) * D + g * 16;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      kb[c] = *reinterpret_cast<const v4i*>(kp + c * 32);
+      vb[c] = *reinterpret_cast<const v4i*>(vp + c * 32);
+    }
+  }
+  const float skw = a.ks[static_cast<size_t>(bh) * (Npad / 64) + k0w / 64];
+  const float svk = a.vs[static_cast<size_t>(bh) * Npad + key];
+  const float* qsh = a.qs + static_cast<size_t>(bh) * (Npad / a.qblk);
+  const float* gsh = a.gs + static_cast<size_t>(bh) * (Npad / 64);
+
+  v16f dkf[NCH], dvf[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dkf[c][i] = dvf[c][i] = 0.f;
+
+  const int qt_begin = CAUSAL ? (kblk * kBW) / kBT : 0;
+  const int qt_end = (N + kBT - 1) / kBT;
+  const unsigned char* qrows = reinterpret_cast<const unsigned char*>(a.qc) + static_cast<size_t>(bh) * Npad * D;
+  const unsigned char* grows = reinterpret_cast<const unsigned char*>(a.gc) + static_cast<size_t>(bh) * Npad * D;
+  const unsigned char* qtr = reinterpret_cast<const unsigned char*>(a.qt) + static_cast<size_t>(bh) * D * Npad;
+  const unsigned char* gtr = reinterpret_cast<const unsigned char*>(a.gt) + static_cast<size_t>(bh) * D * Npad;
+  const float2* ldh = a.ld + static_cast<size_t>(bh) * Npad;
+
+  for (int qt = qt_begin; qt < qt_end; ++qt) {
+    const int q0 = qt * kBT;
+    __syncthreads();   // the previous tile's LDS reads are done
+    for (int i = tid; i < kBT * D / 16; i += 256) {
+      const int row = i / (D / 16), col = (i % (D / 16)) * 16;
+      *reinterpret_cast<uint4*>(sq + row * QROW + col) =
+          *reinterpret_cast<const uint4*>(qrows + static_cast<size_t>(q0 + row) * D + col);
+      *reinterpret_cast<uint4*>(sg + row * QROW + col) =
+          *reinterpret_cast<const uint4*>(grows + static_cast<size_t>(q0 + row) * D + col);
+    }
+    for (int i = tid; i < D * kBT / 16; i += 256) {
+      const int ch = i / (kBT / 16), col = (i % (kBT / 16)) * 16;
+      *reinterpret_cast<uint4*>(sqt + ch * TROW + col) =
+          *reinterpret_cast<const uint4*>(qtr + static_cast<size_t>(ch) * Npad + q0 + col);
+      *reinterpret_cast<uint4*>(sgt + ch * TROW + col) =
+          *reinterpret_cast<const uint4*>(gtr + static_cast<size_t>(ch) * Npad + q0 + col);
+    }
+    if (tid < kBT) sld[tid] = ldh[q0 + tid];
+    __syncthreads();
+
+#pragma unroll 1
+    for (int sb = 0; sb < 2; ++sb) {
+      const int qb = q0 + sb * 32;                   // first query of the sub-block
+      if (CAUSAL && k0w > qb + 31) continue;          // every key of the wave is above every query
+      v16i s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0;
+      const int arow = (sb * 32 + perm32(l32)) * QROW + g * 16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        s = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sq + arow + c * 32), kb[c], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sg + arow + c * 32), vb[c], dp, 0, 0, 0);
+      }
+      const float sqb = qsh[qb / a.qblk];
+      const float gsb = gsh[qb / 64];
+      const float cs = (sqb * skw) * a.sl2;
+      const float gsv = gsb * svk;
+      float p[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qi = qb + g * 16 + i;
+        const float2 lq = sld[sb * 32 + g * 16 + i];
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[i]), cs, -lq.x));
+        if (key >= N || (CAUSAL && key > qi)) pv = 0.f;
+        p[i] = pv;
+        ds[i] = pv * __builtin_fmaf(static_cast<float>(dp[i]), gsv, -lq.y);
+      }
+      v4i pc, dsc;
+      const float sp = tile_codes(p, pc);
+      const float sds = tile_codes(ds, dsc);
+      const float fv = sp * gsb;
+      const float fk = (sds * sqb) * a.sm;
+      const int trow = l32 * TROW + sb * 32 + g * 16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        v16i zv, zk;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zv[i] = zk[i] = 0;
+        zv = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sgt + c * 32 * TROW + trow), pc, zv, 0, 0, 0);
+        zk = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sqt + c * 32 * TROW + trow), dsc, zk, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          dvf[c][i] = __builtin_fmaf(static_cast<float>(zv[i]), fv, dvf[c][i]);
+          dkf[c][i] = __builtin_fmaf(static_cast<float>(zk[i]), fk, dkf[c][i]);
+        }
+      }
+    }
+  }
+
+  // dV^T and dK^T: lane = key, register i of chunk c = channel c*32 + (i/4)*8 + g*4 + i%4
+  if (key < N) {
+    float* dvr = a.dv + (static_cast<size_t>(bh) * N + key) * D;
+    float* dkr = a.dk + (static_cast<size_t>(bh) * N + key) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ch = c * 32 + r * 8 + g * 4;
+        *reinterpret_cast<float4*>(dvr + ch) = make_float4(dvf[c][r * 4], dvf[c][r * 4 + 1], dvf[c][r * 4 + 2], dvf[c][r * 4 + 3]);
+        *reinterpret_cast<float4*>(dkr + ch) = make_float4(dkf[c][r * 4], dkf[c][r * 4 + 1], dkf[c][r * 4 + 2], dkf[c][r * 4 + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NCH = D / 32;
+  constexpr int KROW = D + 16;       // LDS bytes per K / V row
+  constexpr int TROW = kBT + 16;     // LDS bytes per channel row of K^T
+  __shared__ __attribute__((aligned(16))) unsigned char sk[kBT * KROW];
+  __shared__ __attribute__((aligned(16))) unsigned char sv[kBT * KROW];
+  __shared__ __attribute__((aligned(16))) unsigned char skt[D * TROW];
+  __shared__ float ssv[kBT];
+
+  const int Npad = a.Npad, N = a.N;
+  const int nqb = Npad / kBW;
+  int bh, qblk;
+  map_wg(blockIdx.x, a.BH, nqb, bh, qblk);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q0w = qblk * kBW + wave * 32;   // first query of this wave
+  const int query = q0w + l32;
+
+  // B operands of S^T and dP^T: this lane's query
+  v4i qb[NCH], gb[NCH];
+  {
+    const int8_t* qp = a.qc + (static_cast<size_t>(bh) * Npad + query) * D + g * 16;
+    const int8_t* gp = a.gc + (static_cast<size_t>(bh) * Npad + query) * D + g * 16;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      qb[c] = *reinterpret_cast<const v4i*>(qp + c * 32);
+      gb[c] = *reinterpret_cast<const v4i*>(gp + c * 32);
+    }
+  }
+  const float sqw = a.qs[static_cast<size_t>(bh) * (Npad / a.qblk) + q0w / a.qblk];
+  const float gsw = a.gs[static_cast<size_t>(bh) * (Npad / 64) + q0w / 64];
+  const float2 lq = a.ld[static_cast<size_t>(bh) * Npad + query];
+  const float* ksh = a.ks + static_cast<size_t>(bh) * (Npad / 64);
+
+  v16f dqf[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqf[c][i] = 0.f;
+
+  int kt_end = (N + kBT - 1) / kBT;
+  if (CAUSAL) kt_end = min(kt_end, (qblk * kBW + kBW) / kBT);
+  const unsigned char* krows = reinterpret_cast<const unsigned char*>(a.kc) + static_cast<size_t>(bh) * Npad * D;
+  const unsigned char* vrows = reinterpret_cast<const unsigned char*>(a.vc) + static_cast<size_t>(bh) * Npad * D;
+  const unsigned char* ktr = reinterpret_cast<const unsigned char*>(a.kt) + static_cast<size_t>(bh) * D * Npad;
+  const float* vsh = a.vs + static_cast<size_t>(bh) * Npad;
+
+  for (int kt = 0; kt < kt_end; ++kt) {
+    const int k0 = kt * kBT;
+    __syncthreads();
+    for (int i = tid; i < kBT * D / 16; i += 256) {
+      const int row = i / (D / 16), col = (i % (D / 16)) * 16;
+      *reinterpret_cast<uint4*>(sk + row * KROW + col) =
+          *reinterpret_cast<const uint4*>(krows + static_cast<size_t>(k0 + row) * D + col);
+      *reinterpret_cast<uint4*>(sv + row * KROW + col) =
+          *reinterpret_cast<const uint4*>(vrows + static_cast<size_t>(k0 + row) * D + col);
+    }
+    for (int i = tid; i < D * kBT / 16; i += 256) {
+      const int ch = i / (kBT / 16), col = (i % (kBT / 16)) * 16;
+      *reinterpret_cast<uint4*>(skt + ch * TROW + col) =
+          *reinterpret_cast<const uint4*>(ktr + static_cast<size_t>(ch) * Npad + k0 + col);
+    }
+    if (tid < kBT) ssv[tid] = vsh[k0 + tid];
+    __syncthreads();
+
+#pragma unroll 1
+    for (int sb = 0; sb < 2; ++sb) {
+      const int kb0 = k0 + sb * 32;                   // first key of the sub-block
+      if (CAUSAL && kb0 > q0w + 31) continue;
+      v16i s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0;
+      const int arow = (sb * 32 + perm32(l32)) * KROW + g * 16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        s = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sk + arow + c * 32), qb[c], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sv + arow + c * 32), gb[c], dp, 0, 0, 0);
+      }
+      const float skb = ksh[kb0 / 64];
+      const float cs = (sqw * skb) * a.sl2;
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kj = kb0 + g * 16 + i;
+        const float gsv = gsw * ssv[sb * 32 + g * 16 + i];
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[i]), cs, -lq.x));
+        if (kj >= N || (CAUSAL && kj > query)) pv = 0.f;
+        ds[i] = pv * __builtin_fmaf(static_cast<float>(dp[i]), gsv, -lq.y);
+      }
+      v4i dsc;
+      const float sds = tile_codes(ds, dsc);
+      const float fq = (sds * skb) * a.sm;
+      const int trow = l32 * TROW + sb * 32 + g * 16;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        v16i z;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = 0;
+        z = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(skt + c * 32 * TROW + trow), dsc, z, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dqf[c][i] = __builtin_fmaf(static_cast<float>(z[i]), fq, dqf[c][i]);
+      }
+    }
+  }
+
+  if (query < N) {
+    float* dqr = a.dq + (static_cast<size_t>(bh) * N + query) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<float4*>(dqr + c * 32 + r * 8 + g * 4) =
+            make_float4(dqf[c][r * 4], dqf[c][r * 4 + 1], dqf[c][r * 4 + 2], dqf[c][r * 4 + 3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const BwdLaunch& b, hipStream_t s) {
+  const int BH = b.BH, N = b.N, Npad = b.Npad, d = b.d;
+  {
+    const long long rows = static_cast<long long>(BH) * Npad;
+    const dim3 grid(static_cast<unsigned>((rows + 255) / 256));
+    if (d == 128) bwd_rows_kernel<128><<<grid, 256, 0, s>>>(b.o, b.dout, b.lse, b.ld, N, Npad, BH);
+    else bwd_rows_kernel<64><<<grid, 256, 0, s>>>(b.o, b.dout, b.lse, b.ld, N, Npad, BH);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const TJob j0{b.qc, b.qt}, j1{b.kc, b.kt}, j2{b.gc, b.gt};
+    const dim3 grid(BH * (Npad / 64), 3);
+    if (d == 128) transpose_codes_kernel<128><<<grid, 256, 0, s>>>(j0, j1, j2, Npad);
+    else transpose_codes_kernel<64><<<grid, 256, 0, s>>>(j0, j1, j2, Npad);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BwdArgs a;
+  a.qc = b.qc; a.qt = b.qt; a.qs = b.qs; a.qblk = b.qblk;
+  a.kc = b.kc; a.kt = b.kt; a.ks = b.ks;
+  a.vc = b.vc; a.vs = b.vs;
+  a.gc = b.gc; a.gt = b.gt; a.gs = b.gs;
+  a.ld = b.ld; a.dq = b.dq; a.dk = b.dk; a.dv = b.dv;
+  a.N = N; a.Npad = Npad; a.BH = BH; a.sl2 = b.sl2; a.sm = b.sm;
+  const dim3 grid(BH * (Npad / kBW)), block(256);
+#define SAGE_BWD(D_, C_)                                  \
+  do {                                                    \
+    bwd_dkdv_kernel<D_, C_><<<grid, block, 0, s>>>(a);    \
+    bwd_dq_kernel<D_, C_><<<grid, block, 0, s>>>(a);      \
+  } while (0)
+  if (d == 128) {
+    if (b.causal) SAGE_BWD(128, true); else SAGE_BWD(128, false);
+  } else {
+    if (b.causal) SAGE_BWD(64, true); else SAGE_BWD(64, false);
+  }
+#undef SAGE_BWD
+  return hipGetLastError();
+}
+
+}  // namespace sage

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
     const void* __restrict__ qsrc, const void* __restrict__ ksrc, const void* __restrict__ vsrc,
     const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vsc,
     _Float16* __restrict__ out, int N, int Npad, int qblk, float sl2, int BH, int* __restrict__ dump = nullptr,
-    int dbh = 0, int dqt = 0, int dkt = 0) {
+    int dbh = 0, int dqt = 0, int dkt = 0, float* __restrict__ lse = nullptr) {
   constexpr bool PERTOK = SM == kScoresInt8Token;
   constexpr bool F16 = SM == kScoresF16;
   static_assert(!(PV8 && F16), "INT8 P.V goes with INT8 scores");
@@ -930,7 +930,12 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
 #undef SAGE_LOAD_K
 
   // epilogue: O = O^T / l, rows >= N are padding and are not stored
-  const float inv = 1.f / pair_sum(l);
+  const float lsum = pair_sum(l);
+  const float inv = 1.f / lsum;
+  // the row log-sum-exp for a backward pass: m is the reference max and l the
+  // row sum against it, both in log2 units of the scaled scores
+  if (!PV8 && lse != nullptr && g == 0 && qrow < N)
+    lse[static_cast<size_t>(bh) * N + qrow] = (m + __log2f(lsum)) * 0.693147180559945309f;
   const float f0 = PV8 ? __builtin_amdgcn_exp2f(m0 - m) : 1.f;  // of's reference against the final max
   if (qrow < N) {
     _Float16* orow = out + (static_cast<size_t>(bh) * N + qrow) * D;
@@ -972,7 +977,8 @@ hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, con
     constexpr bool pp_ = attn_pingpong(D_, S_, P_, false);                                           \
     const dim3 grid_(a.BH * (a.Npad / (pp_ ? kWGQ : kWGQ / 2))), block_(pp_ ? 512 : 256);            \
     attn_int8_kernel<D_, C_, S_, P_><<<grid_, block_, 0, s>>>(q, k, vt, qs, ks, vs, o, a.N, a.Npad,  \
-                                                              qblk, a.sl2, a.BH);                    \
+                                                              qblk, a.sl2, a.BH, nullptr, 0, 0, 0,   \
+                                                              a.lse);                                \
   } while (0)
 #define SAGE_LAUNCH_SM(D_, C_)                                                    \
   do {                                                                            \

@@ -203,6 +203,7 @@ struct AttnArgs {
   float sl2 = 0.f;  // sm_scale * log2(e)
   int mode = 0;     // SAGE_MODE_* (no flags)
   void* out = nullptr;
+  float* lse = nullptr;  // fp32 [BH, N] row log-sum-exp (natural log), fp16-P modes only; may be null
 };
 // q, k: INT8 codes (padded to Npad rows) with scales qs, ks; or, for
 // SAGE_MODE_FP16, the caller's fp16 Q and K [BH, N, d] (qs, ks unused).
@@ -221,6 +222,51 @@ hipError_t launch_attn_int8_dump(const AttnArgs& a, const void* q, const void* k
 hipError_t launch_attn_mxfp4(const AttnArgs& a, const uint8_t* q4, const uint8_t* qe,
                              const uint8_t* k4, const uint8_t* ke, const uint8_t* v4,
                              const uint8_t* ve, hipStream_t s);
+
+// Workspace of the backward pass: the forward layout of its mode (Q and K_s
+// codes and scales, K sums and mean) followed by the backward's own regions.
+struct BwdLayout {
+  Layout f;
+  size_t qt = 0, kt = 0, gt = 0;   // int8 transposed codes [BH, d, Npad] of Q, K_s, dO
+  size_t vc = 0, gc = 0;           // int8 codes [BH, Npad, d] of V (per token) and dO (per 64 rows)
+  size_t vs = 0, gs = 0;           // fp32 scales [BH, Npad] and [BH, Npad / 64]
+  size_t ld = 0;                   // float2 (L2, D) per row [BH, Npad]
+  size_t total = 0;
+};
+inline BwdLayout make_bwd_layout(long long BH, int N, int d, int mode_lo) {
+  BwdLayout L;
+  L.f = make_layout(BH, N, d, mode_lo, true);
+  size_t off = L.f.total;
+  auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+  const size_t rows = size_t(BH) * L.f.Npad;
+  L.qt = take(rows * d);
+  L.kt = take(rows * d);
+  L.gt = take(rows * d);
+  L.vc = take(rows * d);
+  L.gc = take(rows * d);
+  L.vs = take(rows * 4);
+  L.gs = take(rows / 64 * 4);
+  L.ld = take(rows * 8);
+  L.total = off;
+  return L;
+}
+
+// The backward pass after its quantization: row terms, transposed codes, then
+// the dK/dV and dQ kernels.
+struct BwdLaunch {
+  int BH = 0, N = 0, Npad = 0, d = 0, qblk = 128;
+  bool causal = false;
+  float sl2 = 0.f, sm = 0.f;
+  const _Float16* o = nullptr;     // forward output [BH, N, d]
+  const _Float16* dout = nullptr;  // dO [BH, N, d]
+  const float* lse = nullptr;      // [BH, N]
+  const int8_t* qc = nullptr; const int8_t* kc = nullptr; const int8_t* vc = nullptr; const int8_t* gc = nullptr;
+  int8_t* qt = nullptr; int8_t* kt = nullptr; int8_t* gt = nullptr;
+  const float* qs = nullptr; const float* ks = nullptr; const float* vs = nullptr; const float* gs = nullptr;
+  float2* ld = nullptr;
+  float* dq = nullptr; float* dk = nullptr; float* dv = nullptr;  // fp32 [BH, N, d]
+};
+hipError_t launch_attn_bwd(const BwdLaunch& b, hipStream_t s);
 
 // One wave spins for `cycles` shader clocks and writes to out[0..1] the
 // cycles counted and the device wall-clock ticks over the same interval.

@@ -136,6 +136,61 @@ int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out
                           int d, int causal, float sm_scale, int mode, void* stream);
 
 /*
+ * Training forward: sage_attn_fwd that also writes the row log-sum-exp a
+ * backward pass needs (FlashAttention-2's saved statistic; the SageAttention
+ * page's "Experimental setup" names FlashAttention-2 as the base).
+ *   lse   fp32 [B, H, N] device, written: lse[b,h,i] = ln sum_j exp(s_ij)
+ *         over the scaled (and, with smoothing, mean-smoothed) scores the
+ *         kernel used, where the sum adds the fp16-rounded weights that
+ *         multiply V. 4-byte aligned.
+ *   mode  SAGE_MODE_INT8_Q128_K64 or SAGE_MODE_INT8_Q64_K64, optionally
+ *         | SAGE_FLAG_NO_SMOOTH; other modes return SAGE_ERR_UNSUPPORTED.
+ * Other arguments, the workspace and the errors as sage_attn_fwd (a workspace
+ * of sage_attn_bwd_workspace_size bytes also serves).
+ */
+int sage_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                      int N, int d, int causal, float sm_scale, int mode, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace sage_attn_bwd needs (0 if the arguments are
+ * invalid or the mode is not a per-block INT8 mode).
+ */
+size_t sage_attn_bwd_workspace_size(int B, int H, int N, int d, int mode);
+
+/*
+ * INT8 backward pass: the gradients of the loss sum(out * dout) with respect
+ * to q, k and v, for the 8-bit attention training of "SageAttention3:
+ * Microscaling FP4 Attention for Inference and An Exploration of 8-Bit
+ * Training" (abstract; INT8 per the scifaro.com list of related papers) in
+ * FlashAttention-2's form (recompute the scores from Q and K, P = exp(S -
+ * lse)). Every one of its five matrix products runs on INT8 codes with int32
+ * accumulation: the forward's Q and mean-smoothed K codes for the scores, dO
+ * per 64-token block and V per token for dO V^T, and P and dS quantized per
+ * aligned 32 x 32 tile (max|x| / 127) for P^T dO, dS K and dS^T Q.
+ *   q, k, v      fp16 [B, H, N, d] device: the forward's inputs.
+ *   out, lse     the forward's output (fp16 [B, H, N, d]) and row log-sum-exp
+ *                (fp32 [B, H, N]) from sage_attn_fwd_lse with the same mode,
+ *                causal and sm_scale.
+ *   dout         fp16 [B, H, N, d] device: the gradient of the loss with
+ *                respect to out.
+ *   dq, dk, dv   fp32 [B, H, N, d] device, written (16-byte aligned; may not
+ *                alias the inputs). dk is the gradient with respect to k
+ *                itself: the one through the token mean of the smoothing is
+ *                zero in exact arithmetic (every row of dS sums to zero) and
+ *                is not formed.
+ *   mode         SAGE_MODE_INT8_Q128_K64 or SAGE_MODE_INT8_Q64_K64 (the Q
+ *                block of the scores), optionally | SAGE_FLAG_NO_SMOOTH.
+ *   workspace, workspace_bytes  at least sage_attn_bwd_workspace_size().
+ * Returns SAGE_OK or a negative sage_status_t with the conventions of
+ * sage_attn_fwd.
+ */
+int sage_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                  const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                  int causal, float sm_scale, int mode, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
  * First phase of sage_attn_fwd: the K channel mean and the quantization of
  * Q, K (and of V, in the modes that quantize it: MXFP4, MX-FP8 or INT8 codes)
  * into `workspace`. The steps are those of sage_quant_qk / sage_quant_mxfp4 /

@@ -184,3 +184,29 @@ def test_noalloc_entry_point_validation():
     assert sa.sage_attn_workspace_size(4, 32, 8192, 128, 2) <= sa.SAGE_NOALLOC_SCRATCH_BYTES
     if not _gpu_visible():
         assert f() == NODEV
+
+
+def test_backward_entry_points_validation():
+    # the training forward and the backward pass: per-block INT8 modes only,
+    # every argument checked before any HIP call
+    ws = sa.sage_attn_bwd_workspace_size(1, 2, 256, 64, 0)
+    assert ws > sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
+    assert sa.sage_attn_bwd_workspace_size(1, 2, 256, 64, 1 | sa.SAGE_FLAG_NO_SMOOTH) > 0
+    for bad_mode in (2, 3, 4, 5, 6, 7):
+        assert sa.sage_attn_bwd_workspace_size(1, 2, 256, 64, bad_mode) == 0
+    assert sa.sage_attn_bwd_workspace_size(1, 2, 256, 96, 0) == 0
+    LSE = ctypes.c_void_p(4096)
+    fl = lambda q=A16, out=A16, lse=LSE, N=256, d=64, causal=0, scale=0.125, mode=0, w=A16, nb=1 << 30: \
+        lib.sage_attn_fwd_lse(q, A16, A16, out, lse, 1, 2, N, d, causal, scale, mode, w, nb, None)
+    assert fl(lse=None) == INVALID and fl(q=None) == INVALID and fl(out=A16 + 2) == INVALID
+    assert fl(mode=2) == UNSUP and fl(mode=3) == UNSUP and fl(d=96) == UNSUP
+    assert fl(scale=float("nan")) == INVALID and fl(causal=2) == INVALID
+    assert fl(nb=16) == WS
+    fb = lambda q=A16, dout=A16, lse=LSE, dq=A16, N=256, d=64, causal=0, scale=0.125, mode=0, w=A16, nb=1 << 30: \
+        lib.sage_attn_bwd(q, A16, A16, A16, dout, lse, dq, A16, A16, 1, 2, N, d, causal, scale, mode, w, nb, None)
+    assert fb(dout=None) == INVALID and fb(lse=None) == INVALID and fb(dq=A16 + 4) == INVALID
+    assert fb(mode=6) == UNSUP and fb(mode=4) == UNSUP and fb(d=32) == UNSUP
+    assert fb(scale=-1.0) == INVALID and fb(N=0) == INVALID
+    assert fb(nb=ws - 1) == WS and "needed" in sa.sage_last_error()
+    if not _gpu_visible():
+        assert fl() == NODEV and fb() == NODEV

@@ -28,6 +28,13 @@ Also on the JSON line:
                 GPU is touched. `cores` is the number of workers.
   median_ms_per_step  median of per-step times (separate pass, an event
                 between steps).
+  backward      (INT8 per-block modes) the 8-bit backward pass on the same
+                workload: sage_attn_bwd (quantization of Q, K, V and dO, row
+                terms, transposed codes, the dK/dV and dQ kernels) timed with
+                HIP events, its throughput as 10*B*H*N^2*d (five products,
+                halved if causal) per call, against the INT8 peak; the
+                training forward (sage_attn_fwd_lse) and torch's FP16 SDPA
+                backward on the same inputs for context.
   shader_clock_mhz  the shader clock measured by a probe wave (cycle counter
                 against the device wall clock) on a second stream during the
                 last warm-up steps, and on an idle GPU (throttling shows as
@@ -240,6 +247,44 @@ def select_layers(names, torch, sa):
         torch.cuda.empty_cache()
 
 
+def backward_bench(w, mode, qd, kd, vd, args, sa, torch, sdpa=True):
+    """Times the INT8 backward pass (sage_attn_bwd) on the workload's resident inputs."""
+    from synthetic import make_grad
+    dev = qd.device
+    gd = torch.from_numpy(make_grad(w.B, w.H, w.N, w.d, seed=w.seed)).to(dev)
+    wsb = sa.make_bwd_workspace(w.B, w.H, w.N, w.d, mode, dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    shape = (w.B, w.H, w.N, w.d)
+    dq, dk, dv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
+    fwd = lambda: sa.sage_attn_fwd_lse(qd, kd, vd, out, lse, causal=w.causal, sm_scale=w.sm_scale, mode=mode,
+                                       workspace=wsb)
+    ms_fwd, _ = timed(fwd, args.steps, args.warmup, torch)
+    bwd = lambda: sa.sage_attn_bwd(qd, kd, vd, out, gd, lse, dq, dk, dv, causal=w.causal, sm_scale=w.sm_scale,
+                                   mode=mode, workspace=wsb)
+    ms_bwd, _ = timed(bwd, args.steps, args.warmup, torch)
+    ops = 2.5 * w.attention_ops()    # five products of 2 N^2 d each against the forward's two
+    tops = ops / (ms_bwd * 1e-3) / 1e12
+    log(f"[bench] {w.name}: INT8 backward {ms_bwd:.4f} ms ({tops:.1f} TOPS), training forward {ms_fwd:.4f} ms")
+    rec = {"ms": round(ms_bwd, 4), "tops": round(tops, 2), "ops_per_call": ops, "peak": PEAK["int8"],
+           "frac": round(tops / PEAK["int8"], 4), "fwd_lse_ms": round(ms_fwd, 4),
+           "grad_dtype": "f32", "dout": "standard normal, synthetic"}
+    if sdpa:
+        import torch.nn.functional as F
+        qg, kg, vg = (x.detach().clone().requires_grad_(True) for x in (qd, kd, vd))
+        o = F.scaled_dot_product_attention(qg, kg, vg, is_causal=w.causal, scale=w.sm_scale)
+        g16 = gd
+        tb = lambda: torch.autograd.grad(o, (qg, kg, vg), g16, retain_graph=True)
+        ms_t, _ = timed(tb, max(5, args.steps // 5), 3, torch)
+        rec["torch_sdpa_fp16_bwd_ms"] = round(ms_t, 4)
+        rec["speedup_vs_torch_sdpa_bwd"] = round(ms_t / ms_bwd, 3)
+        log(f"[bench] torch SDPA fp16 backward: {ms_t:.4f} ms")
+        del qg, kg, vg, o
+    del gd, wsb, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +299,7 @@ def main():
                     help="override the workload's quantization mode (ablations; fp16 = unquantized baseline; "
                          "int8_pv* = P and V in INT8 as well)")
     ap.add_argument("--no-smooth", action="store_true", help="skip the K mean subtraction (ablation)")
+    ap.add_argument("--no-bwd", action="store_true", help="skip timing the INT8 backward pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--select", nargs="*", default=None, metavar="WORKLOAD",
@@ -382,6 +428,9 @@ def main():
         sdpa = {"ms": round(ms_sdpa, 4), "tflops": round(ops / (ms_sdpa * 1e-3) / 1e12, 2),
                 "step_speedup": round(ms_sdpa / ms_step, 3), "kernel_speedup": round(ms_sdpa / ms_attn, 3)}
         log(f"[bench] torch SDPA fp16: {ms_sdpa:.4f} ms; this step is {ms_sdpa / ms_step:.2f}x faster")
+    bwd = None
+    if mode in (0, 1) and not args.no_bwd:
+        bwd = backward_bench(w, mode | flags, qd, kd, vd, args, sa, torch, sdpa=not args.no_sdpa)
     del qd, kd, vd, ws, out
     torch.cuda.empty_cache()
 
@@ -412,6 +461,7 @@ def main():
         "cpu_baseline": cpu,
         "torch_sdpa_fp16": sdpa,
         "shader_clock_mhz": {"under_load": round(clk_load), "idle": round(clk_idle)},
+        "backward": bwd,
     }
     print(json.dumps(line), flush=True)
 

@@ -58,26 +58,46 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// INT8 codes of a 32 x 32 tile held as one accumulator (16 values per lane):
-// a = max|x| over the tile, s = fp32(a / 127), code = rint(x * fp32(1 / s)),
-// codes of register i in byte i of the returned operand. Returns s.
-__device__ __forceinline__ float tile_codes(const float (&x)[16], v4i& codes) {
+// Tile maximum of |x| over a 32 x 32 tile held as one accumulator (16 values
+// per lane), and its scale s = fp32(a / 127) with the multiplier fp32(1 / s)
+// (0 for an all-zero tile).
+__device__ __forceinline__ float tile_scale(const float (&x)[16], float& r) {
   float m = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(x[i]));
   const float a = wave_max(m);
   const float s = a / 127.0f;
-  const float r = s > 0.f ? 1.0f / s : 0.f;
+  r = s > 0.f ? 1.0f / s : 0.f;
+  return s;
+}
+
+// INT8 codes rint(x * r) of a tile whose values are >= 0 (P), register i in
+// byte i: v_cvt_pk_u8_f32 rounds to nearest even (0 <= x r <= 127).
+__device__ __forceinline__ float tile_codes_nonneg(const float (&x)[16], v4i& codes) {
+  float r;
+  const float s = tile_scale(x, r);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     unsigned word = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float c = __builtin_rintf(x[w * 4 + b] * r);
-      c = fminf(fmaxf(c, -127.f), 127.f);
-      word |= (static_cast<unsigned>(static_cast<int>(c)) & 0xffu) << (8 * b);
-    }
+    for (int b = 0; b < 4; ++b) word = __builtin_amdgcn_cvt_pk_u8_f32(x[w * 4 + b] * r, b, word);
     codes[w] = static_cast<int>(word);
+  }
+  return s;
+}
+
+// Signed codes: rint(x * r) (|x r| <= 127), offset by 128 to an exact integer in
+// [1, 255], packed by v_cvt_pk_u8_f32, and the offset taken back per byte
+// (XOR 0x80 turns c + 128 into the two's complement byte of c).
+__device__ __forceinline__ float tile_codes_signed(const float (&x)[16], v4i& codes) {
+  float r;
+  const float s = tile_scale(x, r);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    unsigned word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(x[w * 4 + b] * r) + 128.f, b, word);
+    codes[w] = static_cast<int>(word ^ 0x80808080u);
   }
   return s;
 }
@@ -91,24 +111,25 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(const _Float16* __restrict__ o, const _Float16* __restrict__ dout,
                                                        const float* __restrict__ lse, float2* __restrict__ ld,
                                                        int N, int Npad, int BH) {
-  const long long r = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
-  if (r >= static_cast<long long>(BH) * Npad) return;
-  const int bh = static_cast<int>(r / Npad), n = static_cast<int>(r % Npad);
-  float2 out = make_float2(INFINITY, 0.f);
-  if (n < N) {
-    const size_t row = static_cast<size_t>(bh) * N + n;
-    const v8h* op = reinterpret_cast<const v8h*>(o + row * D);
-    const v8h* gp = reinterpret_cast<const v8h*>(dout + row * D);
-    double acc = 0.0;
-#pragma unroll 4
-    for (int c = 0; c < D / 8; ++c) {
-      const v8h a = op[c], b = gp[c];
+  constexpr int LPR = D / 8;          // lanes per row, 8 channels (16 bytes) each
+  constexpr int RPB = 256 / LPR;      // rows per workgroup
+  const long long total = static_cast<long long>(BH) * Npad;
+  const long long r = static_cast<long long>(blockIdx.x) * RPB + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
+  const bool in = r < total;
+  const int bh = in ? static_cast<int>(r / Npad) : 0, n = in ? static_cast<int>(r % Npad) : 0;
+  const bool live = in && n < N;
+  const size_t row = static_cast<size_t>(bh) * N + n;
+  double acc = 0.0;
+  if (live) {
+    const v8h a = *reinterpret_cast<const v8h*>(o + row * D + c * 8);
+    const v8h b = *reinterpret_cast<const v8h*>(dout + row * D + c * 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += static_cast<double>(static_cast<float>(a[e]) * static_cast<float>(b[e]));
-    }
-    out = make_float2(lse[row] * kLog2e, static_cast<float>(acc));
+    for (int e = 0; e < 8; ++e) acc += static_cast<double>(static_cast<float>(a[e]) * static_cast<float>(b[e]));
   }
-  ld[r] = out;
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  if (in && c == 0) ld[r] = live ? make_float2(lse[row] * kLog2e, static_cast<float>(acc)) : make_float2(INFINITY, 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -258,19 +279,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       const float gsb = gsh[qb / 64];
       const float cs = (sqb * skw) * a.sl2;
       const float gsv = gsb * svk;
+      // masking only in sub-blocks with keys >= N or above the diagonal
+      const bool masked = k0w + 31 >= N || (CAUSAL && k0w + 31 > qb);
       float p[16], ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int qi = qb + g * 16 + i;
         const float2 lq = sld[sb * 32 + g * 16 + i];
         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[i]), cs, -lq.x));
-        if (key >= N || (CAUSAL && key > qi)) pv = 0.f;
+        if (masked && (key >= N || (CAUSAL && key > qb + g * 16 + i))) pv = 0.f;
         p[i] = pv;
         ds[i] = pv * __builtin_fmaf(static_cast<float>(dp[i]), gsv, -lq.y);
       }
       v4i pc, dsc;
-      const float sp = tile_codes(p, pc);
-      const float sds = tile_codes(ds, dsc);
+      const float sp = tile_codes_nonneg(p, pc);
+      const float sds = tile_codes_signed(ds, dsc);
       const float fv = sp * gsb;
       const float fk = (sds * sqb) * a.sm;
       const int trow = l32 * TROW + sb * 32 + g * 16;
@@ -389,17 +411,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       }
       const float skb = ksh[kb0 / 64];
       const float cs = (sqw * skb) * a.sl2;
+      const bool masked = kb0 + 31 >= N || (CAUSAL && kb0 + 31 > q0w);
       float ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kj = kb0 + g * 16 + i;
         const float gsv = gsw * ssv[sb * 32 + g * 16 + i];
         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[i]), cs, -lq.x));
-        if (kj >= N || (CAUSAL && kj > query)) pv = 0.f;
+        if (masked && (kj >= N || (CAUSAL && kj > query))) pv = 0.f;
         ds[i] = pv * __builtin_fmaf(static_cast<float>(dp[i]), gsv, -lq.y);
       }
       v4i dsc;
-      const float sds = tile_codes(ds, dsc);
+      const float sds = tile_codes_signed(ds, dsc);
       const float fq = (sds * skb) * a.sm;
       const int trow = l32 * TROW + sb * 32 + g * 16;
 #pragma unroll
@@ -431,7 +454,8 @@ hipError_t launch_attn_bwd(const BwdLaunch& b, hipStream_t s) {
   const int BH = b.BH, N = b.N, Npad = b.Npad, d = b.d;
   {
     const long long rows = static_cast<long long>(BH) * Npad;
-    const dim3 grid(static_cast<unsigned>((rows + 255) / 256));
+    const int rpb = 256 / (d / 8);
+    const dim3 grid(static_cast<unsigned>((rows + rpb - 1) / rpb));
     if (d == 128) bwd_rows_kernel<128><<<grid, 256, 0, s>>>(b.o, b.dout, b.lse, b.ld, N, Npad, BH);
     else bwd_rows_kernel<64><<<grid, 256, 0, s>>>(b.o, b.dout, b.lse, b.ld, N, Npad, BH);
     const hipError_t e = hipGetLastError();

@@ -17,6 +17,9 @@
 //     scaled and added in fp32.
 //
 // Work decomposition
+//   * Tiles are loaded straight into LDS (buffer loads with an LDS
+//     destination) and double-buffered: a tile's loads are issued before the
+//     previous tile's work and waited for after it.
 //   * bwd_dkdv_kernel: a workgroup owns 128 keys of one head (4 waves x 32)
 //     and walks the query tiles (64 queries, two 32-query sub-blocks). Per
 //     sub-block a wave computes S and dP for its 32 keys x 32 queries (K and V
@@ -51,6 +54,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 // (i/4)*8 + g*4 + i%4 in register i of lane group g, and this makes that
 // index g*16 + i.
 __device__ __forceinline__ int perm32(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
+
+// Waits until none of this wave's vector memory operations is outstanding
+// (s_waitcnt with only the vmcnt field set, so LDS and scalar counters are
+// left alone).
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0xF70); }
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// lds + 16 l (buffer_load_dwordx4 with an LDS destination; the LDS address is
+// wave-uniform). A non-template helper: the host-side pass of a kernel
+// template that names this builtin drops the kernel.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -190,18 +206,51 @@ __device__ __forceinline__ void map_wg(int id, int BH, int nblk, int& bh, int& b
 }
 
 // ---------------------------------------------------------------------------
+// Tile staging shared by the two gradient kernels: every tile (64 rows of d
+// code bytes, or d rows of 64 code bytes for a transposed tile) is loaded
+// straight into LDS by buffer loads with an LDS destination (one wave
+// instruction = 1 KiB, lane l's 16 bytes at +16 l), double-buffered: the
+// next tile's loads are issued before the current tile's work and waited for
+// at its end, so they need no staging registers. Rows are unpadded; the
+// 16-byte chunks are permuted within each row (XOR swizzle) so that the
+// matrix ops' LDS reads stay free of bank conflicts: in a row-major tile,
+// chunk c of row r sits at position c ^ swz_rm(r), chosen for the reads of
+// rows perm32(l32) (16 lanes of a read phase hit 16 distinct 16-byte bank
+// groups of the 256-byte bank line); in a transposed tile (64-byte rows),
+// at c ^ swz_tr(r), for reads of 16 consecutive rows.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz_rm(int r) {
+  return D == 128 ? (((r >> 1) & 3) | (((r >> 4) & 1) << 2)) : (((r >> 2) & 1) | (((r >> 4) & 1) << 1));
+}
+__device__ __forceinline__ int swz_tr(int r) { return (r >> 2) & 3; }
+
+// End of a tile: this wave's loads of the next tile have landed, every wave is
+// past its reads of the current stage; the acquire fence keeps the next
+// tile's LDS reads behind the barrier (a release fence would also wait for
+// loads in flight).
+__device__ __forceinline__ void tile_barrier() {
+  wait_vmcnt0();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, const float* __restrict__ qsp,
+                                                            const float* __restrict__ ksp,
+                                                            const float* __restrict__ vsp,
+                                                            const float* __restrict__ gsp) {
   constexpr int NCH = D / 32;        // 32-channel chunks
-  constexpr int QROW = D + 16;       // LDS bytes per Q / dO row
-  constexpr int TROW = kBT + 16;     // LDS bytes per channel row of Q^T / dO^T
-  __shared__ __attribute__((aligned(16))) unsigned char sq[kBT * QROW];
-  __shared__ __attribute__((aligned(16))) unsigned char sg[kBT * QROW];
-  __shared__ __attribute__((aligned(16))) unsigned char sqt[D * TROW];
-  __shared__ __attribute__((aligned(16))) unsigned char sgt[D * TROW];
-  __shared__ float2 sld[kBT];
+  constexpr int TB = kBT * D;        // bytes of a tile (row-major or transposed)
+  constexpr int NI = TB / 4096;      // load instructions per wave and tile (4 waves x 1 KiB)
+  constexpr int CPR = D / 16;        // 16-byte chunks per row-major row
+  static_assert(TB % 4096 == 0, "tiles fill whole wave instructions");
+  __shared__ __attribute__((aligned(16))) unsigned char sq0[TB], sq1[TB], sg0[TB], sg1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char sqt0[TB], sqt1[TB], sgt0[TB], sgt1[TB];
+  __shared__ __attribute__((aligned(16))) float2 sld0[128], sld1[128];
 
   const int Npad = a.Npad, N = a.N;
   const int nkb = Npad / kBW;
@@ -223,10 +272,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       vb[c] = *reinterpret_cast<const v4i*>(vp + c * 32);
     }
   }
-  const float skw = a.ks[static_cast<size_t>(bh) * (Npad / 64) + k0w / 64];
-  const float svk = a.vs[static_cast<size_t>(bh) * Npad + key];
-  const float* qsh = a.qs + static_cast<size_t>(bh) * (Npad / a.qblk);
-  const float* gsh = a.gs + static_cast<size_t>(bh) * (Npad / 64);
+  // the scales are read through restrict-qualified kernel arguments: the
+  // compiler then loads the per-tile ones with scalar loads, which do not
+  // count against (and wait for) the tile loads in flight
+  const float skw = ksp[static_cast<size_t>(bh) * (Npad / 64) + k0w / 64];
+  const float svk = vsp[static_cast<size_t>(bh) * Npad + key];
+  const float* qsh = qsp + static_cast<size_t>(bh) * (Npad / a.qblk);
+  const float* gsh = gsp + static_cast<size_t>(bh) * (Npad / 64);
 
   v16f dkf[NCH], dvf[NCH];
 #pragma unroll
@@ -236,81 +288,115 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int qt_begin = CAUSAL ? (kblk * kBW) / kBT : 0;
   const int qt_end = (N + kBT - 1) / kBT;
-  const unsigned char* qrows = reinterpret_cast<const unsigned char*>(a.qc) + static_cast<size_t>(bh) * Npad * D;
-  const unsigned char* grows = reinterpret_cast<const unsigned char*>(a.gc) + static_cast<size_t>(bh) * Npad * D;
-  const unsigned char* qtr = reinterpret_cast<const unsigned char*>(a.qt) + static_cast<size_t>(bh) * D * Npad;
-  const unsigned char* gtr = reinterpret_cast<const unsigned char*>(a.gt) + static_cast<size_t>(bh) * D * Npad;
-  const float2* ldh = a.ld + static_cast<size_t>(bh) * Npad;
-
-  for (int qt = qt_begin; qt < qt_end; ++qt) {
-    const int q0 = qt * kBT;
-    __syncthreads();   // the previous tile's LDS reads are done
-    for (int i = tid; i < kBT * D / 16; i += 256) {
-      const int row = i / (D / 16), col = (i % (D / 16)) * 16;
-      *reinterpret_cast<uint4*>(sq + row * QROW + col) =
-          *reinterpret_cast<const uint4*>(qrows + static_cast<size_t>(q0 + row) * D + col);
-      *reinterpret_cast<uint4*>(sg + row * QROW + col) =
-          *reinterpret_cast<const uint4*>(grows + static_cast<size_t>(q0 + row) * D + col);
-    }
-    for (int i = tid; i < D * kBT / 16; i += 256) {
-      const int ch = i / (kBT / 16), col = (i % (kBT / 16)) * 16;
-      *reinterpret_cast<uint4*>(sqt + ch * TROW + col) =
-          *reinterpret_cast<const uint4*>(qtr + static_cast<size_t>(ch) * Npad + q0 + col);
-      *reinterpret_cast<uint4*>(sgt + ch * TROW + col) =
-          *reinterpret_cast<const uint4*>(gtr + static_cast<size_t>(ch) * Npad + q0 + col);
-    }
-    if (tid < kBT) sld[tid] = ldh[q0 + tid];
-    __syncthreads();
-
-#pragma unroll 1
-    for (int sb = 0; sb < 2; ++sb) {
-      const int qb = q0 + sb * 32;                   // first query of the sub-block
-      if (CAUSAL && k0w > qb + 31) continue;          // every key of the wave is above every query
-      v16i s, dp;
+  const auto rq = buffer_rsrc(a.qc + static_cast<size_t>(bh) * Npad * D, static_cast<unsigned>(Npad) * D);
+  const auto rg = buffer_rsrc(a.gc + static_cast<size_t>(bh) * Npad * D, static_cast<unsigned>(Npad) * D);
+  const auto rqt = buffer_rsrc(a.qt + static_cast<size_t>(bh) * D * Npad, static_cast<unsigned>(Npad) * D);
+  const auto rgt = buffer_rsrc(a.gt + static_cast<size_t>(bh) * D * Npad, static_cast<unsigned>(Npad) * D);
+  const auto rld = buffer_rsrc(a.ld + static_cast<size_t>(bh) * Npad, static_cast<unsigned>(Npad) * 8);
+  // per-lane sources of this wave's load instructions (tile offset added per tile)
+  int rmo[NI], tro[NI];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0;
-      const int arow = (sb * 32 + perm32(l32)) * QROW + g * 16;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        s = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sq + arow + c * 32), kb[c], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sg + arow + c * 32), vb[c], dp, 0, 0, 0);
-      }
-      const float sqb = qsh[qb / a.qblk];
-      const float gsb = gsh[qb / 64];
-      const float cs = (sqb * skw) * a.sl2;
-      const float gsv = gsb * svk;
-      // masking only in sub-blocks with keys >= N or above the diagonal
-      const bool masked = k0w + 31 >= N || (CAUSAL && k0w + 31 > qb);
-      float p[16], ds[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float2 lq = sld[sb * 32 + g * 16 + i];
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[i]), cs, -lq.x));
-        if (masked && (key >= N || (CAUSAL && key > qb + g * 16 + i))) pv = 0.f;
-        p[i] = pv;
-        ds[i] = pv * __builtin_fmaf(static_cast<float>(dp[i]), gsv, -lq.y);
-      }
-      v4i pc, dsc;
-      const float sp = tile_codes_nonneg(p, pc);
-      const float sds = tile_codes_signed(ds, dsc);
-      const float fv = sp * gsb;
-      const float fk = (sds * sqb) * a.sm;
-      const int trow = l32 * TROW + sb * 32 + g * 16;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        v16i zv, zk;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) zv[i] = zk[i] = 0;
-        zv = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sgt + c * 32 * TROW + trow), pc, zv, 0, 0, 0);
-        zk = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sqt + c * 32 * TROW + trow), dsc, zk, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          dvf[c][i] = __builtin_fmaf(static_cast<float>(zv[i]), fv, dvf[c][i]);
-          dkf[c][i] = __builtin_fmaf(static_cast<float>(zk[i]), fk, dkf[c][i]);
-        }
-      }
-    }
+  for (int u = 0; u < NI; ++u) {
+    const int i = (wave * NI + u) * 64 + lane;
+    const int rr = i / CPR, rp = i % CPR;
+    rmo[u] = rr * D + ((rp ^ swz_rm<D>(rr)) * 16);
+    const int tr = i / 4, tp = i % 4;
+    tro[u] = tr * Npad + ((tp ^ swz_tr(tr)) * 16);
   }
+  // LDS read offsets: S / dP A operands (rows perm32(l32) of each 32-row
+  // half), and the transposed A operands (channel rows l32 of each 32-channel
+  // chunk, for either 32-row half)
+  int aro[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int r = perm32(l32);
+    aro[c] = r * D + (((2 * c + g) ^ swz_rm<D>(r)) * 16);
+  }
+  const int tsw = swz_tr(l32);
+
+  // stage ST_ (0 or 1, a compile-time constant: the stages are distinct
+  // arrays, so the compiler's wait before an LDS read covers only the loads
+  // into the stage being read)
+#define SAGE_STG(A0_, A1_, ST_) ((ST_) == 0 ? (A0_) : (A1_))
+#define SAGE_LOAD_Q(ST_, QT_)                                                                       \
+  do {                                                                                              \
+    const int q0_ = (QT_) * kBT;                                                                    \
+    _Pragma("unroll") for (int u = 0; u < NI; ++u) {                                                \
+      const int at_ = (wave * NI + u) * 1024;                                                       \
+      lds_dma16(rq, SAGE_STG(sq0, sq1, ST_) + at_, rmo[u] + q0_ * D, 0);                            \
+      lds_dma16(rg, SAGE_STG(sg0, sg1, ST_) + at_, rmo[u] + q0_ * D, 0);                            \
+      lds_dma16(rqt, SAGE_STG(sqt0, sqt1, ST_) + at_, tro[u] + q0_, 0);                             \
+      lds_dma16(rgt, SAGE_STG(sgt0, sgt1, ST_) + at_, tro[u] + q0_, 0);                             \
+    }                                                                                               \
+    /* (L2, D) of rows q0 .. q0+127 (the second half unused; past Npad: zeros) */                  \
+    lds_dma16(rld, reinterpret_cast<unsigned char*>(SAGE_STG(sld0, sld1, ST_)), q0_ * 8 + lane * 16, 0); \
+  } while (0)
+
+#define SAGE_TILE_Q(ST_, QT_)                                                                                 \
+  do {                                                                                                       \
+    const int q0 = (QT_) * kBT;                                                                               \
+_Pragma("unroll 1")                                                                                           \
+    for (int sb = 0; sb < 2; ++sb) {                                                                          \
+      const int qb = q0 + sb * 32;  /* first query of the sub-block */                                        \
+      if (CAUSAL && k0w > qb + 31) continue;  /* every key of the wave is above every query */                \
+      const int tao = l32 * kBT + (((2 * sb + g) ^ tsw) * 16);                                                \
+      v16i s, dp;                                                                                             \
+_Pragma("unroll")                                                                                             \
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0;                                                          \
+_Pragma("unroll")                                                                                             \
+      for (int c = 0; c < NCH; ++c) {                                                                         \
+        s = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(SAGE_STG(sq0, sq1, ST_) + sb * 32 * D + aro[c]), kb[c], s, 0, 0, 0);\
+        dp = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(SAGE_STG(sg0, sg1, ST_) + sb * 32 * D + aro[c]), vb[c], dp, 0, 0, 0);\
+      }                                                                                                       \
+      const float sqb = qsh[qb / a.qblk];                                                                     \
+      const float gsb = gsh[qb / 64];                                                                         \
+      const float cs = (sqb * skw) * a.sl2;                                                                   \
+      const float gsv = gsb * svk;                                                                            \
+  /* masking only in sub-blocks with keys >= N or above the diagonal */                                       \
+      const bool masked = k0w + 31 >= N || (CAUSAL && k0w + 31 > qb);                                         \
+      float p[16], ds[16];                                                                                    \
+_Pragma("unroll")                                                                                             \
+      for (int i = 0; i < 16; ++i) {                                                                          \
+        const float2 lq = SAGE_STG(sld0, sld1, ST_)[sb * 32 + g * 16 + i];                                    \
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[i]), cs, -lq.x));               \
+        if (masked && (key >= N || (CAUSAL && key > qb + g * 16 + i))) pv = 0.f;                              \
+        p[i] = pv;                                                                                            \
+        ds[i] = pv * __builtin_fmaf(static_cast<float>(dp[i]), gsv, -lq.y);                                   \
+      }                                                                                                       \
+      v4i pc, dsc;                                                                                            \
+      const float sp = tile_codes_nonneg(p, pc);                                                              \
+      const float sds = tile_codes_signed(ds, dsc);                                                           \
+      const float fv = sp * gsb;                                                                              \
+      const float fk = (sds * sqb) * a.sm;                                                                    \
+_Pragma("unroll")                                                                                             \
+      for (int c = 0; c < NCH; ++c) {                                                                         \
+        v16i zv, zk;                                                                                          \
+_Pragma("unroll")                                                                                             \
+        for (int i = 0; i < 16; ++i) zv[i] = zk[i] = 0;                                                       \
+        zv = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(SAGE_STG(sgt0, sgt1, ST_) + c * 32 * kBT + tao), pc, zv, 0, 0, 0);\
+        zk = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(SAGE_STG(sqt0, sqt1, ST_) + c * 32 * kBT + tao), dsc, zk, 0, 0, 0);\
+_Pragma("unroll")                                                                                             \
+        for (int i = 0; i < 16; ++i) {                                                                        \
+          dvf[c][i] = __builtin_fmaf(static_cast<float>(zv[i]), fv, dvf[c][i]);                               \
+          dkf[c][i] = __builtin_fmaf(static_cast<float>(zk[i]), fk, dkf[c][i]);                               \
+        }                                                                                                     \
+      }                                                                                                       \
+    }                                                                                                         \
+  } while (0)
+
+  if (qt_begin < qt_end) SAGE_LOAD_Q(0, qt_begin);
+  tile_barrier();
+  for (int qt = qt_begin; qt < qt_end; qt += 2) {
+    if (qt + 1 < qt_end) SAGE_LOAD_Q(1, qt + 1);
+    SAGE_TILE_Q(0, qt);
+    tile_barrier();
+    if (qt + 1 >= qt_end) break;
+    if (qt + 2 < qt_end) SAGE_LOAD_Q(0, qt + 2);
+    SAGE_TILE_Q(1, qt + 1);
+    tile_barrier();
+  }
+#undef SAGE_TILE_Q
+#undef SAGE_LOAD_Q
 
   // dV^T and dK^T: lane = key, register i of chunk c = channel c*32 + (i/4)*8 + g*4 + i%4
   if (key < N) {
@@ -331,14 +417,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 // dQ
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, const float* __restrict__ qsp,
+                                                         const float* __restrict__ ksp,
+                                                         const float* __restrict__ vsp,
+                                                         const float* __restrict__ gsp) {
   constexpr int NCH = D / 32;
-  constexpr int KROW = D + 16;       // LDS bytes per K / V row
-  constexpr int TROW = kBT + 16;     // LDS bytes per channel row of K^T
-  __shared__ __attribute__((aligned(16))) unsigned char sk[kBT * KROW];
-  __shared__ __attribute__((aligned(16))) unsigned char sv[kBT * KROW];
-  __shared__ __attribute__((aligned(16))) unsigned char skt[D * TROW];
-  __shared__ float ssv[kBT];
+  constexpr int TB = kBT * D;
+  constexpr int NI = TB / 4096;
+  constexpr int CPR = D / 16;
+  static_assert(TB % 4096 == 0, "tiles fill whole wave instructions");
+  __shared__ __attribute__((aligned(16))) unsigned char sk0[TB], sk1[TB], sv0[TB], sv1[TB], skt0[TB], skt1[TB];
+  __shared__ __attribute__((aligned(16))) float ssv0[256], ssv1[256];
 
   const int Npad = a.Npad, N = a.N;
   const int nqb = Npad / kBW;
@@ -360,10 +449,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       gb[c] = *reinterpret_cast<const v4i*>(gp + c * 32);
     }
   }
-  const float sqw = a.qs[static_cast<size_t>(bh) * (Npad / a.qblk) + q0w / a.qblk];
-  const float gsw = a.gs[static_cast<size_t>(bh) * (Npad / 64) + q0w / 64];
+  const float sqw = qsp[static_cast<size_t>(bh) * (Npad / a.qblk) + q0w / a.qblk];
+  const float gsw = gsp[static_cast<size_t>(bh) * (Npad / 64) + q0w / 64];
   const float2 lq = a.ld[static_cast<size_t>(bh) * Npad + query];
-  const float* ksh = a.ks + static_cast<size_t>(bh) * (Npad / 64);
+  const float* ksh = ksp + static_cast<size_t>(bh) * (Npad / 64);
 
   v16f dqf[NCH];
 #pragma unroll
@@ -373,41 +462,55 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   int kt_end = (N + kBT - 1) / kBT;
   if (CAUSAL) kt_end = min(kt_end, (qblk * kBW + kBW) / kBT);
-  const unsigned char* krows = reinterpret_cast<const unsigned char*>(a.kc) + static_cast<size_t>(bh) * Npad * D;
-  const unsigned char* vrows = reinterpret_cast<const unsigned char*>(a.vc) + static_cast<size_t>(bh) * Npad * D;
-  const unsigned char* ktr = reinterpret_cast<const unsigned char*>(a.kt) + static_cast<size_t>(bh) * D * Npad;
-  const float* vsh = a.vs + static_cast<size_t>(bh) * Npad;
+  const auto rk = buffer_rsrc(a.kc + static_cast<size_t>(bh) * Npad * D, static_cast<unsigned>(Npad) * D);
+  const auto rv = buffer_rsrc(a.vc + static_cast<size_t>(bh) * Npad * D, static_cast<unsigned>(Npad) * D);
+  const auto rkt = buffer_rsrc(a.kt + static_cast<size_t>(bh) * D * Npad, static_cast<unsigned>(Npad) * D);
+  const auto rvs = buffer_rsrc(vsp + static_cast<size_t>(bh) * Npad, static_cast<unsigned>(Npad) * 4);
+  int aro[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int r = perm32(l32);
+    aro[c] = r * D + (((2 * c + g) ^ swz_rm<D>(r)) * 16);
+  }
+  const int tsw = swz_tr(l32);
 
-  for (int kt = 0; kt < kt_end; ++kt) {
+  auto load_tile = [&](unsigned char* dk_, unsigned char* dv_, unsigned char* dkt_, float* dsv_, int kt) __attribute__((always_inline)) {
     const int k0 = kt * kBT;
-    __syncthreads();
-    for (int i = tid; i < kBT * D / 16; i += 256) {
-      const int row = i / (D / 16), col = (i % (D / 16)) * 16;
-      *reinterpret_cast<uint4*>(sk + row * KROW + col) =
-          *reinterpret_cast<const uint4*>(krows + static_cast<size_t>(k0 + row) * D + col);
-      *reinterpret_cast<uint4*>(sv + row * KROW + col) =
-          *reinterpret_cast<const uint4*>(vrows + static_cast<size_t>(k0 + row) * D + col);
+    // this lane's source chunks, recomputed per tile (a few VALU instructions
+    // instead of registers held across the loop; the empty asm keeps the
+    // compiler from hoisting them out of it)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int i = (wave * NI + u) * 64 + ln;
+      const int rr = i / CPR, rp = i % CPR, tr = i / 4, tp = i % 4;
+      const int rmo = rr * D + ((rp ^ swz_rm<D>(rr)) * 16);
+      const int tro = tr * Npad + ((tp ^ swz_tr(tr)) * 16);
+      const int at = (wave * NI + u) * 1024;
+      lds_dma16(rk, dk_ + at, rmo + k0 * D, 0);
+      lds_dma16(rv, dv_ + at, rmo + k0 * D, 0);
+      lds_dma16(rkt, dkt_ + at, tro + k0, 0);
     }
-    for (int i = tid; i < D * kBT / 16; i += 256) {
-      const int ch = i / (kBT / 16), col = (i % (kBT / 16)) * 16;
-      *reinterpret_cast<uint4*>(skt + ch * TROW + col) =
-          *reinterpret_cast<const uint4*>(ktr + static_cast<size_t>(ch) * Npad + k0 + col);
-    }
-    if (tid < kBT) ssv[tid] = vsh[k0 + tid];
-    __syncthreads();
+    // V scales of keys k0 .. k0+255 (the first 64 used; past Npad: zeros)
+    lds_dma16(rvs, reinterpret_cast<unsigned char*>(dsv_), k0 * 4 + lane * 16, 0);
+  };
 
+  auto tile = [&](const unsigned char* sk, const unsigned char* sv, const unsigned char* skt, const float* ssv,
+                  int kt) __attribute__((always_inline)) {
+    const int k0 = kt * kBT;
 #pragma unroll 1
     for (int sb = 0; sb < 2; ++sb) {
       const int kb0 = k0 + sb * 32;                   // first key of the sub-block
       if (CAUSAL && kb0 > q0w + 31) continue;
+      const int tao = l32 * kBT + (((2 * sb + g) ^ tsw) * 16);
       v16i s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0;
-      const int arow = (sb * 32 + perm32(l32)) * KROW + g * 16;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        s = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sk + arow + c * 32), qb[c], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sv + arow + c * 32), gb[c], dp, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sk + sb * 32 * D + aro[c]), qb[c], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(sv + sb * 32 * D + aro[c]), gb[c], dp, 0, 0, 0);
       }
       const float skb = ksh[kb0 / 64];
       const float cs = (sqw * skb) * a.sl2;
@@ -424,17 +527,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       v4i dsc;
       const float sds = tile_codes_signed(ds, dsc);
       const float fq = (sds * skb) * a.sm;
-      const int trow = l32 * TROW + sb * 32 + g * 16;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         v16i z;
 #pragma unroll
         for (int i = 0; i < 16; ++i) z[i] = 0;
-        z = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(skt + c * 32 * TROW + trow), dsc, z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_i32_32x32x32_i8(*reinterpret_cast<const v4i*>(skt + c * 32 * kBT + tao), dsc, z, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) dqf[c][i] = __builtin_fmaf(static_cast<float>(z[i]), fq, dqf[c][i]);
       }
     }
+  };
+
+  if (kt_end > 0) load_tile(sk0, sv0, skt0, ssv0, 0);
+  tile_barrier();
+  for (int kt = 0; kt < kt_end; kt += 2) {
+    if (kt + 1 < kt_end) load_tile(sk1, sv1, skt1, ssv1, kt + 1);
+    tile(sk0, sv0, skt0, ssv0, kt);
+    tile_barrier();
+    if (kt + 1 >= kt_end) break;
+    if (kt + 2 < kt_end) load_tile(sk0, sv0, skt0, ssv0, kt + 2);
+    tile(sk1, sv1, skt1, ssv1, kt + 1);
+    tile_barrier();
   }
 
   if (query < N) {
@@ -479,8 +593,8 @@ hipError_t launch_attn_bwd(const BwdLaunch& b, hipStream_t s) {
   const dim3 grid(BH * (Npad / kBW)), block(256);
 #define SAGE_BWD(D_, C_)                                  \
   do {                                                    \
-    bwd_dkdv_kernel<D_, C_><<<grid, block, 0, s>>>(a);    \
-    bwd_dq_kernel<D_, C_><<<grid, block, 0, s>>>(a);      \
+    bwd_dkdv_kernel<D_, C_><<<grid, block, 0, s>>>(a, a.qs, a.ks, a.vs, a.gs);    \
+    bwd_dq_kernel<D_, C_><<<grid, block, 0, s>>>(a, a.qs, a.ks, a.vs, a.gs);      \
   } while (0)
   if (d == 128) {
     if (b.causal) SAGE_BWD(128, true); else SAGE_BWD(128, false);

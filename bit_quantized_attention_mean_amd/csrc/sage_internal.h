@@ -244,9 +244,12 @@ inline BwdLayout make_bwd_layout(long long BH, int N, int d, int mode_lo) {
   L.gt = take(rows * d);
   L.vc = take(rows * d);
   L.gc = take(rows * d);
-  L.vs = take(rows * 4);
+  // vs and ld are read in 1 KiB tile loads that run up to 768 bytes past a
+  // head's last row (the surplus is unused): 1 KiB of slack keeps even the
+  // last head's reads inside the workspace
+  L.vs = take(rows * 4 + 1024);
   L.gs = take(rows / 64 * 4);
-  L.ld = take(rows * 8);
+  L.ld = take(rows * 8 + 1024);
   L.total = off;
   return L;
 }

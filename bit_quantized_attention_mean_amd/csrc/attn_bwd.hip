@@ -68,14 +68,26 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned cha
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the 64 lanes: DPP within each row of 16 (neighbour swaps, then
+// the half-row and row mirrors), one lane shuffle between the two rows of a
+// half, and the swap of the wave's halves.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  x = fmaxf(x, dpp_f32<0xB1>(x));
+  x = fmaxf(x, dpp_f32<0x4E>(x));
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  x = fmaxf(x, dpp_f32<0x140>(x));
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Tile maximum of |x| over a 32 x 32 tile held as one accumulator (16 values
-// per lane), and its scale s = fp32(a / 127) with the multiplier fp32(1 / s)
+// per lane), and its scale s = fp32(a / 127) with the multiplier r ~ 1 / s
 // (0 for an all-zero tile).
 __device__ __forceinline__ float tile_scale(const float (&x)[16], float& r) {
   float m = 0.f;
@@ -83,7 +95,9 @@ __device__ __forceinline__ float tile_scale(const float (&x)[16], float& r) {
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(x[i]));
   const float a = wave_max(m);
   const float s = a / 127.0f;
-  r = s > 0.f ? 1.0f / s : 0.f;
+  // the codes only need x / s to within a few ulps (a code that close to a
+  // rounding boundary may round either way), so v_rcp_f32 serves
+  r = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
   return s;
 }
 

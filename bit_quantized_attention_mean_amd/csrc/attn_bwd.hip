@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a, const float
 #define SAGE_TILE_Q(ST_, QT_)                                                                                 \
   do {                                                                                                       \
     const int q0 = (QT_) * kBT;                                                                               \
-_Pragma("unroll 1")                                                                                           \
+_Pragma("unroll 1")                                                                                               \
     for (int sb = 0; sb < 2; ++sb) {                                                                          \
       const int qb = q0 + sb * 32;  /* first query of the sub-block */                                        \
       if (CAUSAL && k0w > qb + 31) continue;  /* every key of the wave is above every query */                \
@@ -372,11 +372,16 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                             \
       for (int i = 0; i < 16; ++i) {                                                                          \
         const float2 lq = SAGE_STG(sld0, sld1, ST_)[sb * 32 + g * 16 + i];                                    \
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[i]), cs, -lq.x));               \
-        if (masked && (key >= N || (CAUSAL && key > qb + g * 16 + i))) pv = 0.f;                              \
-        p[i] = pv;                                                                                            \
-        ds[i] = pv * __builtin_fmaf(static_cast<float>(dp[i]), gsv, -lq.y);                                   \
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[i]), cs, -lq.x));                   \
+        ds[i] = __builtin_fmaf(static_cast<float>(dp[i]), gsv, -lq.y);                                        \
       }                                                                                                       \
+      if (masked) {                                                                                           \
+_Pragma("unroll")                                                                                             \
+        for (int i = 0; i < 16; ++i)                                                                          \
+          if (key >= N || (CAUSAL && key > qb + g * 16 + i)) p[i] = 0.f;                                      \
+      }                                                                                                       \
+_Pragma("unroll")                                                                                             \
+      for (int i = 0; i < 16; ++i) ds[i] *= p[i];                                                             \
       v4i pc, dsc;                                                                                            \
       const float sp = tile_codes_nonneg(p, pc);                                                              \
       const float sds = tile_codes_signed(ds, dsc);                                                           \
@@ -513,7 +518,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, const float* 
   auto tile = [&](const unsigned char* sk, const unsigned char* sv, const unsigned char* skt, const float* ssv,
                   int kt) __attribute__((always_inline)) {
     const int k0 = kt * kBT;
-#pragma unroll 1
+#pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int kb0 = k0 + sb * 32;                   // first key of the sub-block
       if (CAUSAL && kb0 > q0w + 31) continue;
@@ -530,14 +535,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, const float* 
       const float cs = (sqw * skb) * a.sl2;
       const bool masked = kb0 + 31 >= N || (CAUSAL && kb0 + 31 > q0w);
       float ds[16];
+      float pv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kj = kb0 + g * 16 + i;
         const float gsv = gsw * ssv[sb * 32 + g * 16 + i];
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[i]), cs, -lq.x));
-        if (masked && (kj >= N || (CAUSAL && kj > query))) pv = 0.f;
-        ds[i] = pv * __builtin_fmaf(static_cast<float>(dp[i]), gsv, -lq.y);
+        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(s[i]), cs, -lq.x));
+        ds[i] = __builtin_fmaf(static_cast<float>(dp[i]), gsv, -lq.y);
       }
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kj = kb0 + g * 16 + i;
+          if (kj >= N || (CAUSAL && kj > query)) pv[i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] *= pv[i];
       v4i dsc;
       const float sds = tile_codes_signed(ds, dsc);
       const float fq = (sds * skb) * a.sm;

@@ -13,6 +13,8 @@ Functions carry the C names:
   sage_attn_fwd_lse(q, k, v, ...)      -> (out, lse)   (the forward a training step saves)
   sage_attn_bwd(q, k, v, out, dout, lse, ...) -> (dq, dk, dv)   (INT8 backward pass)
   sage_attn_bwd_workspace_size(B, H, N, d, mode)
+  sage_attention(q, k, v, ...)         -> out, differentiable: a torch.autograd.Function whose
+                                          forward is sage_attn_fwd_lse and backward sage_attn_bwd
   sage_quant_qk(q, k, blk_q, blk_k, flags)  -> dict of codes/scales/mean
   sage_quant_mxfp4(q, k, v, flags)         -> dict of packed codes/exponents
   sage_quant_v_int8(v)                     -> dict of V^T codes and channel scales
@@ -32,6 +34,7 @@ __all__ = [
     "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_quant_v_int8", "sage_attn_dump_scores", "sage_status_string", "sage_last_error",
     "sage_clock_probe", "sage_wall_clock_khz", "measure_clock_mhz",
     "sage_attn_fwd_lse", "sage_attn_bwd", "sage_attn_bwd_workspace_size", "make_bwd_workspace",
+    "sage_attention",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -241,6 +244,46 @@ def sage_attn_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, *, causal=
                            _stream(stream))
     _check(rc, "sage_attn_bwd")
     return dq, dk, dv
+
+
+_AUTOGRAD_FN = None
+
+
+def _attention_function():
+    """The autograd Function behind sage_attention, made on first use (torch is
+    imported lazily)."""
+    global _AUTOGRAD_FN
+    if _AUTOGRAD_FN is None:
+        torch = _torch()
+
+        class SageAttentionFunction(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, causal, sm_scale, mode):
+                out, lse = sage_attn_fwd_lse(q, k, v, causal=causal, sm_scale=sm_scale, mode=mode)
+                ctx.save_for_backward(q, k, v, out, lse)
+                ctx.causal, ctx.sm_scale, ctx.mode = causal, sm_scale, mode
+                return out
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, out, lse = ctx.saved_tensors
+                dq, dk, dv = sage_attn_bwd(q, k, v, out, dout.contiguous(), lse, causal=ctx.causal,
+                                           sm_scale=ctx.sm_scale, mode=ctx.mode)
+                # float32 gradients; autograd hands them to the fp16 inputs in their dtype
+                return dq, dk, dv, None, None, None
+
+        _AUTOGRAD_FN = SageAttentionFunction
+    return _AUTOGRAD_FN
+
+
+def sage_attention(q, k, v, *, causal=False, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64):
+    """Trainable quantized attention: out = sage_attn_fwd_lse(q, k, v)[0], whose gradient
+    with respect to q, k, v is the INT8 backward pass (sage_attn_bwd) on the saved
+    (out, lse). q, k, v fp16 [B, H, N, d] on the GPU; modes 0 and 1, with or without
+    SAGE_FLAG_NO_SMOOTH."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(_shape4(q)[3])
+    return _attention_function().apply(q, k, v, bool(causal), float(sm_scale), int(mode))
 
 
 def sage_attn_fwd_noalloc(q, k, v, out, *, causal=False, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64, stream=None):

@@ -210,3 +210,14 @@ def test_backward_entry_points_validation():
     assert fb(nb=ws - 1) == WS and "needed" in sa.sage_last_error()
     if not _gpu_visible():
         assert fl() == NODEV and fb() == NODEV
+
+
+def test_trainable_attention_refuses_host_tensors():
+    # sage_attention: the autograd Function's forward goes through the same
+    # binding checks (host tensors are refused before any device call)
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.float16, requires_grad=True)
+    with pytest.raises(TypeError):
+        sa.sage_attention(q, q.detach(), q.detach())
+    with pytest.raises(ValueError):
+        sa.sage_attention(torch.zeros(2, 64, 64, dtype=torch.float16), q, q)

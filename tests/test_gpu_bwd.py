@@ -193,3 +193,28 @@ def test_backward_full_prefill_size_sampled_heads(sa, causal):
         for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
             assert_grad_parity(g[sl].cpu().numpy(), ref[name], ref[name + "_mag"], ref[name + "_allow"],
                                f"bwd prefill head ({b},{h}) {name} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_autograd_function_is_the_c_abi_pair(sa, causal):
+    """sage_attention under torch autograd: the output is sage_attn_fwd_lse's and the
+    gradients reaching fp16 q, k, v are sage_attn_bwd's float32 gradients rounded to
+    fp16 (the same kernels on the same inputs, so bit for bit)."""
+    B, H, N, d = 1, 2, 200, 64
+    say("autograd", (B, H, N, d, causal))
+    q, k, v = make_custom(B, H, N, d, seed=51)
+    do = make_grad(B, H, N, d, seed=51)
+    qd, kd, vd, gd = _dev(q, k, v, do)
+    for t in (qd, kd, vd):
+        t.requires_grad_(True)
+    out = sa.sage_attention(qd, kd, vd, causal=causal)
+    out.backward(gd)
+    torch.cuda.synchronize()
+    with torch.no_grad():
+        ref_out, lse = sa.sage_attn_fwd_lse(qd.detach(), kd.detach(), vd.detach(), causal=causal)
+        dq, dk, dv = sa.sage_attn_bwd(qd.detach(), kd.detach(), vd.detach(), ref_out, gd, lse, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), ref_out)
+    for name, t, g in (("dq", qd, dq), ("dk", kd, dk), ("dv", vd, dv)):
+        assert t.grad is not None and t.grad.dtype == torch.float16, name
+        assert torch.equal(t.grad, g.to(torch.float16)), name

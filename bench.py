@@ -43,6 +43,7 @@ Also on the JSON line:
                 launches of the attention kernel after idling run up to 35%
                 slower.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+       python bench.py --sweep   (kernel TOPS against sequence length, one JSON line per point)
 """
 import argparse
 import hashlib
@@ -285,6 +286,53 @@ def backward_bench(w, mode, qd, kd, vd, args, sa, torch, sdpa=True):
     return rec
 
 
+def sweep(torch, sa, steps):
+    """Kernel throughput against sequence length, as in the pages' speed plots: N
+    from 1K to 32K tokens with B*N = 32K tokens per head slot (H = 32), d = 64 and
+    128, causal or not, for the INT8 kernel (mode 0), the in-repo FP16 kernel
+    (mode 4), the MXFP4 kernel (mode 2) and torch's FP16 SDPA on the same inputs.
+    Inputs are the prefill recipe without outlier channels (N(0, 1), K offset
+    N(0, 3^2)). One JSON line per point, the attention kernel alone (HIP events
+    on its stream, after a warm-up), its TOPS against the INT8 peak."""
+    import torch.nn.functional as F
+    from synthetic import make_custom
+    rows = []
+    for d in (128, 64):
+        for causal in (False, True):
+            for N in (1024, 2048, 4096, 8192, 16384, 32768):
+                B, H = max(1, 32768 // N), 32
+                q, k, v = make_custom(B, H, N, d, seed=7 + N + d)
+                qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+                del q, k, v
+                sm = 1.0 / np.sqrt(d)
+                ops = 4.0 * B * H * N * N * d / (2.0 if causal else 1.0)
+                rec = {"sweep": "attention kernel TOPS", "B": B, "H": H, "N": N, "d": d, "causal": causal}
+                out = torch.empty_like(qd)
+                for name, mode in (("int8", 0), ("fp16", 4), ("mxfp4", 2)):
+                    ws = sa.make_workspace(B, H, N, d, mode, qd.device)
+                    sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode)
+                    comp = lambda: sa.sage_attn_compute(out, ws, causal=causal, sm_scale=sm, mode=mode, q=qd, k=kd, v=vd)
+                    ms, _ = timed(comp, steps, steps, torch)
+                    rec[f"{name}_ms"] = round(ms, 4)
+                    rec[f"{name}_tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
+                    del ws
+                sdpa = lambda: F.scaled_dot_product_attention(qd, kd, vd, is_causal=causal, scale=sm)
+                ms, _ = timed(sdpa, steps, steps, torch)
+                rec["torch_sdpa_fp16_ms"] = round(ms, 4)
+                rec["torch_sdpa_fp16_tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
+                rec["int8_frac_of_int8_peak"] = round(rec["int8_tops"] / PEAK["int8"], 4)
+                print(json.dumps(rec), flush=True)
+                rows.append(rec)
+                del qd, kd, vd, out
+                torch.cuda.empty_cache()
+    log("| d | causal | N | B | INT8 TOPS | % INT8 peak | FP16 kernel TOPS | MXFP4 TOPS | torch SDPA TOPS | INT8 / SDPA |")
+    log("|---:|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for r in rows:
+        log(f"| {r['d']} | {r['causal']} | {r['N']} | {r['B']} | {r['int8_tops']} | {100 * r['int8_frac_of_int8_peak']:.1f}% | "
+            f"{r['fp16_tops']} | {r['mxfp4_tops']} | {r['torch_sdpa_fp16_tops']} | "
+            f"{r['int8_tops'] / r['torch_sdpa_fp16_tops']:.2f}x |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +350,9 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip timing the INT8 backward pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time the attention kernels against sequence length (d 64 and 128, causal or "
+                         "not; INT8, FP16, MXFP4 and torch SDPA), one JSON line per point")
     ap.add_argument("--select", nargs="*", default=None, metavar="WORKLOAD",
                     help="only run the per-layer kernel selection (cos >= 99.8%% vs the FP16 mode, fastest "
                          "wins) on the named synthetic workloads (default: all but mxfp4)")
@@ -323,6 +374,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}), flush=True)
+        return
+
+    if args.sweep:
+        import bit_quantized_attention_mean_amd as sa
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        sweep(torch, sa, max(5, min(args.steps, 20)))
         return
 
     from synthetic import WORKLOADS, make_inputs

@@ -1,8 +1,9 @@
 """Throughput bench of the quantized-attention forward pass on one MI355X.
 
-A step is one sage_attn_fwd call (K mean, quantization of Q and K, V layout or
-V quantization, fused attention kernel) over one synthetic workload whose
-inputs are already resident in HBM. `value` is attention TOPS: 4*B*H*N^2*d
+A step is one sage_attn_fwd call (K mean, quantization of Q and K, V
+quantization where the mode has it, fused attention kernel; in the per-block
+INT8 modes from 65536 token rows on the kernel quantizes Q in its prologue) over
+one synthetic workload whose inputs are already resident in HBM. `value` is attention TOPS: 4*B*H*N^2*d
 per step (halved when causal) divided by the step time.
 
 Default workload: n16k, B=1, H=32, N=16384, d=128, non-causal, INT8 Q/K
@@ -418,10 +419,14 @@ def main():
                                     workspace=ws)
     clk_load = warmup_with_clock_probe(step, args.warmup, sa, torch)
     ms_step, wall_step = timed(step, args.steps, 0, torch)
-    # the two phases separately
-    prep = lambda: sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode | flags)
+    # the two phases separately, as sage_attn_fwd runs them: in the per-block
+    # INT8 modes from 65536 token rows on, Q is quantized inside the attention
+    # kernel (SAGE_FLAG_FUSED_Q) and the prepare phase covers K only
+    fused_q = mode in (0, 1) and w.B * w.H * w.N >= 65536
+    pflags = flags | (sa.SAGE_FLAG_FUSED_Q if fused_q else 0)
+    prep = lambda: sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode | pflags)
     ms_prep, _ = timed(prep, args.steps, args.warmup, torch)
-    comp = lambda: sa.sage_attn_compute(out, ws, causal=w.causal, sm_scale=w.sm_scale, mode=mode | flags, q=qd, k=kd, v=vd)
+    comp = lambda: sa.sage_attn_compute(out, ws, causal=w.causal, sm_scale=w.sm_scale, mode=mode | pflags, q=qd, k=kd, v=vd)
     ms_attn, _ = timed(comp, args.steps, args.warmup, torch)
     log(f"[bench] {w.name}: step {ms_step:.4f} ms (wall {wall_step:.4f}), attention kernel {ms_attn:.4f} ms, "
         f"quantization phase {ms_prep:.4f} ms")
@@ -456,8 +461,9 @@ def main():
     else:
         qblk = 1 if mode in (3, 7) else (64 if mode == 1 else 128)
         kblk = 1 if mode in (3, 7) else 64
-        # Q and K: 2 B read + 1 B code per element, 4 B per scale
-        quant_bytes = n_el * 6 + 4 * (n_rows // qblk + n_rows // kblk)
+        # Q and K: 2 B read + 1 B code per element, 4 B per scale (K only when
+        # the attention kernel quantizes Q itself)
+        quant_bytes = (n_el * 3 + 4 * (n_rows // kblk)) if fused_q else (n_el * 6 + 4 * (n_rows // qblk + n_rows // kblk))
         rereads = n_el * 2 if smooth else 0
         if mode in (6, 7):
             # V: 2 B read + 1 B code per element, one 4 B scale per channel; the
@@ -514,6 +520,7 @@ def main():
         "quant_phase_gbs": round(quant_bytes / (ms_prep * 1e-3) / 1e9, 1) if quant_bytes else None,
         "quant_phase_bytes": int(quant_bytes),
         "quant_phase_rereads_bytes": int(rereads),
+        "q_quantized_in_kernel": bool(fused_q),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "torch_sdpa_fp16": sdpa,

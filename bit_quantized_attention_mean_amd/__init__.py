@@ -29,7 +29,7 @@ import os
 __all__ = [
     "SAGE_MODE_INT8_Q128_K64", "SAGE_MODE_INT8_Q64_K64", "SAGE_MODE_MXFP4", "SAGE_MODE_INT8_PER_TOKEN",
     "SAGE_MODE_FP16", "SAGE_MODE_MXFP4_FP8PV", "SAGE_MODE_INT8_PV", "SAGE_MODE_INT8_PV_PER_TOKEN",
-    "SAGE_FLAG_NO_SMOOTH", "SAGE_FLAG_FP8_V", "SageError", "LIB_PATH", "lib",
+    "SAGE_FLAG_NO_SMOOTH", "SAGE_FLAG_FP8_V", "SAGE_FLAG_FUSED_Q", "SageError", "LIB_PATH", "lib",
     "sage_attn_fwd", "sage_attn_fwd_noalloc", "SAGE_NOALLOC_SCRATCH_BYTES", "sage_attn_prepare", "sage_attn_compute", "sage_attn_workspace_size",
     "sage_quant_workspace_size", "sage_quant_qk", "sage_quant_mxfp4", "sage_quant_v_int8", "sage_attn_dump_scores", "sage_status_string", "sage_last_error",
     "sage_clock_probe", "sage_wall_clock_khz", "measure_clock_mhz",
@@ -48,6 +48,7 @@ SAGE_MODE_INT8_PV = 6
 SAGE_MODE_INT8_PV_PER_TOKEN = 7
 SAGE_FLAG_NO_SMOOTH = 0x100
 SAGE_FLAG_FP8_V = 0x200
+SAGE_FLAG_FUSED_Q = 0x400
 SAGE_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_attn.so")
@@ -315,8 +316,9 @@ def sage_attn_prepare(q, k, v, workspace, *, mode=SAGE_MODE_INT8_Q128_K64, strea
 
 def sage_attn_compute(out, workspace, *, causal=False, sm_scale=None, mode=SAGE_MODE_INT8_Q128_K64, q=None, k=None,
                       v=None, stream=None):
-    """Attention from a prepared workspace. q, k (the tensors given to prepare) are needed by SAGE_MODE_FP16
-    only; v (the V given to prepare) by every mode with an fp16 P.V (all but the MXFP4 and INT8 P.V modes)."""
+    """Attention from a prepared workspace. q, k (the tensors given to prepare) are needed by SAGE_MODE_FP16,
+    and q also with SAGE_FLAG_FUSED_Q; v (the V given to prepare) by every mode with an fp16 P.V (all but the
+    MXFP4 and INT8 P.V modes)."""
     torch = _torch()
     B, H, N, d = _shape4(out)
     if sm_scale is None:

@@ -49,11 +49,27 @@ int check_ptr(const void* p, const char* name, size_t align) {
 }
 
 int check_mode(int mode, bool attention) {
-  if (mode & ~(SAGE_MODE_MASK | SAGE_FLAG_NO_SMOOTH)) return fail(SAGE_ERR_UNSUPPORTED, "unknown flag bits in mode 0x%x", mode);
+  if (mode & ~(SAGE_MODE_MASK | SAGE_FLAG_NO_SMOOTH | SAGE_FLAG_FUSED_Q))
+    return fail(SAGE_ERR_UNSUPPORTED, "unknown flag bits in mode 0x%x", mode);
   const int lo = mode & SAGE_MODE_MASK;
   if (lo > SAGE_MODE_INT8_PV_PER_TOKEN) return fail(SAGE_ERR_UNSUPPORTED, "unknown mode %d", lo);
+  if ((mode & SAGE_FLAG_FUSED_Q) && lo != SAGE_MODE_INT8_Q128_K64 && lo != SAGE_MODE_INT8_Q64_K64)
+    return fail(SAGE_ERR_UNSUPPORTED, "SAGE_FLAG_FUSED_Q goes with the per-block INT8 modes %d and %d (got %d)",
+                SAGE_MODE_INT8_Q128_K64, SAGE_MODE_INT8_Q64_K64, lo);
   (void)attention;
   return SAGE_OK;
+}
+
+// The fused pass: the per-block INT8 modes quantize Q inside the attention
+// kernel (its prologue), so the prepare phase writes no Q codes. Below 64K
+// token rows (B * H * N) the prologue costs more than the Q pass it saves
+// (measured: 9% slower at 2 x 256 rows, 0.6-1.3% faster from 512K rows on).
+constexpr long long kFusedQMinRows = 1 << 16;
+int with_fused_q(int mode, int B, int H, int N) {
+  const int lo = mode & SAGE_MODE_MASK;
+  const bool fuse = (lo == SAGE_MODE_INT8_Q128_K64 || lo == SAGE_MODE_INT8_Q64_K64) &&
+                    static_cast<long long>(B) * H * N >= kFusedQMinRows;
+  return fuse ? (mode | SAGE_FLAG_FUSED_Q) : (mode & ~SAGE_FLAG_FUSED_Q);
 }
 
 // Device check: a HIP device must be current and be gfx950. Cached per device.
@@ -152,7 +168,8 @@ int do_prepare(const void* q, const void* k, const void* v, int B, int H, int N,
   P.k = k; P.v = v; P.ksum = reinterpret_cast<long long*>(at(ws, L.ksum)); P.kmean = mu;
   P.chunk = L.chunk; P.nchunk = L.nchunk; P.smooth = smooth; P.Npad = L.Npad;
   P.jq.src = q; P.jq.codes = reinterpret_cast<int8_t*>(at(ws, L.q_codes)); P.jq.scales = reinterpret_cast<float*>(at(ws, L.q_scales));
-  P.jq.mu = nullptr; P.jq.blk = blk_q; P.jq.code_rows = L.Npad; P.jq.nscale = L.Npad / blk_q; P.jq.ntile = L.Npad / sage::kQTile;
+  P.jq.mu = nullptr; P.jq.blk = blk_q; P.jq.code_rows = L.Npad; P.jq.nscale = L.Npad / blk_q;
+  P.jq.ntile = (mode & SAGE_FLAG_FUSED_Q) ? 0 : L.Npad / sage::kQTile;   // 0: no Q codes
   P.jk.src = k; P.jk.codes = reinterpret_cast<int8_t*>(at(ws, L.k_codes)); P.jk.scales = reinterpret_cast<float*>(at(ws, L.k_scales));
   P.jk.mu = smooth ? mu : nullptr; P.jk.blk = blk_k; P.jk.code_rows = L.Npad; P.jk.nscale = L.Npad / blk_k; P.jk.ntile = L.Npad / sage::kQTile;
   if (sage::mode_pv_int8(lo)) {
@@ -179,7 +196,8 @@ int do_compute(const void* q, const void* k, const void* v, void* out, int B, in
   if (lo == SAGE_MODE_FP16)
     return hip_status(sage::launch_attn_int8(a, q, k, v, nullptr, nullptr, nullptr, s),
                       "FP16 attention kernel");
-  return hip_status(sage::launch_attn_int8(a, at(ws, L.q_codes), at(ws, L.k_codes),
+  a.qin = (mode & SAGE_FLAG_FUSED_Q) != 0;
+  return hip_status(sage::launch_attn_int8(a, a.qin ? q : at(ws, L.q_codes), at(ws, L.k_codes),
                                            sage::mode_pv_int8(lo) ? at(ws, L.vt) : v,
                                            reinterpret_cast<const float*>(at(ws, L.q_scales)),
                                            reinterpret_cast<const float*>(at(ws, L.k_scales)),
@@ -278,6 +296,7 @@ int sage_attn_compute(const void* q, const void* k, const void* v, void* out, in
     SAGE_TRY(check_ptr(q, "q", 16));
     SAGE_TRY(check_ptr(k, "k", 16));
   }
+  if (mode & SAGE_FLAG_FUSED_Q) SAGE_TRY(check_ptr(q, "q", 16));
   if (reads_fp16_v(lo)) SAGE_TRY(check_ptr(v, "v", 16));
   SAGE_TRY(check_ptr(out, "out", 16));
   if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
@@ -300,8 +319,9 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
   SAGE_TRY(validate_attn(B, H, N, d, mode, workspace, workspace_bytes));
   SAGE_TRY(check_device());
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, workspace, s));
-  return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, mode, workspace, s);
+  const int fm = with_fused_q(mode, B, H, N);
+  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, fm, workspace, s));
+  return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, fm, workspace, s);
 }
 
 int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
@@ -327,8 +347,9 @@ int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out
   void* ws = nullptr;
   SAGE_TRY(scratch_address(&ws));
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, ws, s));
-  return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, mode, ws, s);
+  const int fm = with_fused_q(mode, B, H, N);
+  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, fm, ws, s));
+  return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, fm, ws, s);
 }
 
 size_t sage_attn_bwd_workspace_size(int B, int H, int N, int d, int mode) {
@@ -350,8 +371,9 @@ int sage_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, fl
   SAGE_TRY(validate_attn(B, H, N, d, mode, workspace, workspace_bytes));
   SAGE_TRY(check_device());
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, workspace, s));
-  return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, mode, workspace, s, lse);
+  const int fm = with_fused_q(mode, B, H, N);
+  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, fm, workspace, s));
+  return do_compute(q, k, v, out, B, H, N, d, causal, sm_scale, fm, workspace, s, lse);
 }
 
 int sage_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
@@ -381,7 +403,7 @@ int sage_attn_bwd(const void* q, const void* k, const void* v, const void* out, 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   // the forward's codes of Q and K_s (same kernels, same layout), then V per
   // token and dO per 64 rows
-  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode, workspace, s));
+  SAGE_TRY(do_prepare(q, k, v, B, H, N, d, mode & ~SAGE_FLAG_FUSED_Q, workspace, s));
   const int Npad = L.f.Npad;
   sage::Int8Job jv, jg;
   jv.src = v; jv.codes = reinterpret_cast<int8_t*>(at(workspace, L.vc)); jv.scales = reinterpret_cast<float*>(at(workspace, L.vs));
@@ -423,6 +445,9 @@ int sage_attn_dump_scores(const void* v, void* out, int B, int H, int N, int d, 
   const int lo = mode & SAGE_MODE_MASK;
   if (lo != SAGE_MODE_INT8_Q128_K64 && lo != SAGE_MODE_INT8_Q64_K64 && lo != SAGE_MODE_INT8_PER_TOKEN)
     return fail(SAGE_ERR_UNSUPPORTED, "the score dump covers the INT8 modes 0, 1 and 3 (got %d)", lo);
+  if (mode & SAGE_FLAG_FUSED_Q)
+    return fail(SAGE_ERR_UNSUPPORTED, "the score dump reads the Q codes that sage_attn_prepare writes without "
+                "SAGE_FLAG_FUSED_Q");
   const long long BH = static_cast<long long>(B) * H;
   if (bh < 0 || bh >= BH) return fail(SAGE_ERR_INVALID_ARG, "bh = %d is outside [0, %lld)", bh, BH);
   const int nqt = (N + sage::kWGQ - 1) / sage::kWGQ, nkt = (N + sage::kKTile - 1) / sage::kKTile;

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
     const void* __restrict__ qsrc, const void* __restrict__ ksrc, const void* __restrict__ vsrc,
     const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vsc,
     _Float16* __restrict__ out, int N, int Npad, int qblk, float sl2, int BH, int* __restrict__ dump = nullptr,
-    int dbh = 0, int dqt = 0, int dkt = 0, float* __restrict__ lse = nullptr) {
+    int dbh = 0, int dqt = 0, int dkt = 0, float* __restrict__ lse = nullptr, int qin = 0) {
   constexpr bool PERTOK = SM == kScoresInt8Token;
   constexpr bool F16 = SM == kScoresF16;
   static_assert(!(PV8 && F16), "INT8 P.V goes with INT8 scores");
@@ -238,6 +238,13 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   // bank conflicts; the others stage tiles through registers into two
   // buffers of padded rows.
   constexpr bool DMA = PP && !F16;
+  // With qin (a runtime flag), the per-block INT8 ping-pong instances read the
+  // caller's fp16 Q ([N, d] per head) and quantize it in their prologue, with
+  // the arithmetic of the quantization kernel (block maximum over the qblk
+  // rows of the Q block, s = fp32(a / 127), correctly rounded quotients), so
+  // the codes are the ones sage_quant_qk writes. Its fp16 loads are issued
+  // before, and its arithmetic after, the first tile loads.
+  constexpr bool QIN = DMA && SM == kScoresInt8Block && !DUMP;
   // K in LDS: 64 key rows of d codes (fp16: 2d bytes), +16 bytes of padding
   // per row without DMA.
   constexpr int KROW = DMA ? D * EB : D * EB + 16;   // LDS bytes per K row
@@ -295,7 +302,17 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   // INT8 codes are zero-padded to Npad rows; fp16 Q is read as given, with
   // zeros for rows >= N.
   v4i qf[NQF];
-  if (F16) {
+  uint4 qraw[QIN ? 2 * NQF : 1];   // fp16 Q of this lane: channels c*32 + g*16 .. +15 in qraw[2c], qraw[2c+1]
+  if (QIN && qin) {
+    const bool live = qrow < N;
+    const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(qsrc) +
+                                                     (static_cast<size_t>(bh) * N + (live ? qrow : 0)) * D + g * 16);
+#pragma unroll
+    for (int c = 0; c < NQF; ++c) {
+      qraw[2 * c] = live ? qp[c * 4] : make_uint4(0, 0, 0, 0);
+      qraw[2 * c + 1] = live ? qp[c * 4 + 1] : make_uint4(0, 0, 0, 0);
+    }
+  } else if (F16) {
     const bool live = qrow < N;
     const unsigned char* qp = static_cast<const unsigned char*>(qsrc) +
                               (static_cast<size_t>(bh) * N + (live ? qrow : 0)) * D * 2 + g * 16;
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   const float* ksh = nullptr;
   if (!F16) {
     const int nqs = Npad / qblk;
-    sq = qs[static_cast<size_t>(bh) * nqs + (PERTOK ? qrow : wrow0 / qblk)];
+    if (!(QIN && qin)) sq = qs[static_cast<size_t>(bh) * nqs + (PERTOK ? qrow : wrow0 / qblk)];
     const int nks = PERTOK ? Npad : Npad / kKTile;
     ksh = ks + static_cast<size_t>(bh) * nks;
   }
@@ -883,7 +900,53 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
       SAGE_DMA_K(min(1, nkt - 1), 1)
       SAGE_DMA_V(0, 0)
     }
+    __shared__ float qmax_w[QIN ? 8 : 1];   // max |Q| of each wave's 32 rows
+    if (QIN && qin) {
+      float mq = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2 * NQF; ++u) {
+        const unsigned w4[4] = {qraw[u].x, qraw[u].y, qraw[u].z, qraw[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          mq = fmaxf(mq, fabsf(static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w4[j] & 0xffffu)))));
+          mq = fmaxf(mq, fabsf(static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w4[j] >> 16)))));
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) mq = fmaxf(mq, __shfl_xor(mq, off, 64));
+      if (lane == 0) qmax_w[wave] = mq;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    }
     SAGE_END_BARRIER(nvm);   // nvm = this wave's K(1) + V(0) instructions
+    if (QIN && qin) {
+      // the Q block of this wave: qblk / 32 consecutive waves (qblk 128 or 64)
+      const int nw = qblk / 32, b0 = (wave / nw) * nw;
+      float a = qmax_w[b0];
+      for (int i = 1; i < nw; ++i) a = fmaxf(a, qmax_w[b0 + i]);
+      const float sb = a / 127.0f;
+      const bool mk = sb >= kMarksteinMinScale;
+      const float y = mk ? 1.0f / sb : 0.f;
+#pragma unroll
+      for (int c = 0; c < NQF; ++c) {
+        unsigned w[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const unsigned w4[4] = {qraw[2 * c + h].x, qraw[2 * c + h].y, qraw[2 * c + h].z, qraw[2 * c + h].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w4[j] & 0xffffu)));
+            const float x1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w4[j] >> 16)));
+            w[h * 8 + 2 * j] = mk ? int8_code_bits(x0, sb, y) : int8_code_bits_div(x0, sb);
+            w[h * 8 + 2 * j + 1] = mk ? int8_code_bits(x1, sb, y) : int8_code_bits_div(x1, sb);
+          }
+        }
+        qf[c] = v4i{static_cast<int>(pack_low_bytes(w[0], w[1], w[2], w[3])),
+                    static_cast<int>(pack_low_bytes(w[4], w[5], w[6], w[7])),
+                    static_cast<int>(pack_low_bytes(w[8], w[9], w[10], w[11])),
+                    static_cast<int>(pack_low_bytes(w[12], w[13], w[14], w[15]))};
+      }
+      sq = sb;
+    }
 #define SAGE_PERIODS_DMA(G_)                                                                     \
   do {                                                                                           \
     SAGE_PERIOD_DMA(0, 0, true, false, G_);                                                      \
@@ -978,7 +1041,7 @@ hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, con
     const dim3 grid_(a.BH * (a.Npad / (pp_ ? kWGQ : kWGQ / 2))), block_(pp_ ? 512 : 256);            \
     attn_int8_kernel<D_, C_, S_, P_><<<grid_, block_, 0, s>>>(q, k, vt, qs, ks, vs, o, a.N, a.Npad,  \
                                                               qblk, a.sl2, a.BH, nullptr, 0, 0, 0,   \
-                                                              a.lse);                                \
+                                                              a.lse, a.qin ? 1 : 0);                 \
   } while (0)
 #define SAGE_LAUNCH_SM(D_, C_)                                                    \
   do {                                                                            \

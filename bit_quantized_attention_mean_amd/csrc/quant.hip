@@ -135,40 +135,6 @@ __device__ __forceinline__ void unpack8_sub(const uint4 raw, const float* mu, _F
   }
 }
 
-// Codes. fp32(x / s) is formed without a division per element: with
-// y = fp32(1 / s) (one IEEE division per scale) and q0 = fp32(x * y), the
-// remainder x - q0 * s is exact in one fma and q0 + r * y rounded once is the
-// correctly rounded quotient (Markstein's correction step; its preconditions
-// hold here: y is the rounded reciprocal of s, q0 is within one ulp, the
-// quotient is at most 127 in magnitude, and with s >= 2^-60 every x whose
-// code can be nonzero is far above the subnormal range, so the remainder is
-// exact). Smaller scales take the plain division; s = 0 means an all-zero
-// block and zero codes.
-// The result is returned as the bits of t = fp32(q + 1.5 * 2^23), which rounds
-// q to the nearest integer, ties to even (the sum lies in [2^23, 2^24), whose
-// ulp is 1, and 1.5 * 2^23 is even): the low byte of t is that integer as a
-// two's complement int8. |q| <= 127 needs no clamp: q = x / s with |x| <= a and
-// s = fp32(a / 127), so |q| <= 127 * (1 + 2^-24).
-constexpr float kMarksteinMinScale = 0x1p-60f;
-constexpr float kRound = 12582912.0f;
-
-// s >= kMarksteinMinScale, y = fp32(1 / s)
-__device__ __forceinline__ unsigned int8_code_bits(float x, float s, float y) {
-  const float q0 = x * y;
-  const float r = __builtin_fmaf(-q0, s, x);
-  return __float_as_uint(__builtin_fmaf(r, y, q0) + kRound);
-}
-// any s >= 0 (the slow path for tiny scales; s = 0 gives code 0)
-__device__ __forceinline__ unsigned int8_code_bits_div(float x, float s) {
-  return __float_as_uint((s > 0.f ? x / s : 0.f) + kRound);
-}
-
-// Low bytes of w[0..3] -> one word, byte i = low byte of w[i].
-__device__ __forceinline__ unsigned pack_low_bytes(unsigned w0, unsigned w1, unsigned w2, unsigned w3) {
-  return __builtin_amdgcn_perm(__builtin_amdgcn_perm(w3, w2, 0x04000c0cu),
-                               __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u), 0x07060100u);
-}
-
 // One 256-thread block of a quantization job: TR-row tile `bid` (head bid /
 // J.ntile), TR = 128 or 64 (64-row tiles hold half the registers, for jobs
 // with blocks of at most 64 rows).
@@ -480,14 +446,16 @@ __global__ __launch_bounds__(256) void prep_int8_phase1_kernel(PrepInt8 P, int N
 
 hipError_t launch_prepare_int8(const PrepInt8& P, int BH, int N, int d, hipStream_t s) {
   const int n_ksum = P.smooth ? BH * P.nchunk : 0;
-  const int n_q = BH * P.jq.ntile;
+  const int n_q = BH * P.jq.ntile;   // 0 when the attention kernel quantizes Q itself
   // K codes in 64-row tiles (K blocks are 64 rows or one row): half the
   // registers of a 128-row tile, so twice the waves in flight
   Int8Job jk = P.jk;
   jk.ntile = P.jk.ntile * (kQTile / 64);
   const dim3 grid_k(BH * jk.ntile, 1);
-  if (d == 128) prep_int8_phase1_kernel<128><<<n_ksum + n_q, 256, 0, s>>>(P, N, n_ksum, n_q);
-  else prep_int8_phase1_kernel<64><<<n_ksum + n_q, 256, 0, s>>>(P, N, n_ksum, n_q);
+  if (n_ksum + n_q > 0) {
+    if (d == 128) prep_int8_phase1_kernel<128><<<n_ksum + n_q, 256, 0, s>>>(P, N, n_ksum, n_q);
+    else prep_int8_phase1_kernel<64><<<n_ksum + n_q, 256, 0, s>>>(P, N, n_ksum, n_q);
+  }
   if (P.smooth) {
     if (d == 128) kmean_kernel<128><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
     else kmean_kernel<64><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);

@@ -44,6 +44,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uns
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
 }
 
+// INT8 codes of a per-block quantization (shared by the quantization kernels
+// and the attention kernel's in-kernel Q quantization).
+// Codes. fp32(x / s) is formed without a division per element: with
+// y = fp32(1 / s) (one IEEE division per scale) and q0 = fp32(x * y), the
+// remainder x - q0 * s is exact in one fma and q0 + r * y rounded once is the
+// correctly rounded quotient (Markstein's correction step; its preconditions
+// hold here: y is the rounded reciprocal of s, q0 is within one ulp, the
+// quotient is at most 127 in magnitude, and with s >= 2^-60 every x whose
+// code can be nonzero is far above the subnormal range, so the remainder is
+// exact). Smaller scales take the plain division; s = 0 means an all-zero
+// block and zero codes.
+// The result is returned as the bits of t = fp32(q + 1.5 * 2^23), which rounds
+// q to the nearest integer, ties to even (the sum lies in [2^23, 2^24), whose
+// ulp is 1, and 1.5 * 2^23 is even): the low byte of t is that integer as a
+// two's complement int8. |q| <= 127 needs no clamp: q = x / s with |x| <= a and
+// s = fp32(a / 127), so |q| <= 127 * (1 + 2^-24).
+constexpr float kMarksteinMinScale = 0x1p-60f;
+constexpr float kRound = 12582912.0f;
+
+// s >= kMarksteinMinScale, y = fp32(1 / s)
+__device__ __forceinline__ unsigned int8_code_bits(float x, float s, float y) {
+  const float q0 = x * y;
+  const float r = __builtin_fmaf(-q0, s, x);
+  return __float_as_uint(__builtin_fmaf(r, y, q0) + kRound);
+}
+// any s >= 0 (the slow path for tiny scales; s = 0 gives code 0)
+__device__ __forceinline__ unsigned int8_code_bits_div(float x, float s) {
+  return __float_as_uint((s > 0.f ? x / s : 0.f) + kRound);
+}
+
+// Low bytes of w[0..3] -> one word, byte i = low byte of w[i].
+__device__ __forceinline__ unsigned pack_low_bytes(unsigned w0, unsigned w1, unsigned w2, unsigned w3) {
+  return __builtin_amdgcn_perm(__builtin_amdgcn_perm(w3, w2, 0x04000c0cu),
+                               __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u), 0x07060100u);
+}
+
 // Tokens per partial-sum chunk of the K column sum: at least 256 and large
 // enough that no head has more than 64 chunks.
 inline int ksum_chunk(int N) {
@@ -204,9 +240,11 @@ struct AttnArgs {
   int mode = 0;     // SAGE_MODE_* (no flags)
   void* out = nullptr;
   float* lse = nullptr;  // fp32 [BH, N] row log-sum-exp (natural log), fp16-P modes only; may be null
+  bool qin = false;      // per-block INT8 modes: q is the caller's fp16 Q, quantized in the kernel's prologue
 };
 // q, k: INT8 codes (padded to Npad rows) with scales qs, ks; or, for
-// SAGE_MODE_FP16, the caller's fp16 Q and K [BH, N, d] (qs, ks unused).
+// SAGE_MODE_FP16, the caller's fp16 Q and K [BH, N, d] (qs, ks unused); with
+// a.qin (modes 0 and 1), q is the caller's fp16 Q [BH, N, d] and qs unused.
 // v: the caller's fp16 V [BH, N, d], or for the INT8 P.V modes int8 V^T codes
 // [BH, d, Npad] with per-channel scales vs [BH, d] (unused otherwise).
 hipError_t launch_attn_int8(const AttnArgs& a, const void* q, const void* k, const void* v,

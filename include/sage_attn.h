@@ -78,6 +78,8 @@ typedef enum sage_status {
 /* Flags OR-ed into `mode` (or passed as `flags`). */
 #define SAGE_FLAG_NO_SMOOTH 0x100  /* skip the K mean subtraction (ablation only) */
 #define SAGE_FLAG_FP8_V 0x200      /* sage_quant_mxfp4 only: V in MX-FP8 (E4M3) codes */
+#define SAGE_FLAG_FUSED_Q 0x400    /* modes 0 and 1: Q quantized inside the attention kernel (see
+                                      sage_attn_prepare / sage_attn_compute) */
 
 /* Human-readable name of a status code; never NULL. */
 const char* sage_status_string(int status);
@@ -96,7 +98,10 @@ size_t sage_attn_workspace_size(int B, int H, int N, int d, int mode);
  * Full forward pass: out = attention(q, k, v) computed by the quantized
  * method of `mode` (SageAttention page, "Approach"; SageAttention3 abstract
  * for SAGE_MODE_MXFP4). Equivalent to sage_attn_prepare followed by
- * sage_attn_compute on the same stream and workspace.
+ * sage_attn_compute on the same stream and workspace. In modes 0 and 1 with
+ * at least 65536 token rows (B * H * N) both phases run with
+ * SAGE_FLAG_FUSED_Q (whatever `mode` says about that flag): the attention
+ * kernel quantizes Q itself, to the same codes and scales.
  *   q, k, v  fp16 [B, H, N, d] device, read only.
  *   out      fp16 [B, H, N, d] device, written (may not alias q, k, v).
  *   causal   0: no mask; 1: key j is hidden from query i when j > i.
@@ -195,7 +200,11 @@ int sage_attn_bwd(const void* q, const void* k, const void* v, const void* out, 
  * Q, K (and of V, in the modes that quantize it: MXFP4, MX-FP8 or INT8 codes)
  * into `workspace`. The steps are those of sage_quant_qk / sage_quant_mxfp4 /
  * sage_quant_v_int8; the workspace layout is private. SAGE_MODE_FP16 has
- * nothing to prepare (the call only validates its arguments).
+ * nothing to prepare (the call only validates its arguments). With
+ * SAGE_FLAG_FUSED_Q (modes 0 and 1 only; other modes return
+ * SAGE_ERR_UNSUPPORTED) Q is left out: sage_attn_compute with that flag
+ * quantizes it in the attention kernel's prologue (block maxima, scales and
+ * codes as sage_quant_qk defines them).
  */
 int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H, int N, int d,
                       int mode, void* workspace, size_t workspace_bytes, void* stream);
@@ -206,8 +215,8 @@ int sage_attn_prepare(const void* q, const void* k, const void* v, int B, int H,
  * previous sage_attn_prepare with the same B, H, N, d and mode left in
  * `workspace`, writing fp16 `out` [B, H, N, d]. Arguments as for sage_attn_fwd.
  *   q, k  the fp16 tensors given to sage_attn_prepare. Only SAGE_MODE_FP16
- *         reads them here (the quantized modes read their codes from the
- *         workspace and accept NULL).
+ *         reads them here, and q also with SAGE_FLAG_FUSED_Q (the quantized
+ *         modes read their codes from the workspace and accept NULL).
  *   v     the fp16 V given to sage_attn_prepare, read here by every mode whose
  *         P.V runs in fp16 (all but SAGE_MODE_MXFP4, SAGE_MODE_MXFP4_FP8PV and
  *         the INT8 P.V modes, which read V codes from the workspace and
@@ -220,7 +229,8 @@ int sage_attn_compute(const void* q, const void* k, const void* v, void* out, in
 /*
  * Test hook for the integer scores of the INT8 modes (SageAttention page,
  * "Approach": QK^T of the INT8 codes with integer accumulation). Runs the
- * attention kernel of `mode` (0, 1 or 3; non-causal) on a workspace prepared by
+ * attention kernel of `mode` (0, 1 or 3; non-causal; SAGE_FLAG_FUSED_Q is
+ * refused, the hook reads the Q codes) on a workspace prepared by
  * sage_attn_prepare for the same B, H, N, d and mode, writing `out` as
  * sage_attn_compute does (reading fp16 `v`, the V given to sage_attn_prepare),
  * and copies the int32 scores q_codes . k_codes^T that

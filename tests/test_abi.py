@@ -221,3 +221,18 @@ def test_trainable_attention_refuses_host_tensors():
         sa.sage_attention(q, q.detach(), q.detach())
     with pytest.raises(ValueError):
         sa.sage_attention(torch.zeros(2, 64, 64, dtype=torch.float16), q, q)
+
+
+def test_fused_q_flag_validation():
+    # SAGE_FLAG_FUSED_Q goes with the per-block INT8 modes only, and the score
+    # dump (which reads the workspace Q codes) refuses it
+    F = sa.SAGE_FLAG_FUSED_Q
+    fwd = lambda mode: lib.sage_attn_fwd(A16, A16, A16, A16, 1, 2, 256, 64, 0, 0.125, mode, A16, 1 << 30, None)
+    for bad in (2, 3, 4, 5, 6, 7):
+        assert fwd(bad | F) == UNSUP
+    assert lib.sage_attn_prepare(A16, A16, A16, 1, 2, 256, 64, 3 | F, A16, 1 << 30, None) == UNSUP
+    assert lib.sage_attn_compute(None, A16, A16, A16, 1, 2, 256, 64, 0, 0.125, 0 | F, A16, 1 << 30, None) == INVALID
+    ws0 = sa.sage_attn_workspace_size(1, 2, 256, 64, 0)
+    assert lib.sage_attn_dump_scores(A16, A16, 1, 2, 256, 64, 0.1, 0 | F, A16, ws0, 1, 0, 3, A16, None) == UNSUP
+    if not _gpu_visible():
+        assert fwd(0 | F) == NODEV and fwd(1 | F | sa.SAGE_FLAG_NO_SMOOTH) == NODEV

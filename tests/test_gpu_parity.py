@@ -478,3 +478,53 @@ def test_configuration_and_zero_block_edge_cases(sa, case):
     ex = O.exact_attention(q, k, v, causal=causal, sm_scale=sm)
     say(f"  max err vs oracle {err:.2e}; cos vs fp64 gpu {O.metrics(got, ex)['cos']:.6f} "
         f"oracle {O.metrics(ref, ex)['cos']:.6f}")
+
+
+FUSED_CASES = [
+    # B, H, N, d, causal, mode (SAGE_FLAG_FUSED_Q added)
+    (1, 2, 700, 128, True, 0),
+    (2, 1, 333, 64, False, 1),
+    (1, 3, 256, 128, False, 0x100),
+    (1, 1, 1, 64, True, 0x101),
+    (1, 2, 130, 64, True, 0),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "x".join(map(str, c[:4])) + f"-c{int(c[4])}-m{c[5]:#x}")
+def test_fused_q_quantization_is_bit_identical(sa, case):
+    """SAGE_FLAG_FUSED_Q: the attention kernel quantizes Q in its prologue (the
+    prepare phase skips Q) and must reach the very codes and scales of the
+    quantization kernel, so its output equals the two-phase result with Q codes
+    from the workspace bit for bit; the oracle bar holds as well."""
+    B, H, N, d, causal, mode = case
+    say("fused Q", case)
+    q, k, v = make_custom(B, H, N, d, seed=77 + N + d, dist="student_t" if N == 333 else "normal")
+    qd, kd, vd = _dev(q, k, v)
+    sm = 1.0 / np.sqrt(d)
+    fused = mode | sa.SAGE_FLAG_FUSED_Q
+    ws_a, ws_b = sa.make_workspace(B, H, N, d, mode), sa.make_workspace(B, H, N, d, fused)
+    a, b = torch.empty_like(qd), torch.empty_like(qd)
+    sa.sage_attn_prepare(qd, kd, vd, ws_a, mode=mode)
+    sa.sage_attn_compute(a, ws_a, causal=causal, sm_scale=sm, mode=mode, q=qd, k=kd, v=vd)
+    sa.sage_attn_prepare(qd, kd, vd, ws_b, mode=fused)
+    sa.sage_attn_compute(b, ws_b, causal=causal, sm_scale=sm, mode=fused, q=qd, k=kd, v=vd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    bq, bk = _int8_blocks(mode & 0xFF)
+    ref = O.int8_attention(q, k, v, causal=causal, sm_scale=sm, blk_q=bq, blk_k=bk, smooth=not (mode & 0x100))
+    assert_output_parity(b.cpu().numpy(), ref, what=f"fused Q {case}")
+
+
+def test_fwd_fuses_q_on_large_problems(sa):
+    """sage_attn_fwd takes the fused pass from 65536 token rows on: its output
+    equals the two-phase result with workspace Q codes bit for bit."""
+    B, H, N, d = 1, 16, 4096, 64
+    q, k, v = make_custom(B, H, N, d, seed=78)
+    qd, kd, vd = _dev(q, k, v)
+    out = sa.sage_attn_fwd(qd, kd, vd, causal=True)
+    ws = sa.make_workspace(B, H, N, d, 0)
+    c = torch.empty_like(qd)
+    sa.sage_attn_prepare(qd, kd, vd, ws, mode=0)
+    sa.sage_attn_compute(c, ws, causal=True, mode=0, q=qd, k=kd, v=vd)
+    torch.cuda.synchronize()
+    assert torch.equal(out, c)

@@ -919,31 +919,38 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
     }
     SAGE_END_BARRIER(nvm);   // nvm = this wave's K(1) + V(0) instructions
     if (QIN && qin) {
-      // the Q block of this wave: qblk / 32 consecutive waves (qblk 128 or 64)
-      const int nw = qblk / 32, b0 = (wave / nw) * nw;
-      float a = qmax_w[b0];
-      for (int i = 1; i < nw; ++i) a = fmaxf(a, qmax_w[b0 + i]);
+      // the Q block of this wave: qblk / 32 consecutive waves (qblk is 128 or 64)
+      const int nw = qblk >> 5, b0 = wave & -nw;
+      float a = fmaxf(qmax_w[b0], qmax_w[b0 + 1]);
+      if (nw == 4) a = fmaxf(a, fmaxf(qmax_w[b0 + 2], qmax_w[b0 + 3]));
+      // every lane read the same words: a scalar, so that the choice of the
+      // quotient below is one branch for the wave, not one per element
+      a = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a)));
       const float sb = a / 127.0f;
-      const bool mk = sb >= kMarksteinMinScale;
-      const float y = mk ? 1.0f / sb : 0.f;
+      const auto codes = [&](auto code) {
 #pragma unroll
-      for (int c = 0; c < NQF; ++c) {
-        unsigned w[16];
+        for (int c = 0; c < NQF; ++c) {
+          unsigned w[16];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const unsigned w4[4] = {qraw[2 * c + h].x, qraw[2 * c + h].y, qraw[2 * c + h].z, qraw[2 * c + h].w};
+          for (int h = 0; h < 2; ++h) {
+            const unsigned w4[4] = {qraw[2 * c + h].x, qraw[2 * c + h].y, qraw[2 * c + h].z, qraw[2 * c + h].w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w4[j] & 0xffffu)));
-            const float x1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w4[j] >> 16)));
-            w[h * 8 + 2 * j] = mk ? int8_code_bits(x0, sb, y) : int8_code_bits_div(x0, sb);
-            w[h * 8 + 2 * j + 1] = mk ? int8_code_bits(x1, sb, y) : int8_code_bits_div(x1, sb);
+            for (int j = 0; j < 4; ++j) {
+              w[h * 8 + 2 * j] = code(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w4[j] & 0xffffu)));
+              w[h * 8 + 2 * j + 1] = code(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w4[j] >> 16)));
+            }
           }
+          qf[c] = v4i{static_cast<int>(pack_low_bytes(w[0], w[1], w[2], w[3])),
+                      static_cast<int>(pack_low_bytes(w[4], w[5], w[6], w[7])),
+                      static_cast<int>(pack_low_bytes(w[8], w[9], w[10], w[11])),
+                      static_cast<int>(pack_low_bytes(w[12], w[13], w[14], w[15]))};
         }
-        qf[c] = v4i{static_cast<int>(pack_low_bytes(w[0], w[1], w[2], w[3])),
-                    static_cast<int>(pack_low_bytes(w[4], w[5], w[6], w[7])),
-                    static_cast<int>(pack_low_bytes(w[8], w[9], w[10], w[11])),
-                    static_cast<int>(pack_low_bytes(w[12], w[13], w[14], w[15]))};
+      };
+      if (sb >= kMarksteinMinScale) {
+        const float y = 1.0f / sb;
+        codes([&](_Float16 x) { return int8_code_bits_h(x, sb, y); });
+      } else {
+        codes([&](_Float16 x) { return int8_code_bits_div(static_cast<float>(x), sb); });
       }
       sq = sb;
     }

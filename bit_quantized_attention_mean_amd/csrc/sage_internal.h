@@ -69,6 +69,17 @@ __device__ __forceinline__ unsigned int8_code_bits(float x, float s, float y) {
   const float r = __builtin_fmaf(-q0, s, x);
   return __float_as_uint(__builtin_fmaf(r, y, q0) + kRound);
 }
+// The same code for an fp16 x, with the widening folded into the two
+// operations that read x (v_fma_mix_f32 takes an fp16 operand): q0 =
+// fma(x, y, +0) is the rounded product x * y, except that a -0 product
+// becomes +0 (only x = -0 gives one: |x * y| >= 2^-24 * 127 / 65504 otherwise),
+// and for x = +-0 both forms end at t = 1.5 * 2^23. The bits equal
+// int8_code_bits(float(x), s, y).
+__device__ __forceinline__ unsigned int8_code_bits_h(_Float16 x, float s, float y) {
+  const float q0 = __builtin_fmaf(static_cast<float>(x), y, 0.0f);
+  const float r = __builtin_fmaf(-q0, s, static_cast<float>(x));
+  return __float_as_uint(__builtin_fmaf(r, y, q0) + kRound);
+}
 // any s >= 0 (the slow path for tiny scales; s = 0 gives code 0)
 __device__ __forceinline__ unsigned int8_code_bits_div(float x, float s) {
   return __float_as_uint((s > 0.f ? x / s : 0.f) + kRound);

@@ -26,6 +26,7 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr int kMaxN = 1 << 22;
+static_assert(sage::ksum_rows_per_thread(kMaxN) <= 8192, "K column sums: fp64 running sums must stay exact");
 // INT8 P.V: the int32 P.V sums are at most 127 * 127 * N and must stay below 2^31.
 constexpr int kMaxNPv8 = 1 << 17;
 

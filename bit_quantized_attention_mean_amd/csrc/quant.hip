@@ -18,13 +18,14 @@ namespace sage {
 // multiple of 2^-24, so K * 2^24 is an integer below 2^41 and sums exactly in
 // int64. mu = fp32(fp64(sum) * 2^-24 / N): one correctly rounded fp64
 // division and one RNE conversion, identical however the sum was split.
+// A thread first adds its own tokens in fp64: a sum of n such values is a
+// multiple of 2^-24 below n * 2^16, exactly representable (53-bit
+// significand) while n <= 8192, so every one of those additions is exact and
+// the thread's sum, times 2^24, converts to the same int64 as the integer
+// sum; n <= ksum_rows_per_thread(N) <= 4096 for every accepted N. Three VALU
+// instructions per element (two widenings and the fp64 add) instead of an
+// integer decode with a variable 64-bit shift.
 // ---------------------------------------------------------------------------
-
-__device__ __forceinline__ long long f16_to_fixed24(unsigned h) {
-  const unsigned e = (h >> 10) & 31u, m = h & 1023u;
-  const long long mag = e ? (static_cast<long long>(m | 1024u) << (e - 1)) : static_cast<long long>(m);
-  return (h & 0x8000u) ? -mag : mag;
-}
 
 // One 256-thread block of the column sums: chunk `bid` (head bid / nchunk).
 template <int D>
@@ -36,18 +37,18 @@ __device__ __forceinline__ void ksum_partial_block(const uint16_t* __restrict__ 
   const int tid = threadIdx.x, cg = tid % TPR;
   const int n0 = ci * chunk, n1 = min(N, n0 + chunk);
   const uint16_t* src = k + static_cast<size_t>(bh) * N * D + cg * 8;
-  long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int n = n0 + tid / TPR; n < n1; n += RPP) {
     const uint4 raw = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(n) * D);
     const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += f16_to_fixed24(w[j] & 0xffffu);
-      acc[2 * j + 1] += f16_to_fixed24(w[j] >> 16);
+      acc[2 * j] += static_cast<double>(static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j] & 0xffffu))));
+      acc[2 * j + 1] += static_cast<double>(static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j] >> 16))));
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) red[tid][j] = acc[j];
+  for (int j = 0; j < 8; ++j) red[tid][j] = static_cast<long long>(acc[j] * 0x1p24);
   __syncthreads();
   if (tid < D) {
     const int g = tid / 8, j = tid % 8;

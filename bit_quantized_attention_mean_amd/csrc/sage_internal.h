@@ -26,7 +26,7 @@ constexpr int kWGQ = 256;
 constexpr int kKTile = 64;
 constexpr int kRowPad = 256;
 
-inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS reads and
 // writes, then s_barrier. Unlike __syncthreads() it does not wait for
@@ -93,10 +93,13 @@ __device__ __forceinline__ unsigned pack_low_bytes(unsigned w0, unsigned w1, uns
 
 // Tokens per partial-sum chunk of the K column sum: at least 256 and large
 // enough that no head has more than 64 chunks.
-inline int ksum_chunk(int N) {
-  int c = round_up((N + 63) / 64, 64);
-  return c < 256 ? 256 : c;
+constexpr int ksum_chunk(int N) {
+  return round_up((N + 63) / 64, 64) < 256 ? 256 : round_up((N + 63) / 64, 64);
 }
+// Most tokens one thread of the column-sum block adds up (16 threads per token
+// row at d = 128, so 16 rows per pass; 32 at d = 64): the exactness of its
+// fp64 running sums needs at most 8192.
+constexpr int ksum_rows_per_thread(int N) { return ksum_chunk(N) / 16; }
 
 // Byte offsets of the regions of a workspace. All offsets are 256-aligned.
 struct Layout {

@@ -35,6 +35,8 @@
  *     calls are re-entrant; calls that share a workspace (or, for the
  *     allocation-free entry point, a GPU) must be stream-ordered.
  *   - Supported head dims d: 64 and 128. 1 <= N <= 4194304. B, H >= 1.
+ *   - q, k, v (and dout) hold finite fp16 values; outputs for inputs with inf
+ *     or NaN are unspecified (no fault, no error code).
  *   - Every argument check happens before the first HIP call, so every error
  *     except SAGE_ERR_HIP and SAGE_ERR_NO_DEVICE is reported on a host with no
  *     GPU. Errors return a negative sage_status_t and set sage_last_error();

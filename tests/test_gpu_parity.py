@@ -66,6 +66,24 @@ def test_int8_quant_bitexact(sa, case):
         assert np.array_equal(got["k_mean"].cpu().numpy().view(np.uint32), ref["k_mean"].view(np.uint32))
 
 
+@pytest.mark.parametrize("N,d", [(300000, 128), (70001, 64)])
+def test_k_mean_exact_over_the_fp16_range(sa, N, d):
+    """The K mean is the exact rational mean rounded once (reading R1), whatever
+    the values: K is drawn uniformly over all finite fp16 bit patterns
+    (subnormals up to +-65504), with enough tokens that each thread of the
+    column-sum blocks adds a few hundred of them."""
+    say("k mean fp16 range", (1, 2, N, d))
+    rng = np.random.default_rng(N + d)
+    bits = rng.integers(0, 0x7C00, size=(1, 2, N, d), dtype=np.uint16)
+    bits |= rng.integers(0, 2, size=bits.shape, dtype=np.uint16) << 15
+    k = bits.view(np.float16)
+    want = O.k_mean(k)
+    kd, = _dev(k)
+    got = sa.sage_quant_qk(kd, kd, blk_q=128, blk_k=64)
+    torch.cuda.synchronize()
+    assert np.array_equal(got["k_mean"].cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
 MX_CASES = [(1, 2, 256, 64, 0), (2, 2, 1000, 128, 0), (1, 1, 33, 128, 0), (1, 2, 96, 64, 0x100),
             (1, 2, 300, 128, 0x200), (1, 1, 33, 64, 0x300)]   # 0x200: V in MX-FP8 (E4M3)
 

@@ -41,6 +41,24 @@ def test_noalloc_equals_fwd_on_two_calls_in_a_row(sa, mode, causal, d):
         assert torch.equal(o, w)
 
 
+@pytest.mark.parametrize("mode,causal,d", [(0, False, 128), (1, True, 64)])
+def test_noalloc_equals_fwd_across_the_fused_q_threshold(sa, mode, causal, d):
+    """From 65536 token rows on, both entry points quantize Q inside the attention
+    kernel; the first call here is above that threshold, the second below it."""
+    say("no-alloc entry point across the fused-Q threshold, mode", mode, "causal", causal, "d", d)
+    shapes = [(1, 16, 4200), (2, 3, 1500)]      # 67200 token rows, then 9000
+    inputs = [_dev(*make_custom(B, H, N, d, seed=B * N + d + mode)) for (B, H, N) in shapes]
+    want = [sa.sage_attn_fwd(q, k, v, causal=causal, mode=mode) for (q, k, v) in inputs]
+    outs = [torch.full_like(q, float("nan")) for (q, _, _) in inputs]
+    torch.cuda.synchronize()
+    for (q, k, v), o in zip(inputs, outs):
+        sa.sage_attn_fwd_noalloc(q, k, v, o, causal=causal, mode=mode)
+    torch.cuda.synchronize()
+    for w, o in zip(want, outs):
+        assert torch.isfinite(o).all()
+        assert torch.equal(o, w)
+
+
 def test_noalloc_allocates_no_device_memory(sa):
     say("no-alloc entry point: device memory")
     q, k, v = _dev(*make_custom(1, 4, 2048, 128, seed=3))

@@ -93,15 +93,29 @@ __global__ __launch_bounds__(256, (D == 64 && PV8) ? 3 : 2) void attn_mxfp4_kern
   constexpr int NC = D / 64;         // 64-channel steps of the score contraction
   constexpr int NE = D / 32;         // exponent bytes per Q / K row
   constexpr int NT = D / 32;         // 32-row tiles of O^T
-  constexpr int KROW = D / 2 + 16;   // LDS bytes per K row
+  // The K and V^T rows are unpadded and their 16-byte chunks are permuted
+  // within the row (XOR swizzle), so that the 16 lanes of one LDS access
+  // phase hit distinct banks both when a tile is stored (lanes write whole
+  // rows) and when the matrix ops read it (lanes read one chunk of 16
+  // consecutive rows). At d = 64 a K row is 32 bytes and the rows one store
+  // phase writes (keys 8q .. 8q+7) would share bank slots, so K rows are
+  // also placed in a permuted slot order within each group of 16. The MX-FP8
+  // P.V instance at d = 64 keeps padded rows instead: the swizzle's address
+  // registers would not fit its 168 (three workgroups per CU).
+  constexpr bool SWZ = !(PV8 && D == 64);
+  constexpr int KROW = SWZ ? D / 2 : D / 2 + 16;   // LDS bytes per K row
   constexpr int VTB = PV8 ? 64 : 32;  // bytes of one V^T row per key tile (64 keys)
-  constexpr int VROW = VTB + 16;      // LDS bytes per V^T row
+  constexpr int VROW = SWZ ? VTB : VTB + 16;       // LDS bytes per V^T row
   constexpr int KT_BYTES = kKTile * KROW;
   constexpr int KS_BYTES = kKTile * 8;  // per K row: its exponent word, and the word >> 8
   constexpr int VT_BYTES = D * VROW;
   constexpr int VS_BYTES = D * 8;       // per V^T row: likewise
   constexpr int BUF = KT_BYTES + KS_BYTES + VT_BYTES + VS_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+  // LDS slot of K row p, and the position of data chunk c of K row p / V^T row r
+  const auto kslot = [](int p) { return (SWZ && D == 64) ? p ^ (((p >> 3) & 1) << 2) : p; };
+  const auto kpos = [](int p, int c) { return !SWZ ? c : D == 128 ? (c ^ ((p >> 2) & 3)) : (c ^ ((p >> 3) & 1)); };
+  const auto vpos = [](int r, int c) { return !SWZ ? c : PV8 ? (c ^ ((r >> 2) & 3)) : (c ^ ((r >> 3) & 1)); };
 
   const int nqt = Npad / kQTile;
   int bh, qt;
@@ -184,8 +198,8 @@ __global__ __launch_bounds__(256, (D == 64 && PV8) ? 3 : 2) void attn_mxfp4_kern
     unsigned char* vl_ = ks_ + KS_BYTES;                                                             \
     unsigned char* vs_ = vl_ + VT_BYTES;                                                             \
     if (tid < KCHUNKS) {                                                                             \
-      const int row_ = tid / (D / 32), col_ = tid % (D / 32);                                        \
-      *reinterpret_cast<uint4*>(kt_ + lds_row_of_key4(row_) * KROW + col_ * 16) =                    \
+      const int row_ = lds_row_of_key4(tid / (D / 32)), col_ = tid % (D / 32);                       \
+      *reinterpret_cast<uint4*>(kt_ + kslot(row_) * KROW + kpos(row_, col_) * 16) =                  \
           make_uint4(kr[S_][0], kr[S_][1], kr[S_][2], kr[S_][3]);                                    \
     }                                                                                                \
     if (tid < kKTile) *reinterpret_cast<uint2*>(ks_ + lds_row_of_key4(tid) * 8) = make_uint2(ksr[S_], ksr[S_] >> 8); \
@@ -193,7 +207,7 @@ __global__ __launch_bounds__(256, (D == 64 && PV8) ? 3 : 2) void attn_mxfp4_kern
       const int i_ = tid + 256 * u_;                                                                 \
       if (i_ < VCHUNKS) {                                                                            \
         const int row_ = i_ / VCPR, col_ = i_ % VCPR;                                                \
-        *reinterpret_cast<uint4*>(vl_ + row_ * VROW + col_ * 16) =                                   \
+        *reinterpret_cast<uint4*>(vl_ + row_ * VROW + vpos(row_, col_) * 16) =                       \
             make_uint4(vr[S_][4 * u_], vr[S_][4 * u_ + 1], vr[S_][4 * u_ + 2], vr[S_][4 * u_ + 3]);  \
       }                                                                                              \
     }                                                                                                \
@@ -245,7 +259,7 @@ _Pragma("unroll")                                                               
       const unsigned ksw = *reinterpret_cast<const unsigned*>(ksl + krow * 8 + g * 4);              \
 _Pragma("unroll")                                                                                   \
       for (int c = 0; c < NC; ++c) {                                                                \
-        const v4i a = *reinterpret_cast<const v4i*>(kt + krow * KROW + c * 32 + g * 16);            \
+        const v4i a = *reinterpret_cast<const v4i*>(kt + kslot(krow) * KROW + kpos(krow, c * 2 + g) * 16); \
         /* block c*2+g of the K row and of the Q row: byte 2c of ksw and qsw */                     \
         s[t] = (c == 0) ? mfma_fp4<0>(a, qf[c], ksw, qsw, s[t]) : mfma_fp4<2>(a, qf[c], ksw, qsw, s[t]); \
       }                                                                                             \
@@ -347,14 +361,14 @@ _Pragma("unroll")                                                               
       const unsigned vsw = *reinterpret_cast<const unsigned*>(vsl + vrow * 8 + g * 4);              \
       if (PV8) {                                                                                    \
         /* keys g*16 .. +15 and 32 + g*16 .. +15 of the tile (see the P swap) */                    \
-        const v4i a0 = *reinterpret_cast<const v4i*>(vl + vrow * VROW + g * 16);                    \
-        const v4i a1 = *reinterpret_cast<const v4i*>(vl + vrow * VROW + 32 + g * 16);               \
+        const v4i a0 = *reinterpret_cast<const v4i*>(vl + vrow * VROW + vpos(vrow, g) * 16);        \
+        const v4i a1 = *reinterpret_cast<const v4i*>(vl + vrow * VROW + vpos(vrow, 2 + g) * 16);    \
         const v8i a8 = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};                    \
         o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, pq, o[dt], 0, 0, 0,            \
                                                                 static_cast<int>(vsw), 0,           \
                                                                 static_cast<int>(pe8));             \
       } else {                                                                                      \
-        const v4i a = *reinterpret_cast<const v4i*>(vl + vrow * VROW + g * 16);                     \
+        const v4i a = *reinterpret_cast<const v4i*>(vl + vrow * VROW + vpos(vrow, g) * 16);         \
         o[dt] = mfma_fp4<0>(a, v4i{pq[0], pq[1], pq[2], pq[3]}, vsw, pe8, o[dt]);                   \
       }                                                                                             \
     }                                                                                               \

@@ -245,9 +245,14 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   // the codes are the ones sage_quant_qk writes. Its fp16 loads are issued
   // before, and its arithmetic after, the first tile loads.
   constexpr bool QIN = DMA && SM == kScoresInt8Block && !DUMP;
-  // K in LDS: 64 key rows of d codes (fp16: 2d bytes), +16 bytes of padding
-  // per row without DMA.
-  constexpr int KROW = DMA ? D * EB : D * EB + 16;   // LDS bytes per K row
+  // K in LDS: 64 key rows of d codes (fp16: 2d bytes). K rows are unpadded with XOR-swizzled chunks (below) in the LDS-loaded
+  // instances and in the register-staged per-token ones at d = 64, where the
+  // padded 80-byte rows left the tile stores 2-way bank-conflicted. Elsewhere
+  // K rows keep 16 bytes of padding: at d = 128 the padded stores conflict on
+  // one 16-byte unit only, and the INT8 P.V instances have no registers left
+  // for the swizzle's per-lane read offsets.
+  constexpr bool KSWZ = DMA || (!F16 && !PV8 && D == 64);
+  constexpr int KROW = KSWZ ? D * EB : D * EB + 16;   // LDS bytes per K row
   // V in LDS: fp16 V as given, 64 key rows of d channels (without DMA +64
   // bytes, so that the 4 rows x 64 bytes of one transposing read fall in
   // distinct banks; with DMA the 64-byte segments are swizzled instead), or
@@ -360,7 +365,8 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   for (int u = 0; u < KPT; ++u) {
     const int i = tid + NTH * u, row = i / (D * EB / 16), col = i % (D * EB / 16);
     kg[u] = row * D * EB + col * 16;
-    kl[u] = lds_row_of_key(row) * KROW + col * 16;
+    const int lr = lds_row_of_key(row);
+    kl[u] = lr * KROW + (KSWZ ? (col ^ ((lr >> KSH) & (KCPR - 1))) : col) * 16;
     krw[u] = row;
   }
   int vg[VPT], vls[VPT];
@@ -466,7 +472,7 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
     v4i ka_[2 * NQF];                                                                            \
     _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
       _Pragma("unroll") for (int c = 0; c < NQF; ++c)                                            \
-        ka_[t * NQF + c] = *reinterpret_cast<const v4i*>((KB_) + (DMA ? kc[c] : ka + c * 32) + t * 32 * KROW); \
+        ka_[t * NQF + c] = *reinterpret_cast<const v4i*>((KB_) + (KSWZ ? kc[c] : ka + c * 32) + t * 32 * KROW); \
     _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                              \
       _Pragma("unroll") for (int i = 0; i < 16; ++i) s[t][i] = 0;                                \
       _Pragma("unroll") for (int c = 0; c < NQF; ++c) {                                          \

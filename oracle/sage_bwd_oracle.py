@@ -13,8 +13,7 @@ SageAttention page's "Experimental setup" says the method builds on
 FlashAttention-2, whose backward pass recomputes the scores from Q and K and
 the softmax probabilities from the forward's saved row log-sum-exp. Nothing
 else is on the pages: no granularity, no choice of products, no precision of
-the gradients. The readings below fill that in (each also listed in
-DESIGN.md).
+the gradients. The readings below fill that in.
 
   Rb1 structure (FlashAttention-2's backward): with S the forward's scaled
       scores and L its row log-sum-exp, P = exp(S - L); dV = P^T dO;

@@ -31,7 +31,7 @@ Citations name the page and its section:
                   Data Formats for Deep Learning" (the MX format) and "Online
                   normalizer calculation for softmax".
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   R1 K mean: exact int64 sum of K * 2^24 over tokens (every fp16 is a multiple
      of 2^-24), then mu = fp32(fp64(sum) * 2^-24 / N). Order-independent.
   R2 smoothing: K_s = fp32(fp32(K) - mu), one RNE subtraction, not re-rounded

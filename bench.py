@@ -294,7 +294,9 @@ def sweep(torch, sa, steps):
     (mode 4), the MXFP4 kernel (mode 2) and torch's FP16 SDPA on the same inputs.
     Inputs are the prefill recipe without outlier channels (N(0, 1), K offset
     N(0, 3^2)). One JSON line per point, the attention kernel alone (HIP events
-    on its stream, after a warm-up), its TOPS against the INT8 peak."""
+    on its stream, after a warm-up), its TOPS against the INT8 peak. The INT8
+    kernel runs as sage_attn_fwd runs it: every point has B*H*N >= 65536 token
+    rows, so it quantizes Q in its prologue (SAGE_FLAG_FUSED_Q)."""
     import torch.nn.functional as F
     from synthetic import make_custom
     rows = []
@@ -309,8 +311,9 @@ def sweep(torch, sa, steps):
                 ops = 4.0 * B * H * N * N * d / (2.0 if causal else 1.0)
                 rec = {"sweep": "attention kernel TOPS", "B": B, "H": H, "N": N, "d": d, "causal": causal}
                 out = torch.empty_like(qd)
-                for name, mode in (("int8", 0), ("fp16", 4), ("mxfp4", 2)):
-                    ws = sa.make_workspace(B, H, N, d, mode, qd.device)
+                fq = sa.SAGE_FLAG_FUSED_Q if B * H * N >= 65536 else 0
+                for name, mode in (("int8", 0 | fq), ("fp16", 4), ("mxfp4", 2)):
+                    ws = sa.make_workspace(B, H, N, d, mode & 0xff, qd.device)
                     sa.sage_attn_prepare(qd, kd, vd, ws, mode=mode)
                     comp = lambda: sa.sage_attn_compute(out, ws, causal=causal, sm_scale=sm, mode=mode, q=qd, k=kd, v=vd)
                     ms, _ = timed(comp, steps, steps, torch)

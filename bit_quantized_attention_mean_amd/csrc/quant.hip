@@ -66,21 +66,26 @@ __global__ __launch_bounds__(256) void ksum_partial_kernel(const uint16_t* __res
   ksum_partial_block<D>(k, part, N, chunk, nchunk, blockIdx.x, red);
 }
 
+// mu from the partial sums: one block per (head, 32 channels), so that a
+// head's chunks are added by 8 groups of 32 threads in parallel (a short
+// chain of dependent loads per thread), then the 8 results by one group.
+constexpr int kMeanCh = 32;
 template <int D>
 __global__ __launch_bounds__(256) void kmean_kernel(const long long* __restrict__ part,
                                                     float* __restrict__ mu_ws,
                                                     float* __restrict__ mu_out, int N, int nchunk) {
-  constexpr int G = 256 / D;  // chunk groups reduced in parallel
+  constexpr int G = 256 / kMeanCh;  // chunk groups reduced in parallel
   __shared__ long long red[256];
-  const int bh = blockIdx.x, c = threadIdx.x % D, grp = threadIdx.x / D;
+  const int bh = blockIdx.x / (D / kMeanCh);
+  const int cl = threadIdx.x % kMeanCh, c = (blockIdx.x % (D / kMeanCh)) * kMeanCh + cl, grp = threadIdx.x / kMeanCh;
   long long s = 0;
   for (int i = grp; i < nchunk; i += G) s += part[(static_cast<size_t>(bh) * nchunk + i) * D + c];
   red[threadIdx.x] = s;
   __syncthreads();
-  if (threadIdx.x < D) {
+  if (threadIdx.x < kMeanCh) {
     long long t = 0;
 #pragma unroll
-    for (int g = 0; g < G; ++g) t += red[g * D + c];  // integer: order is irrelevant
+    for (int g = 0; g < G; ++g) t += red[g * kMeanCh + cl];  // integer: order is irrelevant
     const float mu = static_cast<float>((static_cast<double>(t) * 0x1p-24) / static_cast<double>(N));
     mu_ws[static_cast<size_t>(bh) * D + c] = mu;
     if (mu_out) mu_out[static_cast<size_t>(bh) * D + c] = mu;
@@ -92,10 +97,10 @@ hipError_t launch_kmean(const void* k, long long* ksum, float* kmean_ws, float* 
   const auto* kk = static_cast<const uint16_t*>(k);
   if (d == 128) {
     ksum_partial_kernel<128><<<BH * nchunk, 256, 0, s>>>(kk, ksum, N, chunk, nchunk);
-    kmean_kernel<128><<<BH, 256, 0, s>>>(ksum, kmean_ws, kmean_out, N, nchunk);
+    kmean_kernel<128><<<BH * (128 / kMeanCh), 256, 0, s>>>(ksum, kmean_ws, kmean_out, N, nchunk);
   } else {
     ksum_partial_kernel<64><<<BH * nchunk, 256, 0, s>>>(kk, ksum, N, chunk, nchunk);
-    kmean_kernel<64><<<BH, 256, 0, s>>>(ksum, kmean_ws, kmean_out, N, nchunk);
+    kmean_kernel<64><<<BH * (64 / kMeanCh), 256, 0, s>>>(ksum, kmean_ws, kmean_out, N, nchunk);
   }
   return hipGetLastError();
 }
@@ -458,8 +463,8 @@ hipError_t launch_prepare_int8(const PrepInt8& P, int BH, int N, int d, hipStrea
     else prep_int8_phase1_kernel<64><<<n_ksum + n_q, 256, 0, s>>>(P, N, n_ksum, n_q);
   }
   if (P.smooth) {
-    if (d == 128) kmean_kernel<128><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
-    else kmean_kernel<64><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
+    if (d == 128) kmean_kernel<128><<<BH * (128 / kMeanCh), 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
+    else kmean_kernel<64><<<BH * (64 / kMeanCh), 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
   }
   if (d == 128) int8_quant_kernel<128, 64><<<grid_k, 256, 0, s>>>(jk, jk, N);
   else int8_quant_kernel<64, 64><<<grid_k, 256, 0, s>>>(jk, jk, N);
@@ -727,8 +732,8 @@ hipError_t launch_prepare_mx(const PrepMx& P, int N, int d, hipStream_t s) {
   else { if (P.v_fp8) SAGE_PHASE1(64, true); else SAGE_PHASE1(64, false); }
 #undef SAGE_PHASE1
   if (P.smooth) {
-    if (d == 128) kmean_kernel<128><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
-    else kmean_kernel<64><<<BH, 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
+    if (d == 128) kmean_kernel<128><<<BH * (128 / kMeanCh), 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
+    else kmean_kernel<64><<<BH * (64 / kMeanCh), 256, 0, s>>>(P.ksum, P.kmean, nullptr, N, P.nchunk);
   }
   const dim3 grid_k(mx_rows_blocks(P.jk, BH, d), 1);
   if (d == 128) mx_rows_kernel<128><<<grid_k, 256, 0, s>>>(P.jk, P.jk, BH, N);

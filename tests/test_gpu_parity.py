@@ -533,6 +533,41 @@ def test_fused_q_quantization_is_bit_identical(sa, case):
     assert_output_parity(b.cpu().numpy(), ref, what=f"fused Q {case}")
 
 
+@pytest.mark.parametrize("d,mode", [(128, 0), (64, 1)])
+def test_fused_q_special_blocks(sa, d, mode):
+    """The prologue quantization on the Q blocks that take its rare branches: an
+    all-zero block (scale 0, codes 0), a block of fp16 subnormals only (the
+    smallest scales the Markstein quotient sees), and a block mixing +-65504
+    with small values; fused and two-phase results equal bit for bit, and the
+    oracle bar holds."""
+    B, H, N = 1, 2, 600
+    blk = 128 if mode == 0 else 64
+    say("fused Q special blocks", (B, H, N, d, mode))
+    q, k, v = make_custom(B, H, N, d, seed=91 + d)
+    rng = np.random.default_rng(92 + d)
+    q[:, :, 0:blk] = 0
+    sub = rng.integers(1, 1024, size=(B, H, blk, d)).astype(np.float64) * 2.0 ** -24
+    q[:, :, blk:2 * blk] = (sub * rng.choice([-1.0, 1.0], size=sub.shape)).astype(np.float16)
+    big = rng.standard_normal((B, H, blk, d)).astype(np.float16)
+    big[..., ::7] = np.float16(65504.0) * rng.choice([-1, 1], size=big[..., ::7].shape).astype(np.float16)
+    q[:, :, 2 * blk:3 * blk] = big
+    qd, kd, vd = _dev(q, k, v)
+    sm = 1.0 / np.sqrt(d)
+    fused = mode | sa.SAGE_FLAG_FUSED_Q
+    ws_a, ws_b = sa.make_workspace(B, H, N, d, mode), sa.make_workspace(B, H, N, d, fused)
+    a, b = torch.empty_like(qd), torch.empty_like(qd)
+    sa.sage_attn_prepare(qd, kd, vd, ws_a, mode=mode)
+    sa.sage_attn_compute(a, ws_a, causal=False, sm_scale=sm, mode=mode, q=qd, k=kd, v=vd)
+    sa.sage_attn_prepare(qd, kd, vd, ws_b, mode=fused)
+    sa.sage_attn_compute(b, ws_b, causal=False, sm_scale=sm, mode=fused, q=qd, k=kd, v=vd)
+    torch.cuda.synchronize()
+    assert torch.isfinite(b).all()
+    assert torch.equal(a, b)
+    bq, bk = _int8_blocks(mode)
+    ref = O.int8_attention(q, k, v, causal=False, sm_scale=sm, blk_q=bq, blk_k=bk)
+    assert_output_parity(b.cpu().numpy(), ref, what=f"fused Q special blocks d={d} mode={mode}")
+
+
 def test_fwd_fuses_q_on_large_problems(sa):
     """sage_attn_fwd takes the fused pass from 65536 token rows on: its output
     equals the two-phase result with workspace Q codes bit for bit."""

@@ -206,7 +206,10 @@ constexpr int kScoresInt8Block = 0, kScoresInt8Token = 1, kScoresF16 = 2;
 // workgroups per CU at d = 64 and two at d = 128, the waves of different
 // workgroups filling each other's gaps (measured +17 to +25% at d = 64, +1 to
 // +9% at d = 128; the plain INT8 modes at d = 64 measured 0.8% slower that way
-// and keep the ping-pong).
+// and keep the ping-pong). The per-block INT8 P.V instance at d = 64 is only
+// bounded to two per CU: it needs 181 registers, and squeezed into the 168 of
+// three per CU it spilled 16 and ran 3-6% slower. (The bound is a minimum;
+// instances that fit in 168 registers still run three per CU.)
 constexpr bool attn_pingpong(int D, int SM, bool PV8, bool DUMP) {
   return DUMP || SM == kScoresF16 || (SM == kScoresInt8Block && !PV8);
 }
@@ -216,7 +219,7 @@ constexpr bool attn_pingpong(int D, int SM, bool PV8, bool DUMP) {
 // of head dbh into dump (int32 [256, 64], query-major).
 template <int D, bool CAUSAL, int SM, bool PV8, bool DUMP = false>
 __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
-                             attn_pingpong(D, SM, PV8, DUMP) ? 1 : (D == 64 ? 3 : 2)) void attn_int8_kernel(
+                             attn_pingpong(D, SM, PV8, DUMP) ? 1 : (D == 64 && !PV8 ? 3 : 2)) void attn_int8_kernel(
     const void* __restrict__ qsrc, const void* __restrict__ ksrc, const void* __restrict__ vsrc,
     const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vsc,
     _Float16* __restrict__ out, int N, int Npad, int qblk, float sl2, int BH, int* __restrict__ dump = nullptr,

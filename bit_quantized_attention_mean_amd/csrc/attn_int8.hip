@@ -248,12 +248,13 @@ __global__ __launch_bounds__(attn_pingpong(D, SM, PV8, DUMP) ? 512 : 256,
   // the codes are the ones sage_quant_qk writes. Its fp16 loads are issued
   // before, and its arithmetic after, the first tile loads.
   constexpr bool QIN = DMA && SM == kScoresInt8Block && !DUMP;
-  // K in LDS: 64 key rows of d codes (fp16: 2d bytes). K rows are unpadded with XOR-swizzled chunks (below) in the LDS-loaded
-  // instances and in the register-staged per-token ones at d = 64, where the
-  // padded 80-byte rows left the tile stores 2-way bank-conflicted. Elsewhere
-  // K rows keep 16 bytes of padding: at d = 128 the padded stores conflict on
-  // one 16-byte unit only, and the INT8 P.V instances have no registers left
-  // for the swizzle's per-lane read offsets.
+  // K in LDS: 64 key rows of d codes (fp16: 2d bytes). The rows are unpadded
+  // with XOR-swizzled chunks (below) in the LDS-loaded instances and in the
+  // register-staged per-token ones at d = 64, where padded 80-byte rows left
+  // the tile stores 2-way bank-conflicted. Elsewhere K rows keep 16 bytes of
+  // padding: at d = 128 the padded stores conflict on one 16-byte unit only,
+  // and the INT8 P.V instances have no registers left for the swizzle's
+  // per-lane read offsets.
   constexpr bool KSWZ = DMA || (!F16 && !PV8 && D == 64);
   constexpr int KROW = KSWZ ? D * EB : D * EB + 16;   // LDS bytes per K row
   // V in LDS: fp16 V as given, 64 key rows of d channels (without DMA +64

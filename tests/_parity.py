@@ -6,7 +6,8 @@ import numpy as np
 OUT_ATOL = 2e-3   # max-abs bar against the quantization-emulating oracle (unit-variance inputs)
 
 # One record per output comparison of this session: (what, elements compared, max
-# error, elements excused by the flip allowance, largest excess over the bar).
+# error, elements excused by the flip allowance, largest excess over the bar, the
+# unit of that excess, largest ratio of an element's error to its own bound).
 # tests/conftest.py prints them at the end of the run, whatever pytest captured.
 RECORDS = []
 
@@ -41,8 +42,9 @@ def assert_output_parity(got: np.ndarray, ref: np.ndarray, atol: float = OUT_ATO
             f"(largest excess over the bar {used:.2e}; allowance capped at {atol:.0e})")
         bound = bound + extra
     bad = err > bound
+    ratio = float(np.max(err / bound)) if err.size else 0.0
     RECORDS.append((what, err.size, float(err.max()) if err.size else 0.0,
-                    n_exc if extra is not None else 0, used if extra is not None else 0.0))
+                    n_exc if extra is not None else 0, used if extra is not None else 0.0, "", ratio))
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} elements over tolerance; worst at {i}: got {got[i]!r} "

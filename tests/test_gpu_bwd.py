@@ -56,7 +56,8 @@ def assert_grad_parity(got, ref, mag, allow, what):
     used = float(np.max((err - bound) / np.maximum(mag, 1e-300), where=excused, initial=0.0))
     say(f"  {what}: {err.size} elements, max err {err.max():.3e} (max|ref| {np.abs(ref).max():.3e}); "
         f"{n_exc} excused by the code-flip allowance (largest excess {used:.2e} of mag)")
-    RECORDS.append((what, err.size, float(err.max()), n_exc, used))
+    RECORDS.append((what, err.size, float(err.max()), n_exc, used, " of mag",
+                    float(np.max(err / (bound + extra)))))
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound - extra), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} elements over tolerance; worst at {i}: got {got[i]!r} "
